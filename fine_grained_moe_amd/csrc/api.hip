@@ -1,0 +1,306 @@
+// C ABI of the MoE layer (declared in include/moe.h): argument checks on the
+// host, workspace layout, and the order of kernel launches on the caller's
+// stream.  Nothing here allocates, synchronises or copies.
+#include <stddef.h>
+#include <stdint.h>
+
+#include <algorithm>
+#include <vector>
+
+#include "kernels.h"
+#include "moe.h"
+
+using namespace fgmoe;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+size_t act_bytes(int act) { return act == MOE_BF16 ? 2 : 4; }
+
+// Workspace regions (byte offsets from the workspace base).
+struct Layout {
+  size_t block_counts, block_base, tile_e, tile_m0, tile_count;
+  size_t H, O, Hs;        // forward intermediates
+  size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
+  size_t total;
+};
+
+moe_status check_dims(const moe_dims* d) {
+  if (!d) return MOE_E_ARG;
+  if (d->T < 0 || d->d < 1 || d->E < 1 || d->F < 1 || d->Fs < 1 || d->k < 1) return MOE_E_ARG;
+  if (d->act != MOE_F32 && d->act != MOE_BF16) return MOE_E_UNSUPPORTED;
+  if (d->w_routed != d->act && d->w_routed != MOE_INT4_G128) return MOE_E_UNSUPPORTED;
+  if (d->E > 64 || d->k > d->E || d->k > 8) return MOE_E_UNSUPPORTED;
+  if (d->d % 128 || d->F % 64 || d->Fs % 64) return MOE_E_UNSUPPORTED;
+  if (d->w_routed == MOE_INT4_G128) return MOE_E_UNSUPPORTED;  // served by the decode path only
+  const long long slots = (long long)d->T * d->k;
+  const long long wide = std::max<long long>(d->d, 2LL * d->F);
+  if (slots * wide >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+  if ((long long)d->T * std::max<long long>(d->d, 2LL * d->Fs) >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+Layout make_layout(const moe_dims& d, int training) {
+  Layout L{};
+  const size_t es = act_bytes(d.act);
+  const size_t nblk = (size_t)route_blocks(d.T);
+  const size_t slots = (size_t)d.T * d.k;
+  const size_t tiles = (size_t)max_group_tiles((long long)slots, d.E);
+  size_t o = 0;
+  auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + std::max<size_t>(bytes, 1)); return at; };
+  L.block_counts = take(nblk * d.E * 4);
+  L.block_base = take(nblk * d.E * 4);
+  L.tile_e = take(tiles * 4);
+  L.tile_m0 = take(tiles * 4);
+  L.tile_count = take(4);
+  L.H = take(slots * d.F * es);
+  L.O = take(slots * d.d * es);
+  L.Hs = take((size_t)d.T * d.Fs * es);
+  if (training) {
+    L.AU = take(slots * 2 * d.F * es);
+    L.Ou = take(slots * d.d * es);
+    L.AUs = take((size_t)d.T * 2 * d.Fs * es);
+  }
+  L.total = o;
+  return L;
+}
+
+struct Range {
+  const void* p;
+  size_t n;
+  bool out;
+};
+
+bool overlaps(const Range& a, const Range& b) {
+  if (!a.p || !b.p || a.n == 0 || b.n == 0) return false;
+  const uintptr_t a0 = (uintptr_t)a.p, a1 = a0 + a.n, b0 = (uintptr_t)b.p, b1 = b0 + b.n;
+  return a0 < b1 && b0 < a1;
+}
+
+// Outputs may overlap nothing; inputs may overlap each other.
+bool any_alias(const std::vector<Range>& rs) {
+  for (size_t i = 0; i < rs.size(); ++i)
+    for (size_t j = i + 1; j < rs.size(); ++j)
+      if ((rs[i].out || rs[j].out) && overlaps(rs[i], rs[j])) return true;
+  return false;
+}
+
+bool null_with_size(const std::vector<Range>& rs) {
+  for (const Range& r : rs)
+    if (!r.p && r.n) return true;
+  return false;
+}
+
+void add_routing_ranges(std::vector<Range>& rs, const moe_dims& d, const moe_routing* r) {
+  const size_t tk = (size_t)d.T * d.k;
+  rs.push_back({r->idx, tk * 4, true});
+  rs.push_back({r->gate, tk * 4, true});
+  rs.push_back({r->counts, (size_t)d.E * 4, true});
+  rs.push_back({r->offsets, (size_t)(d.E + 1) * 4, true});
+  rs.push_back({r->perm, tk * 4, true});
+  rs.push_back({r->pos, tk * 4, true});
+}
+
+template <typename P>
+P* at(void* ws, size_t off) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
+}
+
+// Router + loads + dispatch order; the routing outputs are complete afterwards.
+void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void* w_router, const float* bias,
+                   const moe_routing* r, void* ws, hipStream_t s) {
+  const int nblk = route_blocks(d.T);
+  launch_route_topk(d.act, x, w_router, bias, d.T, d.d, d.E, d.k, r->idx, r->gate, at<int32_t>(ws, L.block_counts), s);
+  launch_route_scan(at<int32_t>(ws, L.block_counts), nblk, d.E, r->counts, r->offsets, at<int32_t>(ws, L.block_base),
+                    at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count), s);
+  launch_route_scatter(r->idx, at<int32_t>(ws, L.block_base), d.T, d.E, d.k, r->perm, r->pos, s);
+}
+
+moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
+
+}  // namespace
+
+extern "C" {
+
+const char* moe_status_str(moe_status s) {
+  switch (s) {
+    case MOE_OK: return "ok";
+    case MOE_E_ARG: return "invalid argument (null pointer or inconsistent size)";
+    case MOE_E_UNSUPPORTED: return "unsupported shape or dtype";
+    case MOE_E_WORKSPACE: return "workspace missing or too small";
+    case MOE_E_ALIAS: return "an output overlaps an input or another output";
+    case MOE_E_DEVICE: return "the HIP runtime rejected a launch";
+  }
+  return "unknown status";
+}
+
+size_t moe_workspace_bytes(const moe_dims* dims, int training) {
+  if (check_dims(dims) != MOE_OK) return 0;
+  return make_layout(*dims, training ? 1 : 0).total;
+}
+
+moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, const float* bias,
+                     const moe_routing* out, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!out) return MOE_E_ARG;
+  const moe_dims& d = *dims;
+  const size_t es = act_bytes(d.act);
+  std::vector<Range> rs = {{x, (size_t)d.T * d.d * es, false},
+                           {w_router, (size_t)d.E * d.d * es, false},
+                           {bias, (size_t)d.E * 4, false}};
+  add_routing_ranges(rs, d, out);
+  if (null_with_size(rs)) return MOE_E_ARG;
+  const Layout L = make_layout(d, 0);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  enqueue_route(d, L, x, w_router, bias, out, ws, s);
+  return device_status();
+}
+
+moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
+                       const moe_routing* routing, int training, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!w || !routing) return MOE_E_ARG;
+  const moe_dims& d = *dims;
+  const size_t es = act_bytes(d.act);
+  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
+  std::vector<Range> rs = {{x, (size_t)d.T * D * es, false},
+                           {w->w_router, E * D * es, false},
+                           {w->w_gate_up, E * 2 * F * D * es, false},
+                           {w->w_down, E * D * F * es, false},
+                           {w->w_sh_gate_up, 2 * Fs * D * es, false},
+                           {w->w_sh_down, D * Fs * es, false},
+                           {bias, E * 4, false},
+                           {y, (size_t)d.T * D * es, true}};
+  add_routing_ranges(rs, d, routing);
+  if (null_with_size(rs)) return MOE_E_ARG;
+  const Layout L = make_layout(d, training ? 1 : 0);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
+  if (d.T == 0) return device_status();
+
+  const long long slots = (long long)d.T * d.k;
+  const int max_tiles = (int)max_group_tiles(slots, d.E);
+  void* H = at<char>(ws, L.H);
+  void* O = at<char>(ws, L.O);
+  void* Hs = at<char>(ws, L.Hs);
+
+  // routed gate/up + SwiGLU: H[slot] = silu(x_t Wg^T) * (x_t Wu^T), x_t gathered by perm
+  GemmArgs g{};
+  g.act = d.act;
+  g.epi = EPI_SWIGLU;
+  g.A = x;
+  g.lda = D;
+  g.a_rows = routing->perm;
+  g.a_div = d.k;
+  g.B = w->w_gate_up;
+  g.ldb = D;
+  g.b_estride = 2LL * F * D;
+  g.K = d.d;
+  g.N = d.F;
+  g.up_off = d.F;
+  g.grouped = 1;
+  g.tile_e = at<int32_t>(ws, L.tile_e);
+  g.tile_m0 = at<int32_t>(ws, L.tile_m0);
+  g.tile_count = at<int32_t>(ws, L.tile_count);
+  g.offsets = routing->offsets;
+  g.counts = routing->counts;
+  g.max_items = max_tiles;
+  g.C = H;
+  g.ldc = F;
+  g.aux = training ? at<char>(ws, L.AU) : nullptr;
+  g.ldaux = 2LL * F;
+  launch_gemm(g, s);
+
+  // routed down, rows scaled by their routing weight: O[slot] = g * (H[slot] Wd^T)
+  GemmArgs dn = g;
+  dn.epi = EPI_ROWSCALE;
+  dn.A = H;
+  dn.lda = F;
+  dn.a_rows = nullptr;
+  dn.a_div = 1;
+  dn.B = w->w_down;
+  dn.ldb = F;
+  dn.b_estride = (long long)D * F;
+  dn.K = d.F;
+  dn.N = d.d;
+  dn.up_off = 0;
+  dn.C = O;
+  dn.ldc = D;
+  dn.aux = training ? at<char>(ws, L.Ou) : nullptr;
+  dn.ldaux = D;
+  dn.gate = routing->gate;
+  dn.perm = routing->perm;
+  launch_gemm(dn, s);
+
+  // shared gate/up + SwiGLU over every token
+  GemmArgs sg{};
+  sg.act = d.act;
+  sg.epi = EPI_SWIGLU;
+  sg.A = x;
+  sg.lda = D;
+  sg.a_div = 1;
+  sg.B = w->w_sh_gate_up;
+  sg.ldb = D;
+  sg.K = d.d;
+  sg.N = d.Fs;
+  sg.up_off = d.Fs;
+  sg.grouped = 0;
+  sg.M = d.T;
+  sg.max_items = (d.T + kTileM - 1) / kTileM;
+  sg.C = Hs;
+  sg.ldc = Fs;
+  sg.aux = training ? at<char>(ws, L.AUs) : nullptr;
+  sg.ldaux = 2LL * Fs;
+  launch_gemm(sg, s);
+
+  // shared down + combine: y[t] = Hs[t] Wsd^T + sum_j O[pos[t, j]]
+  GemmArgs sd = sg;
+  sd.epi = EPI_COMBINE;
+  sd.A = Hs;
+  sd.lda = Fs;
+  sd.B = w->w_sh_down;
+  sd.ldb = Fs;
+  sd.K = d.Fs;
+  sd.N = d.d;
+  sd.up_off = 0;
+  sd.C = y;
+  sd.ldc = D;
+  sd.aux = nullptr;
+  sd.O = O;
+  sd.ldo = D;
+  sd.pos = routing->pos;
+  sd.k = d.k;
+  launch_gemm(sd, s);
+  return device_status();
+}
+
+moe_status moe_bias_update(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma, float* bias,
+                           void* stream) {
+  if (E < 1 || total_assignments < 0 || !counts || !bias) return MOE_E_ARG;
+  if (E > 64) return MOE_E_UNSUPPORTED;
+  std::vector<Range> rs = {{counts, (size_t)E * 4, false}, {bias, (size_t)E * 4, true}};
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  launch_bias_update(E, (long long)total_assignments, counts, gamma, bias, reinterpret_cast<hipStream_t>(stream));
+  return device_status();
+}
+
+moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* w, const moe_routing* routing,
+                        const void* dy, void* dx, const moe_grads* dw, void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  (void)x; (void)w; (void)routing; (void)dy; (void)dx; (void)dw; (void)ws; (void)ws_bytes; (void)stream;
+  return MOE_E_UNSUPPORTED;
+}
+
+}  // extern "C"

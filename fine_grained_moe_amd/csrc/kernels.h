@@ -1,0 +1,69 @@
+// Host-side launchers of the gfx950 kernels (internal to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace fgmoe {
+
+// Tokens handled by one routing workgroup (4 waves x 16 tokens).
+constexpr int kRouteTokensPerBlock = 64;
+// Rows of one grouped-GEMM tile.
+constexpr int kTileM = 128;
+
+inline int route_blocks(int T) { return (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
+// Upper bound of sum_e ceil(count_e / kTileM) over any routing of T*k slots.
+inline long long max_group_tiles(long long slots, int E) { return (slots + (long long)E * (kTileM - 1)) / kTileM; }
+
+// act: 0 = float32, 1 = bfloat16 (moe_dtype values).
+void launch_route_topk(int act, const void* x, const void* w_router, const float* bias, int T, int d, int E,
+                       int k, int32_t* idx, float* gate, int32_t* block_counts, hipStream_t s);
+void launch_route_scan(const int32_t* block_counts, int nblk, int E, int32_t* counts, int32_t* offsets,
+                       int32_t* block_base, int32_t* tile_e, int32_t* tile_m0, int32_t* tile_count,
+                       hipStream_t s);
+void launch_route_scatter(const int32_t* idx, const int32_t* block_base, int T, int E, int k, int32_t* perm,
+                          int32_t* pos, hipStream_t s);
+void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s);
+
+enum Epilogue { EPI_SWIGLU = 0, EPI_ROWSCALE = 1, EPI_COMBINE = 2 };
+
+// C = A . B^T on MFMA with a fused epilogue.  All element offsets in elements.
+struct GemmArgs {
+  int act;                 // dtype of A, B, C, aux, O
+  int epi;                 // Epilogue
+  // A: rows of length >= K.  Row of output row `slot`: gather ? a_rows[slot] / a_div : slot.
+  const void* A;
+  long long lda;
+  const int32_t* a_rows;
+  int a_div;
+  // B: [N_rows, K] per expert, expert e at B + e * b_estride.
+  const void* B;
+  long long ldb;
+  long long b_estride;
+  int K;
+  int N;                   // output columns (SwiGLU: h columns; B then has gate rows 0..N-1 and up rows up_off..)
+  int up_off;
+  // rows: grouped (tile table over experts) or dense [M]
+  int grouped;
+  int M;
+  const int32_t* tile_e;
+  const int32_t* tile_m0;
+  const int32_t* tile_count;
+  const int32_t* offsets;
+  const int32_t* counts;
+  int max_items;
+  // outputs
+  void* C;
+  long long ldc;
+  void* aux;               // SwiGLU: pre-activations [rows, 2N] (gate | up); ROWSCALE: unscaled rows
+  long long ldaux;
+  const float* gate;       // ROWSCALE: row scale gate[perm[slot]]
+  const int32_t* perm;
+  const void* O;           // COMBINE: y[t] = acc + sum_j O[pos[t*k+j]]
+  long long ldo;
+  const int32_t* pos;
+  int k;
+};
+void launch_gemm(const GemmArgs& a, hipStream_t s);
+
+}  // namespace fgmoe

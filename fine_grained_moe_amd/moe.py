@@ -1,0 +1,173 @@
+"""Python binding of libfgmoe.so, the gfx950 MoE-layer library (include/moe.h).
+
+Argument marshalling only: every step of the layer runs in the library's HIP
+kernels.  torch provides device memory and the current stream.  Importing
+this module loads the library and raises if it is missing; there is no other
+implementation to fall back to.
+
+The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
+moe_bias_update, moe_backward, moe_status_str.  Weights, routing buffers and
+gradients are passed as dicts of torch tensors keyed by the C field names.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Dict, Optional
+
+import torch  # first: the library binds to the HIP runtime torch has loaded
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfgmoe.so")
+
+MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_ALIAS, MOE_E_DEVICE = range(6)
+MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2
+
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
+TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
+
+WEIGHT_FIELDS = ("w_router", "w_gate_up", "w_down", "s_gate_up", "s_down", "w_sh_gate_up", "w_sh_down")
+ROUTING_FIELDS = ("idx", "gate", "counts", "offsets", "perm", "pos")
+GRAD_FIELDS = ("dw_router", "dw_gate_up", "dw_down", "dw_sh_gate_up", "dw_sh_down")
+
+
+class MoeDims(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_int32) for n in ("T", "d", "E", "F", "Fs", "k", "act", "w_routed")]
+
+
+class MoeWeights(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+
+
+class MoeRouting(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in ROUTING_FIELDS]
+
+
+class MoeGrads(ctypes.Structure):
+    _fields_ = [(n, ctypes.c_void_p) for n in GRAD_FIELDS]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, where: str):
+        super().__init__(f"{where}: {moe_status_str(code)} (status {code})")
+        self.code = code
+
+
+def _load() -> ctypes.CDLL:
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(f"{LIB_PATH} is missing; build it with `python -m fine_grained_moe_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    dims_p = ctypes.POINTER(MoeDims)
+    lib.moe_workspace_bytes.argtypes = [dims_p, ctypes.c_int]
+    lib.moe_workspace_bytes.restype = SZ
+    lib.moe_route.argtypes = [dims_p, P, P, P, ctypes.POINTER(MoeRouting), P, SZ, P]
+    lib.moe_route.restype = ctypes.c_int
+    lib.moe_forward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, P, ctypes.POINTER(MoeRouting),
+                                ctypes.c_int, P, SZ, P]
+    lib.moe_forward.restype = ctypes.c_int
+    lib.moe_bias_update.argtypes = [I32, I64, P, ctypes.c_float, P, P]
+    lib.moe_bias_update.restype = ctypes.c_int
+    lib.moe_backward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P, P,
+                                 ctypes.POINTER(MoeGrads), P, SZ, P]
+    lib.moe_backward.restype = ctypes.c_int
+    lib.moe_status_str.argtypes = [ctypes.c_int]
+    lib.moe_status_str.restype = ctypes.c_char_p
+    return lib
+
+
+LIB = _load()
+
+
+def moe_status_str(code: int) -> str:
+    return LIB.moe_status_str(int(code)).decode()
+
+
+def make_dims(T: int, d: int, E: int, F: int, Fs: int, k: int, act: str = "bf16", w_routed: Optional[str] = None) -> MoeDims:
+    a = DTYPES[act]
+    return MoeDims(T, d, E, F, Fs, k, a, DTYPES[w_routed] if w_routed else a)
+
+
+def _ptr(t) -> Optional[int]:
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"expected a torch tensor, got {type(t).__name__}")
+    if not t.is_contiguous():
+        raise ValueError("tensors passed to the MoE library must be contiguous")
+    if t.numel() and t.device.type != "cuda":
+        raise ValueError("tensors passed to the MoE library must be on the GPU")
+    return t.data_ptr() if t.numel() else None
+
+
+def _stream(stream) -> int:
+    if stream is None:
+        stream = torch.cuda.current_stream()
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _struct(cls, fields, tensors: Dict[str, torch.Tensor]):
+    return cls(*[_ptr(tensors.get(f)) for f in fields])
+
+
+def _check(code: int, where: str) -> None:
+    if code != MOE_OK:
+        raise MoeError(code, where)
+
+
+def moe_workspace_bytes(dims: MoeDims, training: bool = False) -> int:
+    return int(LIB.moe_workspace_bytes(ctypes.byref(dims), int(bool(training))))
+
+
+def moe_route(dims: MoeDims, x, w_router, bias, routing: Dict[str, torch.Tensor], ws, stream=None) -> None:
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_route(ctypes.byref(dims), _ptr(x), _ptr(w_router), _ptr(bias), ctypes.byref(r), _ptr(ws),
+                         ws.numel() * ws.element_size(), _stream(stream)), "moe_route")
+
+
+def moe_forward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y, routing: Dict[str, torch.Tensor],
+                ws, training: bool = False, stream=None) -> None:
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), _ptr(y), ctypes.byref(r),
+                           int(bool(training)), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_forward")
+
+
+def moe_bias_update(E: int, total_assignments: int, counts, gamma: float, bias, stream=None) -> None:
+    _check(LIB.moe_bias_update(int(E), int(total_assignments), _ptr(counts), float(gamma), _ptr(bias),
+                               _stream(stream)), "moe_bias_update")
+
+
+def moe_backward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], routing: Dict[str, torch.Tensor], dy, dx,
+                 grads: Dict[str, torch.Tensor], ws, stream=None) -> None:
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    g = _struct(MoeGrads, GRAD_FIELDS, grads)
+    _check(LIB.moe_backward(ctypes.byref(dims), _ptr(x), ctypes.byref(w), ctypes.byref(r), _ptr(dy), _ptr(dx),
+                            ctypes.byref(g), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
+           "moe_backward")
+
+
+# ---------------------------------------------------------------- allocation helpers
+
+def alloc_routing(dims: MoeDims, device="cuda") -> Dict[str, torch.Tensor]:
+    T, k, E = dims.T, dims.k, dims.E
+    i32 = dict(dtype=torch.int32, device=device)
+    return dict(idx=torch.empty(T, k, **i32), gate=torch.empty(T, k, dtype=torch.float32, device=device),
+                counts=torch.empty(E, **i32), offsets=torch.empty(E + 1, **i32),
+                perm=torch.empty(T * k, **i32), pos=torch.empty(T, k, **i32))
+
+
+def alloc_workspace(dims: MoeDims, training: bool = False, device="cuda") -> torch.Tensor:
+    n = moe_workspace_bytes(dims, training)
+    if n == 0:
+        raise MoeError(MOE_E_UNSUPPORTED, "moe_workspace_bytes")
+    return torch.empty(n, dtype=torch.uint8, device=device)
+
+
+def alloc_grads(dims: MoeDims, device="cuda") -> Dict[str, torch.Tensor]:
+    E, d, F, Fs = dims.E, dims.d, dims.F, dims.Fs
+    f = dict(dtype=torch.float32, device=device)
+    return dict(dw_router=torch.empty(E, d, **f), dw_gate_up=torch.empty(E, 2 * F, d, **f),
+                dw_down=torch.empty(E, d, F, **f), dw_sh_gate_up=torch.empty(2 * Fs, d, **f),
+                dw_sh_down=torch.empty(d, Fs, **f))

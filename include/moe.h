@@ -1,0 +1,157 @@
+/* moe.h -- C ABI of the MI355X (gfx950) fine-grained mixture-of-experts layer.
+ *
+ * The layer is the NanoColibri / HYV3 MoE FFN described in the seventnews
+ * article "A relay race of rented GPUs trained NanoColibri's 2.7B MoE for $200"
+ * (opening section, architecture paragraph): a sigmoid-plus-bias router over
+ * E routed experts with top-k selection, fine-grained SwiGLU experts of width
+ * F on hidden size d, an always-resident shared expert of width Fs, a weighted
+ * combine, and the aux-loss-free balancing step bias += gamma*sign(target-load).
+ *
+ * Conventions shared by every entry point
+ *  - Every data pointer is a DEVICE pointer owned by the caller, unless the
+ *    comment says (host).  The caller keeps buffers alive until the work on
+ *    `stream` has finished.
+ *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
+ *    Every call only enqueues work on it and returns: no synchronisation, no
+ *    allocation, no host<->device copies.
+ *  - Arguments are checked on the host before anything is enqueued.  A failed
+ *    check returns an error status and enqueues nothing.  MOE_E_DEVICE means a
+ *    launch was rejected by the runtime (hipGetLastError after enqueueing).
+ *  - Layouts are row-major with the contraction dimension last ("weight rows
+ *    are dot-product rows").  act = MOE_F32 means float32, MOE_BF16 bfloat16.
+ *  - Supported shapes: 0 <= T, 1 <= E <= 64, 1 <= k <= min(E, 8),
+ *    d % 128 == 0, F % 64 == 0, Fs % 64 == 0, T*k*max(d, 2F) < 2^31.
+ *  - Outputs may not overlap inputs or each other (MOE_E_ALIAS).
+ *  - Non-finite inputs give undefined (but memory-safe) results.
+ */
+#ifndef FGMOE_MOE_H
+#define FGMOE_MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_ARG = 1,          /* null pointer, negative or inconsistent size        */
+  MOE_E_UNSUPPORTED = 2,  /* valid but outside the supported shapes / dtypes    */
+  MOE_E_WORKSPACE = 3,    /* workspace missing or smaller than required         */
+  MOE_E_ALIAS = 4,        /* an output overlaps an input or another output      */
+  MOE_E_DEVICE = 5        /* the HIP runtime rejected a launch                  */
+} moe_status;
+
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
+
+/* (host) Layer sizes.  T tokens, d hidden, E routed experts of width F, one
+ * shared expert of width Fs, top-k.  act: dtype of x, y, the router and the
+ * shared expert.  w_routed: dtype of the routed expert weights, equal to act,
+ * or MOE_INT4_G128 (requires act = MOE_BF16 and k = 1: top-1 serving). */
+typedef struct {
+  int32_t T, d, E, F, Fs, k;
+  int32_t act;
+  int32_t w_routed;
+} moe_dims;
+
+/* (host struct of device pointers) Layer weights.
+ *  w_router     [E, d]                       act
+ *  w_gate_up    [E, 2F, d]                   act; rows 0..F-1 gate, F..2F-1 up
+ *               int4: packed uint8 [E, 2F, d/2], element 2i in the low nibble
+ *  w_down       [E, d, F]                    act; int4: packed uint8 [E, d, F/2]
+ *  s_gate_up    int4 only: bf16 scales [E, 2F, d/128]   (else ignored)
+ *  s_down       int4 only: bf16 scales [E, d, F/128]    (else ignored)
+ *  w_sh_gate_up [2Fs, d]                     act; rows 0..Fs-1 gate, Fs.. up
+ *  w_sh_down    [d, Fs]                      act
+ * int4 format (an assumed container; the article says only "int4"):
+ * symmetric, one bf16 scale per 128 consecutive elements of a row,
+ * w = q * scale with q a two's-complement nibble in [-8, 7]. */
+typedef struct {
+  const void* w_router;
+  const void* w_gate_up;
+  const void* w_down;
+  const void* s_gate_up;
+  const void* s_down;
+  const void* w_sh_gate_up;
+  const void* w_sh_down;
+} moe_weights;
+
+/* (host struct of device pointers) Routing produced by moe_route/moe_forward.
+ *  idx     [T, k] int32   selected experts, largest s+b first, ties -> lower e
+ *  gate    [T, k] float   s_idx / sum of selected s (exactly 1 when k = 1)
+ *  counts  [E]    int32   load of each expert: number of (t, j) picking it
+ *  offsets [E+1]  int32   exclusive prefix sum of counts
+ *  perm    [T*k]  int32   slot -> t*k + j; slots of expert e are
+ *                         offsets[e] .. offsets[e+1]-1, ascending in t*k + j
+ *  pos     [T, k] int32   (t, j) -> slot, the inverse of perm */
+typedef struct {
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+} moe_routing;
+
+/* (host struct of device pointers) Weight gradients, float32, same shapes as
+ * the weights (act layouts).  Overwritten, not accumulated. */
+typedef struct {
+  float* dw_router;
+  float* dw_gate_up;
+  float* dw_down;
+  float* dw_sh_gate_up;
+  float* dw_sh_down;
+} moe_grads;
+
+/* Bytes of device workspace that moe_route / moe_forward / moe_backward need
+ * for these dims (training = 1 adds the activations moe_backward reads).
+ * Returns 0 when the dims are invalid or unsupported. */
+size_t moe_workspace_bytes(const moe_dims* dims, int training);
+
+/* Router only: logits x.W_r, s = sigmoid, top-k on s + bias, normalised gates,
+ * per-expert loads, offsets and the dispatch order (architecture paragraph:
+ * sigmoid-plus-bias router, top-2).  For callers that must know the selected
+ * experts before computing them (the streaming engine of the proof-of-loop
+ * paragraph).  ws: at least moe_workspace_bytes(dims, 0). */
+moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, const float* bias,
+                     const moe_routing* out, void* ws, size_t ws_bytes, void* stream);
+
+/* The layer: y_t = Shared(x_t) + sum_j gate_tj * Expert_{idx_tj}(x_t), with
+ * Expert(x) = W_d (silu(W_g x) * (W_u x)) and the shared expert ungated
+ * (architecture and proof-of-loop paragraphs; the top-2 paragraph of the
+ * "Relay training" section names the routing weight).  x, y: [T, d] act.
+ * bias: [E] float32, read only (moe_bias_update changes it).  routing: filled
+ * as by moe_route.  training = 1 stores in ws what moe_backward needs.
+ * With w_routed = MOE_INT4_G128 this is the top-1 serving path (k = 1,
+ * gate = 1, int4 experts dequantised inside the kernels). */
+moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias,
+                       void* y, const moe_routing* routing, int training,
+                       void* ws, size_t ws_bytes, void* stream);
+
+/* Aux-loss-free balancing step (architecture paragraph, DeepSeek-V3 recipe):
+ * bias[e] <- fl32(bias[e] + gamma * sign(total_assignments - E * counts[e])),
+ * i.e. the target load total_assignments/E compared exactly in integers,
+ * sign(0) = 0, one float32 addition.  counts: [E] int32 (device, e.g. the
+ * routing of the forward that used the old bias); bias: [E] float32 in/out.
+ * total_assignments = T*k of that forward. */
+moe_status moe_bias_update(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma,
+                           float* bias, void* stream);
+
+/* Backward of a training moe_forward with the selection held fixed: dx [T, d]
+ * act, and the float32 weight gradients.  The router gradient flows only
+ * through the normalised gates (top-2 paragraph of the "Relay training"
+ * section: with k = 1 it is zero).  x, w, routing: those of the forward; ws:
+ * the workspace that forward filled (training = 1), unchanged since. */
+moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* w,
+                        const moe_routing* routing, const void* dy, void* dx, const moe_grads* dw,
+                        void* ws, size_t ws_bytes, void* stream);
+
+/* Static, NUL-terminated description of a status code. */
+const char* moe_status_str(moe_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* FGMOE_MOE_H */

@@ -103,12 +103,16 @@ def route(x, w_router, bias, k: int) -> Routing:
     logits = x @ W.T
     s = sigmoid(logits)
     v = s + b[None, :]
-    # stable sort of -v: equal keys keep ascending expert order
-    order = np.argsort(-v, axis=1, kind="stable")
-    idx = order[:, :k]
+    idx = select_topk(v, k)
     s_sel = np.take_along_axis(s, idx, axis=1)
     gate = s_sel / s_sel.sum(axis=1, keepdims=True)
     return Routing(idx=idx, gate=gate, scores=s, v=v, logits=logits)
+
+
+def select_topk(v, k: int) -> np.ndarray:
+    """The k largest keys of each row, largest first; an exact tie goes to the
+    lower index (R8).  A stable sort of -v keeps equal keys in index order."""
+    return np.argsort(-np.asarray(v, dtype=f64), axis=1, kind="stable")[:, :k]
 
 
 def expert_counts(idx, E: int) -> np.ndarray:

@@ -1,0 +1,109 @@
+"""The C ABI library: it loads, exports every function include/moe.h declares,
+and rejects bad arguments on the host before anything reaches a GPU."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe.h")
+LIBPATH = os.path.join(ROOT, "fine_grained_moe_amd", "libfgmoe.so")
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIBPATH):
+        pytest.fail("libfgmoe.so is not built; run python -m fine_grained_moe_amd.build")
+    import torch  # noqa: F401  (same load order as the binding)
+    from fine_grained_moe_amd import moe
+    return moe
+
+
+def test_header_declares_the_entry_points():
+    assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward",
+                                           "moe_bias_update", "moe_backward", "moe_status_str"])
+
+
+def test_library_exports_every_declared_symbol(lib):
+    raw = ctypes.CDLL(LIBPATH)
+    for name in declared_functions():
+        assert hasattr(raw, name), name
+
+
+def test_status_strings(lib):
+    for code in range(6):
+        assert lib.moe_status_str(code)
+    assert lib.moe_status_str(0) == "ok"
+    assert "unknown" in lib.moe_status_str(99)
+
+
+def test_workspace_bytes(lib):
+    d = lib.make_dims(4096, 1024, 64, 512, 2048, 2, "bf16")
+    n = lib.moe_workspace_bytes(d)
+    slots = 4096 * 2
+    assert n >= slots * 512 * 2 + slots * 1024 * 2 + 4096 * 2048 * 2
+    assert lib.moe_workspace_bytes(d, training=True) > n
+    for bad in (dict(E=65), dict(k=9), dict(k=3, E=2), dict(d=100), dict(F=96), dict(Fs=32)):
+        args = dict(T=16, d=1024, E=64, F=512, Fs=2048, k=2)
+        args.update(bad)
+        assert lib.moe_workspace_bytes(lib.make_dims(act="bf16", **args)) == 0, bad
+    assert lib.moe_workspace_bytes(lib.make_dims(-1, 1024, 64, 512, 2048, 2)) == 0
+
+
+def _call_forward(lib, dims, x, y, ws, ws_bytes, weights=None, routing=None):
+    W = lib.MoeWeights(*(weights or [0x10000000 + i * 0x1000000 for i in range(7)]))
+    R = lib.MoeRouting(*(routing or [0x40000000 + i * 0x1000000 for i in range(6)]))
+    return lib.LIB.moe_forward(ctypes.byref(dims), x, ctypes.byref(W), 0x50000000, y, ctypes.byref(R), 0, ws,
+                               ws_bytes, None)
+
+
+def test_host_checks_reject_before_launch(lib):
+    """Fake addresses: every one of these calls must fail its host checks, so
+    nothing is ever enqueued (there is no GPU here)."""
+    dims = lib.make_dims(16, 128, 8, 64, 256, 2, "f32")
+    need = lib.moe_workspace_bytes(dims)
+    x, y, ws = 0x60000000, 0x70000000, 0x80000000
+    assert _call_forward(lib, dims, x, y, ws, need - 1) == lib.MOE_E_WORKSPACE
+    assert _call_forward(lib, dims, x, y, None, need) == lib.MOE_E_WORKSPACE
+    assert _call_forward(lib, dims, None, y, ws, need) == lib.MOE_E_ARG
+    assert _call_forward(lib, dims, x, x + 64, ws, need) == lib.MOE_E_ALIAS        # y overlaps x
+    assert _call_forward(lib, dims, x, y, y + 16, need) == lib.MOE_E_ALIAS          # ws overlaps y
+    bad_w = [0x10000000 + i * 0x1000000 for i in range(7)]
+    bad_w[2] = None
+    assert _call_forward(lib, dims, x, y, ws, need, weights=bad_w) == lib.MOE_E_ARG
+    bad_r = [0x40000000 + i * 0x1000000 for i in range(6)]
+    bad_r[1] = bad_r[0] + 8                                                         # gate overlaps idx
+    assert _call_forward(lib, dims, x, y, ws, need, routing=bad_r) == lib.MOE_E_ALIAS
+    big = lib.make_dims(16, 128, 65, 64, 256, 2, "f32")
+    assert _call_forward(lib, big, x, y, ws, need) == lib.MOE_E_UNSUPPORTED
+    neg = lib.make_dims(-5, 128, 8, 64, 256, 2, "f32")
+    assert _call_forward(lib, neg, x, y, ws, need) == lib.MOE_E_ARG
+    assert lib.LIB.moe_forward(None, x, None, None, y, None, 0, ws, need, None) == lib.MOE_E_ARG
+    # bias step: null pointers, bad E, counts overlapping bias
+    assert lib.LIB.moe_bias_update(8, 16, None, 1e-3, 0x1000, None) == lib.MOE_E_ARG
+    assert lib.LIB.moe_bias_update(0, 16, 0x2000, 1e-3, 0x1000, None) == lib.MOE_E_ARG
+    assert lib.LIB.moe_bias_update(65, 16, 0x2000, 1e-3, 0x1000, None) == lib.MOE_E_UNSUPPORTED
+    assert lib.LIB.moe_bias_update(8, 16, 0x1000, 1e-3, 0x1010, None) == lib.MOE_E_ALIAS
+
+
+def test_route_host_checks(lib):
+    dims = lib.make_dims(16, 128, 8, 64, 256, 2, "bf16")
+    need = lib.moe_workspace_bytes(dims)
+    R = lib.MoeRouting(*[0x40000000 + i * 0x1000000 for i in range(6)])
+    assert lib.LIB.moe_route(ctypes.byref(dims), 0x1000, 0x20000, 0x30000, ctypes.byref(R), 0x90000000,
+                             need - 1, None) == lib.MOE_E_WORKSPACE
+    assert lib.LIB.moe_route(ctypes.byref(dims), 0x1000, 0x20000, 0x30000, None, 0x90000000, need,
+                             None) == lib.MOE_E_ARG
+
+
+def test_int4_requires_top1_bf16(lib):
+    for act, k in (("f32", 1), ("bf16", 2)):
+        d = lib.make_dims(8, 1024, 64, 512, 2048, k, act, w_routed="int4")
+        assert lib.moe_workspace_bytes(d) == 0

@@ -1,0 +1,200 @@
+"""GPU parity of the router, dispatch, forward and bias step against the oracle.
+
+Bit-exact: expert indices, loads, offsets, dispatch order and the bias after
+each step.  Floating point: relative Frobenius error of y at most 1e-4 (fp32
+workload) or 1e-2 (bf16 workloads, fp32 accumulation); gates within 1e-6.
+Inputs come from the seeded generator with near-tie rows redrawn (the oracle
+decides which), so that a different summation order cannot flip a selection.
+"""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as om
+from fine_grained_moe_amd import synth
+from tests import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+TOL = {"f32": 1e-4, "bf16": 1e-2}
+GAMMA = 1e-3
+
+
+def _case(name, T=None, seed=0, **over):
+    cfg = dict(synth.WORKLOADS[name])
+    if T is not None:
+        cfg["T"] = T
+    cfg.update(over)
+    inp = synth.make_layer(seed=seed, **cfg)
+    H.remove_near_ties(inp)
+    return inp
+
+
+def _check_forward(inp, bias=None):
+    y, rn, dev = H.run_forward(inp, bias)
+    y_ref, r_ref = H.oracle_forward(inp, bias)
+    H.check_routing_exact(rn, r_ref, inp.E)
+    np.testing.assert_allclose(rn["gate"], r_ref.gate, rtol=0, atol=1e-6)
+    err = H.rel_fro(y, y_ref)
+    print(f"[{inp.act} T={inp.T} E={inp.E} k={inp.k}] rel_fro(y) = {err:.3e}", flush=True)
+    assert err <= TOL[inp.act], err
+    return y, rn, dev, r_ref
+
+
+def _check_bias_step(inp, rn, dev, bias_before):
+    import torch
+    from fine_grained_moe_amd import moe
+    moe.moe_bias_update(inp.E, inp.T * inp.k, dev["r"]["counts"], GAMMA, dev["b"])
+    torch.cuda.synchronize()
+    got = dev["b"].cpu().numpy()
+    want = om.bias_update(bias_before, rn["counts"], inp.T * inp.k, GAMMA)
+    assert got.view(np.uint32).tolist() == want.view(np.uint32).tolist()
+    return got
+
+
+def test_tiny_f32_forward_and_bias_step():
+    inp = _case("tiny_f32")
+    y, rn, dev, _ = _check_forward(inp)
+    b = _check_bias_step(inp, rn, dev, inp.bias)
+    assert np.all(np.abs(b) == np.float32(GAMMA)) or np.any(b == 0)
+
+
+def test_layer_t4096_forward_and_bias_step():
+    inp = _case("layer_t4096")
+    y, rn, dev, _ = _check_forward(inp)
+    _check_bias_step(inp, rn, dev, inp.bias)
+    assert rn["counts"].sum() == inp.T * inp.k
+
+
+@pytest.mark.parametrize("T", [1, 5, 63, 64, 65, 1000, 1027])
+def test_ragged_token_counts(T):
+    _check_forward(_case("layer_t4096", T=T, seed=T))
+
+
+@pytest.mark.parametrize("k", [1, 3, 8])
+def test_other_k(k):
+    _check_forward(_case("layer_t4096", T=700, seed=40 + k, k=k))
+
+
+@pytest.mark.parametrize("E", [1, 8, 17, 64])
+def test_other_expert_counts(E):
+    k = min(2, E)
+    _check_forward(_case("layer_t4096", T=300, seed=50 + E, E=E, k=k, d=256, F=128, Fs=256))
+
+
+def test_f32_several_tiles():
+    # fp32, several 128-row tiles per expert and a ragged tail
+    _check_forward(_case("tiny_f32", T=2000, seed=3, d=256, F=128, Fs=384))
+
+
+def test_zero_input_ties_and_zero_output():
+    inp = synth.make_workload("layer_t4096", T=200)
+    inp.x[:] = 0
+    y, rn, _ = H.run_forward(inp)
+    assert np.all(rn["idx"] == np.array([0, 1]))
+    assert np.all(rn["gate"] == 0.5)
+    assert np.all(y == 0)
+
+
+def test_unselected_experts_and_empty_groups():
+    inp = synth.make_workload("layer_t4096", T=512, seed=9)
+    bias = np.zeros(inp.E, np.float32)
+    bias[::2] = -4.0            # even experts can never win: load 0
+    H.remove_near_ties(inp, bias_states=[bias])
+    y, rn, dev, _ = _check_forward(inp, bias)
+    assert np.all(rn["counts"][::2] == 0)
+
+
+def test_identical_experts_reduce_to_dense_ffn():
+    inp = _case("layer_t4096", T=256, seed=12)
+    inp.w_gate_up[:] = inp.w_gate_up[0]
+    inp.w_down[:] = inp.w_down[0]
+    y, _, _ = H.run_forward(inp)
+    F = inp.F
+    dense = om.swiglu_ffn(inp.x, inp.w_gate_up[0, :F], inp.w_gate_up[0, F:], inp.w_down[0])
+    shared = om.swiglu_ffn(inp.x, inp.w_sh_gate_up[:inp.Fs], inp.w_sh_gate_up[inp.Fs:], inp.w_sh_down)
+    assert H.rel_fro(y, shared + dense) <= 1e-2
+
+
+def test_route_only_matches_forward_routing():
+    import torch
+    from fine_grained_moe_amd import moe
+    inp = _case("layer_t4096", T=777, seed=4)
+    _, rn, dev = H.run_forward(inp)
+    r2 = moe.alloc_routing(dev["dims"])
+    ws = moe.alloc_workspace(dev["dims"])
+    moe.moe_route(dev["dims"], dev["x"], dev["w"]["w_router"], dev["b"], r2, ws)
+    torch.cuda.synchronize()
+    for k, v in r2.items():
+        np.testing.assert_array_equal(v.cpu().numpy(), rn[k], err_msg=k)
+
+
+def test_run_to_run_bitwise_equal():
+    import torch
+    from fine_grained_moe_amd import moe
+    inp = _case("layer_t4096", T=1500, seed=5)
+    y1, _, dev = H.run_forward(inp)
+    y2 = torch.empty_like(dev["y"])
+    moe.moe_forward(dev["dims"], dev["x"], dev["w"], dev["b"], y2, dev["r"], dev["ws"])
+    torch.cuda.synchronize()
+    assert torch.equal(dev["y"], y2)
+
+
+def test_empty_batch():
+    import torch
+    from fine_grained_moe_amd import moe
+    dims = moe.make_dims(0, 1024, 64, 512, 2048, 2, "bf16")
+    x = torch.empty(0, 1024, dtype=torch.bfloat16, device="cuda")
+    inp = synth.make_workload("layer_t4096", T=1)
+    _, w = H.to_gpu(inp)
+    b = torch.zeros(64, device="cuda")
+    r = moe.alloc_routing(dims)
+    r["counts"].fill_(7)
+    ws = moe.alloc_workspace(dims)
+    moe.moe_forward(dims, x, w, b, torch.empty_like(x), r, ws)
+    torch.cuda.synchronize()
+    assert torch.all(r["counts"] == 0) and torch.all(r["offsets"] == 0)
+
+
+@pytest.mark.slow
+def test_zipf_t16384_ten_bias_steps():
+    """Skewed routing (Zipf(1) expected loads) and 10 consecutive balancing
+    steps on the same batch: bit-exact routing and bias every step, y checked
+    at the first and the last step."""
+    import torch
+    from fine_grained_moe_amd import moe
+    inp = synth.make_workload("zipf_t16384")
+    for _ in range(3):   # the preset depends on x; redraw until stable
+        b0 = H.zipf_bias(inp)
+        if H.remove_near_ties(inp, bias_states=[b0], steps_after=10) == 0:
+            break
+    states = H.bias_sequence(inp, b0, 10)
+    x, w = H.to_gpu(inp)
+    dims = moe.make_dims(inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k, inp.act)
+    b = torch.from_numpy(b0.copy()).cuda()
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+    y = torch.empty_like(x)
+    loads = []
+    for step in range(10):
+        want_b = states[step]
+        assert b.cpu().numpy().view(np.uint32).tolist() == want_b.view(np.uint32).tolist(), step
+        if step in (0, 9):
+            moe.moe_forward(dims, x, w, b, y, r, ws)
+        else:
+            moe.moe_route(dims, x, w["w_router"], b, r, ws)
+        torch.cuda.synchronize()
+        rn = {k: v.cpu().numpy() for k, v in r.items()}
+        ref = om.route(inp.x, inp.w_router, want_b, inp.k)
+        H.check_routing_exact(rn, ref, inp.E)
+        loads.append(rn["counts"].copy())
+        if step in (0, 9):
+            y_ref, _ = H.oracle_forward(inp, want_b)
+            err = H.rel_fro(y.float().cpu().numpy(), y_ref)
+            print(f"zipf step {step}: rel_fro(y) = {err:.3e}, max load {rn['counts'].max()}, "
+                  f"min load {rn['counts'].min()}", flush=True)
+            assert err <= 1e-2
+        moe.moe_bias_update(inp.E, inp.T * inp.k, r["counts"], GAMMA, b)
+    torch.cuda.synchronize()
+    assert b.cpu().numpy().view(np.uint32).tolist() == states[10].view(np.uint32).tolist()
+    share = loads[0].max() / (inp.T * inp.k)
+    assert share > 0.15, share      # the hottest expert holds ~20% of assignments
