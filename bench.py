@@ -1,0 +1,245 @@
+#!/usr/bin/env python3
+"""Throughput of the NanoColibri MoE layer's hot path on one MI355X.
+
+A step is one pass of the whole path over one batch: moe_forward (router,
+top-2, loads and dispatch, routed gate/up + SwiGLU, routed down + gate
+scaling, shared expert, combine) followed by moe_bias_update, on the one-layer
+workload T = 4096 tokens (batch 2 x seq 2048), d = 1024, 64 experts of width
+512, top-2, shared expert 2048, bf16 with fp32 accumulation.  Inputs come from
+the seeded generator and sit in HBM before timing starts.
+
+Headline `value`: tokens/s with the expert weights rotated over several
+distinct copies (each step reads its weights from HBM, not from the 256 MB
+Infinity Cache); the same loop with one weight set is reported as `warm`.
+Per-phase durations come from HIP events the library records on its stream
+inside the timed region.
+
+Prints one JSON line on stdout; progress goes to stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import sys
+import time
+
+METRIC = "MoE-layer tokens/sec (d=1024,E=64,top-2,bf16) + % MFMA peak / % HBM BW"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+GAMMA = 1e-3
+PHASES = ("route", "gate_up", "routed_down", "shared_down_combine")
+KERNEL_OF_PHASE = {
+    "gate_up": "gemm_kernel<bf16, SWIGLU> (routed + shared experts, one launch)",
+    "routed_down": "gemm_kernel<bf16, ROWSCALE>",
+    "shared_down_combine": "gemm_kernel<bf16, COMBINE>",
+    "route": "route_topk + route_scan + route_scatter",
+}
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def algorithmic_work(T, d, E, F, Fs, k, es=2):
+    """Minimum FLOPs and HBM bytes of each phase: every weight and activation
+    read once, every output written once; routed FLOPs over the T*k
+    assignments only."""
+    slots = T * k
+    w = {}
+    w["route"] = dict(flops=2.0 * T * d * E,
+                      bytes=T * d * es + E * d * es + E * 4 + slots * 4 * 4 + (E * 2 + 1) * 4)
+    w["gate_up"] = dict(flops=2.0 * slots * 2 * F * d + 2.0 * T * 2 * Fs * d,
+                        bytes=E * 2 * F * d * es + 2 * Fs * d * es + T * d * es + slots * F * es
+                        + T * Fs * es + slots * 4)
+    w["routed_down"] = dict(flops=2.0 * slots * d * F,
+                            bytes=E * d * F * es + slots * F * es + slots * d * es + slots * 8)
+    w["shared_down_combine"] = dict(flops=2.0 * T * d * Fs,
+                                    bytes=d * Fs * es + T * Fs * es + slots * d * es + T * d * es + slots * 4)
+    for v in w.values():
+        t_mfma = v["flops"] / PEAK_BF16_FLOPS
+        t_hbm = v["bytes"] / PEAK_HBM_BPS
+        v["bound"] = "mfma" if t_mfma >= t_hbm else "hbm"
+    return w
+
+
+class HipEvents:
+    """hipEvent_t handles from the HIP runtime torch has loaded."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so.7")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self):
+        ev = ctypes.c_void_p()
+        rc = self.hip.hipEventCreate(ctypes.byref(ev))
+        if rc != 0:
+            raise RuntimeError(f"hipEventCreate failed ({rc})")
+        return ev.value
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        rc = self.hip.hipEventElapsedTime(ctypes.byref(ms), ctypes.c_void_p(a), ctypes.c_void_p(b))
+        if rc != 0:
+            raise RuntimeError(f"hipEventElapsedTime failed ({rc})")
+        return ms.value
+
+    def destroy(self, e):
+        self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+
+def cpu_baseline(inp, seconds: float):
+    """The CPU oracle as it stands, on this host's cores, over a bounded sample:
+    whole copies of the benchmark batch until `seconds` have passed."""
+    import numpy as np
+    from oracle import moe_oracle as om
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+    except Exception:
+        cores = os.cpu_count() or 1
+    t0 = time.perf_counter()
+    n = 0
+    while True:
+        om.forward(inp.x, inp.w_router, inp.w_gate_up, inp.w_down, inp.w_sh_gate_up, inp.w_sh_down, inp.bias, inp.k)
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return dict(value=n * inp.T / el, unit="tokens/s", cores=int(cores), kind="oracle",
+                sample=f"{n} x the {inp.T}-token benchmark batch (float64 oracle forward incl. routing), "
+                       f"{el:.1f} s wall")
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--weight-sets", type=int, default=8, help="distinct expert-weight copies rotated per step")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
+    args = ap.parse_args()
+
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(run with --gpus 1)", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+    from fine_grained_moe_amd import moe, synth
+
+    torch.cuda.set_device(0)
+    inp = synth.make_workload("layer_t4096", seed=0)
+    T, d, E, F, Fs, k = inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k
+    log(f"workload layer_t4096: T={T} d={d} E={E} F={F} Fs={Fs} k={k} bf16")
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+
+    def up(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+
+    base = dict(w_router=up(inp.w_router), w_gate_up=up(inp.w_gate_up), w_down=up(inp.w_down),
+                w_sh_gate_up=up(inp.w_sh_gate_up), w_sh_down=up(inp.w_sh_down))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(max(0, args.weight_sets - 1))]
+    x = up(inp.x)
+    y = torch.empty_like(x)
+    bias0 = torch.zeros(E, dtype=torch.float32, device="cuda")
+    bias = bias0.clone()
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+    torch.cuda.synchronize()
+
+    if args.copy_calibration:
+        src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy calibration: 3 x 1 GiB device copies done")
+        del src, dst
+
+    ev = HipEvents()
+    nph = len(PHASES) + 1
+
+    def run(n_sets, steps, warmup):
+        bias.copy_(bias0)
+        for i in range(warmup):
+            moe.moe_forward(dims, x, sets[i % n_sets], bias, y, r, ws)
+            moe.moe_bias_update(E, T * k, r["counts"], GAMMA, bias)
+        events = [[ev.create() for _ in range(nph)] for _ in range(steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(steps):
+            moe.moe_set_phase_events(events[i])
+            moe.moe_forward(dims, x, sets[(warmup + i) % n_sets], bias, y, r, ws)
+            moe.moe_bias_update(E, T * k, r["counts"], GAMMA, bias)
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        moe.moe_set_phase_events(None)
+        ph = {p: 0.0 for p in PHASES}
+        for i in range(steps):
+            for j, p in enumerate(PHASES):
+                ph[p] += ev.elapsed_ms(events[i][j], events[i][j + 1])
+        for row in events:
+            for e_ in row:
+                ev.destroy(e_)
+        return el, {p: v / steps * 1e3 for p, v in ph.items()}   # seconds, microseconds per launch
+
+    log(f"timing {args.steps} steps (+{args.warmup} warm-up) over {args.weight_sets} weight sets")
+    el, phases = run(args.weight_sets, args.steps, args.warmup)
+    value = T * args.steps / el
+    log(f"cold: {value / 1e6:.2f} M tokens/s, {el / args.steps * 1e6:.1f} us/step; phases (us): "
+        + ", ".join(f"{p}={v:.1f}" for p, v in phases.items()))
+
+    work = algorithmic_work(T, d, E, F, Fs, k)
+    dom = max(phases, key=lambda p: phases[p])
+    wd = work[dom]
+    t = phases[dom] * 1e-6
+    if wd["bound"] == "mfma":
+        roof = dict(bound="mfma", achieved=wd["flops"] / t / 1e12, peak=PEAK_BF16_FLOPS / 1e12, unit="TFLOP/s")
+    else:
+        roof = dict(bound="hbm", achieved=wd["bytes"] / t / 1e9, peak=PEAK_HBM_BPS / 1e9, unit="GB/s")
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = None
+    roof["kernel"] = KERNEL_OF_PHASE[dom]
+    roof["avg_us"] = phases[dom]
+
+    out = {
+        "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "layer_t4096", "T": T, "d": d, "E": E, "F": F, "Fs": Fs, "k": k,
+                   "weight_sets": args.weight_sets, "bias_update_every_step": True},
+        "roofline": roof,
+    }
+    phase_report = {}
+    for p, us in phases.items():
+        wp = work[p]
+        phase_report[p] = dict(us=round(us, 2), tflops=round(wp["flops"] / (us * 1e-6) / 1e12, 1),
+                               gbps=round(wp["bytes"] / (us * 1e-6) / 1e9, 1), bound=wp["bound"])
+    out["phases"] = phase_report
+
+    if not args.no_warm:
+        el_w, ph_w = run(1, args.steps, args.warmup)
+        out["warm"] = dict(value=T * args.steps / el_w, ms_per_step=el_w / args.steps * 1e3,
+                           phases_us={p: round(v, 2) for p, v in ph_w.items()})
+        log(f"warm: {out['warm']['value'] / 1e6:.2f} M tokens/s")
+
+    if not args.no_cpu_baseline:
+        log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
+        out["cpu_baseline"] = cpu_baseline(inp, args.cpu_seconds)
+        log(f"CPU oracle: {out['cpu_baseline']['value']:.0f} tokens/s on {out['cpu_baseline']['cores']} threads")
+
+    print(json.dumps(out), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

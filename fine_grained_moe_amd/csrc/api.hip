@@ -120,9 +120,27 @@ void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void
 
 moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
 
+// Phase-boundary events registered by moe_set_phase_events (instrumentation).
+constexpr int kMaxPhaseEvents = 8;
+hipEvent_t g_phase_events[kMaxPhaseEvents];
+int g_n_phase_events = 0;
+
+void mark_phase(int i, hipStream_t s) {
+  if (i < g_n_phase_events) (void)hipEventRecord(g_phase_events[i], s);
+}
+
 }  // namespace
 
 extern "C" {
+
+moe_status moe_set_phase_events(void* const* events, int32_t n) {
+  if (n < 0 || n > kMaxPhaseEvents || (n > 0 && !events)) return MOE_E_ARG;
+  for (int i = 0; i < n; ++i)
+    if (!events[i]) return MOE_E_ARG;
+  for (int i = 0; i < n; ++i) g_phase_events[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  g_n_phase_events = events ? n : 0;
+  return MOE_OK;
+}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {
@@ -186,7 +204,9 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   if (any_alias(rs)) return MOE_E_ALIAS;
 
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  mark_phase(0, s);
   enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
+  mark_phase(1, s);
   if (d.T == 0) return device_status();
 
   const long long slots = (long long)d.T * d.k;
@@ -195,10 +215,9 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   void* O = at<char>(ws, L.O);
   void* Hs = at<char>(ws, L.Hs);
 
-  // routed gate/up + SwiGLU: H[slot] = silu(x_t Wg^T) * (x_t Wu^T), x_t gathered by perm
-  GemmArgs g{};
-  g.act = d.act;
-  g.epi = EPI_SWIGLU;
+  // routed gate/up + SwiGLU: H[slot] = silu(x_t Wg^T) * (x_t Wu^T), x_t gathered by perm;
+  // shared gate/up + SwiGLU over every token, in the same launch.
+  GemmJob g{};
   g.A = x;
   g.lda = D;
   g.a_rows = routing->perm;
@@ -220,11 +239,35 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   g.ldc = F;
   g.aux = training ? at<char>(ws, L.AU) : nullptr;
   g.ldaux = 2LL * F;
-  launch_gemm(g, s);
+
+  GemmJob sg{};
+  sg.A = x;
+  sg.lda = D;
+  sg.a_div = 1;
+  sg.B = w->w_sh_gate_up;
+  sg.ldb = D;
+  sg.K = d.d;
+  sg.N = d.Fs;
+  sg.up_off = d.Fs;
+  sg.grouped = 0;
+  sg.M = d.T;
+  sg.max_items = (d.T + kTileM - 1) / kTileM;
+  sg.C = Hs;
+  sg.ldc = Fs;
+  sg.aux = training ? at<char>(ws, L.AUs) : nullptr;
+  sg.ldaux = 2LL * Fs;
+
+  GemmArgs ga{};
+  ga.act = d.act;
+  ga.epi = EPI_SWIGLU;
+  ga.njobs = 2;
+  ga.job[0] = g;
+  ga.job[1] = sg;
+  launch_gemm(ga, s);
+  mark_phase(2, s);
 
   // routed down, rows scaled by their routing weight: O[slot] = g * (H[slot] Wd^T)
-  GemmArgs dn = g;
-  dn.epi = EPI_ROWSCALE;
+  GemmJob dn = g;
   dn.A = H;
   dn.lda = F;
   dn.a_rows = nullptr;
@@ -241,32 +284,16 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   dn.ldaux = D;
   dn.gate = routing->gate;
   dn.perm = routing->perm;
-  launch_gemm(dn, s);
-
-  // shared gate/up + SwiGLU over every token
-  GemmArgs sg{};
-  sg.act = d.act;
-  sg.epi = EPI_SWIGLU;
-  sg.A = x;
-  sg.lda = D;
-  sg.a_div = 1;
-  sg.B = w->w_sh_gate_up;
-  sg.ldb = D;
-  sg.K = d.d;
-  sg.N = d.Fs;
-  sg.up_off = d.Fs;
-  sg.grouped = 0;
-  sg.M = d.T;
-  sg.max_items = (d.T + kTileM - 1) / kTileM;
-  sg.C = Hs;
-  sg.ldc = Fs;
-  sg.aux = training ? at<char>(ws, L.AUs) : nullptr;
-  sg.ldaux = 2LL * Fs;
-  launch_gemm(sg, s);
+  GemmArgs da{};
+  da.act = d.act;
+  da.epi = EPI_ROWSCALE;
+  da.njobs = 1;
+  da.job[0] = dn;
+  launch_gemm(da, s);
+  mark_phase(3, s);
 
   // shared down + combine: y[t] = Hs[t] Wsd^T + sum_j O[pos[t, j]]
-  GemmArgs sd = sg;
-  sd.epi = EPI_COMBINE;
+  GemmJob sd = sg;
   sd.A = Hs;
   sd.lda = Fs;
   sd.B = w->w_sh_down;
@@ -281,7 +308,13 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   sd.ldo = D;
   sd.pos = routing->pos;
   sd.k = d.k;
-  launch_gemm(sd, s);
+  GemmArgs ca{};
+  ca.act = d.act;
+  ca.epi = EPI_COMBINE;
+  ca.njobs = 1;
+  ca.job[0] = sd;
+  launch_gemm(ca, s);
+  mark_phase(4, s);
   return device_status();
 }
 

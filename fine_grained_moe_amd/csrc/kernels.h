@@ -6,8 +6,8 @@
 
 namespace fgmoe {
 
-// Tokens handled by one routing workgroup (4 waves x 16 tokens).
-constexpr int kRouteTokensPerBlock = 64;
+// Tokens handled by one routing workgroup (4 waves, one 16x16 logit tile each).
+constexpr int kRouteTokensPerBlock = 16;
 // Rows of one grouped-GEMM tile.
 constexpr int kTileM = 128;
 
@@ -27,11 +27,10 @@ void launch_bias_update(int E, long long total, const int32_t* counts, float gam
 
 enum Epilogue { EPI_SWIGLU = 0, EPI_ROWSCALE = 1, EPI_COMBINE = 2 };
 
-// C = A . B^T on MFMA with a fused epilogue.  All element offsets in elements.
-struct GemmArgs {
-  int act;                 // dtype of A, B, C, aux, O
-  int epi;                 // Epilogue
-  // A: rows of length >= K.  Row of output row `slot`: gather ? a_rows[slot] / a_div : slot.
+// One GEMM problem C = A . B^T on MFMA with a fused epilogue.  Element offsets
+// are in elements of the launch's dtype.
+struct GemmJob {
+  // A: rows of length >= K.  Row of output row `slot`: a_rows ? a_rows[slot] / a_div : slot.
   const void* A;
   long long lda;
   const int32_t* a_rows;
@@ -51,7 +50,7 @@ struct GemmArgs {
   const int32_t* tile_count;
   const int32_t* offsets;
   const int32_t* counts;
-  int max_items;
+  int max_items;           // upper bound of the item count (sizes the grid)
   // outputs
   void* C;
   long long ldc;
@@ -63,6 +62,15 @@ struct GemmArgs {
   long long ldo;
   const int32_t* pos;
   int k;
+};
+
+// A launch: one or two jobs sharing dtype and epilogue.
+struct GemmArgs {
+  int act;                 // dtype of A, B, C, aux, O
+  int epi;                 // Epilogue
+  int njobs;
+  int chunks[2];           // filled by launch_gemm
+  GemmJob job[2];
 };
 void launch_gemm(const GemmArgs& a, hipStream_t s);
 

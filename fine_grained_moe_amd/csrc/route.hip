@@ -12,14 +12,15 @@ namespace fgmoe {
 // ---------------------------------------------------------------------------
 // Router logits + sigmoid + bias + wave-level top-k + gates + block histogram.
 //
-// One wave owns 16 tokens.  Logits for 16 tokens x 64 experts are one MFMA
-// tile row (4 tiles of 16x16), accumulated over d in 128-byte chunks read
-// straight from HBM (x) and L2 (the 128 KiB router matrix).  The tile goes
-// through LDS so that each token's 64 logits sit one per lane; the top-k is k
-// rounds of a 64-lane max-reduction over (score+bias, 63-expert) keys, which
-// gives the larger key and, on an exact tie, the lower expert.  Gates are the
-// selected scores divided by their sum.  Per-block expert counts go to
-// block_counts (LDS integer atomics, so the counts are exact).
+// A workgroup owns 16 tokens; wave w computes their logits for experts
+// 16w..16w+15 as one 16x16 MFMA tile, accumulated over d in 128-byte chunks
+// read straight from HBM (x) and L2 (the 128 KiB router matrix).  The tile
+// goes through LDS so that each token's E logits sit one per lane; each wave
+// then selects for 4 tokens: k rounds of a 64-lane max-reduction over
+// (score + bias, 63 - expert) keys, which gives the larger key and, on an
+// exact tie, the lower expert.  Gates are the selected scores divided by
+// their sum.  Per-block expert counts go to block_counts (LDS integer
+// atomics, so the counts are exact).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void route_topk_kernel(const T* __restrict__ x, const T* __restrict__ wr,
@@ -27,90 +28,83 @@ __global__ __launch_bounds__(256) void route_topk_kernel(const T* __restrict__ x
                                                          int k, int32_t* __restrict__ idx,
                                                          float* __restrict__ gate,
                                                          int32_t* __restrict__ block_counts) {
-  __shared__ float lg[4][16][65];
+  __shared__ float lg[16][65];
   __shared__ int hist[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   if (tid < 64) hist[tid] = 0;
 
-  const int tok0 = blockIdx.x * kRouteTokensPerBlock + wave * 16;
-  const bool wave_active = tok0 < T_;
-  if (wave_active) {
-    const int t = tok0 + r;
-    const bool tok_ok = t < T_;
-    const char* xrow = reinterpret_cast<const char*>(x + (long long)(tok_ok ? t : 0) * d) + g * 32;
-    const char* wrow[4];
-    bool e_ok[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      const int e = ni * 16 + r;
-      e_ok[ni] = e < E;
-      wrow[ni] = reinterpret_cast<const char*>(wr + (long long)(e_ok[ni] ? e : 0) * d) + g * 32;
-    }
-    f32x4_t acc[4];
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int tok0 = blockIdx.x * kRouteTokensPerBlock;
+  if (wave * 16 < E) {
+    const int t = min(tok0 + r, T_ - 1);          // rows past T re-read the last token; never used
+    const int e = min(wave * 16 + r, E - 1);      // columns past E likewise
+    const char* xrow = reinterpret_cast<const char*>(x + (long long)t * d) + g * 32;
+    const char* wrow = reinterpret_cast<const char*>(wr + (long long)e * d) + g * 32;
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
     const int nch = (int)((long long)d * sizeof(T) / 128);
-    const u32x4_t z = {0u, 0u, 0u, 0u};
-    for (int c = 0; c < nch; ++c) {
-      Frag a;
-      a.lo = tok_ok ? ld16(xrow + c * 128) : z;
-      a.hi = tok_ok ? ld16(xrow + c * 128 + 16) : z;
+    // four chunks in flight: chunk c + 4 is requested as chunk c is multiplied
+    Frag a[4], b[4];
+    auto load = [&](int c, Frag& fa, Frag& fb) {
+      fa.lo = ld16(xrow + c * 128);
+      fa.hi = ld16(xrow + c * 128 + 16);
+      fb.lo = ld16(wrow + c * 128);
+      fb.hi = ld16(wrow + c * 128 + 16);
+    };
 #pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        Frag b;
-        b.lo = e_ok[ni] ? ld16(wrow[ni] + c * 128) : z;
-        b.hi = e_ok[ni] ? ld16(wrow[ni] + c * 128 + 16) : z;
-        acc[ni] = Mma<T>::run(a, b, acc[ni]);
+    for (int j = 0; j < 4; ++j)
+      if (j < nch) load(j, a[j], b[j]);
+    for (int c = 0; c < nch; c += 4) {
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        if (c + j < nch) {
+          acc = Mma<T>::run(a[j], b[j], acc);
+          if (c + j + 4 < nch) load(c + j + 4, a[j], b[j]);
+        }
       }
     }
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) lg[wave][4 * g + i][ni * 16 + r] = acc[ni][i];
+    for (int i = 0; i < 4; ++i) lg[4 * g + i][wave * 16 + r] = acc[i];
   }
   __syncthreads();
 
-  if (wave_active) {
-    const float b_e = lane < E ? bias[lane] : 0.f;
-    for (int tt = 0; tt < 16; ++tt) {
-      const int tok = tok0 + tt;
-      if (tok >= T_) break;
-      const float l = lg[wave][tt][lane];
-      const float s = 1.0f / (1.0f + expf(-l));
-      const float v = s + b_e;
-      bool taken = lane >= E;
-      int esel[8];
-      float ssel[8];
-      float ssum = 0.f;
+  const float b_e = lane < E ? bias[lane] : 0.f;
+  for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
+    const int tok = tok0 + tt;
+    if (tok >= T_) break;
+    const float l = lane < E ? lg[tt][lane] : 0.f;
+    const float s = 1.0f / (1.0f + expf(-l));
+    const float v = s + b_e;
+    bool taken = lane >= E;
+    int esel[8];
+    float ssel[8];
+    float ssum = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      uint32_t hi = taken ? 0u : float_key(v);
+      uint32_t lo = taken ? 0u : (uint32_t)(63 - lane);
+#pragma unroll
+      for (int off = 32; off >= 1; off >>= 1) {
+        const uint32_t ohi = __shfl_xor(hi, off);
+        const uint32_t olo = __shfl_xor(lo, off);
+        const bool take = (ohi > hi) || (ohi == hi && olo > lo);
+        hi = take ? ohi : hi;
+        lo = take ? olo : lo;
+      }
+      const int w = 63 - (int)lo;
+      const float sw = __shfl(s, w);
+      if (lane == w) taken = true;
+      esel[j] = w;
+      ssel[j] = sw;
+      ssum += sw;
+    }
+    if (lane == 0) {
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         if (j >= k) break;
-        uint32_t hi = taken ? 0u : float_key(v);
-        uint32_t lo = taken ? 0u : (uint32_t)(63 - lane);
-#pragma unroll
-        for (int off = 32; off >= 1; off >>= 1) {
-          const uint32_t ohi = __shfl_xor(hi, off);
-          const uint32_t olo = __shfl_xor(lo, off);
-          const bool take = (ohi > hi) || (ohi == hi && olo > lo);
-          hi = take ? ohi : hi;
-          lo = take ? olo : lo;
-        }
-        const int w = 63 - (int)lo;
-        const float sw = __shfl(s, w);
-        if (lane == w) taken = true;
-        esel[j] = w;
-        ssel[j] = sw;
-        ssum += sw;
-      }
-      if (lane == 0) {
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          if (j >= k) break;
-          idx[(long long)tok * k + j] = esel[j];
-          gate[(long long)tok * k + j] = ssel[j] / ssum;
-          atomicAdd(&hist[esel[j]], 1);
-        }
+        idx[(long long)tok * k + j] = esel[j];
+        gate[(long long)tok * k + j] = ssel[j] / ssum;
+        atomicAdd(&hist[esel[j]], 1);
       }
     }
   }
@@ -139,8 +133,10 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   const int chunk = (nblk + 15) / 16;
   const int b0 = min(nblk, part * chunk), b1 = min(nblk, b0 + chunk);
   int s = 0;
-  if (e < E)
+  if (e < E) {
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) s += block_counts[(long long)b * E + e];
+  }
   part_sum[part][e] = s;
   __syncthreads();
   if (part == 0) {
@@ -178,6 +174,7 @@ __global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restr
   __syncthreads();
   if (e < E) {
     int run = off_s[e] + part_pre[part][e];
+#pragma unroll 8
     for (int b = b0; b < b1; ++b) {
       block_base[(long long)b * E + e] = run;
       run += block_counts[(long long)b * E + e];
@@ -247,7 +244,7 @@ void launch_route_scatter(const int32_t* idx, const int32_t* block_base, int T, 
                           int32_t* pos, hipStream_t s) {
   const int nblk = route_blocks(T);
   if (nblk == 0) return;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(256), 0, s, idx, block_base, T, E, k, perm, pos);
+  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(128), 0, s, idx, block_base, T, E, k, perm, pos);
 }
 
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s) {

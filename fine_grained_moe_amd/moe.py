@@ -70,6 +70,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_backward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P, P,
                                  ctypes.POINTER(MoeGrads), P, SZ, P]
     lib.moe_backward.restype = ctypes.c_int
+    lib.moe_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
+    lib.moe_set_phase_events.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     return lib
@@ -146,6 +148,15 @@ def moe_backward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], routing: Di
     _check(LIB.moe_backward(ctypes.byref(dims), _ptr(x), ctypes.byref(w), ctypes.byref(r), _ptr(dy), _ptr(dx),
                             ctypes.byref(g), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_backward")
+
+
+def moe_set_phase_events(events) -> None:
+    """events: sequence of raw hipEvent_t handles (ints), or None to stop recording."""
+    if not events:
+        _check(LIB.moe_set_phase_events(None, 0), "moe_set_phase_events")
+        return
+    arr = (ctypes.c_void_p * len(events))(*[int(e) for e in events])
+    _check(LIB.moe_set_phase_events(arr, len(events)), "moe_set_phase_events")
 
 
 # ---------------------------------------------------------------- allocation helpers

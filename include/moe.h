@@ -147,6 +147,17 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
                         const moe_routing* routing, const void* dy, void* dx, const moe_grads* dw,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* Instrumentation, not part of the layer.  Registers n (0..8) hipEvent_t
+ * handles, passed as void*, that every later moe_forward records on its
+ * stream at its phase boundaries:
+ *   0 before the router, 1 after routing and dispatch bookkeeping,
+ *   2 after the gate/up launch (routed and shared experts together),
+ *   3 after the routed down GEMM, 4 after the shared down GEMM + combine.
+ * Boundaries beyond n are not recorded; n = 0 (or events = NULL) turns the
+ * recording off.  The registration is process-wide: do not change it while
+ * another thread is inside moe_forward.  The caller owns the events. */
+moe_status moe_set_phase_events(void* const* events, int32_t n);
+
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_str(moe_status s);
 

@@ -28,7 +28,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward",
-                                           "moe_bias_update", "moe_backward", "moe_status_str"])
+                                           "moe_bias_update", "moe_backward", "moe_status_str",
+                                           "moe_set_phase_events"])
 
 
 def test_library_exports_every_declared_symbol(lib):
