@@ -29,12 +29,12 @@ METRIC = "MoE-layer tokens/sec (d=1024,E=64,top-2,bf16) + % MFMA peak / % HBM BW
 PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
 PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
 GAMMA = 1e-3
-PHASES = ("route", "gate_up", "routed_down", "shared_down_combine")
+PHASES = ("route", "gate_up", "down", "combine")
 KERNEL_OF_PHASE = {
-    "gate_up": "gemm_kernel<bf16, SWIGLU> (routed + shared experts, one launch)",
-    "routed_down": "gemm_kernel<bf16, ROWSCALE>",
-    "shared_down_combine": "gemm_kernel<bf16, COMBINE>",
     "route": "route_topk + route_scan + route_scatter",
+    "gate_up": "gemm_kernel<bf16, SwiGLU> (routed + shared gate/up, one launch)",
+    "down": "gemm_kernel<bf16> (routed down with gate scaling + shared down, one launch)",
+    "combine": "combine_kernel<bf16>",
 }
 
 
@@ -53,10 +53,10 @@ def algorithmic_work(T, d, E, F, Fs, k, es=2):
     w["gate_up"] = dict(flops=2.0 * slots * 2 * F * d + 2.0 * T * 2 * Fs * d,
                         bytes=E * 2 * F * d * es + 2 * Fs * d * es + T * d * es + slots * F * es
                         + T * Fs * es + slots * 4)
-    w["routed_down"] = dict(flops=2.0 * slots * d * F,
-                            bytes=E * d * F * es + slots * F * es + slots * d * es + slots * 8)
-    w["shared_down_combine"] = dict(flops=2.0 * T * d * Fs,
-                                    bytes=d * Fs * es + T * Fs * es + slots * d * es + T * d * es + slots * 4)
+    w["down"] = dict(flops=2.0 * slots * d * F + 2.0 * T * d * Fs,
+                     bytes=E * d * F * es + d * Fs * es + slots * F * es + T * Fs * es + slots * d * es
+                     + T * d * es + slots * 8)
+    w["combine"] = dict(flops=float(slots * d), bytes=T * d * es + slots * d * es + T * d * es + slots * 4)
     for v in w.values():
         t_mfma = v["flops"] / PEAK_BF16_FLOPS
         t_hbm = v["bytes"] / PEAK_HBM_BPS

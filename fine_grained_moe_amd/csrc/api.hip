@@ -22,7 +22,7 @@ size_t act_bytes(int act) { return act == MOE_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
   size_t block_counts, block_base, tile_e, tile_m0, tile_count;
-  size_t H, O, Hs;        // forward intermediates
+  size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
   size_t total;
 };
@@ -58,6 +58,7 @@ Layout make_layout(const moe_dims& d, int training) {
   L.H = take(slots * d.F * es);
   L.O = take(slots * d.d * es);
   L.Hs = take((size_t)d.T * d.Fs * es);
+  L.S = take((size_t)d.T * d.d * es);
   if (training) {
     L.AU = take(slots * 2 * d.F * es);
     L.Ou = take(slots * d.d * es);
@@ -214,10 +215,12 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   void* H = at<char>(ws, L.H);
   void* O = at<char>(ws, L.O);
   void* Hs = at<char>(ws, L.Hs);
+  void* S = at<char>(ws, L.S);
 
-  // routed gate/up + SwiGLU: H[slot] = silu(x_t Wg^T) * (x_t Wu^T), x_t gathered by perm;
-  // shared gate/up + SwiGLU over every token, in the same launch.
+  // Launch 1: routed gate/up + SwiGLU (H[slot] = silu(x_t Wg^T) * (x_t Wu^T),
+  // x_t gathered by perm) and shared gate/up + SwiGLU over every token.
   GemmJob g{};
+  g.epi = EPI_SWIGLU;
   g.A = x;
   g.lda = D;
   g.a_rows = routing->perm;
@@ -241,6 +244,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   g.ldaux = 2LL * F;
 
   GemmJob sg{};
+  sg.epi = EPI_SWIGLU;
   sg.A = x;
   sg.lda = D;
   sg.a_div = 1;
@@ -259,15 +263,16 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
 
   GemmArgs ga{};
   ga.act = d.act;
-  ga.epi = EPI_SWIGLU;
   ga.njobs = 2;
   ga.job[0] = g;
   ga.job[1] = sg;
   launch_gemm(ga, s);
   mark_phase(2, s);
 
-  // routed down, rows scaled by their routing weight: O[slot] = g * (H[slot] Wd^T)
+  // Launch 2: routed down, rows scaled by their routing weight
+  // (O[slot] = g * (H[slot] Wd^T)), and shared down (S = Hs Wsd^T).
   GemmJob dn = g;
+  dn.epi = EPI_ROWSCALE;
   dn.A = H;
   dn.lda = F;
   dn.a_rows = nullptr;
@@ -284,16 +289,9 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   dn.ldaux = D;
   dn.gate = routing->gate;
   dn.perm = routing->perm;
-  GemmArgs da{};
-  da.act = d.act;
-  da.epi = EPI_ROWSCALE;
-  da.njobs = 1;
-  da.job[0] = dn;
-  launch_gemm(da, s);
-  mark_phase(3, s);
 
-  // shared down + combine: y[t] = Hs[t] Wsd^T + sum_j O[pos[t, j]]
   GemmJob sd = sg;
+  sd.epi = EPI_STORE;
   sd.A = Hs;
   sd.lda = Fs;
   sd.B = w->w_sh_down;
@@ -301,19 +299,20 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   sd.K = d.Fs;
   sd.N = d.d;
   sd.up_off = 0;
-  sd.C = y;
+  sd.C = S;
   sd.ldc = D;
   sd.aux = nullptr;
-  sd.O = O;
-  sd.ldo = D;
-  sd.pos = routing->pos;
-  sd.k = d.k;
-  GemmArgs ca{};
-  ca.act = d.act;
-  ca.epi = EPI_COMBINE;
-  ca.njobs = 1;
-  ca.job[0] = sd;
-  launch_gemm(ca, s);
+
+  GemmArgs da{};
+  da.act = d.act;
+  da.njobs = 2;
+  da.job[0] = dn;
+  da.job[1] = sd;
+  launch_gemm(da, s);
+  mark_phase(3, s);
+
+  // combine: y[t] = S[t] + sum_j O[pos[t, j]]
+  launch_combine(d.act, S, O, routing->pos, d.T, d.d, d.k, y, s);
   mark_phase(4, s);
   return device_status();
 }

@@ -45,6 +45,11 @@ struct Frag {
 template <typename T> struct Mma;
 
 template <> struct Mma<bf16_t> {
+  // one 16-byte piece per lane: 8 consecutive K of the lane group's slice
+  static __device__ __forceinline__ f32x4_t run1(u32x4_t a, u32x4_t b, f32x4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a), __builtin_bit_cast(bf16x8_t, b), c,
+                                                   0, 0, 0);
+  }
   static __device__ __forceinline__ f32x4_t run(const Frag& a, const Frag& b, f32x4_t c) {
     c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, a.lo),
                                                __builtin_bit_cast(bf16x8_t, b.lo), c, 0, 0, 0);
@@ -55,6 +60,12 @@ template <> struct Mma<bf16_t> {
 };
 
 template <> struct Mma<float> {
+  static __device__ __forceinline__ f32x4_t run1(u32x4_t a, u32x4_t b, f32x4_t c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[i]), __uint_as_float(b[i]), c, 0, 0, 0);
+    return c;
+  }
   static __device__ __forceinline__ f32x4_t run(const Frag& a, const Frag& b, f32x4_t c) {
 #pragma unroll
     for (int i = 0; i < 4; ++i)

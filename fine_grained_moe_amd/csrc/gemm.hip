@@ -5,13 +5,13 @@
 //                    dispatch order, SwiGLU epilogue -> H)
 //   routed down     (grouped, rows scaled by their routing weight -> O)
 //   shared gate/up  (dense, SwiGLU epilogue -> Hs)
-//   shared down     (dense, epilogue adds the token's k routed rows of O -> y)
+//   shared down     (dense, plain store -> S)
 // The experts are the SwiGLU FFNs of widths 512 (routed) and 2048 (shared) of
 // the seventnews article "A relay race of rented GPUs trained NanoColibri's
-// 2.7B MoE for $200" (opening section, architecture paragraph).  A launch may
-// carry two jobs with the same epilogue (the routed and the shared gate/up):
-// their workgroups are interleaved, so the weight-streaming routed tiles and
-// the MFMA-bound shared tiles share the chip.
+// 2.7B MoE for $200" (opening section, architecture paragraph).  A launch
+// carries two jobs with the same B layout (the two gate/up GEMMs, or the two
+// down GEMMs): their workgroups are interleaved, so the weight-streaming
+// routed tiles and the MFMA-bound shared tiles share the chip.
 //
 // Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a 128 x 128 tile;
 // each wave owns 64 x 64 = 4 x 4 MFMA 16x16 tiles.  K advances in 128-byte
@@ -39,17 +39,51 @@ namespace fgmoe {
 namespace {
 
 constexpr int BM = 128, BN = 128, NTHR = 256;
-constexpr int ROWB = 128;                    // bytes of one row per K stage
-constexpr int TILEB = BM * ROWB;             // bytes of one operand tile per stage
+#ifndef FGMOE_GEMM_ROWB
+#define FGMOE_GEMM_ROWB 128
+#endif
+#ifndef FGMOE_GEMM_STAGES
+#define FGMOE_GEMM_STAGES 2
+#endif
+constexpr int kRowB = FGMOE_GEMM_ROWB;       // bytes of one operand row per K stage (64 or 128)
+constexpr int kStages = FGMOE_GEMM_STAGES;   // LDS ring depth: kStages * 2 * 128 * kRowB bytes
 
-// Piece p of LDS row r sits at piece p ^ (r & 7) ^ ((r >> 3) & 1): measured on
-// gfx950, 16 consecutive rows read at one piece index then hit distinct banks.
+// LDS swizzle of 16-byte pieces.  gfx950 serves a 16-byte-per-lane LDS read
+// 32 lanes at a time over 128 four-byte banks (fitted to measured
+// SQ_LDS_BANK_CONFLICT counts of probe access patterns).  An MFMA operand read
+// has 16 consecutive rows x 2 piece indices per half-wave; these XORs make
+// those 32 pieces hit 32 distinct bank groups.
+template <int ROWB>
+__device__ __forceinline__ int swz_piece(int row, int piece) {
+  if constexpr (ROWB == 128) return piece ^ (row & 7) ^ ((row >> 3) & 1);
+  else return piece ^ (((row >> 3) & 1) << 1);
+}
+template <int ROWB>
 __device__ __forceinline__ int swz(int row, int piece) {
-  return row * ROWB + ((piece ^ (row & 7) ^ ((row >> 3) & 1)) << 4);
+  return row * ROWB + (swz_piece<ROWB>(row, piece) << 4);
 }
 
-template <int EPI> __device__ __forceinline__ int n_tiles(const GemmJob& j) {
-  return EPI == EPI_SWIGLU ? j.N / 64 : j.N / BN;
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
+// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// Workgroup barrier without the memory fences of __syncthreads: the direct
+// LDS loads are waited for explicitly with wait_vmcnt.  The empty asm keeps
+// the compiler from moving memory accesses across it.
+__device__ __forceinline__ void block_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+__device__ __host__ __forceinline__ int n_tiles(const GemmJob& j) {
+  return j.epi == EPI_SWIGLU ? j.N / 64 : j.N / BN;
 }
 __device__ __forceinline__ int item_count(const GemmJob& j) {
   return j.grouped ? *j.tile_count : (j.M + BM - 1) / BM;
@@ -70,26 +104,17 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[N]) {
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void load_add4(const T* p, float (&v)[4]) {
-  if constexpr (sizeof(T) == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    v[0] += bf16_to_f32((bf16_t)(w.x & 0xFFFF));
-    v[1] += bf16_to_f32((bf16_t)(w.x >> 16));
-    v[2] += bf16_to_f32((bf16_t)(w.y & 0xFFFF));
-    v[3] += bf16_to_f32((bf16_t)(w.y >> 16));
-  } else {
-    const float4 w = *reinterpret_cast<const float4*>(p);
-    v[0] += w.x;
-    v[1] += w.y;
-    v[2] += w.z;
-    v[3] += w.w;
-  }
-}
-
-template <typename T, int EPI>
+template <typename T, bool SWIGLU, int NS>
 __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) char lds[2 * 2 * TILEB];
+  constexpr int EPI = SWIGLU ? EPI_SWIGLU : EPI_ROWSCALE;   // B-row layout class
+  // (the row width is a namespace constant: as a kernel template parameter it
+  // made this compiler drop the host-side launch stubs)
+  constexpr int ROWB = kRowB;
+  constexpr int TILEB = BM * ROWB;                          // one operand tile of one stage
+  constexpr int PIECES = ROWB / 16;                         // 16-byte pieces per row and stage
+  constexpr int ROWS_PER_DMA = 1024 / ROWB;                 // LDS rows one wave instruction fills
+  constexpr int NDMA = 32 / ROWS_PER_DMA;                   // instructions per wave per operand
+  __shared__ __attribute__((aligned(16))) char lds[NS * 2 * TILEB];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -113,7 +138,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   // ---- work item and N tile
   const int count = item_count(p);
   const int q = (count + 7) >> 3;
-  const int nbn = n_tiles<EPI>(p);
+  const int nbn = n_tiles(p);
   const int xcd = bid & 7, local = bid >> 3;
   int pi, nt;
   if (p.grouped) {
@@ -140,58 +165,50 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   }
   rows = rows < BM ? rows : BM;
 
-  // ---- global -> LDS assignment: thread writes 16-byte piece c16 of LDS rows
-  // r0 + 32 i.  A rows past the item's end re-read its last row: MFMA row r of
-  // the result depends only on A row r, and those rows are never stored.
-  const int c16 = tid & 7, r0 = tid >> 3;
-  const char* a_ptr[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int r = min(r0 + 32 * i, rows - 1);
-    const long long arow = p.a_rows ? (long long)(p.a_rows[row_base + r] / p.a_div) : (long long)(row_base + r);
-    a_ptr[i] = reinterpret_cast<const char*>(p.A) + (arow * p.lda) * (long long)sizeof(T) + c16 * 16;
-  }
-  // LDS B row rho = base + 16 ni + f holds weight row base' + S f + ni (S = 2
-  // for SwiGLU halves, 4 otherwise), so lane f's MFMA columns are adjacent
-  // output columns.
+  // ---- global -> LDS: direct loads (global_load_lds_dwordx4).  Lane i of a
+  // wave instruction lands at LDS byte base + 16 i, so instruction j of wave w
+  // fills LDS rows w*32 + j*ROWS_PER_DMA + i/PIECES at physical piece
+  // i%PIECES; the lane fetches the logical piece the swizzle puts there.  A
+  // rows past the item's end re-read its last row: MFMA row r of the result
+  // depends only on A row r, and those rows are never stored.
+  const int prow = lane / PIECES, ppc = lane % PIECES;
+  const char* a_src[NDMA];
+  const char* b_src[NDMA];
   const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)e * p.b_estride * (long long)sizeof(T);
-  const char* b_ptr[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int rho = r0 + 32 * i;
+  for (int j = 0; j < NDMA; ++j) {
+    const int R = wave * 32 + j * ROWS_PER_DMA + prow;
+    const int c = swz_piece<ROWB>(R, ppc);            // XOR swizzles are their own inverse
+    const int ra = min(R, rows - 1);
+    const long long arow = p.a_rows ? (long long)(p.a_rows[row_base + ra] / p.a_div) : (long long)(row_base + ra);
+    a_src[j] = reinterpret_cast<const char*>(p.A) + (arow * p.lda) * (long long)sizeof(T) + c * 16;
+    // LDS B row rho = base + 16 ni + f holds weight row base' + S f + ni (S = 2
+    // for SwiGLU halves, 4 otherwise), so lane f's MFMA columns are adjacent
+    // output columns.
     long long brow;
     if (EPI == EPI_SWIGLU) {
-      const int h = rho & 63, half = rho >> 6;            // gate block, then up block
+      const int h = R & 63, half = R >> 6;           // gate block, then up block
       const int w32 = h >> 5, ni = (h >> 4) & 1, f = h & 15;
       brow = (long long)(half ? p.up_off : 0) + nt * 64 + w32 * 32 + 2 * f + ni;
     } else {
-      const int w64 = rho >> 6, ni = (rho >> 4) & 3, f = rho & 15;
+      const int w64 = R >> 6, ni = (R >> 4) & 3, f = R & 15;
       brow = (long long)nt * BN + w64 * 64 + 4 * f + ni;
     }
-    b_ptr[i] = bbase + brow * p.ldb * (long long)sizeof(T) + c16 * 16;
+    b_src[j] = bbase + brow * p.ldb * (long long)sizeof(T) + c * 16;
   }
 
   const int nk = (int)((long long)p.K * sizeof(T) / ROWB);
-  // Two register sets: stage s+2 is requested while stage s is multiplied and
-  // stage s+1 waits in registers for its LDS buffer.
-  u32x4_t ra[2][4], rb[2][4];
-  auto gload = [&](int s, u32x4_t (&da)[4], u32x4_t (&db)[4]) {
+  // Stage s lives in LDS buffer s % NS; NS - 1 stages are in flight while one
+  // is multiplied.  A stage is 2 * NDMA loads per lane.
+  auto issue = [&](int s) {
+    char* base = lds + (s % NS) * 2 * TILEB + wave * 32 * ROWB;
     const long long off = (long long)s * ROWB;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      da[i] = ld16(a_ptr[i] + off);
-      db[i] = ld16(b_ptr[i] + off);
-    }
-  };
-  auto lstore = [&](int buf, const u32x4_t (&da)[4], const u32x4_t (&db)[4]) {
-    char* As = lds + buf * 2 * TILEB;
-    char* Bs = As + TILEB;
+    for (int j = 0; j < NDMA; ++j)
+      __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(base + j * 1024), 16, 0, 0);
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int r = r0 + 32 * i;
-      st16(As + swz(r, c16), da[i]);
-      st16(Bs + swz(r, c16), db[i]);
-    }
+    for (int j = 0; j < NDMA; ++j)
+      __builtin_amdgcn_global_load_lds(b_src[j] + off, (lds_ptr_t)(base + TILEB + j * 1024), 16, 0, 0);
   };
 
   // ---- LDS -> MFMA operand rows for this wave (16 consecutive LDS rows per tile)
@@ -216,41 +233,48 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   auto compute = [&](int buf) {
     const char* As = lds + buf * 2 * TILEB;
     const char* Bs = As + TILEB;
-    Frag fa[4], fb[4];
+    if constexpr (ROWB == 128) {
+      Frag fa[4], fb[4];
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) {
-      fa[mi].lo = ld16(As + swz(arow_l[mi], 2 * g));
-      fa[mi].hi = ld16(As + swz(arow_l[mi], 2 * g + 1));
+      for (int mi = 0; mi < 4; ++mi) {
+        fa[mi].lo = ld16(As + swz<ROWB>(arow_l[mi], 2 * g));
+        fa[mi].hi = ld16(As + swz<ROWB>(arow_l[mi], 2 * g + 1));
+      }
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) {
+        fb[ni].lo = ld16(Bs + swz<ROWB>(brow_l[ni], 2 * g));
+        fb[ni].hi = ld16(Bs + swz<ROWB>(brow_l[ni], 2 * g + 1));
+      }
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = Mma<T>::run(fa[mi], fb[ni], acc[mi][ni]);
+    } else {
+      u32x4_t fa[4], fb[4];
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) fa[mi] = ld16(As + swz<ROWB>(arow_l[mi], g));
+#pragma unroll
+      for (int ni = 0; ni < 4; ++ni) fb[ni] = ld16(Bs + swz<ROWB>(brow_l[ni], g));
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = Mma<T>::run1(fa[mi], fb[ni], acc[mi][ni]);
     }
-#pragma unroll
-    for (int ni = 0; ni < 4; ++ni) {
-      fb[ni].lo = ld16(Bs + swz(brow_l[ni], 2 * g));
-      fb[ni].hi = ld16(Bs + swz(brow_l[ni], 2 * g + 1));
-    }
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = Mma<T>::run(fa[mi], fb[ni], acc[mi][ni]);
   };
 
-  gload(0, ra[0], rb[0]);
-  if (nk > 1) gload(1, ra[1], rb[1]);
-  lstore(0, ra[0], rb[0]);
-  __syncthreads();
-  // Unrolled by two so that every register-set index is a constant.
-  for (int s = 0; s < nk; s += 2) {
-    if (s + 2 < nk) gload(s + 2, ra[0], rb[0]);
-    compute(0);
-    if (s + 1 < nk) lstore(1, ra[1], rb[1]);
-    __syncthreads();
-    if (s + 1 >= nk) break;
-    if (s + 3 < nk) gload(s + 3, ra[1], rb[1]);
-    compute(1);
-    if (s + 2 < nk) lstore(0, ra[0], rb[0]);
-    __syncthreads();
+  for (int s = 0; s < NS - 1 && s < nk; ++s) issue(s);
+  for (int s = 0; s < nk; ++s) {
+    // This wave's loads of stage s are done once at most the later stages'
+    // loads are outstanding; the barrier then covers every wave's loads and
+    // every wave's reads of the buffer about to be refilled.
+    if (s + NS - 2 < nk) wait_vmcnt<2 * NDMA * (NS - 2)>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    if (s + NS - 1 < nk) issue(s + NS - 1);
+    compute(s % NS);
   }
 
-  // ---- epilogue.  acc[mi][ni][i] is row wm*64 + mi*16 + 4g + i; its column
+  // ---- epilogue (per job).  acc[mi][ni][i] is row wm*64 + mi*16 + 4g + i; its column
   // is 2f + ni (SwiGLU, ni < 2 gate / ni >= 2 the matching up) or 4f + ni
   // past the wave's column base.
   T* C = reinterpret_cast<T*>(p.C);
@@ -276,7 +300,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
           store_vec<T, 2>(aux + row * p.ldaux + f, a);
           store_vec<T, 2>(aux + row * p.ldaux + p.N + f, u);
         }
-      } else if (EPI == EPI_ROWSCALE) {
+      } else if (p.epi == EPI_ROWSCALE) {
         const int n = nt * BN + wn * 64 + 4 * fr;
         const float sc = p.gate[p.perm[row]];
         float v[4], raw[4];
@@ -287,21 +311,19 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
         }
         store_vec<T, 4>(C + row * p.ldc + n, v);
         if (aux) store_vec<T, 4>(aux + row * p.ldaux + n, raw);
-      } else {  // EPI_COMBINE: row is a token
+      } else {  // EPI_STORE
         const int n = nt * BN + wn * 64 + 4 * fr;
-        const T* O = reinterpret_cast<const T*>(p.O);
         float v[4];
 #pragma unroll
         for (int ni = 0; ni < 4; ++ni) v[ni] = acc[mi][ni][i];
-        for (int j = 0; j < p.k; ++j) load_add4<T>(O + (long long)p.pos[row * p.k + j] * p.ldo + n, v);
         store_vec<T, 4>(C + row * p.ldc + n, v);
       }
     }
   }
 }
 
-int job_chunks(const GemmJob& j, int epi) {
-  const int nbn = epi == EPI_SWIGLU ? j.N / 64 : j.N / BN;
+int job_chunks(const GemmJob& j) {
+  const int nbn = n_tiles(j);
   const long long groups = (j.max_items + 7) / 8;
   return (int)(groups * nbn);
 }
@@ -310,16 +332,15 @@ template <typename T>
 void launch_dtype(GemmArgs a, hipStream_t s) {
   long long total = 0;
   for (int i = 0; i < a.njobs; ++i) {
-    a.chunks[i] = job_chunks(a.job[i], a.epi);
+    a.chunks[i] = job_chunks(a.job[i]);
     total += a.chunks[i];
   }
   if (total == 0) return;
   const dim3 grid((unsigned)(total * 8));
-  switch (a.epi) {
-    case EPI_SWIGLU: hipLaunchKernelGGL((gemm_kernel<T, EPI_SWIGLU>), grid, dim3(NTHR), 0, s, a); break;
-    case EPI_ROWSCALE: hipLaunchKernelGGL((gemm_kernel<T, EPI_ROWSCALE>), grid, dim3(NTHR), 0, s, a); break;
-    default: hipLaunchKernelGGL((gemm_kernel<T, EPI_COMBINE>), grid, dim3(NTHR), 0, s, a); break;
-  }
+  if (a.job[0].epi == EPI_SWIGLU)
+    hipLaunchKernelGGL((gemm_kernel<T, true, kStages>), grid, dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm_kernel<T, false, kStages>), grid, dim3(NTHR), 0, s, a);
 }
 
 }  // namespace

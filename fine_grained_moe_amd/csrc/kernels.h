@@ -25,11 +25,12 @@ void launch_route_scatter(const int32_t* idx, const int32_t* block_base, int T, 
                           int32_t* pos, hipStream_t s);
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s);
 
-enum Epilogue { EPI_SWIGLU = 0, EPI_ROWSCALE = 1, EPI_COMBINE = 2 };
+enum Epilogue { EPI_SWIGLU = 0, EPI_ROWSCALE = 1, EPI_STORE = 2 };
 
 // One GEMM problem C = A . B^T on MFMA with a fused epilogue.  Element offsets
 // are in elements of the launch's dtype.
 struct GemmJob {
+  int epi;                 // Epilogue; both jobs of a launch are SwiGLU or both are not
   // A: rows of length >= K.  Row of output row `slot`: a_rows ? a_rows[slot] / a_div : slot.
   const void* A;
   long long lda;
@@ -58,20 +59,19 @@ struct GemmJob {
   long long ldaux;
   const float* gate;       // ROWSCALE: row scale gate[perm[slot]]
   const int32_t* perm;
-  const void* O;           // COMBINE: y[t] = acc + sum_j O[pos[t*k+j]]
-  long long ldo;
-  const int32_t* pos;
-  int k;
 };
 
-// A launch: one or two jobs sharing dtype and epilogue.
+// A launch: one or two jobs sharing the dtype.
 struct GemmArgs {
-  int act;                 // dtype of A, B, C, aux, O
-  int epi;                 // Epilogue
+  int act;                 // dtype of A, B, C, aux
   int njobs;
   int chunks[2];           // filled by launch_gemm
   GemmJob job[2];
 };
 void launch_gemm(const GemmArgs& a, hipStream_t s);
+
+// y[t] = S[t] + sum_j O[pos[t*k + j]] in fixed j order, rounded once.
+void launch_combine(int act, const void* S, const void* O, const int32_t* pos, int T, int d, int k, void* y,
+                    hipStream_t s);
 
 }  // namespace fgmoe

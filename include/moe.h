@@ -152,7 +152,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
  * stream at its phase boundaries:
  *   0 before the router, 1 after routing and dispatch bookkeeping,
  *   2 after the gate/up launch (routed and shared experts together),
- *   3 after the routed down GEMM, 4 after the shared down GEMM + combine.
+ *   3 after the down launch (routed and shared together), 4 after the combine.
  * Boundaries beyond n are not recorded; n = 0 (or events = NULL) turns the
  * recording off.  The registration is process-wide: do not change it while
  * another thread is inside moe_forward.  The caller owns the events. */

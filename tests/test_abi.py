@@ -108,3 +108,12 @@ def test_int4_requires_top1_bf16(lib):
     for act, k in (("f32", 1), ("bf16", 2)):
         d = lib.make_dims(8, 1024, 64, 512, 2048, k, act, w_routed="int4")
         assert lib.moe_workspace_bytes(d) == 0
+
+
+def test_library_has_no_undefined_kernel_stubs():
+    """Every kernel the library launches is defined in it (a host-side launch
+    stub left undefined only fails when the library is loaded on a GPU machine)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", LIBPATH], stdout=subprocess.PIPE, text=True).stdout
+    undefined = [l for l in out.splitlines() if " U " in l and "fgmoe" in l]
+    assert not undefined, undefined
