@@ -91,6 +91,54 @@ class HipEvents:
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
 
 
+def decode_bytes(T, d, E, F, Fs, unique_experts):
+    """Algorithmic HBM bytes of one top-1 int4 serving forward: the router and
+    the shared expert (bf16), each routed expert a token uses once (packed
+    int4 + bf16 scales), activations in and out."""
+    per_expert = 2 * F * d // 2 + 2 * F * (d // 128) * 2 + d * F // 2 + d * (F // 128) * 2
+    return E * d * 2 + 3 * Fs * d * 2 + unique_experts * per_expert + 2 * T * d * 2
+
+
+def bench_decode(moe, synth, torch, np, n_layers=23, iters=46):
+    """Top-1 int4 serving forward at T = 1, 8, 64, cycling 23 distinct weight
+    copies (one per MoE layer of the model) so every forward reads its
+    weights from HBM."""
+    E, d, F, Fs = 64, 1024, 512, 2048
+    base = synth.make_layer(T=64, d=d, E=E, F=F, Fs=Fs, k=1, act="bf16", seed=11)
+    qg, sg = synth.random_int4(E, 2 * F, d, seed=11)
+    qd, sd = synth.random_int4(E, d, F, seed=12)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+    w0 = dict(w_router=bf(base.w_router), w_gate_up=torch.from_numpy(qg).cuda(), s_gate_up=bf(sg),
+              w_down=torch.from_numpy(qd).cuda(), s_down=bf(sd), w_sh_gate_up=bf(base.w_sh_gate_up),
+              w_sh_down=bf(base.w_sh_down))
+    layers = [w0] + [{n: t.clone() for n, t in w0.items()} for _ in range(n_layers - 1)]
+    bias = torch.zeros(E, device="cuda")
+    out = {}
+    for T in (1, 8, 64):
+        dims = moe.make_dims(T, d, E, F, Fs, 1, "bf16", w_routed="int4")
+        x = bf(base.x[:T])
+        y = torch.empty_like(x)
+        r = moe.alloc_routing(dims)
+        ws = moe.alloc_workspace(dims)
+        for i in range(n_layers):
+            moe.moe_forward(dims, x, layers[i], bias, y, r, ws)
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for i in range(iters):
+            moe.moe_forward(dims, x, layers[i % n_layers], bias, y, r, ws)
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / iters
+        uniq = int((r["counts"] > 0).sum().item())
+        nbytes = decode_bytes(T, d, E, F, Fs, uniq)
+        gbps = nbytes / (us * 1e-6) / 1e9
+        out[f"T{T}"] = dict(us=round(us, 2), unique_experts=uniq, bytes=nbytes, gbps=round(gbps, 1),
+                            frac_hbm=round(gbps / (PEAK_HBM_BPS / 1e9), 4))
+        log(f"decode T={T}: {us:.1f} us, {uniq} experts, {gbps:.0f} GB/s ({gbps / 8000:.1%} of HBM)")
+    return out
+
+
 def cpu_baseline(inp, seconds: float):
     """The CPU oracle as it stands, on this host's cores, over a bounded sample:
     whole copies of the benchmark batch until `seconds` have passed."""
@@ -123,6 +171,7 @@ def main() -> int:
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -231,6 +280,9 @@ def main() -> int:
         out["warm"] = dict(value=T * args.steps / el_w, ms_per_step=el_w / args.steps * 1e3,
                            phases_us={p: round(v, 2) for p, v in ph_w.items()})
         log(f"warm: {out['warm']['value'] / 1e6:.2f} M tokens/s")
+
+    if not args.no_decode:
+        out["decode"] = bench_decode(moe, synth, torch, np)
 
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")

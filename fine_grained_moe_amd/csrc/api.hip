@@ -24,6 +24,7 @@ struct Layout {
   size_t block_counts, block_base, tile_e, tile_m0, tile_count;
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
+  size_t active, n_active; // int4 serving path: experts with a non-zero load
   size_t total;
 };
 
@@ -34,7 +35,11 @@ moe_status check_dims(const moe_dims* d) {
   if (d->w_routed != d->act && d->w_routed != MOE_INT4_G128) return MOE_E_UNSUPPORTED;
   if (d->E > 64 || d->k > d->E || d->k > 8) return MOE_E_UNSUPPORTED;
   if (d->d % 128 || d->F % 64 || d->Fs % 64) return MOE_E_UNSUPPORTED;
-  if (d->w_routed == MOE_INT4_G128) return MOE_E_UNSUPPORTED;  // served by the decode path only
+  if (d->w_routed == MOE_INT4_G128) {
+    // top-1 serving path: bf16 activations, one expert per token, small batches
+    if (d->act != MOE_BF16 || d->k != 1 || d->T > kDecodeMaxT || !decode_shape_supported(d->d, d->F, d->Fs))
+      return MOE_E_UNSUPPORTED;
+  }
   const long long slots = (long long)d->T * d->k;
   const long long wide = std::max<long long>(d->d, 2LL * d->F);
   if (slots * wide >= (1LL << 31)) return MOE_E_UNSUPPORTED;
@@ -56,8 +61,14 @@ Layout make_layout(const moe_dims& d, int training) {
   L.tile_m0 = take(tiles * 4);
   L.tile_count = take(4);
   L.H = take(slots * d.F * es);
-  L.O = take(slots * d.d * es);
   L.Hs = take((size_t)d.T * d.Fs * es);
+  if (d.w_routed == MOE_INT4_G128) {
+    L.active = take((size_t)d.E * 3 * 4);
+    L.n_active = take(4);
+    L.total = o;
+    return L;
+  }
+  L.O = take(slots * d.d * es);
   L.S = take((size_t)d.T * d.d * es);
   if (training) {
     L.AU = take(slots * 2 * d.F * es);
@@ -181,11 +192,67 @@ moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, 
   return device_status();
 }
 
+// Top-1 serving with int4 routed experts.
+moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, const float* bias, void* y,
+                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s) {
+  if (training) return MOE_E_UNSUPPORTED;
+  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
+  std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
+                           {w->w_router, E * D * 2, false},
+                           {w->w_gate_up, E * 2 * F * D / 2, false},
+                           {w->s_gate_up, E * 2 * F * (D / 128) * 2, false},
+                           {w->w_down, E * D * F / 2, false},
+                           {w->s_down, E * D * (F / 128) * 2, false},
+                           {w->w_sh_gate_up, 2 * Fs * D * 2, false},
+                           {w->w_sh_down, D * Fs * 2, false},
+                           {bias, E * 4, false},
+                           {y, (size_t)d.T * D * 2, true}};
+  add_routing_ranges(rs, d, routing);
+  if (null_with_size(rs)) return MOE_E_ARG;
+  const Layout L = make_layout(d, 0);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  DecodeArgs a{};
+  a.T = d.T;
+  a.d = d.d;
+  a.E = d.E;
+  a.F = d.F;
+  a.Fs = d.Fs;
+  a.k = d.k;
+  a.x = (const uint16_t*)x;
+  a.w_router = (const uint16_t*)w->w_router;
+  a.bias = bias;
+  a.w_sh_gate_up = (const uint16_t*)w->w_sh_gate_up;
+  a.w_sh_down = (const uint16_t*)w->w_sh_down;
+  a.q_gate_up = (const uint8_t*)w->w_gate_up;
+  a.s_gate_up = (const uint16_t*)w->s_gate_up;
+  a.q_down = (const uint8_t*)w->w_down;
+  a.s_down = (const uint16_t*)w->s_down;
+  a.idx = routing->idx;
+  a.gate = routing->gate;
+  a.counts = routing->counts;
+  a.offsets = routing->offsets;
+  a.perm = routing->perm;
+  a.pos = routing->pos;
+  a.active = at<int32_t>(ws, L.active);
+  a.n_active = at<int32_t>(ws, L.n_active);
+  a.Hs = at<uint16_t>(ws, L.Hs);
+  a.H = at<uint16_t>(ws, L.H);
+  a.y = (uint16_t*)y;
+  mark_phase(0, s);
+  launch_decode(a, s);
+  mark_phase(1, s);
+  return device_status();
+}
+
 moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (!w || !routing) return MOE_E_ARG;
+  if (dims->w_routed == MOE_INT4_G128)
+    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
   const moe_dims& d = *dims;
   const size_t es = act_bytes(d.act);
   const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;

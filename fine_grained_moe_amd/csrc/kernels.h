@@ -70,6 +70,36 @@ struct GemmArgs {
 };
 void launch_gemm(const GemmArgs& a, hipStream_t s);
 
+// Top-1 serving with int4 routed experts, T <= 64 tokens (decode.hip), built
+// for the NanoColibri layer shape.
+constexpr int kDecodeMaxT = 64;
+constexpr int kDecodeD = 1024, kDecodeF = 512, kDecodeFs = 2048;
+bool decode_shape_supported(int d, int F, int Fs);
+struct DecodeArgs {
+  int T, d, E, F, Fs, k;
+  const uint16_t* x;                 // [T, d] bf16
+  const uint16_t* w_router;          // [E, d] bf16
+  const float* bias;                 // [E]
+  const uint16_t* w_sh_gate_up;      // [2Fs, d] bf16
+  const uint16_t* w_sh_down;         // [d, Fs] bf16
+  const uint8_t* q_gate_up;          // [E, 2F, d/2] int4 pairs
+  const uint16_t* s_gate_up;         // [E, 2F, d/128] bf16
+  const uint8_t* q_down;             // [E, d, F/2]
+  const uint16_t* s_down;            // [E, d, F/128]
+  int32_t* idx;
+  float* gate;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* perm;
+  int32_t* pos;
+  int32_t* active;                   // [E][3] (expert, first slot, load) of each expert with a load, ascending
+  int32_t* n_active;                 // [1]
+  uint16_t* Hs;                      // [T, Fs] bf16 (workspace)
+  uint16_t* H;                       // [T*k, F] bf16 (workspace)
+  uint16_t* y;                       // [T, d] bf16
+};
+void launch_decode(const DecodeArgs& a, hipStream_t s);
+
 // y[t] = S[t] + sum_j O[pos[t*k + j]] in fixed j order, rounded once.
 void launch_combine(int act, const void* S, const void* O, const int32_t* pos, int T, int d, int k, void* y,
                     hipStream_t s);

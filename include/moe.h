@@ -124,7 +124,9 @@ moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, 
  * bias: [E] float32, read only (moe_bias_update changes it).  routing: filled
  * as by moe_route.  training = 1 stores in ws what moe_backward needs.
  * With w_routed = MOE_INT4_G128 this is the top-1 serving path (k = 1,
- * gate = 1, int4 experts dequantised inside the kernels). */
+ * gate = 1, int4 experts dequantised inside the kernels), built for the
+ * NanoColibri shape (d = 1024, F = 512, Fs = 2048) and T <= 64; other shapes
+ * return MOE_E_UNSUPPORTED. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias,
                        void* y, const moe_routing* routing, int training,
                        void* ws, size_t ws_bytes, void* stream);
