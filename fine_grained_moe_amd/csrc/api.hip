@@ -24,6 +24,10 @@ struct Layout {
   size_t block_counts, block_base, tile_e, tile_m0, tile_count;
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
+  // backward scratch (training): padded contraction tables and transposed operands
+  size_t kofs, klen, ksh, pcol, dl, dAU, dAUT, XpT, dOT, HT, dXp, WdT, WguT, WsdT, WsguT, dAUs, dAUsT, xT, dyT, HsT,
+      dXs;
+  long long P, Tp;        // padded column counts of the routed and shared transposes
   size_t active, n_active; // int4 serving path: experts with a non-zero load
   size_t total;
 };
@@ -44,6 +48,13 @@ moe_status check_dims(const moe_dims* d) {
   const long long wide = std::max<long long>(d->d, 2LL * d->F);
   if (slots * wide >= (1LL << 31)) return MOE_E_UNSUPPORTED;
   if ((long long)d->T * std::max<long long>(d->d, 2LL * d->Fs) >= (1LL << 31)) return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
+// Training needs the backward GEMM tiles (128 output columns over F and Fs)
+// and the bf16/fp32 routed experts.
+moe_status check_training(const moe_dims& d) {
+  if (d.w_routed == MOE_INT4_G128 || d.F % 128 || d.Fs % 128) return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -74,6 +85,31 @@ Layout make_layout(const moe_dims& d, int training) {
     L.AU = take(slots * 2 * d.F * es);
     L.Ou = take(slots * d.d * es);
     L.AUs = take((size_t)d.T * 2 * d.Fs * es);
+    const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs, T = d.T;
+    L.P = (long long)slots + (long long)E * (kPadK - 1);
+    L.Tp = pad_k(d.T);
+    const size_t P = (size_t)L.P, Tp = (size_t)L.Tp;
+    L.kofs = take(E * 4);
+    L.klen = take(E * 4);
+    L.ksh = take(2 * 4);
+    L.pcol = take(P * 4);
+    L.dl = take(slots * 4);
+    L.dAU = take(slots * 2 * F * es);
+    L.dAUT = take(2 * F * P * es);
+    L.XpT = take(D * P * es);
+    L.dOT = take(D * P * es);
+    L.HT = take(F * P * es);
+    L.dXp = take(slots * D * es);
+    L.WdT = take(E * F * D * es);
+    L.WguT = take(E * D * 2 * F * es);
+    L.WsdT = take(Fs * D * es);
+    L.WsguT = take(D * 2 * Fs * es);
+    L.dAUs = take(T * 2 * Fs * es);
+    L.dAUsT = take(2 * Fs * Tp * es);
+    L.xT = take(D * Tp * es);
+    L.dyT = take(D * Tp * es);
+    L.HsT = take(Fs * Tp * es);
+    L.dXs = take(T * D * es);
   }
   L.total = o;
   return L;
@@ -168,6 +204,7 @@ const char* moe_status_str(moe_status s) {
 
 size_t moe_workspace_bytes(const moe_dims* dims, int training) {
   if (check_dims(dims) != MOE_OK) return 0;
+  if (training && check_training(*dims) != MOE_OK) return 0;
   return make_layout(*dims, training ? 1 : 0).total;
 }
 
@@ -254,6 +291,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   if (dims->w_routed == MOE_INT4_G128)
     return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
   const moe_dims& d = *dims;
+  if (training && check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
   const size_t es = act_bytes(d.act);
   const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
   std::vector<Range> rs = {{x, (size_t)d.T * D * es, false},
@@ -398,8 +436,240 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
                         const void* dy, void* dx, const moe_grads* dw, void* ws, size_t ws_bytes, void* stream) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
-  (void)x; (void)w; (void)routing; (void)dy; (void)dx; (void)dw; (void)ws; (void)ws_bytes; (void)stream;
-  return MOE_E_UNSUPPORTED;
+  if (!w || !routing || !dw) return MOE_E_ARG;
+  const moe_dims& d = *dims;
+  if (check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
+  const size_t es = act_bytes(d.act);
+  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs, T = d.T;
+  std::vector<Range> rs = {{x, T * D * es, false},
+                           {w->w_router, E * D * es, false},
+                           {w->w_gate_up, E * 2 * F * D * es, false},
+                           {w->w_down, E * D * F * es, false},
+                           {w->w_sh_gate_up, 2 * Fs * D * es, false},
+                           {w->w_sh_down, D * Fs * es, false},
+                           {dy, T * D * es, false},
+                           {dx, T * D * es, true},
+                           {dw->dw_router, E * D * 4, true},
+                           {dw->dw_gate_up, E * 2 * F * D * 4, true},
+                           {dw->dw_down, E * D * F * 4, true},
+                           {dw->dw_sh_gate_up, 2 * Fs * D * 4, true},
+                           {dw->dw_sh_down, D * Fs * 4, true}};
+  const size_t tk = T * d.k;
+  rs.push_back({routing->idx, tk * 4, false});
+  rs.push_back({routing->gate, tk * 4, false});
+  rs.push_back({routing->counts, E * 4, false});
+  rs.push_back({routing->offsets, (E + 1) * 4, false});
+  rs.push_back({routing->perm, tk * 4, false});
+  rs.push_back({routing->pos, tk * 4, false});
+  if (null_with_size(rs)) return MOE_E_ARG;
+  const Layout L = make_layout(d, 1);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (T == 0) {
+    // no tokens: every gradient is zero
+    launch_fill_zero(dw->dw_router, E * D * 4, s);
+    launch_fill_zero(dw->dw_gate_up, E * 2 * F * D * 4, s);
+    launch_fill_zero(dw->dw_down, E * D * F * 4, s);
+    launch_fill_zero(dw->dw_sh_gate_up, 2 * Fs * D * 4, s);
+    launch_fill_zero(dw->dw_sh_down, D * Fs * 4, s);
+    return device_status();
+  }
+
+  const int act = d.act;
+  const int P = (int)L.P, Tp = (int)L.Tp;
+  int32_t* kofs = at<int32_t>(ws, L.kofs);
+  int32_t* klen = at<int32_t>(ws, L.klen);
+  int32_t* ksh = at<int32_t>(ws, L.ksh);
+  int32_t* pcol = at<int32_t>(ws, L.pcol);
+  float* dl = at<float>(ws, L.dl);
+  void* dAU = at<char>(ws, L.dAU);
+  void* dAUT = at<char>(ws, L.dAUT);
+  void* XpT = at<char>(ws, L.XpT);
+  void* dOT = at<char>(ws, L.dOT);
+  void* HT = at<char>(ws, L.HT);
+  void* dXp = at<char>(ws, L.dXp);
+  void* WdT = at<char>(ws, L.WdT);
+  void* WguT = at<char>(ws, L.WguT);
+  void* WsdT = at<char>(ws, L.WsdT);
+  void* WsguT = at<char>(ws, L.WsguT);
+  void* dAUs = at<char>(ws, L.dAUs);
+  void* dAUsT = at<char>(ws, L.dAUsT);
+  void* xT = at<char>(ws, L.xT);
+  void* dyT = at<char>(ws, L.dyT);
+  void* HsT = at<char>(ws, L.HsT);
+  void* dXs = at<char>(ws, L.dXs);
+
+  mark_phase(0, s);
+  // 1. padded per-expert contraction ranges
+  launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, kofs, klen, ksh, pcol, s);
+
+  // 2. transposed weights: W_d^T [E][F][d], W_gu^T [E][d][2F], W_sd^T [Fs][d], W_sgu^T [d][2Fs]
+  auto transpose = [&](const void* src, long long ld_src, long long sb, void* dst, long long ld_dst, long long db, int R,
+                       int C, int batch, int n_in, const int32_t* map1, const int32_t* map2, int div,
+                       const float* scale) {
+    TransposeArgs t{};
+    t.src = src;
+    t.ld_src = ld_src;
+    t.src_bstride = sb;
+    t.dst = dst;
+    t.ld_dst = ld_dst;
+    t.dst_bstride = db;
+    t.R = R;
+    t.C = C;
+    t.batch = batch;
+    t.n_in = n_in;
+    t.map1 = map1;
+    t.map2 = map2;
+    t.div = div;
+    t.scale = scale;
+    launch_transpose(act, t, s);
+  };
+  transpose(w->w_down, d.F, (long long)D * F, WdT, d.d, (long long)F * D, d.F, d.d, d.E, d.d, nullptr, nullptr, 1,
+            nullptr);
+  transpose(w->w_gate_up, d.d, 2LL * F * D, WguT, 2 * d.F, 2LL * F * D, d.d, 2 * d.F, d.E, 2 * d.F, nullptr, nullptr, 1,
+            nullptr);
+  transpose(w->w_sh_down, d.Fs, 0, WsdT, d.d, 0, d.Fs, d.d, 1, d.d, nullptr, nullptr, 1, nullptr);
+  transpose(w->w_sh_gate_up, d.d, 0, WsguT, 2 * d.Fs, 0, d.d, 2 * d.Fs, 1, 2 * d.Fs, nullptr, nullptr, 1, nullptr);
+
+  // 3. router and gate gradients
+  launch_bwd_gate(act, dy, at<char>(ws, L.Ou), x, w->w_router, routing->idx, routing->gate, routing->pos, d.T, d.d, d.k,
+                  dl, s);
+
+  const long long slots = (long long)d.T * d.k;
+  const int max_tiles = (int)max_group_tiles(slots, d.E);
+  // 4. dH (gate-scaled) -> SwiGLU backward -> dAU (routed) and dAUs (shared)
+  GemmJob hr{};
+  hr.epi = EPI_SWIGLU_BWD;
+  hr.A = dy;
+  hr.lda = D;
+  hr.a_rows = routing->perm;
+  hr.a_div = d.k;
+  hr.B = WdT;
+  hr.ldb = D;
+  hr.b_estride = (long long)F * D;
+  hr.K = d.d;
+  hr.N = d.F;
+  hr.grouped = 1;
+  hr.tile_e = at<int32_t>(ws, L.tile_e);
+  hr.tile_m0 = at<int32_t>(ws, L.tile_m0);
+  hr.tile_count = at<int32_t>(ws, L.tile_count);
+  hr.offsets = routing->offsets;
+  hr.counts = routing->counts;
+  hr.max_items = max_tiles;
+  hr.C = dAU;
+  hr.ldc = 2LL * F;
+  hr.aux = at<char>(ws, L.AU);
+  hr.ldaux = 2LL * F;
+  hr.gate = routing->gate;
+  hr.perm = routing->perm;
+  GemmJob hs{};
+  hs.epi = EPI_SWIGLU_BWD;
+  hs.A = dy;
+  hs.lda = D;
+  hs.a_div = 1;
+  hs.B = WsdT;
+  hs.ldb = D;
+  hs.K = d.d;
+  hs.N = d.Fs;
+  hs.M = d.T;
+  hs.max_items = (d.T + kTileM - 1) / kTileM;
+  hs.C = dAUs;
+  hs.ldc = 2LL * Fs;
+  hs.aux = at<char>(ws, L.AUs);
+  hs.ldaux = 2LL * Fs;
+  GemmArgs g1{};
+  g1.act = act;
+  g1.njobs = 2;
+  g1.job[0] = hr;
+  g1.job[1] = hs;
+  launch_gemm(g1, s);
+
+  // 5. input gradients: dXp = dAU W_gu (per expert), dXs = dAUs W_sgu
+  GemmJob xr = hr;
+  xr.epi = EPI_STORE;
+  xr.A = dAU;
+  xr.lda = 2LL * F;
+  xr.a_rows = nullptr;
+  xr.a_div = 1;
+  xr.B = WguT;
+  xr.ldb = 2LL * F;
+  xr.b_estride = 2LL * F * D;
+  xr.K = 2 * d.F;
+  xr.N = d.d;
+  xr.C = dXp;
+  xr.ldc = D;
+  xr.aux = nullptr;
+  xr.gate = nullptr;
+  GemmJob xs = hs;
+  xs.epi = EPI_STORE;
+  xs.A = dAUs;
+  xs.lda = 2LL * Fs;
+  xs.B = WsguT;
+  xs.ldb = 2LL * Fs;
+  xs.K = 2 * d.Fs;
+  xs.N = d.d;
+  xs.C = dXs;
+  xs.ldc = D;
+  xs.aux = nullptr;
+  GemmArgs g2{};
+  g2.act = act;
+  g2.njobs = 2;
+  g2.job[0] = xr;
+  g2.job[1] = xs;
+  launch_gemm(g2, s);
+
+  // 6. transposed activations over padded slot columns (routed) and token columns (shared)
+  transpose(dAU, 2LL * F, 0, dAUT, P, 0, 2 * d.F, P, 1, 0, pcol, nullptr, 1, nullptr);
+  transpose(x, D, 0, XpT, P, 0, d.d, P, 1, 0, pcol, routing->perm, d.k, nullptr);
+  transpose(dy, D, 0, dOT, P, 0, d.d, P, 1, 0, pcol, routing->perm, d.k, routing->gate);
+  transpose(at<char>(ws, L.H), F, 0, HT, P, 0, d.F, P, 1, 0, pcol, nullptr, 1, nullptr);
+  transpose(dAUs, 2LL * Fs, 0, dAUsT, Tp, 0, 2 * d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+  transpose(x, D, 0, xT, Tp, 0, d.d, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+  transpose(dy, D, 0, dyT, Tp, 0, d.d, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+  transpose(at<char>(ws, L.Hs), Fs, 0, HsT, Tp, 0, d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+
+  // 7. weight gradients, contracting over each expert's padded slot range
+  auto kjob = [&](const void* A, long long lda, const void* B, long long ldb, int M, int N, int nexp,
+                  const int32_t* ko, const int32_t* kl, void* C, long long ldc, long long cstride) {
+    GemmJob j{};
+    j.epi = EPI_STORE_F32;
+    j.A = A;
+    j.lda = lda;
+    j.a_div = 1;
+    j.B = B;
+    j.ldb = ldb;
+    j.N = N;
+    j.M = M;
+    j.kgroup = 1;
+    j.nexp = nexp;
+    j.kofs = ko;
+    j.klen = kl;
+    j.max_items = nexp * ((M + kTileM - 1) / kTileM);
+    j.C = C;
+    j.ldc = ldc;
+    j.c_estride = cstride;
+    return j;
+  };
+  GemmArgs g3{};
+  g3.act = act;
+  g3.njobs = 2;
+  g3.job[0] = kjob(dAUT, P, XpT, P, 2 * d.F, d.d, d.E, kofs, klen, dw->dw_gate_up, D, 2LL * F * D);
+  g3.job[1] = kjob(dAUsT, Tp, xT, Tp, 2 * d.Fs, d.d, 1, ksh, ksh + 1, dw->dw_sh_gate_up, D, 0);
+  launch_gemm(g3, s);
+  GemmArgs g4{};
+  g4.act = act;
+  g4.njobs = 2;
+  g4.job[0] = kjob(dOT, P, HT, P, d.d, d.F, d.E, kofs, klen, dw->dw_down, F, (long long)D * F);
+  g4.job[1] = kjob(dyT, Tp, HsT, Tp, d.d, d.Fs, 1, ksh, ksh + 1, dw->dw_sh_down, Fs, 0);
+  launch_gemm(g4, s);
+
+  // 8. router weight gradient and the input gradient
+  launch_bwd_dwr(act, x, dl, routing->perm, routing->counts, routing->offsets, d.E, d.d, d.k, dw->dw_router, s);
+  launch_bwd_dx(act, dXs, dXp, w->w_router, dl, routing->idx, routing->pos, d.T, d.d, d.k, dx, s);
+  mark_phase(1, s);
+  return device_status();
 }
 
 }  // extern "C"

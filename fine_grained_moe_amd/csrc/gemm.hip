@@ -86,6 +86,7 @@ __device__ __host__ __forceinline__ int n_tiles(const GemmJob& j) {
   return j.epi == EPI_SWIGLU ? j.N / 64 : j.N / BN;
 }
 __device__ __forceinline__ int item_count(const GemmJob& j) {
+  if (j.kgroup) return j.nexp * ((j.M + BM - 1) / BM);
   return j.grouped ? *j.tile_count : (j.M + BM - 1) / BM;
 }
 
@@ -101,6 +102,23 @@ __device__ __forceinline__ void store_vec(T* p, const float (&v)[N]) {
   } else {
     if constexpr (N == 2) *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
     else *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+}
+
+template <typename T>
+__device__ __forceinline__ void load_vec4(const T* p, float (&v)[4]) {
+  if constexpr (sizeof(T) == 2) {
+    const uint2 w = *reinterpret_cast<const uint2*>(p);
+    v[0] = bf16_to_f32((bf16_t)(w.x & 0xFFFF));
+    v[1] = bf16_to_f32((bf16_t)(w.x >> 16));
+    v[2] = bf16_to_f32((bf16_t)(w.y & 0xFFFF));
+    v[3] = bf16_to_f32((bf16_t)(w.y >> 16));
+  } else {
+    const float4 w = *reinterpret_cast<const float4*>(p);
+    v[0] = w.x;
+    v[1] = w.y;
+    v[2] = w.z;
+    v[3] = w.w;
   }
 }
 
@@ -141,7 +159,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   const int nbn = n_tiles(p);
   const int xcd = bid & 7, local = bid >> 3;
   int pi, nt;
-  if (p.grouped) {
+  if (p.grouped || p.kgroup) {
     pi = local / nbn;
     nt = local - pi * nbn;
   } else {
@@ -153,7 +171,17 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   const int item = xcd * q + pi;
   if (item >= count) return;
   int e = 0, rows, row_base;
-  if (p.grouped) {
+  long long kofs = 0;
+  int klen = p.K;
+  if (p.kgroup) {
+    const int mt = (p.M + BM - 1) / BM;
+    e = item / mt;
+    const int m0 = (item - e * mt) * BM;
+    rows = p.M - m0;
+    row_base = m0;
+    kofs = p.kofs[e];
+    klen = p.klen[e];
+  } else if (p.grouped) {
     e = p.tile_e[item];
     const int m0 = p.tile_m0[item];
     rows = p.counts[e] - m0;
@@ -181,7 +209,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
     const int c = swz_piece<ROWB>(R, ppc);            // XOR swizzles are their own inverse
     const int ra = min(R, rows - 1);
     const long long arow = p.a_rows ? (long long)(p.a_rows[row_base + ra] / p.a_div) : (long long)(row_base + ra);
-    a_src[j] = reinterpret_cast<const char*>(p.A) + (arow * p.lda) * (long long)sizeof(T) + c * 16;
+    a_src[j] = reinterpret_cast<const char*>(p.A) + (arow * p.lda + kofs) * (long long)sizeof(T) + c * 16;
     // LDS B row rho = base + 16 ni + f holds weight row base' + S f + ni (S = 2
     // for SwiGLU halves, 4 otherwise), so lane f's MFMA columns are adjacent
     // output columns.
@@ -194,10 +222,10 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
       const int w64 = R >> 6, ni = (R >> 4) & 3, f = R & 15;
       brow = (long long)nt * BN + w64 * 64 + 4 * f + ni;
     }
-    b_src[j] = bbase + brow * p.ldb * (long long)sizeof(T) + c * 16;
+    b_src[j] = bbase + (brow * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
   }
 
-  const int nk = (int)((long long)p.K * sizeof(T) / ROWB);
+  const int nk = (int)((long long)klen * sizeof(T) / ROWB);
   // Stage s lives in LDS buffer s % NS; NS - 1 stages are in flight while one
   // is multiplied.  A stage is 2 * NDMA loads per lane.
   auto issue = [&](int s) {
@@ -311,6 +339,31 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
         }
         store_vec<T, 4>(C + row * p.ldc + n, v);
         if (aux) store_vec<T, 4>(aux + row * p.ldaux + n, raw);
+      } else if (p.epi == EPI_SWIGLU_BWD) {
+        // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u)
+        const int n = nt * BN + wn * 64 + 4 * fr;
+        const float sc = p.gate ? p.gate[p.perm[row]] : 1.f;
+        const T* au = reinterpret_cast<const T*>(p.aux) + row * p.ldaux;
+        float a[4], u[4], da[4], du[4];
+        load_vec4<T>(au + n, a);
+        load_vec4<T>(au + p.N + n, u);
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) {
+          const float dh = acc[mi][ni][i] * sc;
+          const float sg = sigmoidf_(a[ni]);
+          const float si = a[ni] * sg;
+          da[ni] = dh * u[ni] * (sg * (1.f + a[ni] * (1.f - sg)));
+          du[ni] = dh * si;
+        }
+        store_vec<T, 4>(C + row * p.ldc + n, da);
+        store_vec<T, 4>(C + row * p.ldc + p.N + n, du);
+      } else if (p.epi == EPI_STORE_F32) {
+        const int n = nt * BN + wn * 64 + 4 * fr;
+        float v[4];
+#pragma unroll
+        for (int ni = 0; ni < 4; ++ni) v[ni] = acc[mi][ni][i];
+        float* Cf = reinterpret_cast<float*>(p.C) + (long long)e * p.c_estride;
+        store_vec<float, 4>(Cf + row * p.ldc + n, v);
       } else {  // EPI_STORE
         const int n = nt * BN + wn * 64 + 4 * fr;
         float v[4];

@@ -25,7 +25,14 @@ void launch_route_scatter(const int32_t* idx, const int32_t* block_base, int T, 
                           int32_t* pos, hipStream_t s);
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s);
 
-enum Epilogue { EPI_SWIGLU = 0, EPI_ROWSCALE = 1, EPI_STORE = 2 };
+enum Epilogue {
+  EPI_SWIGLU = 0,       // C[row, f] = silu(acc_gate) * acc_up; aux = (gate | up) pre-activations
+  EPI_ROWSCALE = 1,     // C[row, n] = gate[perm[row]] * acc; aux = acc
+  EPI_STORE = 2,        // C[row, n] = acc (operand dtype)
+  EPI_SWIGLU_BWD = 3,   // dH = s * acc (s = gate[perm[row]] or 1); from a = aux[row, n], u = aux[row, N + n]:
+                        //   C[row, n] = dH * u * silu'(a), C[row, N + n] = dH * silu(a)
+  EPI_STORE_F32 = 4     // C[row, n] = acc as float32
+};
 
 // One GEMM problem C = A . B^T on MFMA with a fused epilogue.  Element offsets
 // are in elements of the launch's dtype.
@@ -52,6 +59,14 @@ struct GemmJob {
   const int32_t* offsets;
   const int32_t* counts;
   int max_items;           // upper bound of the item count (sizes the grid)
+  // per-expert contraction ranges (weight gradients): item = (expert, 128-row
+  // tile of M); expert e contracts over K elements [kofs[e], kofs[e] + klen[e])
+  // of every A and B row and writes C + e * c_estride.  klen[e] % (128 bytes) == 0.
+  int kgroup;
+  int nexp;
+  const int32_t* kofs;
+  const int32_t* klen;
+  long long c_estride;
   // outputs
   void* C;
   long long ldc;
@@ -99,6 +114,37 @@ struct DecodeArgs {
   uint16_t* y;                       // [T, d] bf16
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);
+
+// Backward helpers (backward.hip).  Contraction ranges of the weight-gradient
+// GEMMs are padded to kPadK elements with zero columns.
+constexpr int kPadK = 64;
+inline long long pad_k(long long n) { return (n + kPadK - 1) / kPadK * kPadK; }
+
+// dst[b][r][c] = scale * src[b][row(c)][r]; see transpose_kernel.
+struct TransposeArgs {
+  const void* src;
+  long long ld_src;
+  long long src_bstride;
+  void* dst;
+  long long ld_dst;
+  long long dst_bstride;
+  int R, C, batch;
+  int n_in;                  // without map1: columns >= n_in are zero
+  const int32_t* map1;       // column -> index (or -1 for a zero column)
+  const int32_t* map2;       // index -> source index; source row = map2[...] / div
+  int div;
+  const float* scale;        // optional, indexed by the source index before division
+};
+void launch_fill_zero(void* p, size_t bytes, hipStream_t s);   // bytes % 4 == 0
+void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int32_t* kofs,
+                     int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s);
+void launch_transpose(int act, const TransposeArgs& a, hipStream_t s);
+void launch_bwd_gate(int act, const void* dy, const void* ou, const void* x, const void* wr, const int32_t* idx,
+                     const float* gate, const int32_t* pos, int T, int d, int k, float* dl, hipStream_t s);
+void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* counts,
+                    const int32_t* offsets, int E, int d, int k, float* dwr, hipStream_t s);
+void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, const float* dl, const int32_t* idx,
+                   const int32_t* pos, int T, int d, int k, void* dx, hipStream_t s);
 
 // y[t] = S[t] + sum_j O[pos[t*k + j]] in fixed j order, rounded once.
 void launch_combine(int act, const void* S, const void* O, const int32_t* pos, int T, int d, int k, void* y,

@@ -1,0 +1,95 @@
+"""GPU parity of the training backward against the oracle's exact derivatives.
+
+Each gradient (dx and the five weight gradients) must be within relative
+Frobenius error 1e-2 of the oracle for bf16 (1e-4 for fp32).  The routing is
+the forward's (held fixed), which is compared bit-exactly first.
+"""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as om
+from fine_grained_moe_amd import synth
+from tests import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+GRADS = ("dx", "dw_router", "dw_gate_up", "dw_down", "dw_sh_gate_up", "dw_sh_down")
+
+
+def _case(T, d, E, F, Fs, k, act, seed, bias=None):
+    inp = synth.make_layer(T=T, d=d, E=E, F=F, Fs=Fs, k=k, act=act, seed=seed, rms_norm=(act == "bf16"),
+                           with_dy=True)
+    if bias is not None:
+        inp.bias = np.asarray(bias, np.float32)
+    H.remove_near_ties(inp)
+    return inp
+
+
+def _run(inp):
+    import torch
+    from fine_grained_moe_amd import moe
+    dims = moe.make_dims(inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k, inp.act)
+    x, w = H.to_gpu(inp)
+    dt = x.dtype
+    dy = torch.from_numpy(inp.dy).to(device="cuda", dtype=dt)
+    b = torch.from_numpy(inp.bias).cuda()
+    y = torch.empty_like(x)
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims, training=True)
+    moe.moe_forward(dims, x, w, b, y, r, ws, training=True)
+    dx = torch.empty_like(x)
+    g = moe.alloc_grads(dims)
+    moe.moe_backward(dims, x, w, r, dy, dx, g, ws)
+    torch.cuda.synchronize()
+    out = {"dx": dx.float().cpu().numpy()}
+    out.update({n: t.cpu().numpy() for n, t in g.items()})
+    rn = {n: t.cpu().numpy() for n, t in r.items()}
+    return out, rn
+
+
+def _check(inp, tol):
+    got, rn = _run(inp)
+    y_ref, ref = H.oracle_forward(inp)
+    H.check_routing_exact(rn, ref, inp.E)
+    gref = om.backward(inp.x, inp.w_router, inp.w_gate_up, inp.w_down, inp.w_sh_gate_up, inp.w_sh_down, ref, inp.dy)
+    errs = {n: H.rel_fro(got[n], getattr(gref, n)) for n in GRADS}
+    print(f"[{inp.act} T={inp.T} E={inp.E} k={inp.k}] " + ", ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+    return got, gref, rn
+
+
+def test_backward_small_bf16():
+    _check(_case(300, 256, 8, 128, 256, 2, "bf16", seed=1), 1e-2)
+
+
+def test_backward_small_f32():
+    _check(_case(200, 128, 8, 128, 256, 2, "f32", seed=2), 1e-4)
+
+
+def test_backward_ragged_many_tiles_bf16():
+    _check(_case(1100, 256, 16, 128, 384, 3, "bf16", seed=3), 1e-2)
+
+
+def test_backward_top1_router_gradient_is_zero():
+    """Top-2 paragraph of the "Relay training" section: with top_k = 1 the
+    routing weight is a constant, so the router gets no gradient."""
+    got, gref, _ = _check(_case(256, 256, 8, 128, 256, 1, "bf16", seed=4), 1e-2)
+    assert np.all(got["dw_router"] == 0.0)
+
+
+def test_backward_unloaded_experts_get_zero_gradient():
+    bias = np.zeros(8, np.float32)
+    bias[[1, 6]] = -4.0
+    got, _, rn = _check(_case(300, 256, 8, 128, 256, 2, "bf16", seed=5, bias=bias), 1e-2)
+    assert rn["counts"][1] == 0 and rn["counts"][6] == 0
+    for n in ("dw_gate_up", "dw_down", "dw_router"):
+        assert np.all(got[n][[1, 6]] == 0.0), n
+
+
+@pytest.mark.slow
+def test_backward_train_t32768():
+    """The training workload: T = 32768 (16 x 2048), one NanoColibri layer."""
+    inp = synth.make_workload("train_t32768", with_dy=True)
+    H.remove_near_ties(inp)
+    _check(inp, 1e-2)
