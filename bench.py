@@ -139,6 +139,42 @@ def bench_decode(moe, synth, torch, np, n_layers=23, iters=46):
     return out
 
 
+def bench_train(moe, synth, torch, np, steps=10, warmup=3):
+    """One training step of the layer at T = 32768 (16 x 2048): forward with
+    saved activations, backward (dx and every weight gradient), bias step."""
+    inp = synth.make_workload("train_t32768", with_dy=True)
+    T, d, E, F, Fs, k = inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+    w = dict(w_router=bf(inp.w_router), w_gate_up=bf(inp.w_gate_up), w_down=bf(inp.w_down),
+             w_sh_gate_up=bf(inp.w_sh_gate_up), w_sh_down=bf(inp.w_sh_down))
+    x, dy = bf(inp.x), bf(inp.dy)
+    y, dx = torch.empty_like(x), torch.empty_like(x)
+    bias = torch.zeros(E, device="cuda")
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims, training=True)
+    g = moe.alloc_grads(dims)
+
+    def step():
+        moe.moe_forward(dims, x, w, bias, y, r, ws, training=True)
+        moe.moe_backward(dims, x, w, r, dy, dx, g, ws)
+        moe.moe_bias_update(E, T * k, r["counts"], GAMMA, bias)
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(steps):
+        step()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    flops = 3 * (2.0 * T * k * 3 * d * F + 2.0 * T * 3 * d * Fs + 2.0 * T * d * E)
+    out = dict(T=T, ms_per_step=round(el * 1e3, 3), tokens_per_s=T / el, algorithmic_tflop=round(flops / 1e12, 3),
+               tflops=round(flops / el / 1e12, 1), frac_mfma=round(flops / el / PEAK_BF16_FLOPS, 4))
+    log(f"train T={T}: {el * 1e3:.2f} ms/step, {T / el / 1e6:.2f} M tokens/s, {flops / el / 1e12:.0f} TFLOP/s")
+    return out
+
+
 def cpu_baseline(inp, seconds: float):
     """The CPU oracle as it stands, on this host's cores, over a bounded sample:
     whole copies of the benchmark batch until `seconds` have passed."""
@@ -172,6 +208,7 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-warm", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -283,6 +320,8 @@ def main() -> int:
 
     if not args.no_decode:
         out["decode"] = bench_decode(moe, synth, torch, np)
+    if not args.no_train:
+        out["train"] = bench_train(moe, synth, torch, np)
 
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
