@@ -1,36 +1,49 @@
 // Expert GEMMs of the MoE layer on gfx950 MFMA, with fused epilogues.
 //
-// One kernel template serves the four GEMMs of the forward:
+// One kernel serves the GEMMs of the forward and of the backward:
 //   routed gate/up  (grouped over experts, A rows gathered from x through the
 //                    dispatch order, SwiGLU epilogue -> H)
 //   routed down     (grouped, rows scaled by their routing weight -> O)
 //   shared gate/up  (dense, SwiGLU epilogue -> Hs)
 //   shared down     (dense, plain store -> S)
+//   backward: SwiGLU-backward epilogue, plain stores, and fp32 weight
+//   gradients contracting over each expert's own slot range.
 // The experts are the SwiGLU FFNs of widths 512 (routed) and 2048 (shared) of
 // the seventnews article "A relay race of rented GPUs trained NanoColibri's
 // 2.7B MoE for $200" (opening section, architecture paragraph).  A launch
-// carries two jobs with the same B layout (the two gate/up GEMMs, or the two
-// down GEMMs): their workgroups are interleaved, so the weight-streaming
+// carries up to two jobs with the same B layout (the two gate/up GEMMs, or the
+// two down GEMMs): their workgroups are interleaved, so the weight-streaming
 // routed tiles and the MFMA-bound shared tiles share the chip.
 //
-// Tiling: a 256-thread workgroup (4 waves, 2 x 2) computes a 128 x 128 tile;
-// each wave owns 64 x 64 = 4 x 4 MFMA 16x16 tiles.  K advances in 128-byte
-// row chunks (64 bf16 or 32 float) staged through LDS, double-buffered, with
-// two stages of global loads in flight.  The 16-byte pieces of each LDS row
-// are XOR-swizzled (see swz) so that both the 16-row operand reads and the
-// loader's writes are free of bank conflicts.
-// B rows are permuted on their way into LDS so that each lane's output
-// columns are adjacent and the epilogue writes 4- to 16-byte vectors.
+// Workgroup: 4 waves (2 x 2), two workgroups per CU.  Every wave owns a
+// 64 x 128 piece of a 128 x 256 output tile (4 x 8 MFMA 16x16x32 tiles).  K
+// advances in 64-byte row chunks through a 3-deep LDS ring (24 KiB stages:
+// the tile's 128 A rows then its 256 B rows) filled by direct global->LDS
+// loads (global_load_lds_dwordx4), each wave loading a quarter of a stage.
+// Measured on gfx950: a CU's address unit takes global->LDS loads at about
+// 64 bytes per clock, so a 128 x 128 x 32 step (16 KiB per MFMA-MFLOP) would
+// need all of it to keep the MFMA pipes busy, 128 x 256 about three
+// quarters; and a wave that issues its stage's loads as one burst stalls
+// behind the other waves' loads for about as long as its MFMAs take, so the
+// loads of the next stage but one are spread between the current stage's
+// MFMAs instead.
+//
+// The 16-byte pieces of each LDS row are XOR-swizzled (see swz) so that the
+// 16-row operand reads are free of bank conflicts.  B rows are permuted on
+// their way into LDS so that each lane's output columns are adjacent and the
+// epilogue writes 8- to 32-byte vectors.  Rows past an item's end re-read its
+// last row and columns past N re-read row N - 1; neither is stored.
 //
 // Scheduling: work items are 128-row tiles (dense: row blocks; grouped: the
-// tile table the router wrote, in expert order).  Workgroups are dealt to the
-// 8 XCDs round-robin by block index, so block b runs on XCD b % 8; XCD x gets
-// the contiguous item range [x*q, (x+1)*q).  Grouped jobs run all N tiles of
-// an item back to back (an expert's weights and an item's rows stay in that
-// XCD's L2); dense jobs run all of the XCD's row blocks for one N tile before
-// the next (the XCD's A rows stay in L2 while the large weight matrix streams
-// through once).  No host synchronisation: the item count is read on the
-// device.
+// tile table the router wrote, in expert order).  Workgroups are
+// dealt to the 8 XCDs round-robin by block index, so block b runs on XCD
+// b % 8; XCD x gets the contiguous item range [x*q, (x+1)*q).  Grouped jobs
+// run all N tiles of an item back to back (an expert's weights and an item's
+// rows stay in that XCD's L2); dense jobs run all of the XCD's row blocks for
+// one N tile before the next.  No host synchronisation: the item count of a
+// grouped job is read on the device.
+#include <type_traits>
+
 #include "common.h"
 #include "kernels.h"
 
@@ -38,30 +51,23 @@ namespace fgmoe {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, NTHR = 256;
-#ifndef FGMOE_GEMM_ROWB
-#define FGMOE_GEMM_ROWB 128
-#endif
-#ifndef FGMOE_GEMM_STAGES
-#define FGMOE_GEMM_STAGES 2
-#endif
-constexpr int kRowB = FGMOE_GEMM_ROWB;       // bytes of one operand row per K stage (64 or 128)
-constexpr int kStages = FGMOE_GEMM_STAGES;   // LDS ring depth: kStages * 2 * 128 * kRowB bytes
+constexpr int NTHR = 256;                    // 4 waves
+constexpr int BM = 128, BN = 256;            // workgroup tile
+constexpr int WM = 64, WN = 128, NI = WN / 16, HN = NI / 2;   // one wave's output piece
+constexpr int kRowB = 64;                    // bytes of one operand row per K stage
+constexpr int kStages = 3;                   // LDS ring depth
+constexpr int ATILE = BM * kRowB, BTILE = BN * kRowB;        // one stage of each operand
+constexpr int kStageBytes = ATILE + BTILE;
+constexpr int NDA = BM / 4 / 16, NDB = BN / 4 / 16;          // loads per wave and stage: A 2, B 4
+constexpr int kLoads = NDA + NDB;
 
-// LDS swizzle of 16-byte pieces.  gfx950 serves a 16-byte-per-lane LDS read
-// 32 lanes at a time over 128 four-byte banks (fitted to measured
-// SQ_LDS_BANK_CONFLICT counts of probe access patterns).  An MFMA operand read
-// has 16 consecutive rows x 2 piece indices per half-wave; these XORs make
-// those 32 pieces hit 32 distinct bank groups.
-template <int ROWB>
-__device__ __forceinline__ int swz_piece(int row, int piece) {
-  if constexpr (ROWB == 128) return piece ^ (row & 7) ^ ((row >> 3) & 1);
-  else return piece ^ (((row >> 3) & 1) << 1);
-}
-template <int ROWB>
-__device__ __forceinline__ int swz(int row, int piece) {
-  return row * ROWB + (swz_piece<ROWB>(row, piece) << 4);
-}
+// LDS swizzle of 16-byte pieces of 64-byte rows.  gfx950 serves a
+// 16-byte-per-lane LDS read 32 lanes at a time over 128 four-byte banks
+// (fitted to measured SQ_LDS_BANK_CONFLICT counts of probe access patterns).
+// An MFMA operand read has 16 consecutive rows x 2 piece indices per
+// half-wave; this XOR makes those 32 pieces hit 32 distinct bank groups.
+__device__ __forceinline__ int swz_piece(int row, int piece) { return piece ^ (((row >> 3) & 1) << 1); }
+__device__ __forceinline__ int swz(int row, int piece) { return row * kRowB + (swz_piece(row, piece) << 4); }
 
 typedef __attribute__((address_space(3))) void* lds_ptr_t;
 
@@ -82,57 +88,70 @@ __device__ __forceinline__ void block_barrier() {
   asm volatile("" ::: "memory");
 }
 
+
+
+// SwiGLU tiles hold BN / 2 gate and the matching BN / 2 up rows of B.
 __device__ __host__ __forceinline__ int n_tiles(const GemmJob& j) {
-  return j.epi == EPI_SWIGLU ? j.N / 64 : j.N / BN;
+  const int w = j.epi == EPI_SWIGLU ? BN / 2 : BN;
+  return (j.N + w - 1) / w;
 }
 __device__ __forceinline__ int item_count(const GemmJob& j) {
   if (j.kgroup) return j.nexp * ((j.M + BM - 1) / BM);
   return j.grouped ? *j.tile_count : (j.M + BM - 1) / BM;
 }
+// Upper bound of item_count, on the host.
+inline long long max_item_count(const GemmJob& j) {
+  if (j.kgroup) return (long long)j.nexp * ((j.M + BM - 1) / BM);
+  return j.grouped ? j.max_items : (j.M + BM - 1) / BM;
+}
 
+// N consecutive outputs (N = 2, 4 or 8), rounded to T.
 template <typename T, int N>
 __device__ __forceinline__ void store_vec(T* p, const float (&v)[N]) {
   if constexpr (sizeof(T) == 2) {
-    uint32_t w[(N + 1) / 2];
+    uint32_t w[N / 2];
 #pragma unroll
     for (int i = 0; i < N; i += 2)
       w[i / 2] = (uint32_t)f32_to_bf16(v[i]) | ((uint32_t)f32_to_bf16(v[i + 1]) << 16);
     if constexpr (N == 2) *reinterpret_cast<uint32_t*>(p) = w[0];
-    else *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    else if constexpr (N == 4) *reinterpret_cast<uint2*>(p) = make_uint2(w[0], w[1]);
+    else *reinterpret_cast<uint4*>(p) = make_uint4(w[0], w[1], w[2], w[3]);
+  } else if constexpr (N == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
   } else {
-    if constexpr (N == 2) *reinterpret_cast<float2*>(p) = make_float2(v[0], v[1]);
-    else *reinterpret_cast<float4*>(p) = make_float4(v[0], v[1], v[2], v[3]);
+#pragma unroll
+    for (int i = 0; i < N; i += 4)
+      *reinterpret_cast<float4*>(p + i) = make_float4(v[i], v[i + 1], v[i + 2], v[i + 3]);
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void load_vec4(const T* p, float (&v)[4]) {
+// N consecutive values (N = 4 or 8) of T, widened to float.
+template <typename T, int N>
+__device__ __forceinline__ void load_vec(const T* p, float (&v)[N]) {
   if constexpr (sizeof(T) == 2) {
-    const uint2 w = *reinterpret_cast<const uint2*>(p);
-    v[0] = bf16_to_f32((bf16_t)(w.x & 0xFFFF));
-    v[1] = bf16_to_f32((bf16_t)(w.x >> 16));
-    v[2] = bf16_to_f32((bf16_t)(w.y & 0xFFFF));
-    v[3] = bf16_to_f32((bf16_t)(w.y >> 16));
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const uint2 w = *reinterpret_cast<const uint2*>(p + i);
+      v[i] = bf16_to_f32((bf16_t)(w.x & 0xFFFF));
+      v[i + 1] = bf16_to_f32((bf16_t)(w.x >> 16));
+      v[i + 2] = bf16_to_f32((bf16_t)(w.y & 0xFFFF));
+      v[i + 3] = bf16_to_f32((bf16_t)(w.y >> 16));
+    }
   } else {
-    const float4 w = *reinterpret_cast<const float4*>(p);
-    v[0] = w.x;
-    v[1] = w.y;
-    v[2] = w.z;
-    v[3] = w.w;
+#pragma unroll
+    for (int i = 0; i < N; i += 4) {
+      const float4 w = *reinterpret_cast<const float4*>(p + i);
+      v[i] = w.x;
+      v[i + 1] = w.y;
+      v[i + 2] = w.z;
+      v[i + 3] = w.w;
+    }
   }
 }
 
-template <typename T, bool SWIGLU, int NS>
+template <typename T, bool SWIGLU>
 __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
-  constexpr int EPI = SWIGLU ? EPI_SWIGLU : EPI_ROWSCALE;   // B-row layout class
-  // (the row width is a namespace constant: as a kernel template parameter it
-  // made this compiler drop the host-side launch stubs)
-  constexpr int ROWB = kRowB;
-  constexpr int TILEB = BM * ROWB;                          // one operand tile of one stage
-  constexpr int PIECES = ROWB / 16;                         // 16-byte pieces per row and stage
-  constexpr int ROWS_PER_DMA = 1024 / ROWB;                 // LDS rows one wave instruction fills
-  constexpr int NDMA = 32 / ROWS_PER_DMA;                   // instructions per wave per operand
-  __shared__ __attribute__((aligned(16))) char lds[NS * 2 * TILEB];
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -193,183 +212,185 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   }
   rows = rows < BM ? rows : BM;
 
-  // ---- global -> LDS: direct loads (global_load_lds_dwordx4).  Lane i of a
-  // wave instruction lands at LDS byte base + 16 i, so instruction j of wave w
-  // fills LDS rows w*32 + j*ROWS_PER_DMA + i/PIECES at physical piece
-  // i%PIECES; the lane fetches the logical piece the swizzle puts there.  A
-  // rows past the item's end re-read its last row: MFMA row r of the result
-  // depends only on A row r, and those rows are never stored.
-  const int prow = lane / PIECES, ppc = lane % PIECES;
-  const char* a_src[NDMA];
-  const char* b_src[NDMA];
+  // ---- global -> LDS.  A stage holds the A tile (128 rows) then the B tile
+  // (256 rows).  Lane i of a wave instruction lands at LDS byte base + 16 i,
+  // so A load j of wave w fills A rows 32w + 16j + i/4 and B load j fills B
+  // rows 64w + 16j + i/4, at physical piece i%4; the lane fetches the logical
+  // piece the swizzle puts there.  LDS B row wn*128 + ni*16 + f holds output
+  // column (tile base) + wn*128 + 8f + ni, so lane f's MFMA columns are 8
+  // adjacent output columns; for SwiGLU the first 128 B rows are gate rows
+  // and the next 128 the matching up rows, with h column (tile base) +
+  // wn*64 + 4f + ni.
+  const char* a_src[NDA];
+  const char* b_src[NDB];
   const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)e * p.b_estride * (long long)sizeof(T);
 #pragma unroll
-  for (int j = 0; j < NDMA; ++j) {
-    const int R = wave * 32 + j * ROWS_PER_DMA + prow;
-    const int c = swz_piece<ROWB>(R, ppc);            // XOR swizzles are their own inverse
+  for (int j = 0; j < NDA; ++j) {
+    const int R = wave * (BM / 4) + j * 16 + (lane >> 2);
+    const int c = swz_piece(R, lane & 3);            // XOR swizzles are their own inverse
     const int ra = min(R, rows - 1);
     const long long arow = p.a_rows ? (long long)(p.a_rows[row_base + ra] / p.a_div) : (long long)(row_base + ra);
     a_src[j] = reinterpret_cast<const char*>(p.A) + (arow * p.lda + kofs) * (long long)sizeof(T) + c * 16;
-    // LDS B row rho = base + 16 ni + f holds weight row base' + S f + ni (S = 2
-    // for SwiGLU halves, 4 otherwise), so lane f's MFMA columns are adjacent
-    // output columns.
+  }
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    const int R = wave * (BN / 4) + j * 16 + (lane >> 2);
+    const int c = swz_piece(R, lane & 3);
     long long brow;
-    if (EPI == EPI_SWIGLU) {
-      const int h = R & 63, half = R >> 6;           // gate block, then up block
-      const int w32 = h >> 5, ni = (h >> 4) & 1, f = h & 15;
-      brow = (long long)(half ? p.up_off : 0) + nt * 64 + w32 * 32 + 2 * f + ni;
+    if (SWIGLU) {
+      const int half = R >> 7, h = R & 127;
+      const int w = h >> 6, ni = (h >> 4) & 3, f = h & 15;
+      const int col = min(nt * (BN / 2) + w * 64 + 4 * f + ni, p.N - 1);
+      brow = (long long)(half ? p.up_off : 0) + col;
     } else {
-      const int w64 = R >> 6, ni = (R >> 4) & 3, f = R & 15;
-      brow = (long long)nt * BN + w64 * 64 + 4 * f + ni;
+      const int w = R >> 7, ni = (R >> 4) & 7, f = R & 15;
+      brow = min(nt * BN + w * 128 + 8 * f + ni, p.N - 1);
     }
     b_src[j] = bbase + (brow * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
   }
-
-  const int nk = (int)((long long)klen * sizeof(T) / ROWB);
-  // Stage s lives in LDS buffer s % NS; NS - 1 stages are in flight while one
-  // is multiplied.  A stage is 2 * NDMA loads per lane.
+  const int nk = (int)((long long)klen * sizeof(T) / kRowB);
+  // load j of this wave for stage s (j < NDA: A, else B)
+  auto issue_one = [&](int s, int j) {
+    char* st = lds + (s % kStages) * kStageBytes;
+    const long long off = (long long)s * kRowB;
+    if (j < NDA)
+      __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(st + wave * (BM / 4) * kRowB + j * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + off,
+                                       (lds_ptr_t)(st + ATILE + wave * (BN / 4) * kRowB + (j - NDA) * 1024), 16, 0, 0);
+  };
   auto issue = [&](int s) {
-    char* base = lds + (s % NS) * 2 * TILEB + wave * 32 * ROWB;
-    const long long off = (long long)s * ROWB;
 #pragma unroll
-    for (int j = 0; j < NDMA; ++j)
-      __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(base + j * 1024), 16, 0, 0);
-#pragma unroll
-    for (int j = 0; j < NDMA; ++j)
-      __builtin_amdgcn_global_load_lds(b_src[j] + off, (lds_ptr_t)(base + TILEB + j * 1024), 16, 0, 0);
+    for (int j = 0; j < kLoads; ++j) issue_one(s, j);
   };
 
-  // ---- LDS -> MFMA operand rows for this wave (16 consecutive LDS rows per tile)
+  // ---- LDS -> MFMA operand rows of this wave (16 consecutive LDS rows per tile)
   const int fr = lane & 15, g = lane >> 4;
-  int arow_l[4], brow_l[4];
+  int arow_l[4], brow_l[NI];
 #pragma unroll
-  for (int mi = 0; mi < 4; ++mi) arow_l[mi] = wm * 64 + mi * 16 + fr;
+  for (int mi = 0; mi < 4; ++mi) arow_l[mi] = wm * WM + mi * 16 + fr;
 #pragma unroll
-  for (int ni = 0; ni < 4; ++ni) {
-    if (EPI == EPI_SWIGLU)
-      brow_l[ni] = (ni < 2 ? wn * 32 + ni * 16 : 64 + wn * 32 + (ni - 2) * 16) + fr;
-    else
-      brow_l[ni] = wn * 64 + ni * 16 + fr;
-  }
+  for (int ni = 0; ni < NI; ++ni)
+    brow_l[ni] = (SWIGLU ? (ni < HN ? wn * 64 + ni * 16 : BN / 2 + wn * 64 + (ni - HN) * 16) : wn * WN + ni * 16) + fr;
 
-  f32x4_t acc[4][4];
+  f32x4_t acc[4][NI];
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi)
 #pragma unroll
-    for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](int buf) {
-    const char* As = lds + buf * 2 * TILEB;
-    const char* Bs = As + TILEB;
-    if constexpr (ROWB == 128) {
-      Frag fa[4], fb[4];
+  // One stage: lane group g owns 16-byte piece g of each 64-byte row chunk
+  // (the same for both operands, so the products pair up whatever the order
+  // of K inside).  With loads, this wave's loads of stage snext go after
+  // MFMAs 4, 9, 14, 19, 24 and 29.
+  constexpr int SP = 4 * NI / kLoads;                      // MFMAs between two loads (5)
+  auto compute = [&](int s, int snext, auto with_loads) {
+    const char* As = lds + (s % kStages) * kStageBytes;
+    const char* Bs = As + ATILE;
+    u32x4_t fa[4], fb[NI];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) {
-        fa[mi].lo = ld16(As + swz<ROWB>(arow_l[mi], 2 * g));
-        fa[mi].hi = ld16(As + swz<ROWB>(arow_l[mi], 2 * g + 1));
+    for (int mi = 0; mi < 4; ++mi) fa[mi] = ld16(As + swz(arow_l[mi], g));
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) fb[ni] = ld16(Bs + swz(brow_l[ni], g));
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        acc[mi][ni] = Mma<T>::run1(fa[mi], fb[ni], acc[mi][ni]);
+        if constexpr (decltype(with_loads)::value) {
+          const int qq = mi * NI + ni;
+          if (qq % SP == SP - 1 && qq / SP < kLoads) {
+            issue_one(snext, qq / SP);
+            __builtin_amdgcn_sched_barrier(0);   // keep the loads spread out
+          }
+        }
       }
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) {
-        fb[ni].lo = ld16(Bs + swz<ROWB>(brow_l[ni], 2 * g));
-        fb[ni].hi = ld16(Bs + swz<ROWB>(brow_l[ni], 2 * g + 1));
-      }
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = Mma<T>::run(fa[mi], fb[ni], acc[mi][ni]);
-    } else {
-      u32x4_t fa[4], fb[4];
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi) fa[mi] = ld16(As + swz<ROWB>(arow_l[mi], g));
-#pragma unroll
-      for (int ni = 0; ni < 4; ++ni) fb[ni] = ld16(Bs + swz<ROWB>(brow_l[ni], g));
-#pragma unroll
-      for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-        for (int ni = 0; ni < 4; ++ni) acc[mi][ni] = Mma<T>::run1(fa[mi], fb[ni], acc[mi][ni]);
-    }
   };
 
-  for (int s = 0; s < NS - 1 && s < nk; ++s) issue(s);
-  for (int s = 0; s < nk; ++s) {
-    // This wave's loads of stage s are done once at most the later stages'
-    // loads are outstanding; the barrier then covers every wave's loads and
-    // every wave's reads of the buffer about to be refilled.
-    if (s + NS - 2 < nk) wait_vmcnt<2 * NDMA * (NS - 2)>();
+  // ---- main loop.  Stage s is waited for with the next stage's loads still
+  // in flight; the barrier then covers every wave's loads of stage s and
+  // every wave's reads of stage s-1, whose buffer stage s+2 refills.  The
+  // last two stages have nothing left to load.
+  for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
+  int s = 0;
+  for (; s + kStages - 1 < nk; ++s) {
+    wait_vmcnt<kLoads>();
+    block_barrier();
+    compute(s, s + kStages - 1, std::true_type{});
+  }
+  for (; s < nk; ++s) {
+    if (s + 1 < nk) wait_vmcnt<kLoads>();
     else wait_vmcnt<0>();
     block_barrier();
-    if (s + NS - 1 < nk) issue(s + NS - 1);
-    compute(s % NS);
+    compute(s, 0, std::false_type{});
   }
 
-  // ---- epilogue (per job).  acc[mi][ni][i] is row wm*64 + mi*16 + 4g + i; its column
-  // is 2f + ni (SwiGLU, ni < 2 gate / ni >= 2 the matching up) or 4f + ni
-  // past the wave's column base.
+  // ---- epilogue (per job).  acc[mi][ni][i] is tile row wm*64 + mi*16 + 4g + i.
+  // Its column, past the wave's base, is 8f + ni (f = lane % 16); for SwiGLU,
+  // blocks ni < 4 are gate columns 4f + ni and ni >= 4 the matching up.
   T* C = reinterpret_cast<T*>(p.C);
   T* aux = reinterpret_cast<T*>(p.aux);
+  const int n = nt * BN + wn * WN + NI * fr;               // first column of this lane (not SwiGLU)
+  const int fh = nt * (BN / 2) + wn * (WN / 2) + HN * fr;  // first h column of this lane (SwiGLU)
+  if (SWIGLU ? fh >= p.N : n >= p.N) return;
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int lr = wm * 64 + mi * 16 + 4 * g + i;
+      const int lr = wm * WM + mi * 16 + 4 * g + i;
       if (lr >= rows) continue;
       const long long row = row_base + lr;
-      if (EPI == EPI_SWIGLU) {
-        const int f = nt * 64 + wn * 32 + 2 * fr;
-        float h[2], a[2], u[2];
+      if (SWIGLU) {
+        float h[HN], a[HN], u[HN];
 #pragma unroll
-        for (int ni = 0; ni < 2; ++ni) {
+        for (int ni = 0; ni < HN; ++ni) {
           a[ni] = acc[mi][ni][i];
-          u[ni] = acc[mi][ni + 2][i];
+          u[ni] = acc[mi][ni + HN][i];
           h[ni] = siluf_(a[ni]) * u[ni];
         }
-        store_vec<T, 2>(C + row * p.ldc + f, h);
+        store_vec<T, HN>(C + row * p.ldc + fh, h);
         if (aux) {
-          store_vec<T, 2>(aux + row * p.ldaux + f, a);
-          store_vec<T, 2>(aux + row * p.ldaux + p.N + f, u);
+          store_vec<T, HN>(aux + row * p.ldaux + fh, a);
+          store_vec<T, HN>(aux + row * p.ldaux + p.N + fh, u);
         }
       } else if (p.epi == EPI_ROWSCALE) {
-        const int n = nt * BN + wn * 64 + 4 * fr;
         const float sc = p.gate[p.perm[row]];
-        float v[4], raw[4];
+        float v[NI], raw[NI];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+        for (int ni = 0; ni < NI; ++ni) {
           raw[ni] = acc[mi][ni][i];
           v[ni] = raw[ni] * sc;
         }
-        store_vec<T, 4>(C + row * p.ldc + n, v);
-        if (aux) store_vec<T, 4>(aux + row * p.ldaux + n, raw);
+        store_vec<T, NI>(C + row * p.ldc + n, v);
+        if (aux) store_vec<T, NI>(aux + row * p.ldaux + n, raw);
       } else if (p.epi == EPI_SWIGLU_BWD) {
         // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u)
-        const int n = nt * BN + wn * 64 + 4 * fr;
         const float sc = p.gate ? p.gate[p.perm[row]] : 1.f;
         const T* au = reinterpret_cast<const T*>(p.aux) + row * p.ldaux;
-        float a[4], u[4], da[4], du[4];
-        load_vec4<T>(au + n, a);
-        load_vec4<T>(au + p.N + n, u);
+        float a[NI], u[NI], da[NI], du[NI];
+        load_vec<T, NI>(au + n, a);
+        load_vec<T, NI>(au + p.N + n, u);
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) {
+        for (int ni = 0; ni < NI; ++ni) {
           const float dh = acc[mi][ni][i] * sc;
           const float sg = sigmoidf_(a[ni]);
           const float si = a[ni] * sg;
           da[ni] = dh * u[ni] * (sg * (1.f + a[ni] * (1.f - sg)));
           du[ni] = dh * si;
         }
-        store_vec<T, 4>(C + row * p.ldc + n, da);
-        store_vec<T, 4>(C + row * p.ldc + p.N + n, du);
+        store_vec<T, NI>(C + row * p.ldc + n, da);
+        store_vec<T, NI>(C + row * p.ldc + p.N + n, du);
       } else if (p.epi == EPI_STORE_F32) {
-        const int n = nt * BN + wn * 64 + 4 * fr;
-        float v[4];
+        float v[NI];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) v[ni] = acc[mi][ni][i];
+        for (int ni = 0; ni < NI; ++ni) v[ni] = acc[mi][ni][i];
         float* Cf = reinterpret_cast<float*>(p.C) + (long long)e * p.c_estride;
-        store_vec<float, 4>(Cf + row * p.ldc + n, v);
+        store_vec<float, NI>(Cf + row * p.ldc + n, v);
       } else {  // EPI_STORE
-        const int n = nt * BN + wn * 64 + 4 * fr;
-        float v[4];
+        float v[NI];
 #pragma unroll
-        for (int ni = 0; ni < 4; ++ni) v[ni] = acc[mi][ni][i];
-        store_vec<T, 4>(C + row * p.ldc + n, v);
+        for (int ni = 0; ni < NI; ++ni) v[ni] = acc[mi][ni][i];
+        store_vec<T, NI>(C + row * p.ldc + n, v);
       }
     }
   }
@@ -377,7 +398,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
 
 int job_chunks(const GemmJob& j) {
   const int nbn = n_tiles(j);
-  const long long groups = (j.max_items + 7) / 8;
+  const long long groups = (max_item_count(j) + 7) / 8;
   return (int)(groups * nbn);
 }
 
@@ -391,9 +412,9 @@ void launch_dtype(GemmArgs a, hipStream_t s) {
   if (total == 0) return;
   const dim3 grid((unsigned)(total * 8));
   if (a.job[0].epi == EPI_SWIGLU)
-    hipLaunchKernelGGL((gemm_kernel<T, true, kStages>), grid, dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<T, true>), grid, dim3(NTHR), 0, s, a);
   else
-    hipLaunchKernelGGL((gemm_kernel<T, false, kStages>), grid, dim3(NTHR), 0, s, a);
+    hipLaunchKernelGGL((gemm_kernel<T, false>), grid, dim3(NTHR), 0, s, a);
 }
 
 }  // namespace

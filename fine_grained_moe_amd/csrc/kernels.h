@@ -58,10 +58,10 @@ struct GemmJob {
   const int32_t* tile_count;
   const int32_t* offsets;
   const int32_t* counts;
-  int max_items;           // upper bound of the item count (sizes the grid)
-  // per-expert contraction ranges (weight gradients): item = (expert, 128-row
+  int max_items;           // grouped jobs: upper bound of the tile count (sizes the grid)
+  // per-expert contraction ranges (weight gradients): item = (expert, row
   // tile of M); expert e contracts over K elements [kofs[e], kofs[e] + klen[e])
-  // of every A and B row and writes C + e * c_estride.  klen[e] % (128 bytes) == 0.
+  // of every A and B row and writes C + e * c_estride.  klen[e] % (64 bytes) == 0.
   int kgroup;
   int nexp;
   const int32_t* kofs;
