@@ -21,7 +21,7 @@ size_t act_bytes(int act) { return act == MOE_BF16 ? 2 : 4; }
 
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
-  size_t block_counts, block_base, tile_e, tile_m0, tile_count;
+  size_t block_counts, rank, tile_e, tile_m0, tile_count;
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
   // backward scratch (training): padded contraction tables and transposed operands
@@ -67,7 +67,7 @@ Layout make_layout(const moe_dims& d, int training) {
   size_t o = 0;
   auto take = [&](size_t bytes) { const size_t at = o; o = align_up(o + std::max<size_t>(bytes, 1)); return at; };
   L.block_counts = take(nblk * d.E * 4);
-  L.block_base = take(nblk * d.E * 4);
+  L.rank = take(slots * 4);
   L.tile_e = take(tiles * 4);
   L.tile_m0 = take(tiles * 4);
   L.tile_count = take(4);
@@ -160,10 +160,12 @@ P* at(void* ws, size_t off) {
 void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void* w_router, const float* bias,
                    const moe_routing* r, void* ws, hipStream_t s) {
   const int nblk = route_blocks(d.T);
-  launch_route_topk(d.act, x, w_router, bias, d.T, d.d, d.E, d.k, r->idx, r->gate, at<int32_t>(ws, L.block_counts), s);
-  launch_route_scan(at<int32_t>(ws, L.block_counts), nblk, d.E, r->counts, r->offsets, at<int32_t>(ws, L.block_base),
-                    at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count), s);
-  launch_route_scatter(r->idx, at<int32_t>(ws, L.block_base), d.T, d.E, d.k, r->perm, r->pos, s);
+  launch_route_topk(d.act, x, w_router, bias, d.T, d.d, d.E, d.k, r->idx, r->gate, at<int32_t>(ws, L.block_counts),
+                    at<int32_t>(ws, L.rank), s);
+  launch_route_dispatch(at<int32_t>(ws, L.block_counts), r->idx, at<int32_t>(ws, L.rank), nblk, d.T, d.E, d.k,
+                        r->counts, r->offsets,
+                        at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count), r->perm,
+                        r->pos, s);
 }
 
 moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }

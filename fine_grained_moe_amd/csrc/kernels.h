@@ -17,12 +17,10 @@ inline long long max_group_tiles(long long slots, int E) { return (slots + (long
 
 // act: 0 = float32, 1 = bfloat16 (moe_dtype values).
 void launch_route_topk(int act, const void* x, const void* w_router, const float* bias, int T, int d, int E,
-                       int k, int32_t* idx, float* gate, int32_t* block_counts, hipStream_t s);
-void launch_route_scan(const int32_t* block_counts, int nblk, int E, int32_t* counts, int32_t* offsets,
-                       int32_t* block_base, int32_t* tile_e, int32_t* tile_m0, int32_t* tile_count,
-                       hipStream_t s);
-void launch_route_scatter(const int32_t* idx, const int32_t* block_base, int T, int E, int k, int32_t* perm,
-                          int32_t* pos, hipStream_t s);
+                       int k, int32_t* idx, float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s);
+void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
+                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* tile_e, int32_t* tile_m0,
+                           int32_t* tile_count, int32_t* perm, int32_t* pos, hipStream_t s);
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s);
 
 enum Epilogue {

@@ -10,199 +10,262 @@
 namespace fgmoe {
 
 // ---------------------------------------------------------------------------
-// Router logits + sigmoid + bias + wave-level top-k + gates + block histogram.
+// Router logits + sigmoid + bias + top-k + gates + per-block loads and ranks.
 //
-// A workgroup owns 16 tokens; wave w computes their logits for experts
-// 16w..16w+15 as one 16x16 MFMA tile, accumulated over d in 128-byte chunks
-// read straight from HBM (x) and L2 (the 128 KiB router matrix).  The tile
-// goes through LDS so that each token's E logits sit one per lane; each wave
-// then selects for 4 tokens: k rounds of a 64-lane max-reduction over
-// (score + bias, 63 - expert) keys, which gives the larger key and, on an
-// exact tie, the lower expert.  Gates are the selected scores divided by
-// their sum.  Per-block expert counts go to block_counts (LDS integer
-// atomics, so the counts are exact).
+// A workgroup of 8 waves owns 16 tokens.  The contraction over d is cut into
+// 128-byte chunks dealt to the waves round-robin; for each of its chunks a
+// wave multiplies the 16 token rows by all 64 router rows (four 16x16 MFMA
+// tiles), so every byte of x and of the 128 KiB router matrix is loaded once
+// per workgroup, and all of a wave's loads are requested before its first
+// product (the kernel is bound by load latency).  The 8 partial tiles meet in
+// LDS and are added in a fixed order.
+//
+// Selection: 32 lanes per token, two experts per lane.  A lane keeps its k
+// best keys (score + bias, then the lower expert on an exact tie, packed as
+// one 64-bit key), then five butterfly merges combine the 32 lanes, which
+// gives the top-k of s + b in descending order with ties to the lower expert.  Gates are the selected scores divided by their sum.
+// Per-block expert counts go to block_counts; rank[t*k + j] is the number of
+// earlier assignments (t', j') of the same block with the same expert, which
+// the dispatch kernel turns into the slot.
 // ---------------------------------------------------------------------------
-template <typename T>
-__global__ __launch_bounds__(256) void route_topk_kernel(const T* __restrict__ x, const T* __restrict__ wr,
+constexpr int kRouteWaves = 8;
+constexpr int kRouteMaxK = 8;
+
+__device__ __forceinline__ uint64_t route_key(float v, int e) {
+  return ((uint64_t)float_key(v) << 32) | (uint32_t)(63 - e);
+}
+// Insert key c into the descending list l[0..K-1] (K is a compile-time
+// constant, so this is straight-line compare-and-select code).
+template <int K>
+__device__ __forceinline__ void route_insert(uint64_t (&l)[K], uint64_t c) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) {
+    const bool gt = c > l[i];
+    const uint64_t t = l[i];
+    l[i] = gt ? c : t;
+    c = gt ? t : c;
+  }
+}
+
+template <typename T, int K>
+__global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x, const T* __restrict__ wr,
                                                          const float* __restrict__ bias, int T_, int d, int E,
-                                                         int k, int32_t* __restrict__ idx,
+                                                         int32_t* __restrict__ idx,
                                                          float* __restrict__ gate,
-                                                         int32_t* __restrict__ block_counts) {
-  __shared__ float lg[16][65];
+                                                         int32_t* __restrict__ block_counts,
+                                                         int32_t* __restrict__ rank) {
+  __shared__ float part[kRouteWaves][16][65];
+  __shared__ float lgs[16][65];
+  __shared__ int sel[16 * K];
+  constexpr int k = K;
   __shared__ int hist[64];
+  __shared__ float bias_s[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
-  if (tid < 64) hist[tid] = 0;
+  if (tid < 64) {
+    hist[tid] = 0;
+    bias_s[tid] = tid < E ? bias[tid] : 0.f;
+  }
 
+  // ---- partial logits of this wave's chunks
   const int tok0 = blockIdx.x * kRouteTokensPerBlock;
-  if (wave * 16 < E) {
-    const int t = min(tok0 + r, T_ - 1);          // rows past T re-read the last token; never used
-    const int e = min(wave * 16 + r, E - 1);      // columns past E likewise
-    const char* xrow = reinterpret_cast<const char*>(x + (long long)t * d) + g * 32;
-    const char* wrow = reinterpret_cast<const char*>(wr + (long long)e * d) + g * 32;
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    const int nch = (int)((long long)d * sizeof(T) / 128);
-    // four chunks in flight: chunk c + 4 is requested as chunk c is multiplied
-    Frag a[4], b[4];
-    auto load = [&](int c, Frag& fa, Frag& fb) {
-      fa.lo = ld16(xrow + c * 128);
-      fa.hi = ld16(xrow + c * 128 + 16);
-      fb.lo = ld16(wrow + c * 128);
-      fb.hi = ld16(wrow + c * 128 + 16);
-    };
+  const int t = min(tok0 + r, T_ - 1);          // rows past T re-read the last token; never used
+  const char* xrow = reinterpret_cast<const char*>(x + (long long)t * d) + g * 32;
+  const char* wrow[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (j < nch) load(j, a[j], b[j]);
-    for (int c = 0; c < nch; c += 4) {
+  for (int et = 0; et < 4; ++et)                 // rows past E re-read the last expert; never selected
+    wrow[et] = reinterpret_cast<const char*>(wr + (long long)min(et * 16 + r, E - 1) * d) + g * 32;
+  const int nch = (int)((long long)d * sizeof(T) / 128);
+  f32x4_t acc[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        if (c + j < nch) {
-          acc = Mma<T>::run(a[j], b[j], acc);
-          if (c + j + 4 < nch) load(c + j + 4, a[j], b[j]);
-        }
+  for (int et = 0; et < 4; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int c0 = wave; c0 < nch; c0 += 2 * kRouteWaves) {
+    // up to two chunks (c0 and c0 + 8) in flight; a missing second chunk
+    // re-reads the first and is multiplied as zeros
+    const int c1 = c0 + kRouteWaves < nch ? c0 + kRouteWaves : c0;
+    Frag a[2], b[2][4];
+#pragma unroll
+    for (int h = 0; h < 2; ++h) {
+      const int c = h ? c1 : c0;
+      a[h].lo = ld16(xrow + c * 128);
+      a[h].hi = ld16(xrow + c * 128 + 16);
+#pragma unroll
+      for (int et = 0; et < 4; ++et) {
+        b[h][et].lo = ld16(wrow[et] + c * 128);
+        b[h][et].hi = ld16(wrow[et] + c * 128 + 16);
       }
     }
+    __builtin_amdgcn_sched_barrier(0);   // keep every load ahead of the products
+    if (c1 == c0) a[1].lo = a[1].hi = u32x4_t{0u, 0u, 0u, 0u};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) lg[4 * g + i][wave * 16 + r] = acc[i];
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int et = 0; et < 4; ++et) acc[et] = Mma<T>::run(a[h], b[h][et], acc[et]);
+  }
+#pragma unroll
+  for (int et = 0; et < 4; ++et)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) part[wave][4 * g + i][et * 16 + r] = acc[et][i];
+  __syncthreads();
+  for (int q = tid; q < 16 * 64; q += 512) {     // fixed-order sum of the 8 partial tiles
+    const int tt = q >> 6, e = q & 63;
+    float l = 0.f;
+#pragma unroll
+    for (int w = 0; w < kRouteWaves; ++w) l += part[w][tt][e];
+    lgs[tt][e] = l;
   }
   __syncthreads();
 
-  const float b_e = lane < E ? bias[lane] : 0.f;
-  for (int tt = wave * 4; tt < wave * 4 + 4; ++tt) {
-    const int tok = tok0 + tt;
-    if (tok >= T_) break;
-    const float l = lane < E ? lg[tt][lane] : 0.f;
-    const float s = 1.0f / (1.0f + expf(-l));
-    const float v = s + b_e;
-    bool taken = lane >= E;
-    int esel[8];
-    float ssel[8];
-    float ssum = 0.f;
+  // ---- selection: wave w takes tokens 2w and 2w+1; lane (t = lane / 32,
+  // u = lane % 32) holds experts 2u and 2u+1 of its token, and five butterfly
+  // merges over the token's 32 lanes leave the token's top-k in every one.
+  {
+    const int tt = 2 * wave + (lane >> 5), u = lane & 31;
+    uint64_t best[K];
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      if (j >= k) break;
-      uint32_t hi = taken ? 0u : float_key(v);
-      uint32_t lo = taken ? 0u : (uint32_t)(63 - lane);
+    for (int i = 0; i < K; ++i) best[i] = 0;
 #pragma unroll
-      for (int off = 32; off >= 1; off >>= 1) {
-        const uint32_t ohi = __shfl_xor(hi, off);
-        const uint32_t olo = __shfl_xor(lo, off);
-        const bool take = (ohi > hi) || (ohi == hi && olo > lo);
-        hi = take ? ohi : hi;
-        lo = take ? olo : lo;
-      }
-      const int w = 63 - (int)lo;
-      const float sw = __shfl(s, w);
-      if (lane == w) taken = true;
-      esel[j] = w;
-      ssel[j] = sw;
-      ssum += sw;
+    for (int i = 0; i < 2; ++i) {
+      const int e = 2 * u + i;
+      const float sc = 1.0f / (1.0f + expf(-lgs[tt][min(e, 63)]));
+      if (e < E) route_insert<K>(best, route_key(sc + bias_s[e], e));
     }
-    if (lane == 0) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        if (j >= k) break;
-        idx[(long long)tok * k + j] = esel[j];
-        gate[(long long)tok * k + j] = ssel[j] / ssum;
-        atomicAdd(&hist[esel[j]], 1);
+    for (int off = 1; off <= 16; off <<= 1) {
+      uint64_t other[K];
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const uint32_t lo = __shfl_xor((uint32_t)best[i], off), hi = __shfl_xor((uint32_t)(best[i] >> 32), off);
+        other[i] = ((uint64_t)hi << 32) | lo;
       }
+#pragma unroll
+      for (int i = 0; i < K; ++i) route_insert<K>(best, other[i]);
+    }
+    const int tok = tok0 + tt;
+    if (u == 0 && tok < T_) {
+      float ssel[K];
+      float ssum = 0.f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int e = 63 - (int)(uint32_t)best[j];
+        ssel[j] = 1.0f / (1.0f + expf(-lgs[tt][e]));
+        ssum += ssel[j];
+        sel[tt * K + j] = e;
+        idx[(long long)tok * K + j] = e;
+        atomicAdd(&hist[e], 1);
+      }
+#pragma unroll
+      for (int j = 0; j < K; ++j) gate[(long long)tok * K + j] = ssel[j] / ssum;
     }
   }
   __syncthreads();
   if (tid < E) block_counts[(long long)blockIdx.x * E + tid] = hist[tid];
+  const int na = min(kRouteTokensPerBlock, T_ - tok0) * k;
+  if (tid < na) {
+    const int e = sel[tid];
+    int rk = 0;
+    for (int b = 0; b < tid; ++b) rk += (sel[b] == e) ? 1 : 0;
+    rank[(long long)tok0 * k + tid] = rk;
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Loads, offsets and the grouped-GEMM tile table (one workgroup of 1024).
-// counts[e] = sum over routing blocks; offsets = exclusive scan over experts;
-// block_base[b][e] = offsets[e] + loads of expert e in blocks before b; the
-// tile table lists (expert, first row) for every kTileM rows of each expert,
-// in expert order.
+// Loads, offsets, the grouped-GEMM tile table and the dispatch order, in one
+// launch without a grid-wide barrier.  A dispatch block of 1024 threads owns
+// kDispatchSub router blocks (256 tokens); it sums the per-router-block expert
+// counts itself (all of them for the loads, those before its first router
+// block for its prefix), so every block knows
+//   slot(t, j) = offsets[e] + sum over earlier router blocks of their loads of e
+//                + rank(t, j) (earlier assignments to e in t's router block),
+// i.e. slots of an expert ascend in t*k + j, independent of scheduling.
+// Block 0 also writes counts, offsets and the tile table, which lists
+// (expert, first row) for every kTileM rows of each expert, in expert order.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void route_scan_kernel(const int32_t* __restrict__ block_counts, int nblk,
-                                                          int E, int32_t* __restrict__ counts,
-                                                          int32_t* __restrict__ offsets,
-                                                          int32_t* __restrict__ block_base,
-                                                          int32_t* __restrict__ tile_e,
-                                                          int32_t* __restrict__ tile_m0,
-                                                          int32_t* __restrict__ tile_count) {
-  __shared__ int part_sum[16][64];
+constexpr int kDispatchSub = 16;
+constexpr int kDispatchBatch = 16;   // count loads a thread keeps in flight
+__global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __restrict__ block_counts,
+                                                              const int32_t* __restrict__ idx,
+                                                              const int32_t* __restrict__ rank, int nblk, int T_,
+                                                              int E, int k, int32_t* __restrict__ counts,
+                                                              int32_t* __restrict__ offsets,
+                                                              int32_t* __restrict__ tile_e,
+                                                              int32_t* __restrict__ tile_m0,
+                                                              int32_t* __restrict__ tile_count,
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+  __shared__ int part_tot[16][64];
   __shared__ int part_pre[16][64];
-  __shared__ int off_s[64];
+  __shared__ int sub_cnt[kDispatchSub][64];
+  __shared__ int base[kDispatchSub][64];
   const int tid = threadIdx.x, e = tid & 63, part = tid >> 6;
-  const int chunk = (nblk + 15) / 16;
-  const int b0 = min(nblk, part * chunk), b1 = min(nblk, b0 + chunk);
-  int s = 0;
-  if (e < E) {
-#pragma unroll 8
-    for (int b = b0; b < b1; ++b) s += block_counts[(long long)b * E + e];
-  }
-  part_sum[part][e] = s;
-  __syncthreads();
-  if (part == 0) {
-    int run = 0;
-    for (int p = 0; p < 16; ++p) {
-      part_pre[p][e] = run;
-      run += part_sum[p][e];
+  const int first = blockIdx.x * kDispatchSub;   // first router block of this dispatch block
+
+  // loads of every router block: thread (part, e) takes blocks part, part + 16, ...;
+  // the prefix counts only blocks before `first`
+  int tot = 0, pre = 0;
+  const int ec = min(e, E - 1);
+  for (int b0 = part; b0 < nblk; b0 += 16 * kDispatchBatch) {
+    int v[kDispatchBatch];
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j)
+      v[j] = block_counts[(long long)min(b0 + 16 * j, nblk - 1) * E + ec];
+#pragma unroll
+    for (int j = 0; j < kDispatchBatch; ++j) {
+      const int b = b0 + 16 * j;
+      const int vv = (b < nblk && e < E) ? v[j] : 0;
+      tot += vv;
+      pre += b < first ? vv : 0;
     }
-    const int cnt = e < E ? run : 0;
+  }
+  part_tot[part][e] = tot;
+  part_pre[part][e] = pre;
+  sub_cnt[part][e] = (e < E && first + part < nblk) ? block_counts[(long long)(first + part) * E + e] : 0;
+  __syncthreads();
+
+  if (part == 0) {
+    int cnt = 0, pr = 0;
+    for (int q = 0; q < 16; ++q) {
+      cnt += part_tot[q][e];
+      pr += part_pre[q][e];
+    }
+    if (e >= E) cnt = 0;
     int incl = cnt;
     for (int off = 1; off < 64; off <<= 1) {
       const int o = __shfl_up(incl, off);
       if (e >= off) incl += o;
     }
     const int excl = incl - cnt;
-    off_s[e] = excl;
-    if (e < E) {
-      counts[e] = cnt;
-      offsets[e] = excl;
+    int run = excl + pr;
+    for (int sb = 0; sb < kDispatchSub; ++sb) {
+      base[sb][e] = run;
+      run += sub_cnt[sb][e];
     }
-    if (e == E - 1) offsets[E] = incl;
-    const int nt = (cnt + kTileM - 1) / kTileM;
-    int tincl = nt;
-    for (int off = 1; off < 64; off <<= 1) {
-      const int o = __shfl_up(tincl, off);
-      if (e >= off) tincl += o;
+    if (blockIdx.x == 0) {
+      if (e < E) {
+        counts[e] = cnt;
+        offsets[e] = excl;
+      }
+      if (e == E - 1) offsets[E] = incl;
+      const int nt = (cnt + kTileM - 1) / kTileM;
+      int tincl = nt;
+      for (int off = 1; off < 64; off <<= 1) {
+        const int o = __shfl_up(tincl, off);
+        if (e >= off) tincl += o;
+      }
+      const int texcl = tincl - nt;
+      for (int m = 0; m < nt; ++m) {
+        tile_e[texcl + m] = e;
+        tile_m0[texcl + m] = m * kTileM;
+      }
+      if (e == 63) *tile_count = tincl;
     }
-    const int texcl = tincl - nt;
-    for (int m = 0; m < nt; ++m) {
-      tile_e[texcl + m] = e;
-      tile_m0[texcl + m] = m * kTileM;
-    }
-    if (e == 63) *tile_count = tincl;
   }
   __syncthreads();
-  if (e < E) {
-    int run = off_s[e] + part_pre[part][e];
-#pragma unroll 8
-    for (int b = b0; b < b1; ++b) {
-      block_base[(long long)b * E + e] = run;
-      run += block_counts[(long long)b * E + e];
-    }
-  }
-}
 
-// ---------------------------------------------------------------------------
-// Dispatch order: slot of (t, j) = block_base[block][e] + number of earlier
-// assignments of the same block to e.  Slots of an expert therefore ascend in
-// t*k + j, independent of scheduling.
-// ---------------------------------------------------------------------------
-__global__ __launch_bounds__(256) void route_scatter_kernel(const int32_t* __restrict__ idx,
-                                                            const int32_t* __restrict__ block_base, int T_,
-                                                            int E, int k, int32_t* __restrict__ perm,
-                                                            int32_t* __restrict__ pos) {
-  __shared__ int ids[kRouteTokensPerBlock * 8];
-  const int blk = blockIdx.x;
-  const long long a0 = (long long)blk * kRouteTokensPerBlock * k;
-  const int nt = min(kRouteTokensPerBlock, T_ - blk * kRouteTokensPerBlock);
-  const int na = nt * k;
-  for (int a = threadIdx.x; a < na; a += blockDim.x) ids[a] = idx[a0 + a];
-  __syncthreads();
-  for (int a = threadIdx.x; a < na; a += blockDim.x) {
-    const int e = ids[a];
-    int rank = 0;
-    for (int b = 0; b < a; ++b) rank += (ids[b] == e) ? 1 : 0;
-    const int slot = block_base[(long long)blk * E + e] + rank;
+  const long long a0 = (long long)first * kRouteTokensPerBlock * k;
+  const int ntok = max(0, min(kDispatchSub * kRouteTokensPerBlock, T_ - first * kRouteTokensPerBlock));
+  const int na = ntok * k, per = kRouteTokensPerBlock * k;
+  for (int a = tid; a < na; a += 1024) {
+    const int slot = base[a / per][idx[a0 + a]] + rank[a0 + a];
     perm[slot] = (int32_t)(a0 + a);
     pos[a0 + a] = slot;
   }
@@ -221,30 +284,41 @@ __global__ void bias_update_kernel(int E, long long total, const int32_t* __rest
   }
 }
 
+template <typename A, int K>
+void launch_topk_k(const void* x, const void* w_router, const float* bias, int T, int d, int E, int32_t* idx,
+                   float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
+  hipLaunchKernelGGL((route_topk_kernel<A, K>), dim3(route_blocks(T)), dim3(512), 0, s, (const A*)x,
+                     (const A*)w_router, bias, T, d, E, idx, gate, block_counts, rank);
+}
+template <typename A>
+void launch_topk_t(const void* x, const void* w_router, const float* bias, int T, int d, int E, int k, int32_t* idx,
+                   float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
+  switch (k) {
+    case 1: launch_topk_k<A, 1>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    case 2: launch_topk_k<A, 2>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    case 3: launch_topk_k<A, 3>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    case 4: launch_topk_k<A, 4>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    case 5: launch_topk_k<A, 5>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    case 6: launch_topk_k<A, 6>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    case 7: launch_topk_k<A, 7>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+    default: launch_topk_k<A, 8>(x, w_router, bias, T, d, E, idx, gate, block_counts, rank, s); break;
+  }
+}
+
+// k is 1..8 (checked on the host).
 void launch_route_topk(int act, const void* x, const void* w_router, const float* bias, int T, int d, int E,
-                       int k, int32_t* idx, float* gate, int32_t* block_counts, hipStream_t s) {
-  const int nblk = route_blocks(T);
-  if (nblk == 0) return;
-  if (act == 1)
-    hipLaunchKernelGGL(route_topk_kernel<bf16_t>, dim3(nblk), dim3(256), 0, s, (const bf16_t*)x,
-                       (const bf16_t*)w_router, bias, T, d, E, k, idx, gate, block_counts);
-  else
-    hipLaunchKernelGGL(route_topk_kernel<float>, dim3(nblk), dim3(256), 0, s, (const float*)x,
-                       (const float*)w_router, bias, T, d, E, k, idx, gate, block_counts);
+                       int k, int32_t* idx, float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
+  if (route_blocks(T) == 0) return;
+  if (act == 1) launch_topk_t<bf16_t>(x, w_router, bias, T, d, E, k, idx, gate, block_counts, rank, s);
+  else launch_topk_t<float>(x, w_router, bias, T, d, E, k, idx, gate, block_counts, rank, s);
 }
 
-void launch_route_scan(const int32_t* block_counts, int nblk, int E, int32_t* counts, int32_t* offsets,
-                       int32_t* block_base, int32_t* tile_e, int32_t* tile_m0, int32_t* tile_count,
-                       hipStream_t s) {
-  hipLaunchKernelGGL(route_scan_kernel, dim3(1), dim3(1024), 0, s, block_counts, nblk, E, counts, offsets,
-                     block_base, tile_e, tile_m0, tile_count);
-}
-
-void launch_route_scatter(const int32_t* idx, const int32_t* block_base, int T, int E, int k, int32_t* perm,
-                          int32_t* pos, hipStream_t s) {
-  const int nblk = route_blocks(T);
-  if (nblk == 0) return;
-  hipLaunchKernelGGL(route_scatter_kernel, dim3(nblk), dim3(128), 0, s, idx, block_base, T, E, k, perm, pos);
+void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
+                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* tile_e, int32_t* tile_m0,
+                           int32_t* tile_count, int32_t* perm, int32_t* pos, hipStream_t s) {
+  const int grid = nblk > 0 ? (nblk + kDispatchSub - 1) / kDispatchSub : 1;   // block 0 runs even for T = 0
+  hipLaunchKernelGGL(route_dispatch_kernel, dim3(grid), dim3(1024), 0, s, block_counts, idx, rank, nblk, T, E, k,
+                     counts, offsets, tile_e, tile_m0, tile_count, perm, pos);
 }
 
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s) {
