@@ -109,6 +109,9 @@ struct DecodeArgs {
   int32_t* n_active;                 // [1]
   uint16_t* Hs;                      // [T, Fs] bf16 (workspace)
   uint16_t* H;                       // [T*k, F] bf16 (workspace)
+  float* lpart;                      // [4, T, 64] fp32 router logit partials (workspace)
+  float* part_sh;                    // [4, T, d] fp32 shared down partials (workspace)
+  float* rout;                       // [T*k, d] fp32 routed down rows (workspace)
   uint16_t* y;                       // [T, d] bf16
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);

@@ -93,3 +93,36 @@ def test_int4_rejects_unsupported_shapes():
     assert moe.moe_workspace_bytes(moe.make_dims(65, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")) == 0
     assert moe.moe_workspace_bytes(moe.make_dims(8, 1024, 64, 512, 2048, 2, "bf16", w_routed="int4")) == 0
     assert moe.moe_workspace_bytes(moe.make_dims(8, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")) > 0
+
+
+def test_int4_decode_graph_replay_matches_eager(weights):
+    """The serving forward captured in a HIP graph gives, on every replay,
+    exactly the eager result (bitwise), with other eager work and host
+    synchronisations between the replays."""
+    import torch
+    from fine_grained_moe_amd import moe
+    dev, _ = weights
+    T = 8
+    inp = synth.make_layer(T=T, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=55)
+    dims = moe.make_dims(T, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+    x = torch.from_numpy(inp.x).to(device="cuda", dtype=torch.bfloat16)
+    bias = torch.zeros(64, device="cuda")
+    y_eager, r_eager, ws_eager = torch.empty_like(x), moe.alloc_routing(dims), moe.alloc_workspace(dims)
+    moe.moe_forward(dims, x, dev, bias, y_eager, r_eager, ws_eager)
+    torch.cuda.synchronize()
+    y, r, ws = torch.empty_like(x), moe.alloc_routing(dims), moe.alloc_workspace(dims)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        moe.moe_forward(dims, x, dev, bias, y, r, ws)
+    other = torch.roll(x, 1, 0).contiguous()
+    y_other = torch.empty_like(x)
+    for rep in range(3):
+        y.fill_(0)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_eager), rep
+        for n in ("idx", "gate", "counts", "offsets", "perm", "pos"):
+            assert torch.equal(r[n], r_eager[n]), (rep, n)
+        # eager work between replays, on the same weights and its own buffers
+        moe.moe_forward(dims, other, dev, bias, y_other, moe.alloc_routing(dims), moe.alloc_workspace(dims))
+        torch.cuda.synchronize()
