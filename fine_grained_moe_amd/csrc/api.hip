@@ -25,7 +25,7 @@ struct Layout {
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
   // backward scratch (training): padded contraction tables and transposed operands
-  size_t kofs, klen, ksh, pcol, dl, dAU, dAUT, XpT, dOT, HT, dXp, WdT, WguT, WsdT, WsguT, dAUs, dAUsT, xT, dyT, HsT,
+  size_t kofs, klen, ksh, pcol, dwr_part, dwpart, dl, dAU, dAUT, XpT, dOT, HT, dXp, WdT, WguT, WsdT, WsguT, dAUs, dAUsT, xT, dyT, HsT,
       dXs;
   long long P, Tp;        // padded column counts of the routed and shared transposes
   size_t active, n_active, lpart, part_sh, rout; // int4 serving path: active experts, fp32 partials
@@ -89,13 +89,16 @@ Layout make_layout(const moe_dims& d, int training) {
     L.Ou = take(slots * d.d * es);
     L.AUs = take((size_t)d.T * 2 * d.Fs * es);
     const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs, T = d.T;
-    L.P = (long long)slots + (long long)E * (kPadK - 1);
+    L.P = pad_k((long long)slots + (long long)E * (kPadK - 1));   // whole 8-element vectors for the transposes
     L.Tp = pad_k(d.T);
     const size_t P = (size_t)L.P, Tp = (size_t)L.Tp;
     L.kofs = take(E * 4);
     L.klen = take(E * 4);
-    L.ksh = take(2 * 4);
+    L.ksh = take(2 * kMaxSplitK * 4);
     L.pcol = take(P * 4);
+    L.dwr_part = take(P / kPadK * D * 4);
+    const int S = splitk_count((long long)Tp);
+    L.dwpart = take(S > 1 ? (size_t)S * std::max(2 * Fs * D, D * Fs) * 4 : 0);
     L.dl = take(slots * 4);
     L.dAU = take(slots * 2 * F * es);
     L.dAUT = take(2 * F * P * es);
@@ -511,7 +514,8 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
 
   mark_phase(0, s);
   // 1. padded per-expert contraction ranges
-  launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, kofs, klen, ksh, pcol, s);
+  const int S = splitk_count(Tp), step = (int)splitk_step(Tp);
+  launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, S, step, kofs, klen, ksh, pcol, s);
 
   // 2. transposed weights: W_d^T [E][F][d], W_gu^T [E][d][2F], W_sd^T [Fs][d], W_sgu^T [d][2Fs]
   auto transpose = [&](const void* src, long long ld_src, long long sb, void* dst, long long ld_dst, long long db, int R,
@@ -664,17 +668,24 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   g3.act = act;
   g3.njobs = 2;
   g3.job[0] = kjob(dAUT, P, XpT, P, 2 * d.F, d.d, d.E, kofs, klen, dw->dw_gate_up, D, 2LL * F * D);
-  g3.job[1] = kjob(dAUsT, Tp, xT, Tp, 2 * d.Fs, d.d, 1, ksh, ksh + 1, dw->dw_sh_gate_up, D, 0);
+  // shared expert: S contraction slices into fp32 partials, then added in order
+  float* dwpart = at<float>(ws, L.dwpart);
+  g3.job[1] = kjob(dAUsT, Tp, xT, Tp, 2 * d.Fs, d.d, S, ksh, ksh + S, S > 1 ? (void*)dwpart : dw->dw_sh_gate_up, D,
+                   2LL * Fs * D);
   launch_gemm(g3, s);
+  if (S > 1) launch_splitk_reduce(dwpart, 2LL * Fs * D, S, (float*)dw->dw_sh_gate_up, s);
   GemmArgs g4{};
   g4.act = act;
   g4.njobs = 2;
   g4.job[0] = kjob(dOT, P, HT, P, d.d, d.F, d.E, kofs, klen, dw->dw_down, F, (long long)D * F);
-  g4.job[1] = kjob(dyT, Tp, HsT, Tp, d.d, d.Fs, 1, ksh, ksh + 1, dw->dw_sh_down, Fs, 0);
+  g4.job[1] = kjob(dyT, Tp, HsT, Tp, d.d, d.Fs, S, ksh, ksh + S, S > 1 ? (void*)dwpart : dw->dw_sh_down, Fs,
+                   (long long)D * Fs);
   launch_gemm(g4, s);
+  if (S > 1) launch_splitk_reduce(dwpart, (long long)D * Fs, S, (float*)dw->dw_sh_down, s);
 
   // 8. router weight gradient and the input gradient
-  launch_bwd_dwr(act, x, dl, routing->perm, routing->counts, routing->offsets, d.E, d.d, d.k, dw->dw_router, s);
+  launch_bwd_dwr(act, x, dl, routing->perm, pcol, P, kofs, klen, d.E, d.d, d.k, at<float>(ws, L.dwr_part),
+                 dw->dw_router, s);
   launch_bwd_dx(act, dXs, dXp, w->w_router, dl, routing->idx, routing->pos, d.T, d.d, d.k, dx, s);
   mark_phase(1, s);
   return device_status();

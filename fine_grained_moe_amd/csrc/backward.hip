@@ -12,7 +12,8 @@
 //
 // The weight gradients contract over tokens, i.e. over the rows of the
 // stored activations; they run on the same NT GEMM as the forward after the
-// operands are transposed here.  Each expert's rows are laid out in its own
+// operands are transposed here.  (d, F and Fs are multiples of 128, so every
+// row here is a whole number of 8-element vectors.)  Each expert's rows are laid out in its own
 // column range padded to a multiple of 64 with zeros, so that a grouped GEMM
 // with a per-expert contraction range can run over it.
 #include "common.h"
@@ -25,13 +26,15 @@ namespace {
 // ---------------------------------------------------------------------------
 // Per-expert padded column ranges: klen[e] = roundup(count[e], 64),
 // kofs = exclusive scan; pcol[c] = slot held by padded column c, or -1.
-// Also the single-range tables of the shared expert: kofs_sh = 0, klen_sh = Tp.
-// One workgroup of 1024 threads.
+// Also the tables of the shared expert's weight gradients, whose contraction
+// over Tp tokens is split into S slices of `step` columns (a multiple of 64):
+// ksh[i] = i * step, ksh[S + i] = its length.  One workgroup of 1024 threads.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int32_t* __restrict__ counts,
                                                         const int32_t* __restrict__ offsets, int E, int Pmax, int Tp,
-                                                        int32_t* __restrict__ kofs, int32_t* __restrict__ klen,
-                                                        int32_t* __restrict__ ksh, int32_t* __restrict__ pcol) {
+                                                        int S, int step, int32_t* __restrict__ kofs,
+                                                        int32_t* __restrict__ klen, int32_t* __restrict__ ksh,
+                                                        int32_t* __restrict__ pcol) {
   __shared__ int s_kofs[64], s_klen[64];
   const int tid = threadIdx.x;
   if (tid < 64) {
@@ -49,9 +52,9 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int32_t* __restric
       klen[tid] = kl;
     }
   }
-  if (tid == 0) {
-    ksh[0] = 0;
-    ksh[1] = Tp;
+  if (tid < S) {
+    ksh[tid] = tid * step;
+    ksh[S + tid] = max(0, min(step, Tp - tid * step));
   }
   __syncthreads();
   for (int c = tid; c < Pmax; c += blockDim.x) pcol[c] = -1;
@@ -62,24 +65,58 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int32_t* __restric
   }
 }
 
+// 8 consecutive values of T as float, and back (16 bytes for bf16, 32 for float).
+template <typename T>
+__device__ __forceinline__ void load8(const T* p, float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    const u32x4_t w = ld16(p);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[2 * i] = bf16_to_f32((bf16_t)(w[i] & 0xFFFFu));
+      v[2 * i + 1] = bf16_to_f32((bf16_t)(w[i] >> 16));
+    }
+  } else {
+    const u32x4_t a = ld16(p), b = ld16(p + 4);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      v[i] = __uint_as_float(a[i]);
+      v[4 + i] = __uint_as_float(b[i]);
+    }
+  }
+}
+template <typename T>
+__device__ __forceinline__ void store8(T* p, const float (&v)[8]) {
+  if constexpr (sizeof(T) == 2) {
+    u32x4_t w;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) w[i] = (uint32_t)f32_to_bf16(v[2 * i]) | ((uint32_t)f32_to_bf16(v[2 * i + 1]) << 16);
+    st16(p, w);
+  } else {
+    st16(p, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
+    st16(p + 4, u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]), __float_as_uint(v[6]), __float_as_uint(v[7])});
+  }
+}
+
 // ---------------------------------------------------------------------------
 // Gather-transpose: dst[b][r][c] = scale * src[b][row(c)][r], for r < R and
 // c < C, where row(c) is c (c < n_in), map1[c] (>= 0), or, with map2,
 // map2[map1[c]] / div; a column without a row is zero.  The scale is
-// scale[map2 ? map2[map1[c]] : map1[c]] when given.  64 x 64 tiles via LDS.
+// scale[map2 ? map2[map1[c]] : map1[c]] when given.  64 x 64 tiles through
+// LDS; every global access moves 8 consecutive elements (R and C are
+// multiples of 8, as are the leading dimensions).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
-  __shared__ float tile[64][65];
-  const int tx = threadIdx.x & 63, ty = threadIdx.x >> 6;
+  __shared__ float tile[64][65];                     // [c][r]
+  const int tid = threadIdx.x;
   const int c0 = blockIdx.x * 64, r0 = blockIdx.y * 64;
   const T* src = reinterpret_cast<const T*>(a.src) + (long long)blockIdx.z * a.src_bstride;
   T* dst = reinterpret_cast<T*>(a.dst) + (long long)blockIdx.z * a.dst_bstride;
-  const int r = r0 + tx;
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int cl = ty * 16 + i, c = c0 + cl;
-    float v = 0.f;
+  // load: thread (cl = tid / 8 + 32h, rq = tid % 8) reads r0 + 8rq .. +7 of column c0 + cl's source row
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int cl = (tid >> 3) + 32 * h, rq = tid & 7, c = c0 + cl, r = r0 + 8 * rq;
+    float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     if (c < a.C && r < a.R) {
       int m = a.map1 ? a.map1[c] : (c < a.n_in ? c : -1);
       if (m >= 0) {
@@ -88,24 +125,36 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
           sidx = a.map2[m];
           m = sidx / a.div;
         }
-        v = to_f32<T>(src[(long long)m * a.ld_src + r]);
-        if (a.scale) v *= a.scale[sidx];
+        load8<T>(src + (long long)m * a.ld_src + r, v);
+        if (a.scale) {
+          const float sc = a.scale[sidx];
+#pragma unroll
+          for (int i = 0; i < 8; ++i) v[i] *= sc;
+        }
       }
     }
-    tile[cl][tx] = v;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) tile[cl][8 * rq + i] = v[i];
   }
   __syncthreads();
-#pragma unroll 4
-  for (int i = 0; i < 16; ++i) {
-    const int rl = ty * 16 + i, rr = r0 + rl, c = c0 + tx;
-    if (rr < a.R && c < a.C) dst[(long long)rr * a.ld_dst + c] = from_f32<T>(tile[tx][rl]);
+  // store: thread (rl = tid / 8 + 32h, cq = tid % 8) writes c0 + 8cq .. +7 of row r0 + rl
+#pragma unroll
+  for (int h = 0; h < 2; ++h) {
+    const int rl = (tid >> 3) + 32 * h, cq = tid & 7, rr = r0 + rl, c = c0 + 8 * cq;
+    if (rr < a.R && c < a.C) {
+      float v[8];
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v[i] = tile[8 * cq + i][rl];
+      store8<T>(dst + (long long)rr * a.ld_dst + c, v);
+    }
   }
 }
 
 // ---------------------------------------------------------------------------
 // Router and gate gradients, one wave per token: dg_j = <dy_t, o_j>; the
 // selected scores are recomputed from the logits x_t . W_r[e_j]; then the
-// formulas at the top of this file.  dl: [T, k] fp32.
+// formulas at the top of this file.  dl: [T, k] fp32.  Each lane takes 16
+// consecutive elements of every row (all of its loads in flight at once).
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy, const T* __restrict__ ou,
@@ -116,17 +165,43 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
+  int e[8];
+  long long slot[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (j < k) {
+      e[j] = idx[(long long)t * k + j];
+      slot[j] = pos[(long long)t * k + j];
+    }
+  float dga[8], sb[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) dga[j] = sb[j] = 0.f;
+  for (int c = lane * 16; c < d; c += 1024) {
+    float vdy[16], vx[16];
+    load8<T>(dy + (long long)t * d + c, *reinterpret_cast<float(*)[8]>(vdy));
+    load8<T>(dy + (long long)t * d + c + 8, *reinterpret_cast<float(*)[8]>(vdy + 8));
+    load8<T>(x + (long long)t * d + c, *reinterpret_cast<float(*)[8]>(vx));
+    load8<T>(x + (long long)t * d + c + 8, *reinterpret_cast<float(*)[8]>(vx + 8));
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      if (j >= k) break;
+      float vo[16], vw[16];
+      load8<T>(ou + slot[j] * d + c, *reinterpret_cast<float(*)[8]>(vo));
+      load8<T>(ou + slot[j] * d + c + 8, *reinterpret_cast<float(*)[8]>(vo + 8));
+      load8<T>(wr + (long long)e[j] * d + c, *reinterpret_cast<float(*)[8]>(vw));
+      load8<T>(wr + (long long)e[j] * d + c + 8, *reinterpret_cast<float(*)[8]>(vw + 8));
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        dga[j] += vdy[i] * vo[i];
+        sb[j] += vx[i] * vw[i];
+      }
+    }
+  }
   float dg[8], s[8];
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
     if (j >= k) break;
-    const int e = idx[(long long)t * k + j];
-    const long long slot = pos[(long long)t * k + j];
-    float a = 0.f, b = 0.f;
-    for (int c = lane; c < d; c += 64) {
-      a += to_f32<T>(dy[(long long)t * d + c]) * to_f32<T>(ou[slot * d + c]);
-      b += to_f32<T>(x[(long long)t * d + c]) * to_f32<T>(wr[(long long)e * d + c]);
-    }
+    float a = dga[j], b = sb[j];
 #pragma unroll
     for (int o = 32; o >= 1; o >>= 1) {
       a += __shfl_xor(a, o);
@@ -152,43 +227,123 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
 }
 
 // ---------------------------------------------------------------------------
-// dW_r[e][c] = sum over the slots of e, in slot order, of dl[perm[s]] * x[token][c].
+// Router weight gradient dW_r[e][c] = sum over the slots of e of
+// dl[perm[s]] * x[token][c], in two passes.  Pass 1: one workgroup per
+// 64-column chunk of the padded slot layout (every chunk lies inside one
+// expert's range); its two halves each sum 32 slots in slot order for every
+// column, and chunk partial = half 0 + half 1.  Pass 2: dW_r[e] = the
+// partials of e's chunks added in chunk order.
 // ---------------------------------------------------------------------------
 template <typename T>
-__global__ __launch_bounds__(256) void bwd_dwr_kernel(const T* __restrict__ x, const float* __restrict__ dl,
-                                                      const int32_t* __restrict__ perm,
-                                                      const int32_t* __restrict__ counts,
-                                                      const int32_t* __restrict__ offsets, int d, int k,
-                                                      float* __restrict__ dwr) {
+__global__ __launch_bounds__(256) void bwd_dwr_chunk_kernel(const T* __restrict__ x, const float* __restrict__ dl,
+                                                            const int32_t* __restrict__ perm,
+                                                            const int32_t* __restrict__ pcol, int P, int d, int k,
+                                                            float* __restrict__ part) {
+  __shared__ int s_tok[64];
+  __shared__ float s_dl[64];
+  __shared__ float half1[1024];                     // half 1's sums for one block of 1024 columns
+  const int tid = threadIdx.x, h = tid >> 7, co = tid & 127;
+  const int ch = blockIdx.x;
+  if (tid < 64) {
+    const int col = ch * 64 + tid;
+    const int sl = col < P ? pcol[col] : -1;
+    const int a = sl >= 0 ? perm[sl] : -1;
+    s_tok[tid] = a >= 0 ? a / k : -1;
+    s_dl[tid] = a >= 0 ? dl[a] : 0.f;
+  }
+  __syncthreads();
+  for (int cb = 0; cb < d; cb += 1024) {
+    const int c = cb + co * 8;
+    float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+    if (c < d) {
+#pragma unroll 8
+      for (int i = 0; i < 32; ++i) {
+        const int sl = h * 32 + i, tk = s_tok[sl];
+        if (tk >= 0) {
+          float v[8];
+          load8<T>(x + (long long)tk * d + c, v);
+          const float w = s_dl[sl];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) acc[q] += w * v[q];
+        }
+      }
+    }
+    if (h == 1 && c < d)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) half1[co * 8 + q] = acc[q];
+    __syncthreads();
+    if (h == 0 && c < d) {
+      float out[8];
+#pragma unroll
+      for (int q = 0; q < 8; ++q) out[q] = acc[q] + half1[co * 8 + q];
+      float* dst = part + (long long)ch * d + c;
+      st16(dst, u32x4_t{__float_as_uint(out[0]), __float_as_uint(out[1]), __float_as_uint(out[2]), __float_as_uint(out[3])});
+      st16(dst + 4, u32x4_t{__float_as_uint(out[4]), __float_as_uint(out[5]), __float_as_uint(out[6]), __float_as_uint(out[7])});
+    }
+    __syncthreads();
+  }
+}
+
+__global__ __launch_bounds__(256) void bwd_dwr_reduce_kernel(const float* __restrict__ part,
+                                                             const int32_t* __restrict__ kofs,
+                                                             const int32_t* __restrict__ klen, int d,
+                                                             float* __restrict__ dwr) {
   const int e = blockIdx.x;
   const int c = blockIdx.y * 256 + threadIdx.x;
   if (c >= d) return;
-  const int o = offsets[e], n = counts[e];
+  const int c0 = kofs[e] / kPadK, c1 = (kofs[e] + klen[e]) / kPadK;
   float acc = 0.f;
-  for (int i = 0; i < n; ++i) {
-    const int a = perm[o + i];
-    acc += dl[a] * to_f32<T>(x[(long long)(a / k) * d + c]);
-  }
+  for (int ch = c0; ch < c1; ++ch) acc += part[(long long)ch * d + c];
   dwr[(long long)e * d + c] = acc;
 }
 
 // ---------------------------------------------------------------------------
 // dx[t] = dXs[t] + sum_j dXp[pos[t, j]] + sum_j dl[t, j] W_r[idx[t, j]], in that
-// order in fp32, rounded once.
+// order in fp32, rounded once.  Each thread takes 8 consecutive columns.
 // ---------------------------------------------------------------------------
 template <typename T>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const T* __restrict__ dxs, const T* __restrict__ dxp,
                                                      const T* __restrict__ wr, const float* __restrict__ dl,
                                                      const int32_t* __restrict__ idx, const int32_t* __restrict__ pos,
                                                      int T_, int d, int k, T* __restrict__ dx) {
-  const long long i = (long long)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= (long long)T_ * d) return;
-  const int t = (int)(i / d), c = (int)(i - (long long)t * d);
-  float v = to_f32<T>(dxs[i]);
-  for (int j = 0; j < k; ++j) v += to_f32<T>(dxp[(long long)pos[(long long)t * k + j] * d + c]);
-  for (int j = 0; j < k; ++j)
-    v += dl[(long long)t * k + j] * to_f32<T>(wr[(long long)idx[(long long)t * k + j] * d + c]);
-  dx[i] = from_f32<T>(v);
+  const long long i8 = (long long)blockIdx.x * blockDim.x + threadIdx.x;
+  const int per = d / 8;
+  if (i8 >= (long long)T_ * per) return;
+  const int t = (int)(i8 / per), c = (int)(i8 - (long long)t * per) * 8;
+  float v[8];
+  load8<T>(dxs + (long long)t * d + c, v);
+  for (int j = 0; j < k; ++j) {
+    float u[8];
+    load8<T>(dxp + (long long)pos[(long long)t * k + j] * d + c, u);
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += u[q];
+  }
+  for (int j = 0; j < k; ++j) {
+    float u[8];
+    load8<T>(wr + (long long)idx[(long long)t * k + j] * d + c, u);
+    const float w = dl[(long long)t * k + j];
+#pragma unroll
+    for (int q = 0; q < 8; ++q) v[q] += w * u[q];
+  }
+  store8<T>(dx + (long long)t * d + c, v);
+}
+
+// ---------------------------------------------------------------------------
+// out[i] = part[0][i] + part[1][i] + ... + part[S-1][i], in that order (the
+// contraction slices of a split weight gradient).  4 floats per thread.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* __restrict__ part, long long n, int S,
+                                                            float* __restrict__ out) {
+  const long long i4 = ((long long)blockIdx.x * blockDim.x + threadIdx.x) * 4;
+  if (i4 >= n) return;
+  u32x4_t a = ld16(part + i4);
+  float v[4] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]), __uint_as_float(a[3])};
+  for (int sl = 1; sl < S; ++sl) {
+    a = ld16(part + (long long)sl * n + i4);
+#pragma unroll
+    for (int q = 0; q < 4; ++q) v[q] += __uint_as_float(a[q]);
+  }
+  st16(out + i4, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
 }
 
 __global__ void fill_zero_kernel(uint32_t* __restrict__ p, long long n) {
@@ -211,9 +366,15 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
   hipLaunchKernelGGL(fill_zero_kernel, dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s, (uint32_t*)p, n);
 }
 
-void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int32_t* kofs,
-                     int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s) {
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, Pmax, Tp, kofs, klen, ksh, pcol);
+void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int S, int step,
+                     int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s) {
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, Pmax, Tp, S, step, kofs, klen, ksh,
+                     pcol);
+}
+
+void launch_splitk_reduce(const float* part, long long n, int S, float* out, hipStream_t s) {
+  if (n <= 0) return;
+  hipLaunchKernelGGL(splitk_reduce_kernel, dim3((unsigned)((n / 4 + 255) / 256)), dim3(256), 0, s, part, n, S, out);
 }
 
 void launch_transpose(int act, const TransposeArgs& a, hipStream_t s) {
@@ -233,20 +394,24 @@ void launch_bwd_gate(int act, const void* dy, const void* ou, const void* x, con
                        (const float*)x, (const float*)wr, idx, gate, pos, T, d, k, dl);
 }
 
-void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* counts,
-                    const int32_t* offsets, int E, int d, int k, float* dwr, hipStream_t s) {
-  const dim3 grid(E, (d + 255) / 256);
-  if (act == 1)
-    hipLaunchKernelGGL(bwd_dwr_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)x, dl, perm, counts, offsets, d,
-                       k, dwr);
-  else
-    hipLaunchKernelGGL(bwd_dwr_kernel<float>, grid, dim3(256), 0, s, (const float*)x, dl, perm, counts, offsets, d, k,
-                       dwr);
+void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* pcol, int P,
+                    const int32_t* kofs, const int32_t* klen, int E, int d, int k, float* part, float* dwr,
+                    hipStream_t s) {
+  const int nch = (P + kPadK - 1) / kPadK;
+  if (nch > 0) {
+    if (act == 1)
+      hipLaunchKernelGGL(bwd_dwr_chunk_kernel<bf16_t>, dim3(nch), dim3(256), 0, s, (const bf16_t*)x, dl, perm, pcol, P,
+                         d, k, part);
+    else
+      hipLaunchKernelGGL(bwd_dwr_chunk_kernel<float>, dim3(nch), dim3(256), 0, s, (const float*)x, dl, perm, pcol, P, d,
+                         k, part);
+  }
+  hipLaunchKernelGGL(bwd_dwr_reduce_kernel, dim3(E, (d + 255) / 256), dim3(256), 0, s, part, kofs, klen, d, dwr);
 }
 
 void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, const float* dl, const int32_t* idx,
                    const int32_t* pos, int T, int d, int k, void* dx, hipStream_t s) {
-  const long long n = (long long)T * d;
+  const long long n = (long long)T * (d / 8);
   if (n == 0) return;
   const dim3 grid((unsigned)((n + 255) / 256));
   if (act == 1)

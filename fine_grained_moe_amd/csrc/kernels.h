@@ -1,6 +1,8 @@
 // Host-side launchers of the gfx950 kernels (internal to the library).
 #pragma once
 
+#include <algorithm>
+
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
@@ -137,13 +139,20 @@ struct TransposeArgs {
   const float* scale;        // optional, indexed by the source index before division
 };
 void launch_fill_zero(void* p, size_t bytes, hipStream_t s);   // bytes % 4 == 0
-void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int32_t* kofs,
-                     int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s);
+void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int S, int step,
+                     int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s);
+// Contraction slices of the shared expert's weight gradients (a function of
+// the padded token count Tp): S slices of `step` columns, step % kPadK == 0.
+constexpr int kMaxSplitK = 8;
+inline int splitk_count(long long Tp) { return (int)std::max(1LL, std::min<long long>(kMaxSplitK, Tp / 4096)); }
+inline long long splitk_step(long long Tp) { return pad_k((Tp + splitk_count(Tp) - 1) / splitk_count(Tp)); }
+void launch_splitk_reduce(const float* part, long long n, int S, float* out, hipStream_t s);   // n % 4 == 0
 void launch_transpose(int act, const TransposeArgs& a, hipStream_t s);
 void launch_bwd_gate(int act, const void* dy, const void* ou, const void* x, const void* wr, const int32_t* idx,
                      const float* gate, const int32_t* pos, int T, int d, int k, float* dl, hipStream_t s);
-void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* counts,
-                    const int32_t* offsets, int E, int d, int k, float* dwr, hipStream_t s);
+void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* pcol, int P,
+                    const int32_t* kofs, const int32_t* klen, int E, int d, int k, float* part, float* dwr,
+                    hipStream_t s);
 void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, const float* dl, const int32_t* idx,
                    const int32_t* pos, int T, int d, int k, void* dx, hipStream_t s);
 
