@@ -30,8 +30,12 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
-__device__ __forceinline__ float sigmoidf_(float z) { return 1.0f / (1.0f + __expf(-z)); }
-__device__ __forceinline__ float siluf_(float z) { return z / (1.0f + __expf(-z)); }
+// Activations of the expert FFNs (not the router): exp2 and the hardware
+// reciprocal (about 1 ulp each) instead of an IEEE divide, whose sequence is
+// several times longer; the results are rounded to bf16 or feed bf16 data.
+// exp(-z) overflows to +inf for very negative z, and rcp(inf) = 0.
+__device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
+__device__ __forceinline__ float siluf_(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 
 // A 32-byte slice of one operand row held by one lane: 16 bf16 or 8 float.
 struct Frag {

@@ -151,7 +151,11 @@ __device__ __forceinline__ void load_vec(const T* p, float (&v)[N]) {
 
 template <typename T, bool SWIGLU>
 __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
-  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+  // One LDS object (the ring, then the row scales): with a second __shared__
+  // array the compiler could no longer tell which LDS reads the direct loads
+  // feed and waited for every load in flight before each stage.
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes + BM * 4];
+  float* const row_scale = reinterpret_cast<float*>(lds + kStages * kStageBytes);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -211,6 +215,13 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
     row_base = m0;
   }
   rows = rows < BM ? rows : BM;
+
+  // Row scales of the gate-scaled epilogues: thread r < 128 fetches perm of
+  // row r now (it lands with the first stage), the gate itself after the
+  // main loop, and the scales reach the waves through LDS.
+  const bool scaled = p.gate != nullptr && (p.epi == EPI_ROWSCALE || p.epi == EPI_SWIGLU_BWD);
+  int my_perm = 0;
+  if (scaled && tid < BM) my_perm = p.perm[row_base + min(tid, rows - 1)];
 
   // ---- global -> LDS.  A stage holds the A tile (128 rows) then the B tile
   // (256 rows).  Lane i of a wave instruction lands at LDS byte base + 16 i,
@@ -325,6 +336,10 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
     compute(s, 0, std::false_type{});
   }
 
+  if (scaled) {
+    if (tid < BM) row_scale[tid] = p.gate[my_perm];
+    __syncthreads();
+  }
   // ---- epilogue (per job).  acc[mi][ni][i] is tile row wm*64 + mi*16 + 4g + i.
   // Its column, past the wave's base, is 8f + ni (f = lane % 16); for SwiGLU,
   // blocks ni < 4 are gate columns 4f + ni and ni >= 4 the matching up.
@@ -354,7 +369,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
           store_vec<T, HN>(aux + row * p.ldaux + p.N + fh, u);
         }
       } else if (p.epi == EPI_ROWSCALE) {
-        const float sc = p.gate[p.perm[row]];
+        const float sc = row_scale[lr];
         float v[NI], raw[NI];
 #pragma unroll
         for (int ni = 0; ni < NI; ++ni) {
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
         if (aux) store_vec<T, NI>(aux + row * p.ldaux + n, raw);
       } else if (p.epi == EPI_SWIGLU_BWD) {
         // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u)
-        const float sc = p.gate ? p.gate[p.perm[row]] : 1.f;
+        const float sc = p.gate ? row_scale[lr] : 1.f;
         const T* au = reinterpret_cast<const T*>(p.aux) + row * p.ldaux;
         float a[NI], u[NI], da[NI], du[NI];
         load_vec<T, NI>(au + n, a);
