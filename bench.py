@@ -234,6 +234,8 @@ def main() -> int:
     ap.add_argument("--no-warm", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true")
+    ap.add_argument("--leg", choices=("decode", "train"),
+                    help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
     args = ap.parse_args()
@@ -248,6 +250,10 @@ def main() -> int:
     from fine_grained_moe_amd import moe, synth
 
     torch.cuda.set_device(0)
+    if args.leg is not None:
+        fn = bench_decode if args.leg == "decode" else bench_train
+        print(json.dumps({args.leg: fn(moe, synth, torch, np)}), flush=True)
+        return 0
     inp = synth.make_workload("layer_t4096", seed=0)
     T, d, E, F, Fs, k = inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k
     log(f"workload layer_t4096: T={T} d={d} E={E} F={F} Fs={Fs} k={k} bf16")

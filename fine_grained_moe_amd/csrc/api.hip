@@ -28,7 +28,7 @@ struct Layout {
   size_t kofs, klen, ksh, pcol, dwr_part, dwpart, dl, dAU, dAUT, XpT, dOT, HT, dXp, WdT, WguT, WsdT, WsguT, dAUs, dAUsT, xT, dyT, HsT,
       dXs;
   long long P, Tp;        // padded column counts of the routed and shared transposes
-  size_t active, n_active, lpart, part_sh, rout; // int4 serving path: active experts, fp32 partials
+  size_t active, n_active, rkey, rscore, part_sh;   // int4 serving path: active experts, router tile maxima, fp32 shared-down partials
   size_t total;
 };
 
@@ -76,9 +76,9 @@ Layout make_layout(const moe_dims& d, int training) {
   if (d.w_routed == MOE_INT4_G128) {
     L.active = take((size_t)d.E * 3 * 4);
     L.n_active = take(4);
-    L.lpart = take((size_t)4 * d.T * 64 * 4);
+    L.rkey = take(4 * 64 * 8);
+    L.rscore = take(4 * 64 * 4);
     L.part_sh = take((size_t)4 * d.T * d.d * 4);
-    L.rout = take(slots * d.d * 4);
     L.total = o;
     return L;
   }
@@ -282,11 +282,11 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.pos = routing->pos;
   a.active = at<int32_t>(ws, L.active);
   a.n_active = at<int32_t>(ws, L.n_active);
+  a.rkey = at<uint64_t>(ws, L.rkey);
+  a.rscore = at<float>(ws, L.rscore);
   a.Hs = at<uint16_t>(ws, L.Hs);
   a.H = at<uint16_t>(ws, L.H);
-  a.lpart = at<float>(ws, L.lpart);
   a.part_sh = at<float>(ws, L.part_sh);
-  a.rout = at<float>(ws, L.rout);
   a.y = (uint16_t*)y;
   mark_phase(0, s);
   launch_decode(a, s);

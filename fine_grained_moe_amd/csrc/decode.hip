@@ -9,28 +9,38 @@
 // element 2i in the low nibble) is this library's reading; the article names
 // only "int4".
 //
-// Five launches for a batch of at most 64 tokens:
-//   decode_logits     router logits, 16 workgroups, fp32 partial sums;
-//   decode_select     one workgroup: top-1 selection, gates, loads, offsets,
-//                     dispatch order and the list of active experts;
-//   decode_gate_up    H = silu(x Wg^T) * (x Wu^T) for the shared expert
-//                     (bf16) and for each active routed expert over its own
-//                     tokens (int4, dequantised in registers);
-//   decode_down       fp32 partial sums of Hs Wsd^T (four contraction
-//                     quarters) and of H Wd^T (per active expert);
-//   decode_combine    y = the four shared partials + the token's routed row,
-//                     added in a fixed order and rounded once.
-// The weights are read by many small workgroups (one 16-row MFMA tile of a
-// weight matrix each, its contraction split over the 4 waves) so that every
-// CU streams: with one workgroup per 32 columns the shared expert alone
-// occupied only 64 CUs.  At this size the host's launch cost (about 3 us per
-// kernel) exceeds the GPU time, so serving callers should capture the
-// forward in a HIP graph; nothing here allocates, synchronises or clears
-// memory with hipMemsetAsync, so the calls are capturable.
-// int4 products: the nibbles are exact small integers in bf16, so each
+// Three launches for a batch of at most 64 tokens (a launch costs about
+// 1.3 us on the device even when empty, so the work is packed into as few
+// dependent steps as the data flow allows):
+//   stage 1  router (one workgroup per 16 tokens: logits on MFMA, top-1,
+//            gate) beside the shared expert's gate/up, which does not
+//            depend on the routing;
+//   stage 2  one workgroup writes the routing outputs (loads, offsets,
+//            dispatch order, active experts); the shared down in four
+//            contraction quarters (fp32 partials); the routed gate/up of each
+//            active expert over its own tokens (int4 dequantised in
+//            registers);
+//   stage 3  the routed down of each active expert, fused with the combine:
+//            y = (the four shared partials added in order) + the token's
+//            routed row, rounded once (top-1: the gate is 1).
+// Every workgroup streams 8 to 32 KiB of weights, all of it requested before
+// the first product, so that every CU has its loads in flight at once.
+// Operands reach the MFMAs through LDS: an MFMA operand held in registers
+// puts 16 different rows in consecutive lanes, and a CU's address unit then
+// spends 64 cycles instead of 16 on each 1 KiB wave load (measured with the
+// TA busy counter), which made the address units, not HBM, the limit.
+// Weight rows are copied with direct global->LDS loads in which four
+// consecutive lanes fetch 64 contiguous bytes of one row; activation rows
+// are copied row-contiguously (only the rows that exist) into XOR-swizzled
+// LDS rows; each wave then reads its fragments from LDS.
+// Serving callers should capture the forward in a HIP graph (the host's
+// launch cost exceeds the GPU time at this size); nothing here allocates,
+// synchronises or clears memory with hipMemsetAsync, so the calls are
+// capturable.
+// int4 products: nibbles are exact small integers in bf16, so each
 // 128-element group is multiplied on MFMA into a fresh accumulator and then
 // scaled once in fp32 (w = q * scale is never rounded to bf16).
-// The path is HBM-bound: every weight byte is read once per launch.
+// The path is HBM-bound: every weight byte is read once per call.
 #include "common.h"
 #include "kernels.h"
 
@@ -38,382 +48,510 @@ namespace fgmoe {
 
 namespace {
 
+
 constexpr int kGroup = 128;   // int4 scale group along the contraction dimension
 
-// 16 nibbles (8 bytes) -> 16 bf16 values of the integers they hold, as the two
-// 16-byte MFMA operand halves.
-__device__ __forceinline__ Frag int4x16_to_bf16(uint2 p) {
-  uint32_t out[8];
+// 8 nibbles (one 32-bit word, element 2i in the low nibble of byte i) -> the
+// 8 bf16 values of the signed integers they hold, in element order (one
+// 16-byte MFMA operand).  Exact: every integer in [-8, 7] is a bf16.
+__device__ __forceinline__ u32x4_t int4x8_to_bf16(uint32_t w) {
+  u32x4_t r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const uint32_t byte = ((i < 4 ? p.x : p.y) >> (8 * (i & 3))) & 0xFFu;
-    const int lo = (int)(byte & 0xF) - (int)((byte & 0x8) << 1);
-    const int hi = (int)(byte >> 4) - (int)((byte & 0x80) >> 3);
-    out[i] = (__float_as_uint((float)lo) >> 16) | (__float_as_uint((float)hi) & 0xFFFF0000u);
+  for (int j = 0; j < 4; ++j) {
+    const float lo = (float)(((int)(w << (28 - 8 * j))) >> 28);
+    const float hi = (float)(((int)(w << (24 - 8 * j))) >> 28);
+    r[j] = __builtin_amdgcn_perm(__float_as_uint(hi), __float_as_uint(lo), 0x07060302u);
   }
-  Frag f;
-  f.lo = u32x4_t{out[0], out[1], out[2], out[3]};
-  f.hi = u32x4_t{out[4], out[5], out[6], out[7]};
-  return f;
+  return r;
+}
+
+__device__ __forceinline__ float sum4(const float* p, int stride) {
+  return ((p[0] + p[stride]) + p[2 * stride]) + p[3 * stride];
+}
+
+// Pack 8 floats as 8 bf16 (round to nearest even).
+__device__ __forceinline__ u32x4_t pack8(const float* v) {
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) r[j] = (uint32_t)f32_to_bf16(v[2 * j]) | ((uint32_t)f32_to_bf16(v[2 * j + 1]) << 16);
+  return r;
+}
+
+
+
+typedef __attribute__((address_space(3))) void* lds_ptr_t;
+
+// Weight blocks in LDS: 16 rows x 64 bytes (1 KiB), the 16-byte piece p of
+// row r at physical piece p ^ wswz(r), so that the 32 pieces of a half-wave
+// MFMA operand read (16 rows x 2 pieces) fall in distinct bank groups.
+__device__ __forceinline__ int wswz(int row) { return ((row >> 3) & 1) << 1; }
+
+// Copy NB consecutive 64-byte blocks of 16 weight rows into LDS (block b at
+// dst + 1024 b).  Lane l fetches piece (l % 4) ^ wswz(l / 4) of row l / 4;
+// row_k is this lane's row address at the first block.
+template <int NB>
+__device__ __forceinline__ void dma_w(const char* row_k, char* dst, int lane) {
+  const char* src = row_k + (((lane & 3) ^ wswz(lane >> 2)) << 4);
+#pragma unroll
+  for (int b = 0; b < NB; ++b) __builtin_amdgcn_global_load_lds(src + b * 64, (lds_ptr_t)(dst + b * 1024), 16, 0, 0);
+}
+
+// Lane (fr, g)'s MFMA operand from a weight block: piece g of row fr.
+__device__ __forceinline__ u32x4_t wfrag(const char* blk, int fr, int g) {
+  return *reinterpret_cast<const u32x4_t*>(blk + fr * 64 + ((g ^ wswz(fr)) << 4));
+}
+
+// Activation rows in LDS: 16 rows of Q bytes, piece c of row r at c ^ xsw(r).
+// The XOR makes the bf16 MFMA reads (pieces 4b + g of rows 0..15) hit 32
+// distinct bank groups per half-wave.
+template <int Q> __device__ __forceinline__ int xsw(int r) { return Q == 512 ? (2 * r) & 31 : r & 14; }
+
+// Copy rows 0 .. n-1 (1 <= n <= 16) of this wave's Q-byte slice of an
+// activation operand into LDS.  Row r is read at base + idx(r) * stride with
+// idx(r) = list[r] (or r).  Lane l of step i copies piece 64 i + l of the 16
+// rows, so the reads are row-contiguous; all loads are issued before the
+// stores, unconditionally (lanes past row n - 1 re-read it): a load under a
+// lane condition would be waited for at the end of its branch.
+template <int Q>
+__device__ __forceinline__ void stage_rows(char* dst, const char* base, long long stride, const int* list, int n,
+                                           int lane) {
+  constexpr int PR = Q / 16, NS = 16 * PR / 64;
+  u32x4_t v[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int pc = i * 64 + lane, r = min(pc / PR, n - 1), c = pc % PR;
+    v[i] = ld16(base + (long long)(list ? list[r] : r) * stride + c * 16);
+  }
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int pc = i * 64 + lane, r = pc / PR, c = pc % PR;
+    if (r < n) st16(dst + r * Q + ((c ^ xsw<Q>(r)) << 4), v[i]);
+  }
+}
+
+// Lane fr's operand piece `piece` of activation row fr.  Rows >= n hold stale
+// data; they only feed MFMA output rows that are never stored.
+template <int Q>
+__device__ __forceinline__ u32x4_t xfrag(const char* src, int fr, int piece) {
+  return *reinterpret_cast<const u32x4_t*>(src + fr * Q + ((piece ^ xsw<Q>(fr)) << 4));
+}
+
+// This wave's direct LDS loads and LDS stores have completed
+// (s_waitcnt vmcnt(0) expcnt(0) lgkmcnt(0)).
+__device__ __forceinline__ void wait_all() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0);
+  asm volatile("" ::: "memory");
+}
+
+// Token-tiled items: item i of a launch goes to weight block `blk` and token
+// tile `tile` such that the tiles of one weight block share i % 8, hence the
+// XCD (consecutive workgroups are dealt to the 8 XCDs in turn), and read the
+// block's weights through one L2.  nblk must be a multiple of 8.
+__device__ __forceinline__ void xcd_item(int i, int ntile, int& blk, int& tile) {
+  const int x = i & 7, j = i >> 3;
+  const int jb = j / ntile;
+  blk = jb * 8 + x;
+  tile = j - jb * ntile;
 }
 
 // ---------------------------------------------------------------------------
-// Router logits for a small batch (T <= 64), split over 16 workgroups so that
-// the 128 KiB router matrix is read by 16 CUs at once: workgroup b takes
-// experts 16 (b / 4) .. +15 and contraction quarter b % 4; its wave w takes
-// 128-byte chunk 4 (b % 4) + w of every row.  The 4 wave tiles are added in
-// LDS in a fixed order and written as lpart[b % 4][t][e] (fp32); the
-// consumer adds the 4 quarters in a fixed order.
+// Stage 1.  A workgroup multiplies 16 bf16 weight rows by 16 tokens of x over
+// the whole contraction d; wave w takes contraction quarter w (8 MFMA steps
+// of 32); the 4 partial 16x16 tiles are added in LDS in a fixed order.
+//   shared gate/up item (hb, tt): rows = 8 gate rows 8 hb .. + 7 (MFMA
+//     columns 0-7) and the matching up rows (8-15); h = silu(gate) * up.
+//   router item (tt, et): rows = experts 16 et .. + 15 (rows past E re-read
+//     expert E - 1 and are not used).  s = sigmoid(logit); key = (order key
+//     of s + b, 63 - e), so the largest key is the largest s + b and an exact
+//     tie goes to the lower expert.  Each token's largest key in the tile
+//     and its s go to rkey/rscore [et][t]; the top-1 is the largest of the 4
+//     tile keys (stage 2).
+// LDS per wave: 8 weight blocks (8 KiB), then 16 x rows (8 KiB), whose space
+// takes the wave's partial tile [16][17] after the products.
 // ---------------------------------------------------------------------------
+constexpr int kS1Wave = 16384;
+
 template <int D>
-__global__ __launch_bounds__(256) void decode_logits_kernel(DecodeArgs p) {
-  __shared__ float part[4][64][17];
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+__device__ f32x4_t stage1_tile(const char* wrow, int tt, int T, const DecodeArgs& p, char* wreg) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int fr = lane & 15, g = lane >> 4;
-  const int kq = blockIdx.x & 3, et = blockIdx.x >> 2;
-  if (et * 16 >= p.E) return;
-  const int c = kq * 4 + wave;                       // this wave's 128-byte chunk of a row
-  const int e = min(et * 16 + fr, p.E - 1);          // rows past E re-read the last expert; never used
-  const char* wrow = reinterpret_cast<const char*>(p.w_router + (long long)e * D) + g * 32 + c * 128;
-  Frag wf;
-  wf.lo = ld16(wrow);
-  wf.hi = ld16(wrow + 16);
-  for (int m0 = 0; m0 < p.T; m0 += 16) {
-    const int t = min(m0 + fr, p.T - 1);
-    const char* xrow = reinterpret_cast<const char*>(p.x + (long long)t * D) + g * 32 + c * 128;
-    Frag xa;
-    xa.lo = ld16(xrow);
-    xa.hi = ld16(xrow + 16);
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    acc = Mma<bf16_t>::run(xa, wf, acc);
+  static_assert(D == 1024, "one contraction quarter is 512 bytes");
+  dma_w<8>(wrow + wave * (D / 2), wreg, lane);
+  stage_rows<512>(wreg + 8192, reinterpret_cast<const char*>(p.x) + (long long)tt * 16 * D * 2 + wave * (D / 2),
+                  (long long)D * 2, nullptr, min(16, T - tt * 16), lane);
+  wait_all();
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][(m0 + 4 * g + i) & 63][fr] = acc[i];
-  }
-  __syncthreads();
-  for (int i = tid; i < p.T * 16; i += 256) {
-    const int t = i >> 4, cc = i & 15;
-    const float v = ((part[0][t][cc] + part[1][t][cc]) + part[2][t][cc]) + part[3][t][cc];
-    p.lpart[((long long)kq * p.T + t) * 64 + et * 16 + cc] = v;
-  }
+  for (int b = 0; b < 8; ++b) acc = Mma<bf16_t>::run1(xfrag<512>(wreg + 8192, fr, 4 * b + g), wfrag(wreg + b * 1024, fr, g), acc);
+  // acc[i]: token row 4g + i, weight row fr
+  float* part = reinterpret_cast<float*>(wreg + 8192);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) part[(4 * g + i) * 17 + fr] = acc[i];
+  return acc;
 }
 
-// ---------------------------------------------------------------------------
-// Top-1 selection and dispatch bookkeeping for T <= 64 tokens, run by a whole
-// workgroup from the partial logits: logits = the 4 quarters in order;
-// s = sigmoid; each token's expert is the largest s + b (an exact tie goes
-// to the lower expert); gate = s / s = 1; loads, offsets, the stable
-// dispatch order (slots of an expert ascend in t) and the ascending list of
-// experts with a load.  Thread (t = tid / 4, q = tid % 4) scans experts
-// 16q..16q+15 of token t; two quad merges combine the quarters.
-// ---------------------------------------------------------------------------
-struct DecodeSel {
-  float lg[64][65];
-  int ids[64], cnt[64], off[65], perm[64], pos[64];
-  int act_e[64], act_s0[64], act_n[64];
-  int n_active;
-  float bias[64];
-};
+// the sum over the 4 waves of partial element (r, c), in wave order
+__device__ __forceinline__ float part_sum(const char* lds, int wave_bytes, int off_bytes, int idx) {
+  const float* q = reinterpret_cast<const float*>(lds + off_bytes) + idx;
+  const int st = wave_bytes / 4;
+  return ((q[0] + q[st]) + q[2 * st]) + q[3 * st];
+}
 
-__device__ void decode_select(const DecodeArgs& p, DecodeSel& S) {
-  const int tid = threadIdx.x;
-  const int T_ = p.T, E = p.E;
-  if (tid < 64) {
-    S.bias[tid] = tid < E ? p.bias[tid] : 0.f;
-    S.cnt[tid] = 0;
-  }
-  const long long q1 = (long long)T_ * 64;
-  for (int i = tid; i < T_ * 64; i += 256)
-    S.lg[i >> 6][i & 63] = ((p.lpart[i] + p.lpart[q1 + i]) + p.lpart[2 * q1 + i]) + p.lpart[3 * q1 + i];
-  __syncthreads();
-  {
-    const int t = tid >> 2, q = tid & 3;
-    uint64_t best = 0;
-    if (t < T_) {
-      float l[16];
+template <int D, int FS>
+__global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs p, int ntile) {
+  __shared__ __align__(16) char lds[4 * kS1Wave];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  char* wreg = lds + wave * kS1Wave;
+  const int n_sh = (FS / 8) * ntile;
+  const int blk = blockIdx.x, T = p.T;
+  const int r = lane >> 2;                            // the weight row this lane's direct loads fetch
+  if (blk < n_sh) {
+    int hb, tt;
+    xcd_item(blk, ntile, hb, tt);
+    const int f = hb * 8 + (r & 7);
+    const int wr = r < 8 ? f : FS + f;
+    stage1_tile<D>(reinterpret_cast<const char*>(p.w_sh_gate_up) + (long long)wr * D * 2, tt, T, p, wreg);
+    __syncthreads();
+    const int t = tt * 16 + tid;
+    if (tid < 16 && t < T) {
+      float h[8];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) l[i] = S.lg[t][q * 16 + i];
+      for (int c = 0; c < 8; ++c)
+        h[c] = siluf_(part_sum(lds, kS1Wave, 8192, tid * 17 + c)) * part_sum(lds, kS1Wave, 8192, tid * 17 + 8 + c);
+      st16(p.Hs + (long long)t * FS + hb * 8, pack8(h));
+    }
+  } else {
+    const int rr = blk - n_sh, tt = rr >> 2, et = rr & 3;
+    const int t = tid >> 4, c = tid & 15, e = et * 16 + c;
+    const float b = e < p.E ? p.bias[e] : 0.f;
+    stage1_tile<D>(reinterpret_cast<const char*>(p.w_router) + (long long)min(et * 16 + r, p.E - 1) * D * 2, tt, T, p,
+                   wreg);
+    __syncthreads();
+    const float sc = 1.0f / (1.0f + expf(-part_sum(lds, kS1Wave, 8192, t * 17 + c)));
+    uint64_t key = e < p.E ? (((uint64_t)float_key(sc + b) << 32) | (uint32_t)(63 - e)) : 0ull;
+    float ks = sc;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const int e = q * 16 + i;
-        const float sc = 1.0f / (1.0f + expf(-l[i]));
-        const uint64_t key = ((uint64_t)float_key(sc + S.bias[e]) << 32) | (uint32_t)(63 - e);
-        best = (e < E && key > best) ? key : best;
+    for (int off = 1; off < 16; off <<= 1) {
+      const uint32_t lo = __shfl_xor((uint32_t)key, off), hi = __shfl_xor((uint32_t)(key >> 32), off);
+      const float os = __shfl_xor(ks, off);
+      const uint64_t o = ((uint64_t)hi << 32) | lo;
+      if (o > key) {
+        key = o;
+        ks = os;
       }
     }
-#pragma unroll
-    for (int off = 1; off <= 2; off <<= 1) {
-      const uint32_t lo = __shfl_xor((uint32_t)best, off), hi = __shfl_xor((uint32_t)(best >> 32), off);
-      const uint64_t o = ((uint64_t)hi << 32) | lo;
-      best = o > best ? o : best;
-    }
-    if (q == 0 && t < T_) {
-      const int e = 63 - (int)(uint32_t)best;
-      S.ids[t] = e;
-      atomicAdd(&S.cnt[e], 1);
+    if (c == 0 && tt * 16 + t < T) {
+      p.rkey[et * 64 + tt * 16 + t] = key;
+      p.rscore[et * 64 + tt * 16 + t] = ks;
     }
   }
+}
+
+// ---------------------------------------------------------------------------
+// Top-1 dispatch bookkeeping for T <= 64 tokens from the router's tile keys:
+// each token's expert (largest of its 4 tile keys) and s, loads, offsets,
+// the stable dispatch order (slots of an expert ascend in t) and the
+// ascending list of experts with a load.  Computed by every stage-2
+// workgroup that needs it (a few hundred cycles), so no launch is spent on
+// it.
+// ---------------------------------------------------------------------------
+struct Book {
+  unsigned long long mask[64];   // tokens of each expert, one bit per token
+  int idx[64], off[64], perm[64], pos[64];
+  int act_e[64], act_s0[64], act_n[64];
+  float sc[64];
+  int n_active;
+};
+
+__device__ void decode_book(const DecodeArgs& p, Book& B) {
+  const int tid = threadIdx.x, T = p.T;
+  int e = -1;
+  if (tid < 64) {
+    // the first wave alone loads the keys (entries past T are stale and not
+    // used); they are consumed inside this branch, so only this wave waits
+    uint64_t k[4];
+    float s[4];
+#pragma unroll
+    for (int et = 0; et < 4; ++et) {
+      k[et] = p.rkey[et * 64 + tid];
+      s[et] = p.rscore[et * 64 + tid];
+    }
+    uint64_t kb = k[0];
+    float sc = s[0];
+#pragma unroll
+    for (int et = 1; et < 4; ++et)
+      if (k[et] > kb) {
+        kb = k[et];
+        sc = s[et];
+      }
+    if (tid < T) e = min(63 - (int)(uint32_t)kb, p.E - 1);   // a NaN score can leave every key 0; keep idx in range
+    B.mask[tid] = 0ull;
+    B.idx[tid] = e;
+    B.sc[tid] = sc;
+  }
+  __syncthreads();
+  if (tid < T) atomicOr(&B.mask[e], 1ull << tid);
   __syncthreads();
   if (tid < 64) {
-    const int c = S.cnt[tid];
+    const int c = __popcll(B.mask[tid]);
     int incl = c;
+#pragma unroll
     for (int o = 1; o < 64; o <<= 1) {
       const int v = __shfl_up(incl, o);
       if (tid >= o) incl += v;
     }
-    S.off[tid] = incl - c;
-    if (tid == 63) S.off[64] = incl;
-    const bool act = c > 0;
-    const unsigned long long m = __ballot(act);
-    const int before = __popcll(m & ((1ull << tid) - 1ull));
-    if (act) {
-      S.act_e[before] = tid;
-      S.act_s0[before] = incl - c;
-      S.act_n[before] = c;
+    B.off[tid] = incl - c;
+    const unsigned long long m = __ballot(c > 0);
+    const int r = __popcll(m & ((1ull << tid) - 1ull));
+    if (c > 0) {
+      B.act_e[r] = tid;
+      B.act_s0[r] = incl - c;
+      B.act_n[r] = c;
     }
-    if (tid == 0) S.n_active = __popcll(m);
+    if (tid == 0) B.n_active = __popcll(m);
   }
   __syncthreads();
-  if (tid < T_) {
-    const int e = S.ids[tid];
-    int rank = 0;
-    for (int b = 0; b < tid; ++b) rank += S.ids[b] == e ? 1 : 0;
-    const int slot = S.off[e] + rank;
-    S.perm[slot] = tid;
-    S.pos[tid] = slot;
+  if (tid < T) {
+    const int slot = B.off[e] + __popcll(B.mask[e] & ((1ull << tid) - 1ull));
+    B.perm[slot] = tid;
+    B.pos[tid] = slot;
   }
   __syncthreads();
 }
 
-// The routing outputs of the call.
-__device__ void decode_write_routing(const DecodeArgs& p, const DecodeSel& S) {
+// The routing outputs of the call (stage 3 reads perm and the active list).
+__device__ void decode_write_routing(const DecodeArgs& p, const Book& B) {
   const int tid = threadIdx.x;
   if (tid < p.T) {
-    const int e = S.ids[tid];
-    const float sc = 1.0f / (1.0f + expf(-S.lg[tid][e]));
-    p.idx[tid] = e;
-    p.gate[tid] = sc / sc;
-    p.perm[tid] = S.perm[tid];
-    p.pos[tid] = S.pos[tid];
+    p.idx[tid] = B.idx[tid];
+    p.gate[tid] = B.sc[tid] / B.sc[tid];
+    p.perm[tid] = B.perm[tid];
+    p.pos[tid] = B.pos[tid];
   }
   if (tid < p.E) {
-    p.counts[tid] = S.cnt[tid];
-    p.offsets[tid] = S.off[tid];
+    p.counts[tid] = __popcll(B.mask[tid]);
+    p.offsets[tid] = B.off[tid];
   }
-  if (tid == p.E - 1) p.offsets[p.E] = S.off[tid] + S.cnt[tid];
-  if (tid < S.n_active) {
-    p.active[3 * tid] = S.act_e[tid];
-    p.active[3 * tid + 1] = S.act_s0[tid];
-    p.active[3 * tid + 2] = S.act_n[tid];
+  if (tid == p.E - 1) p.offsets[p.E] = B.off[tid] + __popcll(B.mask[tid]);
+  if (tid < B.n_active) {
+    p.active[3 * tid] = B.act_e[tid];
+    p.active[3 * tid + 1] = B.act_s0[tid];
+    p.active[3 * tid + 2] = B.act_n[tid];
   }
-  if (tid == 0) *p.n_active = S.n_active;
-}
-
-// One workgroup: selection, bookkeeping and the routing outputs (the
-// large-batch router's rules; top-1).
-__global__ __launch_bounds__(256) void decode_select_kernel(DecodeArgs p) {
-  __shared__ DecodeSel S;
-  decode_select(p, S);
-  decode_write_routing(p, S);
+  if (tid == 0) *p.n_active = B.n_active;
 }
 
 // ---------------------------------------------------------------------------
-// Gate/up.  Item i < FS/8: shared expert, h columns 8i .. 8i+7; item >= FS/8:
-// routed expert active[(i - FS/8) / (FR/8)], h columns 8 * ((i - FS/8) % (FR/8)).
-// The item's 16 weight rows (8 gate rows in MFMA columns 0-7, the matching 8
-// up rows in columns 8-15) form one 16x16 MFMA tile; wave w multiplies the
-// w-th quarter of the contraction for every 16-token tile and the 4 partial
-// tiles are added in LDS in a fixed order, then silu(gate) * up.
-// int4 products: each 128-element group goes through MFMA into a fresh
-// accumulator and is scaled once in fp32.
+// Stage 2.  Operands go to the MFMAs straight from global memory: these
+// workgroups are bound by the latency of their two dependent round trips
+// (bookkeeping, then operands), not by the address units, and the LDS
+// staging of stage 1 cost them occupancy (measured).
+//   shared down item (j, tt): output columns 16 (j / 4) .. + 15, contraction
+//     quarter j % 4 of Fs, tokens 16 tt .. + 15; wave w takes a quarter of
+//     that quarter (128 elements, 4 MFMA steps).  The partial tiles are added
+//     in a fixed order and written as fp32 part_sh[quarter][slot][n], in
+//     dispatch (slot) order so that stage 3 reads one expert's rows
+//     contiguously.
+//   routed gate/up item i: active expert a = i / (F/16), h columns 16 fb ..
+//     + 15 (fb = i % (F/16)) over that expert's tokens: a gate tile (rows
+//     16 fb + r) and an up tile (rows F + 16 fb + r).  Wave w takes
+//     contraction quarter w (two scale groups).  A lane's 16-byte weight
+//     load holds 32 consecutive nibbles of one group; its 4 words feed 4
+//     MFMAs with the matching 8-element pieces of x.  h = silu(gate) * up.
+// Rows past a tile's tokens re-read its last token (loads under a lane
+// condition would be waited for at the end of their branch) and are not
+// stored.
 // ---------------------------------------------------------------------------
-template <int D, int FR, int FS>
-__global__ __launch_bounds__(256) void decode_gate_up_kernel(DecodeArgs p) {
-  __shared__ float part[4][64][17];                  // [wave][token][MFMA column]
+template <int D, int FS>
+__device__ void decode_shared_down(const DecodeArgs& p, int j, int tt, float* lds, Book& B) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
-  constexpr int n_sh = FS / 8, nfb = FR / 8;
-  const int item = blockIdx.x;
-  const bool shared = item < n_sh;
-  int e = 0, fblk, ntok, slot0 = 0;
-  if (shared) {
-    fblk = item;
-    ntok = p.T;
-  } else {
-    const int a = (item - n_sh) / nfb;
-    if (a >= *p.n_active) return;
-    e = p.active[3 * a];
-    slot0 = p.active[3 * a + 1];
-    ntok = p.active[3 * a + 2];
-    fblk = (item - n_sh) - a * nfb;
+  constexpr int J = FS / 16 / 32;                    // MFMA K-steps per wave (4)
+  const int cb = j >> 2, quarter = j & 3, T = p.T;
+  const int kofs = quarter * (FS / 2) + wave * (FS / 8) + g * 16;   // bytes into a row
+  const char* wr = reinterpret_cast<const char*>(p.w_sh_down + (long long)(cb * 16 + fr) * FS) + kofs;
+  const char* hr = reinterpret_cast<const char*>(p.Hs + (long long)min(tt * 16 + fr, T - 1) * FS) + kofs;
+  u32x4_t wv[J], ha[J];
+#pragma unroll
+  for (int i = 0; i < J; ++i) {
+    wv[i] = ld16(wr + i * 64);
+    ha[i] = ld16(hr + i * 64);
   }
-  const int N = shared ? FS : FR;                    // rows per half (gate | up)
-  const int f = fblk * 8 + (fr & 7);                 // h column of MFMA column fr
-  const int wrow = (fr < 8) ? f : N + f;             // its weight row (gate, then up)
-  constexpr int nq = D * 2 / 128 / 4;                // 128-byte chunks of a bf16 row per quarter (4)
-  const int c0 = wave * nq;
-
-  // this lane's quarter of its weight row, requested before any product
-  Frag wbf[nq];
-  uint2 wq4[nq];
-  uint16_t wsc[nq / 2];
-  if (shared) {
-    const char* wb = reinterpret_cast<const char*>(p.w_sh_gate_up) + (long long)wrow * D * 2 + g * 32;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int c = 0; c < nq; ++c) {
-      wbf[c].lo = ld16(wb + (c0 + c) * 128);
-      wbf[c].hi = ld16(wb + (c0 + c) * 128 + 16);
-    }
-  } else {
-    const long long r = (long long)e * 2 * FR + wrow;
-    const uint8_t* wq = p.q_gate_up + r * (D / 2) + g * 8;
-    const bf16_t* ws = p.s_gate_up + r * (D / kGroup);
+  for (int i = 0; i < J; ++i) acc = Mma<bf16_t>::run1(ha[i], wv[i], acc);
 #pragma unroll
-    for (int c = 0; c < nq; ++c) wq4[c] = *reinterpret_cast<const uint2*>(wq + (c0 + c) * 32);
+  for (int i = 0; i < 4; ++i) lds[(wave * 16 + 4 * g + i) * 17 + fr] = acc[i];
+  decode_book(p, B);                                 // its loads follow the operand loads; it ends with a barrier
+  const int m = tid >> 2, c4 = (tid & 3) * 4, t = tt * 16 + m;
+  if (tid < 64 && t < T) {
+    f32x4_t v;
 #pragma unroll
-    for (int c = 0; c < nq / 2; ++c) wsc[c] = ws[c0 / 2 + c];
+    for (int c = 0; c < 4; ++c) v[c] = sum4(lds + m * 17 + c4 + c, 16 * 17);
+    *reinterpret_cast<f32x4_t*>(p.part_sh + ((long long)quarter * T + B.pos[t]) * D + cb * 16 + c4) = v;
   }
+}
 
-  for (int m0 = 0; m0 < ntok; m0 += 16) {
-    const int mm = min(m0 + fr, ntok - 1);
-    const int tok = shared ? mm : p.perm[slot0 + mm];
-    const char* xrow = reinterpret_cast<const char*>(p.x + (long long)tok * D) + g * 32;
-    Frag xa[nq];
+template <int D, int FR>
+__device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds, Book& B) {
+  decode_book(p, B);
+  constexpr int nfb = FR / 16;
+  const int a = item / nfb, fb = item - a * nfb;
+  if (a >= B.n_active) return;                       // uniform over the workgroup
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+  const int e = B.act_e[a], s0 = B.act_s0[a], n = B.act_n[a];
+  const long long rg = (long long)e * 2 * FR + fb * 16 + fr, ru = rg + FR;
+  const int qofs = wave * (D / 8) + g * 16;          // bytes into a packed row
+  u32x4_t wg[2], wu[2];
 #pragma unroll
-    for (int c = 0; c < nq; ++c) {
-      xa[c].lo = ld16(xrow + (c0 + c) * 128);
-      xa[c].hi = ld16(xrow + (c0 + c) * 128 + 16);
-    }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (shared) {
+  for (int grp = 0; grp < 2; ++grp) {
+    wg[grp] = ld16(p.q_gate_up + rg * (D / 2) + qofs + grp * 64);
+    wu[grp] = ld16(p.q_gate_up + ru * (D / 2) + qofs + grp * 64);
+  }
+  const uint32_t sg = *reinterpret_cast<const uint32_t*>(p.s_gate_up + rg * (D / kGroup) + wave * 2);
+  const uint32_t su = *reinterpret_cast<const uint32_t*>(p.s_gate_up + ru * (D / kGroup) + wave * 2);
+  for (int m0 = 0; m0 < n; m0 += 16) {
+    const int nt = min(16, n - m0);
+    const int tok = B.perm[s0 + m0 + min(fr, nt - 1)];
+    const char* xr = reinterpret_cast<const char*>(p.x + (long long)tok * D) + wave * (D / 2) + g * 64;
+    u32x4_t xa[2][4];
 #pragma unroll
-      for (int c = 0; c < nq; ++c) acc = Mma<bf16_t>::run(xa[c], wbf[c], acc);
-    } else {
+    for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
-      for (int c = 0; c < nq; c += 2) {              // one scale group = 2 chunks of 64 elements
-        f32x4_t tmp = {0.f, 0.f, 0.f, 0.f};
-        tmp = Mma<bf16_t>::run(xa[c], int4x16_to_bf16(wq4[c]), tmp);
-        tmp = Mma<bf16_t>::run(xa[c + 1], int4x16_to_bf16(wq4[c + 1]), tmp);
+      for (int j = 0; j < 4; ++j) xa[grp][j] = ld16(xr + grp * 256 + j * 16);
+    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < 4; ++i) acc[i] += tmp[i] * bf16_to_f32(wsc[c / 2]);
+    for (int grp = 0; grp < 2; ++grp) {
+      f32x4_t tg = {0.f, 0.f, 0.f, 0.f}, tu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        tg = Mma<bf16_t>::run1(xa[grp][j], int4x8_to_bf16(wg[grp][j]), tg);
+        tu = Mma<bf16_t>::run1(xa[grp][j], int4x8_to_bf16(wu[grp][j]), tu);
+      }
+      const float scg = bf16_to_f32((bf16_t)(grp ? sg >> 16 : sg & 0xFFFFu));
+      const float scu = bf16_to_f32((bf16_t)(grp ? su >> 16 : su & 0xFFFFu));
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        ag[i] += tg[i] * scg;
+        au[i] += tu[i] * scu;
       }
     }
-    // acc[i]: token row m0 + 4g + i, MFMA column fr
+    // lds: [wave][token][column], row stride 33 (gate columns 0-15, up 16-31)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][(m0 + 4 * g + i) & 63][fr] = acc[i];
+    for (int i = 0; i < 4; ++i) {
+      lds[(wave * 16 + 4 * g + i) * 33 + fr] = ag[i];
+      lds[(wave * 16 + 4 * g + i) * 33 + 16 + fr] = au[i];
+    }
+    __syncthreads();
+    if (tid < 2 * nt) {
+      const int m = tid >> 1, c8 = (tid & 1) * 8;
+      float h[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c)
+        h[c] = siluf_(sum4(lds + m * 33 + c8 + c, 16 * 33)) * sum4(lds + m * 33 + 16 + c8 + c, 16 * 33);
+      st16(p.H + (long long)(s0 + m0 + m) * FR + fb * 16 + c8, pack8(h));
+    }
+    __syncthreads();                                 // before the next tile reuses the partials
   }
-  __syncthreads();
-  // h = silu(gate) * up from the 4 quarters, added in order
-  for (int i = tid; i < ntok * 8; i += 256) {
-    const int m = i >> 3, c = i & 7;
-    const float a = ((part[0][m][c] + part[1][m][c]) + part[2][m][c]) + part[3][m][c];
-    const float u = ((part[0][m][c + 8] + part[1][m][c + 8]) + part[2][m][c + 8]) + part[3][m][c + 8];
-    const float h = siluf_(a) * u;
-    const int col = fblk * 8 + c;
-    if (shared) p.Hs[(long long)m * FS + col] = f32_to_bf16(h);
-    else p.H[(long long)(slot0 + m) * FR + col] = f32_to_bf16(h);
+}
+
+// Block 0 writes the routing; then the shared down (256 items x token
+// tiles); then the routed gate/up (items of experts past the active count
+// exit after the bookkeeping).
+template <int D, int FR, int FS>
+__global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int ntile) {
+  __shared__ float lds[4 * 16 * 33];
+  __shared__ Book B;
+  const int n_sd = 4 * (D / 16) * ntile;
+  const int blk = blockIdx.x;
+  if (blk == 0) {
+    decode_book(p, B);
+    decode_write_routing(p, B);
+  } else if (blk <= n_sd) {
+    int j, tt;
+    xcd_item(blk - 1, ntile, j, tt);
+    decode_shared_down<D, FS>(p, j, tt, lds, B);
+  } else {
+    decode_routed_gate_up<D, FR>(p, blk - 1 - n_sd, lds, B);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Down.  Item i < 4 * D/16: shared expert, output columns 16 (i / 4) .. +15,
-// contraction quarter i % 4 of Fs; item >= 4 * D/16: routed expert
-// active[(i - 4D/16) / (D/16)] over its own tokens, output columns
-// 16 ((i - 4D/16) % (D/16)), whole contraction F.  The 16 weight rows (output
-// columns) form one MFMA tile; the 4 waves split the item's contraction and
-// their partial tiles are added in LDS in a fixed order.  Results are fp32:
-// shared partials in part_sh[quarter][t][n], routed rows in rout[slot][n].
+// Stage 3, routed down + combine: item i takes active expert a = i / (D/32)
+// and output columns 32 cb .. 32 cb + 31 (cb = i % (D/32)), two 16-row
+// tiles; wave w takes scale group w of the contraction F.  For each of the
+// expert's tokens t (slot s): y[t] = (((sh0 + sh1) + sh2) + sh3)[s] + o,
+// rounded once, where sh_q are the shared-down partials and o the routed row
+// (top-1: gate 1).  Every token belongs to exactly one active expert, so
+// every y row is written once.  Operands come straight from global memory
+// (as in stage 2).
 // ---------------------------------------------------------------------------
-template <int D, int FR, int FS>
-__global__ __launch_bounds__(256) void decode_down_kernel(DecodeArgs p) {
-  __shared__ float part[4][64][17];                  // [wave][token][column]
+template <int D, int FR>
+__global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
+  __shared__ float lds[4 * 16 * 33];
+  static_assert(FR / kGroup == 4, "one scale group per wave");
+  constexpr int ncb = D / 32;
+  const int a = blockIdx.x / ncb, cb = blockIdx.x - a * ncb;
+  // the active entry is read together with the count; a < E keeps it in bounds
+  const int na = *p.n_active;
+  const int e = min(max(p.active[3 * a], 0), p.E - 1), s0 = p.active[3 * a + 1], n = p.active[3 * a + 2];
+  if (a >= na) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
-  constexpr int nblk = D / 16, n_sh = 4 * nblk;
-  const int item = blockIdx.x;
-  const bool shared = item < n_sh;
-  int e = 0, cblk, quarter = 0, ntok, slot0 = 0;
-  if (shared) {
-    cblk = item >> 2;
-    quarter = item & 3;
-    ntok = p.T;
-  } else {
-    const int a = (item - n_sh) / nblk;
-    if (a >= *p.n_active) return;
-    e = p.active[3 * a];
-    slot0 = p.active[3 * a + 1];
-    ntok = p.active[3 * a + 2];
-    cblk = (item - n_sh) - a * nblk;
+  u32x4_t wq[2];
+  float sc[2];
+#pragma unroll
+  for (int tile = 0; tile < 2; ++tile) {
+    const long long r = (long long)e * D + cb * 32 + tile * 16 + fr;
+    wq[tile] = ld16(p.q_down + r * (FR / 2) + wave * 64 + g * 16);
+    sc[tile] = bf16_to_f32(p.s_down[r * (FR / kGroup) + wave]);
   }
-  const int n = cblk * 16 + fr;                      // this lane's weight row = output column
-  // shared: wave w takes chunks [quarter * 8 + 2w, +2) of the 32 chunks of Fs;
-  // routed: wave w takes chunks [2w, 2w + 2) of the 8 chunks of F (one scale group)
-  constexpr int nch = 2;
-  Frag wf[nch];
-  uint2 q4[nch];
-  uint16_t sc = 0;
-  int cbase;
-  if (shared) {
-    cbase = quarter * (FS * 2 / 128 / 4) + wave * nch;
-    const char* wb = reinterpret_cast<const char*>(p.w_sh_down) + (long long)n * FS * 2 + g * 32;
+  const long long q1 = (long long)p.T * D;
+  for (int m0 = 0; m0 < n; m0 += 16) {
+    const int nt = min(16, n - m0);
+    const char* hr = reinterpret_cast<const char*>(p.H + (long long)(s0 + m0 + min(fr, nt - 1)) * FR) + wave * 256 + g * 64;
+    u32x4_t ha[4];
 #pragma unroll
-    for (int c = 0; c < nch; ++c) {
-      wf[c].lo = ld16(wb + (cbase + c) * 128);
-      wf[c].hi = ld16(wb + (cbase + c) * 128 + 16);
-    }
-  } else {
-    cbase = wave * nch;
-    const long long r = (long long)e * D + n;
-    const uint8_t* wq = p.q_down + r * (FR / 2) + g * 8;
+    for (int j = 0; j < 4; ++j) ha[j] = ld16(hr + j * 16);
+    // combine operands of this thread's output piece (4 nt <= 64 threads, all
+    // in the first wave), requested after the operands, before the products
+    const bool out = tid < 4 * nt;
+    const int m = tid >> 2, c8 = (tid & 3) * 8;
+    int tok = 0;
+    f32x4_t sh[4][2];
+    if (tid < 64) {
+      const int mc = min(m, nt - 1);
+      tok = p.perm[s0 + m0 + mc];
 #pragma unroll
-    for (int c = 0; c < nch; ++c) q4[c] = *reinterpret_cast<const uint2*>(wq + (cbase + c) * 32);
-    sc = p.s_down[r * (FR / kGroup) + wave];
-  }
-  const bf16_t* A = shared ? p.Hs : p.H;
-  const int lda = shared ? FS : FR;
-  for (int m0 = 0; m0 < ntok; m0 += 16) {
-    const int mm = min(m0 + fr, ntok - 1);
-    const char* arow = reinterpret_cast<const char*>(A + (long long)(slot0 + mm) * lda) + g * 32;
-    Frag ha[nch];
-#pragma unroll
-    for (int c = 0; c < nch; ++c) {
-      ha[c].lo = ld16(arow + (cbase + c) * 128);
-      ha[c].hi = ld16(arow + (cbase + c) * 128 + 16);
-    }
-    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
-    if (shared) {
-#pragma unroll
-      for (int c = 0; c < nch; ++c) acc = Mma<bf16_t>::run(ha[c], wf[c], acc);
-    } else {
-      acc = Mma<bf16_t>::run(ha[0], int4x16_to_bf16(q4[0]), acc);
-      acc = Mma<bf16_t>::run(ha[1], int4x16_to_bf16(q4[1]), acc);
-      const float s = bf16_to_f32(sc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) acc[i] *= s;
+      for (int q = 0; q < 4; ++q) {
+        const float* src = p.part_sh + q * q1 + (long long)(s0 + m0 + mc) * D + cb * 32 + c8;
+        sh[q][0] = *reinterpret_cast<const f32x4_t*>(src);
+        sh[q][1] = *reinterpret_cast<const f32x4_t*>(src + 4);
+      }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][(m0 + 4 * g + i) & 63][fr] = acc[i];
+    for (int tile = 0; tile < 2; ++tile) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; ++j) acc = Mma<bf16_t>::run1(ha[j], int4x8_to_bf16(wq[tile][j]), acc);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) lds[(wave * 16 + 4 * g + i) * 33 + tile * 16 + fr] = acc[i] * sc[tile];
+    }
+    __syncthreads();
+    if (out) {
+      float v[8];
+#pragma unroll
+      for (int c = 0; c < 8; ++c) {
+        const float o = sum4(lds + m * 33 + c8 + c, 16 * 33);
+        const float s = ((sh[0][c >> 2][c & 3] + sh[1][c >> 2][c & 3]) + sh[2][c >> 2][c & 3]) + sh[3][c >> 2][c & 3];
+        v[c] = s + o;
+      }
+      st16(p.y + (long long)tok * D + cb * 32 + c8, pack8(v));
+    }
+    __syncthreads();                                 // before the next tile reuses the partials
   }
-  __syncthreads();
-  float* dst = shared ? p.part_sh + (long long)quarter * p.T * D : p.rout;
-  for (int i = tid; i < ntok * 16; i += 256) {
-    const int m = i >> 4, c = i & 15;
-    const float v = ((part[0][m][c] + part[1][m][c]) + part[2][m][c]) + part[3][m][c];
-    dst[(long long)(slot0 + m) * D + cblk * 16 + c] = v;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// y[t, n] = (((sh0 + sh1) + sh2) + sh3)[t, n] + rout[pos[t], n], rounded once
-// (top-1: the token's single routed row carries gate 1).
-// ---------------------------------------------------------------------------
-template <int D>
-__global__ __launch_bounds__(256) void decode_combine_kernel(DecodeArgs p) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= p.T * D) return;
-  const int t = i / D, n = i - t * D;
-  const long long q = (long long)p.T * D;
-  const float sh = ((p.part_sh[i] + p.part_sh[q + i]) + p.part_sh[2 * q + i]) + p.part_sh[3 * q + i];
-  p.y[i] = f32_to_bf16(sh + p.rout[(long long)p.pos[t] * D + n]);
 }
 
 }  // namespace
@@ -422,13 +560,17 @@ bool decode_shape_supported(int d, int F, int Fs) { return d == kDecodeD && F ==
 
 void launch_decode(const DecodeArgs& a, hipStream_t s) {
   constexpr int D = kDecodeD, FR = kDecodeF, FS = kDecodeFs;
-  if (a.T > 0) hipLaunchKernelGGL(decode_logits_kernel<D>, dim3(16), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(decode_select_kernel, dim3(1), dim3(256), 0, s, a);   // also writes the empty routing of T = 0
-  if (a.T == 0) return;
+  static_assert((FS / 8) % 8 == 0 && (4 * (D / 16)) % 8 == 0, "token-tiled items need weight blocks in eights");
+  const int ntile = (a.T + 15) / 16;
+  if (a.T == 0) {   // only the (empty) routing outputs
+    hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS>), dim3(1), dim3(256), 0, s, a, 0);
+    return;
+  }
   const int max_active = a.T * a.k < a.E ? a.T * a.k : a.E;
-  hipLaunchKernelGGL((decode_gate_up_kernel<D, FR, FS>), dim3(FS / 8 + max_active * (FR / 8)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL((decode_down_kernel<D, FR, FS>), dim3(4 * (D / 16) + max_active * (D / 16)), dim3(256), 0, s, a);
-  hipLaunchKernelGGL(decode_combine_kernel<D>, dim3((a.T * D + 255) / 256), dim3(256), 0, s, a);
+  hipLaunchKernelGGL((decode_stage1_kernel<D, FS>), dim3((FS / 8) * ntile + 4 * ntile), dim3(256), 0, s, a, ntile);
+  hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS>), dim3(1 + 4 * (D / 16) * ntile + max_active * (FR / 16)),
+                     dim3(256), 0, s, a, ntile);
+  hipLaunchKernelGGL((decode_stage3_kernel<D, FR>), dim3(max_active * (D / 32)), dim3(256), 0, s, a);
 }
 
 }  // namespace fgmoe

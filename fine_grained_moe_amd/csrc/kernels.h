@@ -109,11 +109,11 @@ struct DecodeArgs {
   int32_t* pos;
   int32_t* active;                   // [E][3] (expert, first slot, load) of each expert with a load, ascending
   int32_t* n_active;                 // [1]
+  uint64_t* rkey;                    // [4][64] per expert tile: each token's largest selection key (workspace)
+  float* rscore;                     // [4][64] the sigmoid score that goes with it (workspace)
   uint16_t* Hs;                      // [T, Fs] bf16 (workspace)
   uint16_t* H;                       // [T*k, F] bf16 (workspace)
-  float* lpart;                      // [4, T, 64] fp32 router logit partials (workspace)
   float* part_sh;                    // [4, T, d] fp32 shared down partials (workspace)
-  float* rout;                       // [T*k, d] fp32 routed down rows (workspace)
   uint16_t* y;                       // [T, d] bf16
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);
