@@ -380,6 +380,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   GemmArgs ga{};
   ga.act = d.act;
   ga.njobs = 2;
+  ga.order = 1;                                      // routed tiles first: they run longest
   ga.job[0] = g;
   ga.job[1] = sg;
   launch_gemm(ga, s);
@@ -422,6 +423,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   GemmArgs da{};
   da.act = d.act;
   da.njobs = 2;
+  da.order = 2;                                      // shared tiles first: twice the contraction of a routed tile
   da.job[0] = dn;
   da.job[1] = sd;
   launch_gemm(da, s);

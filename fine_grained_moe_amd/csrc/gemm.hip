@@ -160,18 +160,26 @@ __global__ __launch_bounds__(NTHR, 2) void gemm_kernel(GemmArgs args) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
 
-  // ---- which job: chunks of 8 blocks (one per XCD) alternate between the
-  // two jobs while both have chunks left.
+  // ---- which job: chunks of 8 blocks (one per XCD) either alternate
+  // between the two jobs while both have chunks left, or come job by job
+  // (the hardware starts blocks in index order, so the job whose tiles take
+  // longest goes first).
   const int chunk = blockIdx.x >> 3;
   const int c0 = args.chunks[0], c1 = args.njobs > 1 ? args.chunks[1] : 0;
-  const int both = c0 < c1 ? c0 : c1;
   int jid, jc;
-  if (chunk < 2 * both) {
-    jid = chunk & 1;
-    jc = chunk >> 1;
+  if (args.njobs > 1 && args.order != 0) {
+    const int f = args.order - 1, cf = f ? c1 : c0;
+    jid = chunk < cf ? f : 1 - f;
+    jc = chunk < cf ? chunk : chunk - cf;
   } else {
-    jid = c0 > c1 ? 0 : 1;
-    jc = both + (chunk - 2 * both);
+    const int both = c0 < c1 ? c0 : c1;
+    if (chunk < 2 * both) {
+      jid = chunk & 1;
+      jc = chunk >> 1;
+    } else {
+      jid = c0 > c1 ? 0 : 1;
+      jc = both + (chunk - 2 * both);
+    }
   }
   const GemmJob& p = args.job[jid];
   const int bid = jc * 8 + (blockIdx.x & 7);

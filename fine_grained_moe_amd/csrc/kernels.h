@@ -80,6 +80,7 @@ struct GemmJob {
 struct GemmArgs {
   int act;                 // dtype of A, B, C, aux
   int njobs;
+  int order;               // two jobs: 0 = chunks alternate, 1 = job 0's chunks first, 2 = job 1's first
   int chunks[2];           // filled by launch_gemm
   GemmJob job[2];
 };
