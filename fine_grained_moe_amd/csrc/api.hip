@@ -21,7 +21,7 @@ size_t act_bytes(int act) { return act == MOE_BF16 ? 2 : 4; }
 
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
-  size_t block_counts, rank, tile_e, tile_m0, tile_count;
+  size_t block_counts, rank, tile_e, tile_m0, tile_count, tile2_e, tile2_m0, tile2_count;
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
   // backward scratch (training): padded contraction tables and transposed operands
@@ -71,6 +71,10 @@ Layout make_layout(const moe_dims& d, int training) {
   L.tile_e = take(tiles * 4);
   L.tile_m0 = take(tiles * 4);
   L.tile_count = take(4);
+  const size_t tiles2 = (size_t)max_group_tiles((long long)slots, d.E, kTileMFwd);
+  L.tile2_e = take(tiles2 * 4);
+  L.tile2_m0 = take(tiles2 * 4);
+  L.tile2_count = take(4);
   L.H = take(slots * d.F * es);
   L.Hs = take((size_t)d.T * d.Fs * es);
   if (d.w_routed == MOE_INT4_G128) {
@@ -83,7 +87,9 @@ Layout make_layout(const moe_dims& d, int training) {
     return L;
   }
   L.O = take(slots * d.d * es);
-  L.S = take((size_t)d.T * d.d * es);
+  // bf16: the shared down is split over two contraction halves, written as
+  // two slices S, S2 that the combine adds
+  L.S = take((size_t)d.T * d.d * es * (d.act == MOE_BF16 ? 2 : 1));
   if (training) {
     L.AU = take(slots * 2 * d.F * es);
     L.Ou = take(slots * d.d * es);
@@ -168,10 +174,10 @@ void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void
   const int nblk = route_blocks(d.T);
   launch_route_topk(d.act, x, w_router, bias, d.T, d.d, d.E, d.k, r->idx, r->gate, at<int32_t>(ws, L.block_counts),
                     at<int32_t>(ws, L.rank), s);
+  const TileTable tiles{at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count)};
+  const TileTable tiles_fwd{at<int32_t>(ws, L.tile2_e), at<int32_t>(ws, L.tile2_m0), at<int32_t>(ws, L.tile2_count)};
   launch_route_dispatch(at<int32_t>(ws, L.block_counts), r->idx, at<int32_t>(ws, L.rank), nblk, d.T, d.E, d.k,
-                        r->counts, r->offsets,
-                        at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count), r->perm,
-                        r->pos, s);
+                        r->counts, r->offsets, tiles, tiles_fwd, r->perm, r->pos, s);
 }
 
 moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
@@ -327,7 +333,12 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   if (d.T == 0) return device_status();
 
   const long long slots = (long long)d.T * d.k;
-  const int max_tiles = (int)max_group_tiles(slots, d.E);
+  // bf16 runs on the 256 x 256 tiles of gemm_fwd.hip (grouped jobs index the
+  // 256-row tile table), fp32 on gemm.hip's 128 x 256 tiles.
+  const bool big = d.act == MOE_BF16;
+  const int tm = big ? kTileMFwd : kTileM;
+  const int max_tiles = (int)max_group_tiles(slots, d.E, tm);
+  auto gemm = big ? launch_gemm_fwd256 : launch_gemm;
   void* H = at<char>(ws, L.H);
   void* O = at<char>(ws, L.O);
   void* Hs = at<char>(ws, L.Hs);
@@ -348,9 +359,9 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   g.N = d.F;
   g.up_off = d.F;
   g.grouped = 1;
-  g.tile_e = at<int32_t>(ws, L.tile_e);
-  g.tile_m0 = at<int32_t>(ws, L.tile_m0);
-  g.tile_count = at<int32_t>(ws, L.tile_count);
+  g.tile_e = at<int32_t>(ws, big ? L.tile2_e : L.tile_e);
+  g.tile_m0 = at<int32_t>(ws, big ? L.tile2_m0 : L.tile_m0);
+  g.tile_count = at<int32_t>(ws, big ? L.tile2_count : L.tile_count);
   g.offsets = routing->offsets;
   g.counts = routing->counts;
   g.max_items = max_tiles;
@@ -371,7 +382,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   sg.up_off = d.Fs;
   sg.grouped = 0;
   sg.M = d.T;
-  sg.max_items = (d.T + kTileM - 1) / kTileM;
+  sg.max_items = (d.T + tm - 1) / tm;
   sg.C = Hs;
   sg.ldc = Fs;
   sg.aux = training ? at<char>(ws, L.AUs) : nullptr;
@@ -383,7 +394,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   ga.order = 1;                                      // routed tiles first: they run longest
   ga.job[0] = g;
   ga.job[1] = sg;
-  launch_gemm(ga, s);
+  gemm(ga, s);
   mark_phase(2, s);
 
   // Launch 2: routed down, rows scaled by their routing weight
@@ -419,6 +430,13 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   sd.C = S;
   sd.ldc = D;
   sd.aux = nullptr;
+  // 64 tiles of 256 x 256 with a 2048-long contraction would hold a quarter
+  // of the chip for the whole launch: two contraction halves instead
+  const bool split_sd = big;
+  if (split_sd) {
+    sd.ksplit = 2;
+    sd.c_kstride = (long long)d.T * D;
+  }
 
   GemmArgs da{};
   da.act = d.act;
@@ -426,11 +444,12 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   da.order = 2;                                      // shared tiles first: twice the contraction of a routed tile
   da.job[0] = dn;
   da.job[1] = sd;
-  launch_gemm(da, s);
+  gemm(da, s);
   mark_phase(3, s);
 
   // combine: y[t] = S[t] + sum_j O[pos[t, j]]
-  launch_combine(d.act, S, O, routing->pos, d.T, d.d, d.k, y, s);
+  launch_combine(d.act, S, split_sd ? static_cast<char*>(S) + (size_t)d.T * D * es : nullptr, O, routing->pos, d.T,
+                 d.d, d.k, y, s);
   mark_phase(4, s);
   return device_status();
 }

@@ -1,0 +1,352 @@
+// Forward expert GEMMs of the MoE layer in bf16 on gfx950 MFMA: 256 x 256
+// output tiles, one workgroup of 8 waves per CU.
+//
+// The two forward launches of a bf16 layer run here:
+//   gate/up: routed (grouped over experts, A rows gathered from x through the
+//            dispatch order) + shared (dense), SwiGLU epilogue -> H, Hs
+//   down:    routed (grouped, rows scaled by their routing weight) + shared
+//            (dense, plain store) -> O, S
+// The experts are the SwiGLU FFNs of widths 512 (routed) and 2048 (shared) of
+// the seventnews article "A relay race of rented GPUs trained NanoColibri's
+// 2.7B MoE for $200" (opening section, architecture paragraph).
+//
+// Why a second tile shape next to gemm.hip's 128 x 256 pair of workgroups:
+// a CU's operand traffic per MFMA flop falls by a third (32 KiB per 4.2 MFLOP
+// of K step instead of 2 x 24 KiB per 2 x 2.1 MFLOP), which is the resource
+// that bounds the smaller tiles.  A grouped item is
+// up to 256 rows of one expert, so an expert of up to 256 rows streams its
+// weights once; the waves whose 64-row band lies past the item's rows skip
+// their operand reads and MFMAs (they still load their share of the stage).
+//
+// Workgroup: 8 waves (4 x 2), each owning a 64 x 128 piece (4 x 8 MFMA
+// 16x16x32 tiles).  K advances in 64-byte row chunks through a 5-deep LDS
+// ring of 32 KiB stages (256 A rows, then 256 B rows; 160 KiB, all of a
+// CU's LDS), filled by direct global->LDS loads (global_load_lds_dwordx4)
+// spread between the MFMAs; a stage's loads have three K steps to land.
+// Measured on gfx950 with per-workgroup clock stamps: with the operands read
+// from LDS right after each K step's barrier, the MFMA pipes waited about a
+// third of the loop for those reads; here each K step's MFMAs run from
+// registers while the next step's operands are read behind them.  The LDS
+// rows are XOR-swizzled (swz) and B rows permuted so that each lane's output
+// columns are adjacent, as in gemm.hip.
+//
+// Scheduling: as in gemm.hip.  Items are 256-row tiles (dense: row blocks,
+// times the contraction slices of a split dense job; grouped: the 256-row
+// tile table the router wrote).  Block b runs on XCD
+// b % 8; XCD x gets the contiguous item range [x*q, (x+1)*q); grouped jobs
+// run all N tiles of an item back to back, dense jobs all of the XCD's row
+// blocks for one N tile before the next.
+#include <type_traits>
+
+#include "gemm_tile.h"
+
+namespace fgmoe {
+
+namespace {
+
+constexpr int NTHR = 512;                    // 8 waves
+constexpr int BM = kTileMFwd, BN = 256;      // workgroup tile
+constexpr int WM = 64, WN = 128, NI = WN / 16, HN = NI / 2;   // one wave's output piece
+constexpr int kStages = 5;                   // LDS ring depth (5 x 32 KiB: all of a CU's LDS)
+constexpr int ATILE = BM * kRowB, BTILE = BN * kRowB;        // one stage of each operand
+constexpr int kStageBytes = ATILE + BTILE;
+constexpr int NDA = BM / 8 / 16, NDB = BN / 8 / 16;          // loads per wave and stage: A 2, B 2
+constexpr int kLoads = NDA + NDB;
+static_assert(BM == 256, "the wave layout covers 256 rows");
+
+__device__ __host__ __forceinline__ int n_tiles(const GemmJob& j) {
+  const int w = j.epi == EPI_SWIGLU ? BN / 2 : BN;
+  return (j.N + w - 1) / w;
+}
+// contraction slices of a dense job
+__device__ __host__ __forceinline__ int k_slices(const GemmJob& j) { return j.ksplit > 1 ? j.ksplit : 1; }
+__device__ __forceinline__ int item_count(const GemmJob& j) {
+  return j.grouped ? *j.tile_count : (j.M + BM - 1) / BM * k_slices(j);
+}
+inline long long max_item_count(const GemmJob& j) {
+  return j.grouped ? j.max_items : (long long)(j.M + BM - 1) / BM * k_slices(j);
+}
+
+template <bool SWIGLU>
+__global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
+  typedef bf16_t T;
+  // The ring; after the main loop its first buffer holds the row scales.
+  __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave >> 1, wn = wave & 1;
+
+  int jid, bid;
+  select_job(args, blockIdx.x, jid, bid);
+  const GemmJob& p = args.job[jid];
+
+  // ---- work item and N tile
+  const int count = item_count(p);
+  const int q = (count + 7) >> 3;
+  const int nbn = n_tiles(p);
+  const int xcd = bid & 7, local = bid >> 3;
+  int pi, nt;
+  if (p.grouped) {
+    pi = local / nbn;
+    nt = local - pi * nbn;
+  } else {
+    nt = local / (q > 0 ? q : 1);
+    pi = local - nt * q;
+    if (nt >= nbn) return;
+  }
+  if (pi >= q) return;
+  const int item = xcd * q + pi;
+  if (item >= count) return;
+  int e = 0, rows, row_base, kz = 0;
+  if (p.grouped) {
+    e = p.tile_e[item];
+    const int m0 = p.tile_m0[item];
+    rows = p.counts[e] - m0;
+    row_base = p.offsets[e] + m0;
+  } else {
+    // dense items: row blocks of contraction slice 0, then of slice 1, ...
+    const int nrb = (p.M + BM - 1) / BM;
+    kz = item / nrb;
+    const int m0 = (item - kz * nrb) * BM;
+    rows = p.M - m0;
+    row_base = m0;
+  }
+  const int klen = p.K / k_slices(p);
+  const long long kofs = (long long)kz * klen;
+  rows = rows < BM ? rows : BM;
+  // this wave's 64-row band holds rows of the item
+  const bool active = wm * WM < rows;
+
+  // Row scales of the gate-scaled epilogue: thread r < 256 fetches perm of
+  // row r now, the gate after the main loop; the scales reach the waves
+  // through LDS.
+  const bool scaled = p.gate != nullptr && p.epi == EPI_ROWSCALE;
+  int my_perm = 0;
+  if (scaled && tid < BM) my_perm = p.perm[row_base + min(tid, rows - 1)];
+
+  // ---- global -> LDS.  Lane i of a wave instruction lands at LDS byte
+  // base + 16 i, so A load j of wave w fills A rows 32w + 16j + i/4 and B
+  // load j fills B rows 32w + 16j + i/4, at physical piece i%4; the lane
+  // fetches the logical piece the swizzle puts there.  LDS B row
+  // wn*128 + ni*16 + f holds output column (tile base) + wn*128 + 8f + ni; for
+  // SwiGLU the first 128 B rows are gate rows and the next 128 the matching
+  // up rows, with h column (tile base) + wn*64 + 4f + ni.
+  const char* a_src[NDA];
+  const char* b_src[NDB];
+  const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)e * p.b_estride * (long long)sizeof(T);
+#pragma unroll
+  for (int j = 0; j < NDA; ++j) {
+    const int R = wave * (BM / 8) + j * 16 + (lane >> 2);
+    const int c = swz_piece(R, lane & 3);            // XOR swizzles are their own inverse
+    const int ra = min(R, rows - 1);
+    const long long arow = p.a_rows ? (long long)(p.a_rows[row_base + ra] / p.a_div) : (long long)(row_base + ra);
+    a_src[j] = reinterpret_cast<const char*>(p.A) + (arow * p.lda + kofs) * (long long)sizeof(T) + c * 16;
+  }
+#pragma unroll
+  for (int j = 0; j < NDB; ++j) {
+    const int R = wave * (BN / 8) + j * 16 + (lane >> 2);
+    const int c = swz_piece(R, lane & 3);
+    long long brow;
+    if (SWIGLU) {
+      const int half = R >> 7, h = R & 127;
+      const int w = h >> 6, ni = (h >> 4) & 3, f = h & 15;
+      const int col = min(nt * (BN / 2) + w * 64 + 4 * f + ni, p.N - 1);
+      brow = (long long)(half ? p.up_off : 0) + col;
+    } else {
+      const int w = R >> 7, ni = (R >> 4) & 7, f = R & 15;
+      brow = min(nt * BN + w * 128 + 8 * f + ni, p.N - 1);
+    }
+    b_src[j] = bbase + (brow * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
+  }
+  const int nk = (int)((long long)klen * sizeof(T) / kRowB);
+  auto issue_one = [&](int s, int j) {
+    char* st = lds + (s % kStages) * kStageBytes;
+    const long long off = (long long)s * kRowB;
+    if (j < NDA)
+      __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(st + wave * (BM / 8) * kRowB + j * 1024), 16, 0, 0);
+    else
+      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + off,
+                                       (lds_ptr_t)(st + ATILE + wave * (BN / 8) * kRowB + (j - NDA) * 1024), 16, 0, 0);
+  };
+  auto issue = [&](int s) {
+#pragma unroll
+    for (int j = 0; j < kLoads; ++j) issue_one(s, j);
+  };
+
+  // ---- LDS -> MFMA operand rows of this wave (16 consecutive LDS rows per tile)
+  const int fr = lane & 15, g = lane >> 4;
+  int arow_l[4], brow_l[NI];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) arow_l[mi] = wm * WM + mi * 16 + fr;
+#pragma unroll
+  for (int ni = 0; ni < NI; ++ni)
+    brow_l[ni] = (SWIGLU ? (ni < HN ? wn * 64 + ni * 16 : BN / 2 + wn * 64 + (ni - HN) * 16) : wn * WN + ni * 16) + fr;
+
+  f32x4_t acc[4][NI];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Operands of one stage: lane group g owns 16-byte piece g of each 64-byte
+  // row chunk.  The MFMAs of stage s run from registers (fa, fb) while the
+  // operands of stage s + 1 are read from LDS behind them: fb[ni] is reloaded
+  // as soon as the four MFMAs that use it are issued, the A pieces go to a
+  // second set (fa of the next stage).  This wave's global loads of stage
+  // s + kStages - 1 go between the MFMAs (after blocks ni = 1, 3, 5, 7).
+  u32x4_t fa0[4], fa1[4], fb[NI];
+  auto read_a = [&](int s, u32x4_t (&fa)[4]) {
+    const char* As = lds + (s % kStages) * kStageBytes;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) fa[mi] = ld16(As + swz(arow_l[mi], g));
+  };
+  auto read_b = [&](int s) {
+    const char* Bs = lds + (s % kStages) * kStageBytes + ATILE;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) fb[ni] = ld16(Bs + swz(brow_l[ni], g));
+  };
+  // stage s from (fa, fb); prefetch: read stage s + 1 into (fn, fb); loads:
+  // issue stage s + kStages - 1
+  auto compute = [&](int s, u32x4_t (&fa)[4], u32x4_t (&fn)[4], auto prefetch, auto with_loads) {
+    if (!active) {
+      if constexpr (decltype(with_loads)::value) issue(s + kStages - 1);
+      return;
+    }
+    const char* An = lds + ((s + 1) % kStages) * kStageBytes;
+    const char* Bn = An + ATILE;
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) {
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = Mma<T>::run1(fa[mi], fb[ni], acc[mi][ni]);
+      if constexpr (decltype(prefetch)::value) {
+        fb[ni] = ld16(Bn + swz(brow_l[ni], g));
+        if (ni < 4) fn[ni] = ld16(An + swz(arow_l[ni], g));
+      }
+      if constexpr (decltype(with_loads)::value) {
+        if (ni & 1) issue_one(s + kStages - 1, ni >> 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);   // keep the reads and loads spread out
+    }
+  };
+
+  // ---- main loop.  Iteration s waits for stage s + 1 (its loads went out
+  // two iterations earlier) and passes a barrier, so stage s + 1 is complete
+  // in LDS for the prefetch, and every wave has finished the MFMAs of stage
+  // s - 1, whose operands it read in iteration s - 2: buffer (s - 1) % 5 is
+  // free for the loads of stage s + 4.
+  static_assert(kStages == 5, "the waits below assume a 5-deep ring");
+  for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
+  if (nk >= 4) wait_vmcnt<3 * kLoads>();
+  else if (nk == 3) wait_vmcnt<2 * kLoads>();
+  else if (nk == 2) wait_vmcnt<kLoads>();
+  else wait_vmcnt<0>();
+  block_barrier();
+  if (active) {
+    read_a(0, fa0);
+    read_b(0);
+  }
+  // Stages issued before iteration s: min(nk, s + 4); in flight after stage
+  // s + 1: that minus s + 2.
+  int s = 0;
+  for (; s + kStages - 1 < nk; ++s) {
+    wait_vmcnt<2 * kLoads>();
+    block_barrier();
+    compute(s, fa0, fa1, std::true_type{}, std::true_type{});
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
+  }
+  for (; s + 1 < nk; ++s) {
+    if (nk - s - 2 >= 2) wait_vmcnt<2 * kLoads>();
+    else if (nk - s - 2 == 1) wait_vmcnt<kLoads>();
+    else wait_vmcnt<0>();
+    block_barrier();
+    compute(s, fa0, fa1, std::true_type{}, std::false_type{});
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
+  }
+  compute(s, fa0, fa1, std::false_type{}, std::false_type{});
+
+  // Row scales, staged in ring buffer 0 once every wave is past its last
+  // read of the ring.
+  float* const row_scale = reinterpret_cast<float*>(lds);
+  if (scaled) {
+    __syncthreads();
+    if (tid < BM) row_scale[tid] = p.gate[my_perm];
+    __syncthreads();
+  }
+  if (!active) return;
+  // ---- epilogue.  acc[mi][ni][i] is tile row wm*64 + mi*16 + 4g + i.  Its
+  // column, past the wave's base, is 8f + ni (f = lane % 16); for SwiGLU,
+  // blocks ni < 4 are gate columns 4f + ni and ni >= 4 the matching up.
+  T* C = reinterpret_cast<T*>(p.C) + kz * p.c_kstride;
+  T* aux = reinterpret_cast<T*>(p.aux);
+  const int n = nt * BN + wn * WN + NI * fr;               // first column of this lane (not SwiGLU)
+  const int fh = nt * (BN / 2) + wn * (WN / 2) + HN * fr;  // first h column of this lane (SwiGLU)
+  if (SWIGLU ? fh >= p.N : n >= p.N) return;
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int lr = wm * WM + mi * 16 + 4 * g + i;
+      if (lr >= rows) continue;
+      const long long row = row_base + lr;
+      if (SWIGLU) {
+        float h[HN], a[HN], u[HN];
+#pragma unroll
+        for (int ni = 0; ni < HN; ++ni) {
+          a[ni] = acc[mi][ni][i];
+          u[ni] = acc[mi][ni + HN][i];
+          h[ni] = siluf_(a[ni]) * u[ni];
+        }
+        store_vec<T, HN>(C + row * p.ldc + fh, h);
+        if (aux) {
+          store_vec<T, HN>(aux + row * p.ldaux + fh, a);
+          store_vec<T, HN>(aux + row * p.ldaux + p.N + fh, u);
+        }
+      } else if (p.epi == EPI_ROWSCALE) {
+        const float sc = row_scale[lr];
+        float v[NI], raw[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          raw[ni] = acc[mi][ni][i];
+          v[ni] = raw[ni] * sc;
+        }
+        store_vec<T, NI>(C + row * p.ldc + n, v);
+        if (aux) store_vec<T, NI>(aux + row * p.ldaux + n, raw);
+      } else {  // EPI_STORE
+        float v[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) v[ni] = acc[mi][ni][i];
+        store_vec<T, NI>(C + row * p.ldc + n, v);
+      }
+    }
+  }
+}
+
+int job_chunks(const GemmJob& j) {
+  const int nbn = n_tiles(j);
+  const long long groups = (max_item_count(j) + 7) / 8;
+  return (int)(groups * nbn);
+}
+
+}  // namespace
+
+// bf16 forward jobs only: epilogues SwiGLU, row scale or plain store, no
+// per-expert contraction ranges, K / ksplit a multiple of 32 (checked by the
+// caller); a split job's slices each write their own output.
+void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
+  GemmArgs a = in;
+  long long total = 0;
+  for (int i = 0; i < a.njobs; ++i) {
+    a.chunks[i] = job_chunks(a.job[i]);
+    total += a.chunks[i];
+  }
+  if (total == 0) return;
+  const dim3 grid((unsigned)(total * 8));
+  if (a.job[0].epi == EPI_SWIGLU)
+    hipLaunchKernelGGL((gemm256_kernel<true>), grid, dim3(NTHR), 0, s, a);
+  else
+    hipLaunchKernelGGL((gemm256_kernel<false>), grid, dim3(NTHR), 0, s, a);
+}
+
+}  // namespace fgmoe

@@ -10,19 +10,32 @@ namespace fgmoe {
 
 // Tokens handled by one routing workgroup (4 waves, one 16x16 logit tile each).
 constexpr int kRouteTokensPerBlock = 16;
-// Rows of one grouped-GEMM tile.
+// Rows of one grouped-GEMM tile: gemm.hip (fp32 forward, backward) and
+// gemm_fwd.hip (bf16 forward).  The router writes a tile table for each.
 constexpr int kTileM = 128;
+constexpr int kTileMFwd = 256;
 
 inline int route_blocks(int T) { return (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
 // Upper bound of sum_e ceil(count_e / kTileM) over any routing of T*k slots.
-inline long long max_group_tiles(long long slots, int E) { return (slots + (long long)E * (kTileM - 1)) / kTileM; }
+inline long long max_group_tiles(long long slots, int E, int tm = kTileM) {
+  return (slots + (long long)E * (tm - 1)) / tm;
+}
+
+// (expert, first row) of every tm rows of each expert, in expert order, and
+// the number of entries.
+struct TileTable {
+  int32_t* e;
+  int32_t* m0;
+  int32_t* count;
+};
 
 // act: 0 = float32, 1 = bfloat16 (moe_dtype values).
 void launch_route_topk(int act, const void* x, const void* w_router, const float* bias, int T, int d, int E,
                        int k, int32_t* idx, float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s);
+// tiles: kTileM rows per entry; tiles_fwd: kTileMFwd rows (may be null).
 void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
-                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* tile_e, int32_t* tile_m0,
-                           int32_t* tile_count, int32_t* perm, int32_t* pos, hipStream_t s);
+                           int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
+                           int32_t* perm, int32_t* pos, hipStream_t s);
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s);
 
 enum Epilogue {
@@ -67,6 +80,10 @@ struct GemmJob {
   const int32_t* kofs;
   const int32_t* klen;
   long long c_estride;
+  // dense jobs of launch_gemm_fwd256: the contraction is cut into ksplit
+  // equal slices (K / ksplit a multiple of 32); slice z writes C + z * c_kstride.
+  int ksplit;
+  long long c_kstride;
   // outputs
   void* C;
   long long ldc;
@@ -85,6 +102,9 @@ struct GemmArgs {
   GemmJob job[2];
 };
 void launch_gemm(const GemmArgs& a, hipStream_t s);
+// bf16 forward jobs (SwiGLU, row-scale or store epilogue, K % 32 == 0) on
+// 256 x 256 tiles; grouped jobs index the kTileMFwd tile table.
+void launch_gemm_fwd256(const GemmArgs& a, hipStream_t s);
 
 // Top-1 serving with int4 routed experts, T <= 64 tokens (decode.hip), built
 // for the NanoColibri layer shape.
@@ -157,8 +177,9 @@ void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm
 void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, const float* dl, const int32_t* idx,
                    const int32_t* pos, int T, int d, int k, void* dx, hipStream_t s);
 
-// y[t] = S[t] + sum_j O[pos[t*k + j]] in fixed j order, rounded once.
-void launch_combine(int act, const void* S, const void* O, const int32_t* pos, int T, int d, int k, void* y,
-                    hipStream_t s);
+// y[t] = S[t] (+ S2[t]) + sum_j O[pos[t*k + j]] in that order, rounded once.
+// S2 (may be null) is the second contraction slice of the shared down.
+void launch_combine(int act, const void* S, const void* S2, const void* O, const int32_t* pos, int T, int d, int k,
+                    void* y, hipStream_t s);
 
 }  // namespace fgmoe

@@ -178,19 +178,35 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 //   slot(t, j) = offsets[e] + sum over earlier router blocks of their loads of e
 //                + rank(t, j) (earlier assignments to e in t's router block),
 // i.e. slots of an expert ascend in t*k + j, independent of scheduling.
-// Block 0 also writes counts, offsets and the tile table, which lists
-// (expert, first row) for every kTileM rows of each expert, in expert order.
+// Block 0 also writes counts, offsets and the tile tables, which list
+// (expert, first row) for every kTileM (kTileMFwd) rows of each expert, in
+// expert order.
 // ---------------------------------------------------------------------------
 constexpr int kDispatchSub = 16;
+
+// Lane e (one wave, 64 lanes) lists the tm-row tiles of expert e, which has
+// cnt rows, after those of experts 0..e-1.
+__device__ __forceinline__ void write_tiles(TileTable t, int tm, int cnt, int e) {
+  const int nt = (cnt + tm - 1) / tm;
+  int tincl = nt;
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(tincl, off);
+    if (e >= off) tincl += o;
+  }
+  const int texcl = tincl - nt;
+  for (int m = 0; m < nt; ++m) {
+    t.e[texcl + m] = e;
+    t.m0[texcl + m] = m * tm;
+  }
+  if (e == 63) *t.count = tincl;
+}
 constexpr int kDispatchBatch = 16;   // count loads a thread keeps in flight
 __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __restrict__ block_counts,
                                                               const int32_t* __restrict__ idx,
                                                               const int32_t* __restrict__ rank, int nblk, int T_,
                                                               int E, int k, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
-                                                              int32_t* __restrict__ tile_e,
-                                                              int32_t* __restrict__ tile_m0,
-                                                              int32_t* __restrict__ tile_count,
+                                                              TileTable tiles, TileTable tiles_fwd,
                                                               int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
   __shared__ int part_tot[16][64];
   __shared__ int part_pre[16][64];
@@ -245,18 +261,8 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
         offsets[e] = excl;
       }
       if (e == E - 1) offsets[E] = incl;
-      const int nt = (cnt + kTileM - 1) / kTileM;
-      int tincl = nt;
-      for (int off = 1; off < 64; off <<= 1) {
-        const int o = __shfl_up(tincl, off);
-        if (e >= off) tincl += o;
-      }
-      const int texcl = tincl - nt;
-      for (int m = 0; m < nt; ++m) {
-        tile_e[texcl + m] = e;
-        tile_m0[texcl + m] = m * kTileM;
-      }
-      if (e == 63) *tile_count = tincl;
+      write_tiles(tiles, kTileM, cnt, e);
+      if (tiles_fwd.e) write_tiles(tiles_fwd, kTileMFwd, cnt, e);
     }
   }
   __syncthreads();
@@ -314,11 +320,11 @@ void launch_route_topk(int act, const void* x, const void* w_router, const float
 }
 
 void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
-                           int E, int k, int32_t* counts, int32_t* offsets, int32_t* tile_e, int32_t* tile_m0,
-                           int32_t* tile_count, int32_t* perm, int32_t* pos, hipStream_t s) {
+                           int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
+                           int32_t* perm, int32_t* pos, hipStream_t s) {
   const int grid = nblk > 0 ? (nblk + kDispatchSub - 1) / kDispatchSub : 1;   // block 0 runs even for T = 0
   hipLaunchKernelGGL(route_dispatch_kernel, dim3(grid), dim3(1024), 0, s, block_counts, idx, rank, nblk, T, E, k,
-                     counts, offsets, tile_e, tile_m0, tile_count, perm, pos);
+                     counts, offsets, tiles, tiles_fwd, perm, pos);
 }
 
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s) {
