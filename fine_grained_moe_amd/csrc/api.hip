@@ -58,6 +58,12 @@ moe_status check_training(const moe_dims& d) {
   return MOE_OK;
 }
 
+// Contraction slices of the shared down GEMM (bf16 forward): 256 x 256
+// tiles over the whole 2048-long contraction would be 64 tiles holding a
+// quarter of the chip for the whole launch.  Two halves measured best on
+// the 4096-token layer (four: more combine traffic, no shorter launch).
+int shared_down_slices(const moe_dims& d) { return d.act == MOE_BF16 ? 2 : 1; }
+
 Layout make_layout(const moe_dims& d, int training) {
   Layout L{};
   const size_t es = act_bytes(d.act);
@@ -87,9 +93,9 @@ Layout make_layout(const moe_dims& d, int training) {
     return L;
   }
   L.O = take(slots * d.d * es);
-  // bf16: the shared down is split over two contraction halves, written as
-  // two slices S, S2 that the combine adds
-  L.S = take((size_t)d.T * d.d * es * (d.act == MOE_BF16 ? 2 : 1));
+  // bf16: the shared down is split over contraction slices, each written as
+  // its own [T, d] block that the combine adds
+  L.S = take((size_t)d.T * d.d * es * shared_down_slices(d));
   if (training) {
     L.AU = take(slots * 2 * d.F * es);
     L.Ou = take(slots * d.d * es);
@@ -430,13 +436,9 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   sd.C = S;
   sd.ldc = D;
   sd.aux = nullptr;
-  // 64 tiles of 256 x 256 with a 2048-long contraction would hold a quarter
-  // of the chip for the whole launch: two contraction halves instead
-  const bool split_sd = big;
-  if (split_sd) {
-    sd.ksplit = 2;
-    sd.c_kstride = (long long)d.T * D;
-  }
+  const int nsd = shared_down_slices(d);
+  sd.ksplit = nsd;
+  sd.c_kstride = (long long)d.T * D;
 
   GemmArgs da{};
   da.act = d.act;
@@ -448,8 +450,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   mark_phase(3, s);
 
   // combine: y[t] = S[t] + sum_j O[pos[t, j]]
-  launch_combine(d.act, S, split_sd ? static_cast<char*>(S) + (size_t)d.T * D * es : nullptr, O, routing->pos, d.T,
-                 d.d, d.k, y, s);
+  launch_combine(d.act, S, nsd, O, routing->pos, d.T, d.d, d.k, y, s);
   mark_phase(4, s);
   return device_status();
 }

@@ -1,12 +1,12 @@
 // Weighted combine of the MoE layer (gfx950): y_t = S_t + sum_j O[pos(t, j)].
-// With a contraction-split shared down, S_t arrives as two slices S_t + S2_t.
+// With a contraction-split shared down, S_t arrives as nS slices added in order.
 //
 // O rows already carry their routing weight (the routed down GEMM scaled
 // them), S is the shared expert's output; the article's proof-of-loop
 // paragraph (seventnews, "A relay race of rented GPUs trained NanoColibri's
 // 2.7B MoE for $200", opening section) has every token use the shared expert
 // plus its routed experts.  The sum runs in fp32 in a fixed order (S, then
-// S2, j = 0..k-1) and is rounded once, so the result does not depend on
+// slice by slice, j = 0..k-1) and is rounded once, so the result does not depend on
 // scheduling.  HBM-bound: each thread moves 16 bytes of every operand.
 #include "common.h"
 #include "kernels.h"
@@ -30,7 +30,7 @@ __device__ __forceinline__ void add_vec(float (&acc)[16 / sizeof(T)], const u32x
 }
 
 template <typename T>
-__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, const T* __restrict__ S2,
+__global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, int nS, long long s_stride,
                                                       const T* __restrict__ O,
                                                       const int32_t* __restrict__ pos, int T_, int d, int k,
                                                       T* __restrict__ y) {
@@ -43,8 +43,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, c
   float acc[V];
 #pragma unroll
   for (int i = 0; i < V; ++i) acc[i] = 0.f;
-  add_vec<T>(acc, ld16(S + (long long)t * d + c));
-  if (S2) add_vec<T>(acc, ld16(S2 + (long long)t * d + c));
+  for (int z = 0; z < nS; ++z) add_vec<T>(acc, ld16(S + z * s_stride + (long long)t * d + c));
   for (int j = 0; j < k; ++j) {
     const long long slot = pos[(long long)t * k + j];
     add_vec<T>(acc, ld16(O + slot * d + c));
@@ -62,17 +61,18 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, c
 
 }  // namespace
 
-void launch_combine(int act, const void* S, const void* S2, const void* O, const int32_t* pos, int T, int d, int k,
-                    void* y, hipStream_t s) {
+void launch_combine(int act, const void* S, int nS, const void* O, const int32_t* pos, int T, int d, int k, void* y,
+                    hipStream_t s) {
+  const long long s_stride = (long long)T * d;
   const int es = act == 1 ? 2 : 4;
   const long long n = (long long)T * (d * es / 16);
   if (n == 0) return;
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (act == 1)
-    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)S, (const bf16_t*)S2, (const bf16_t*)O,
+    hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)S, nS, s_stride, (const bf16_t*)O,
                        pos, T, d, k, (bf16_t*)y);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)S, (const float*)S2, (const float*)O, pos,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)S, nS, s_stride, (const float*)O, pos,
                        T, d, k, (float*)y);
 }
 

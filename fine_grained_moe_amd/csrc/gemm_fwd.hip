@@ -118,8 +118,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   const bool active = wm * WM < rows;
 
   // Row scales of the gate-scaled epilogue: thread r < 256 fetches perm of
-  // row r now, the gate after the main loop; the scales reach the waves
-  // through LDS.
+  // row r now and the gate two K steps before the end (after the wait that
+  // drains every stage load, so no stage wait counts it); the scales reach
+  // the waves through LDS.
   const bool scaled = p.gate != nullptr && p.epi == EPI_ROWSCALE;
   int my_perm = 0;
   if (scaled && tid < BM) my_perm = p.perm[row_base + min(tid, rows - 1)];
@@ -255,11 +256,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
   }
+  float my_gate = 0.f;
   for (; s + 1 < nk; ++s) {
     if (nk - s - 2 >= 2) wait_vmcnt<2 * kLoads>();
     else if (nk - s - 2 == 1) wait_vmcnt<kLoads>();
     else wait_vmcnt<0>();
     block_barrier();
+    if (scaled && s == nk - 2 && tid < BM) my_gate = p.gate[my_perm];
     compute(s, fa0, fa1, std::true_type{}, std::false_type{});
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
@@ -271,7 +274,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   float* const row_scale = reinterpret_cast<float*>(lds);
   if (scaled) {
     __syncthreads();
-    if (tid < BM) row_scale[tid] = p.gate[my_perm];
+    if (tid < BM) row_scale[tid] = nk >= 2 ? my_gate : p.gate[my_perm];
     __syncthreads();
   }
   if (!active) return;

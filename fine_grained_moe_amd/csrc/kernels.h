@@ -177,9 +177,10 @@ void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm
 void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, const float* dl, const int32_t* idx,
                    const int32_t* pos, int T, int d, int k, void* dx, hipStream_t s);
 
-// y[t] = S[t] (+ S2[t]) + sum_j O[pos[t*k + j]] in that order, rounded once.
-// S2 (may be null) is the second contraction slice of the shared down.
-void launch_combine(int act, const void* S, const void* S2, const void* O, const int32_t* pos, int T, int d, int k,
-                    void* y, hipStream_t s);
+// y[t] = S_0[t] + ... + S_{nS-1}[t] + sum_j O[pos[t*k + j]] in that order,
+// rounded once.  The S_z ([T, d] each, consecutive) are the contraction
+// slices of the shared down.
+void launch_combine(int act, const void* S, int nS, const void* O, const int32_t* pos, int T, int d, int k, void* y,
+                    hipStream_t s);
 
 }  // namespace fgmoe

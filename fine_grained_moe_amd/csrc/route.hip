@@ -47,19 +47,96 @@ __device__ __forceinline__ void route_insert(uint64_t (&l)[K], uint64_t c) {
   }
 }
 
-template <typename T, int K>
+typedef __attribute__((address_space(3))) void* route_lds_ptr_t;
+
+// Partial logits of the bf16 router with coalesced operand loads: the
+// contraction runs in chunks of 256 elements (512-byte rows) through a
+// two-deep LDS ring, x rows then router rows, copied by direct global->LDS
+// loads in which every four lanes fetch 64 contiguous bytes.  (Loads straight
+// into the MFMA operand layout put 16 different rows in consecutive lanes;
+// measured on gfx950 that made the address unit the bound of the router at
+// about 5 us per block.)  The 16-byte pieces of row r are XOR-swizzled by
+// 2 (r mod 16), so the 16-row operand reads hit distinct LDS banks.  Wave w
+// multiplies k step w of every chunk (16 tokens x 64 experts x 32).
+constexpr int kRouteChunk = 256;                        // elements per row chunk
+constexpr int kRouteRowB = kRouteChunk * 2;             // 512 bytes
+constexpr int kRouteXB = 16 * kRouteRowB;               // 8 KiB of x per chunk
+constexpr int kRouteStageB = kRouteXB + 64 * kRouteRowB;   // + 32 KiB of router rows
+__device__ __forceinline__ int route_swz(int row, int piece) { return piece ^ ((row & 15) << 1); }
+
+__device__ __forceinline__ void route_logits_staged(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
+                                                    int T_, int d, int E, int tok0, char* ring, f32x4_t (&acc)[4]) {
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  // wave w copies x rows 2w, 2w+1 and router rows 8w .. 8w+7 of each chunk;
+  // one instruction moves two 512-byte rows (lane i: row i / 32, piece i % 32)
+  const int half = lane >> 5, ph = lane & 31;
+  const char* src[5];
+  int dst[5];
+  {
+    const int r = 2 * wave + half;
+    const int t = min(tok0 + r, T_ - 1);              // rows past T re-read the last token; never used
+    src[0] = reinterpret_cast<const char*>(x + (long long)t * d) + route_swz(r, ph) * 16;
+    dst[0] = 2 * wave * kRouteRowB;
+  }
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 8 * wave + 2 * j + half;            // router row (expert)
+    src[1 + j] = reinterpret_cast<const char*>(wr + (long long)min(r, E - 1) * d) + route_swz(r, ph) * 16;
+    dst[1 + j] = kRouteXB + (8 * wave + 2 * j) * kRouteRowB;
+  }
+  auto issue = [&](int c) {
+    char* st = ring + (c & 1) * kRouteStageB;
+#pragma unroll
+    for (int j = 0; j < 5; ++j)
+      __builtin_amdgcn_global_load_lds(src[j] + c * kRouteRowB, (route_lds_ptr_t)(st + dst[j]), 16, 0, 0);
+  };
+  const int nch = d / kRouteChunk;
+  const int r = lane & 15, g = lane >> 4;
+  issue(0);
+  if (nch > 1) issue(1);
+  for (int c = 0; c < nch; ++c) {
+    if (c + 1 < nch) __builtin_amdgcn_s_waitcnt((5 & 0xF) | (0x7 << 4) | (0xF << 8));   // vmcnt(5)
+    else __builtin_amdgcn_s_waitcnt((0x7 << 4) | (0xF << 8));                            // vmcnt(0)
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* st = ring + (c & 1) * kRouteStageB;
+    const int piece = 4 * wave + g;                    // k step `wave`, lane group g
+    const u32x4_t a = ld16(st + r * kRouteRowB + route_swz(r, piece) * 16);
+#pragma unroll
+    for (int et = 0; et < 4; ++et) {
+      const int er = et * 16 + r;
+      const u32x4_t b = ld16(st + kRouteXB + er * kRouteRowB + route_swz(er, piece) * 16);
+      acc[et] = Mma<bf16_t>::run1(a, b, acc[et]);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();                      // every wave is done with buffer c % 2
+    asm volatile("" ::: "memory");
+    if (c + 2 < nch) issue(c + 2);
+  }
+}
+
+// STAGED: the bf16 path above (d a multiple of 256); otherwise operands are
+// loaded straight into registers.
+template <typename T, int K, bool STAGED>
 __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x, const T* __restrict__ wr,
                                                          const float* __restrict__ bias, int T_, int d, int E,
                                                          int32_t* __restrict__ idx,
                                                          float* __restrict__ gate,
                                                          int32_t* __restrict__ block_counts,
                                                          int32_t* __restrict__ rank) {
-  __shared__ float part[kRouteWaves][16][65];
-  __shared__ float lgs[16][65];
-  __shared__ int sel[16 * K];
+  // One LDS object: the staging ring, whose start later holds the partial
+  // logit tiles, then the reduced logits, selections, histogram and bias.
+  constexpr int kRingB = STAGED ? 2 * kRouteStageB : 0;
+  constexpr int kPartB = kRouteWaves * 16 * 65 * 4;
+  constexpr int kHeadB = kRingB > kPartB ? kRingB : kPartB;
+  __shared__ __attribute__((aligned(16))) char lds[kHeadB + 16 * 65 * 4 + 16 * K * 4 + 64 * 4 + 64 * 4];
+  float (*part)[16][65] = reinterpret_cast<float (*)[16][65]>(lds);
+  float (*lgs)[65] = reinterpret_cast<float (*)[65]>(lds + kHeadB);
+  int* sel = reinterpret_cast<int*>(lds + kHeadB + 16 * 65 * 4);
+  int* hist = sel + 16 * K;
+  float* bias_s = reinterpret_cast<float*>(hist + 64);
   constexpr int k = K;
-  __shared__ int hist[64];
-  __shared__ float bias_s[64];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   if (tid < 64) {
@@ -67,8 +144,14 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
     bias_s[tid] = tid < E ? bias[tid] : 0.f;
   }
 
-  // ---- partial logits of this wave's chunks
+  // ---- partial logits of this wave
   const int tok0 = blockIdx.x * kRouteTokensPerBlock;
+  f32x4_t acc[4];
+#pragma unroll
+  for (int et = 0; et < 4; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  if constexpr (STAGED) {
+    route_logits_staged(x, wr, T_, d, E, tok0, lds, acc);
+  } else {
   const int t = min(tok0 + r, T_ - 1);          // rows past T re-read the last token; never used
   const char* xrow = reinterpret_cast<const char*>(x + (long long)t * d) + g * 32;
   const char* wrow[4];
@@ -76,9 +159,6 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
   for (int et = 0; et < 4; ++et)                 // rows past E re-read the last expert; never selected
     wrow[et] = reinterpret_cast<const char*>(wr + (long long)min(et * 16 + r, E - 1) * d) + g * 32;
   const int nch = (int)((long long)d * sizeof(T) / 128);
-  f32x4_t acc[4];
-#pragma unroll
-  for (int et = 0; et < 4; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   for (int c0 = wave; c0 < nch; c0 += 2 * kRouteWaves) {
     // up to two chunks (c0 and c0 + 8) in flight; a missing second chunk
     // re-reads the first and is multiplied as zeros
@@ -101,6 +181,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
     for (int h = 0; h < 2; ++h)
 #pragma unroll
       for (int et = 0; et < 4; ++et) acc[et] = Mma<T>::run(a[h], b[h][et], acc[et]);
+  }
   }
 #pragma unroll
   for (int et = 0; et < 4; ++et)
@@ -293,8 +374,15 @@ __global__ void bias_update_kernel(int E, long long total, const int32_t* __rest
 template <typename A, int K>
 void launch_topk_k(const void* x, const void* w_router, const float* bias, int T, int d, int E, int32_t* idx,
                    float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
-  hipLaunchKernelGGL((route_topk_kernel<A, K>), dim3(route_blocks(T)), dim3(512), 0, s, (const A*)x,
-                     (const A*)w_router, bias, T, d, E, idx, gate, block_counts, rank);
+  if constexpr (sizeof(A) == 2) {
+    if (d % kRouteChunk == 0) {
+      hipLaunchKernelGGL((route_topk_kernel<A, K, true>), dim3(route_blocks(T)), dim3(512), 0, s, (const A*)x,
+                         (const A*)w_router, bias, T, d, E, idx, gate, block_counts, rank);
+      return;
+    }
+  }
+  hipLaunchKernelGGL((route_topk_kernel<A, K, false>), dim3(route_blocks(T)), dim3(512), 0, s, (const A*)x,
+                       (const A*)w_router, bias, T, d, E, idx, gate, block_counts, rank);
 }
 template <typename A>
 void launch_topk_t(const void* x, const void* w_router, const float* bias, int T, int d, int E, int k, int32_t* idx,
