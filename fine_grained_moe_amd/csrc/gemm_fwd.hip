@@ -208,8 +208,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   };
   // stage s from (fa, fb); prefetch: read stage s + 1 into (fn, fb); loads:
   // issue stage s + kStages - 1
-  auto compute = [&](int s, u32x4_t (&fa)[4], u32x4_t (&fn)[4], auto prefetch, auto with_loads) {
-    if (!active) {
+  // ACT: this wave's row band holds rows (compile-time, so the loop below is
+  // instantiated once per case and its LDS waits stay exact).
+  auto compute = [&](int s, u32x4_t (&fa)[4], u32x4_t (&fn)[4], auto act, auto prefetch, auto with_loads) {
+    if constexpr (!decltype(act)::value) {
       if constexpr (decltype(with_loads)::value) issue(s + kStages - 1);
       return;
     }
@@ -242,32 +244,39 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   else if (nk == 2) wait_vmcnt<kLoads>();
   else wait_vmcnt<0>();
   block_barrier();
-  if (active) {
-    read_a(0, fa0);
-    read_b(0);
-  }
-  // Stages issued before iteration s: min(nk, s + 4); in flight after stage
-  // s + 1: that minus s + 2.
-  int s = 0;
-  for (; s + kStages - 1 < nk; ++s) {
-    wait_vmcnt<2 * kLoads>();
-    block_barrier();
-    compute(s, fa0, fa1, std::true_type{}, std::true_type{});
-#pragma unroll
-    for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
-  }
   float my_gate = 0.f;
-  for (; s + 1 < nk; ++s) {
-    if (nk - s - 2 >= 2) wait_vmcnt<2 * kLoads>();
-    else if (nk - s - 2 == 1) wait_vmcnt<kLoads>();
-    else wait_vmcnt<0>();
-    block_barrier();
-    if (scaled && s == nk - 2 && tid < BM) my_gate = p.gate[my_perm];
-    compute(s, fa0, fa1, std::true_type{}, std::false_type{});
+  auto run = [&](auto act) {
+    using A = decltype(act);
+    if constexpr (A::value) {
+      read_a(0, fa0);
+      read_b(0);
+    }
+    // Stages issued before iteration s: min(nk, s + 4); in flight after stage
+    // s + 1: that minus s + 2.  Two K steps per trip, so the two A sets swap
+    // roles without a copy (a copy would wait for every LDS read in flight
+    // before each barrier).
+    int s = 0;
+    for (; s + kStages - 1 < nk; ++s) {
+      wait_vmcnt<2 * kLoads>();
+      block_barrier();
+      compute(s, fa0, fa1, A{}, std::true_type{}, std::true_type{});
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
-  }
-  compute(s, fa0, fa1, std::false_type{}, std::false_type{});
+      for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
+    }
+    for (; s + 1 < nk; ++s) {
+      if (nk - s - 2 >= 2) wait_vmcnt<2 * kLoads>();
+      else if (nk - s - 2 == 1) wait_vmcnt<kLoads>();
+      else wait_vmcnt<0>();
+      block_barrier();
+      if (scaled && s == nk - 2 && tid < BM) my_gate = p.gate[my_perm];
+      compute(s, fa0, fa1, A{}, std::true_type{}, std::false_type{});
+#pragma unroll
+      for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
+    }
+    compute(s, fa0, fa1, A{}, std::false_type{}, std::false_type{});
+  };
+  if (active) run(std::true_type{});
+  else run(std::false_type{});
 
   // Row scales, staged in ring buffer 0 once every wave is past its last
   // read of the ring.
