@@ -572,7 +572,12 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
                   dl, s);
 
   const long long slots = (long long)d.T * d.k;
-  const int max_tiles = (int)max_group_tiles(slots, d.E);
+  // bf16: the input-gradient launches run on gemm_fwd.hip's 256 x 256 tiles
+  // (grouped jobs over the 256-row tile table), fp32 on gemm.hip.
+  const bool big = act == MOE_BF16;
+  const int tm = big ? kTileMFwd : kTileM;
+  const int max_tiles = (int)max_group_tiles(slots, d.E, tm);
+  auto gemm_in = big ? launch_gemm_fwd256 : launch_gemm;
   // 4. dH (gate-scaled) -> SwiGLU backward -> dAU (routed) and dAUs (shared)
   GemmJob hr{};
   hr.epi = EPI_SWIGLU_BWD;
@@ -586,9 +591,9 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hr.K = d.d;
   hr.N = d.F;
   hr.grouped = 1;
-  hr.tile_e = at<int32_t>(ws, L.tile_e);
-  hr.tile_m0 = at<int32_t>(ws, L.tile_m0);
-  hr.tile_count = at<int32_t>(ws, L.tile_count);
+  hr.tile_e = at<int32_t>(ws, big ? L.tile2_e : L.tile_e);
+  hr.tile_m0 = at<int32_t>(ws, big ? L.tile2_m0 : L.tile_m0);
+  hr.tile_count = at<int32_t>(ws, big ? L.tile2_count : L.tile_count);
   hr.offsets = routing->offsets;
   hr.counts = routing->counts;
   hr.max_items = max_tiles;
@@ -608,7 +613,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hs.K = d.d;
   hs.N = d.Fs;
   hs.M = d.T;
-  hs.max_items = (d.T + kTileM - 1) / kTileM;
+  hs.max_items = (d.T + tm - 1) / tm;
   hs.C = dAUs;
   hs.ldc = 2LL * Fs;
   hs.aux = at<char>(ws, L.AUs);
@@ -618,7 +623,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   g1.njobs = 2;
   g1.job[0] = hr;
   g1.job[1] = hs;
-  launch_gemm(g1, s);
+  gemm_in(g1, s);
 
   // 5. input gradients: dXp = dAU W_gu (per expert), dXs = dAUs W_sgu
   GemmJob xr = hr;
@@ -652,7 +657,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   g2.njobs = 2;
   g2.job[0] = xr;
   g2.job[1] = xs;
-  launch_gemm(g2, s);
+  gemm_in(g2, s);
 
   // 6. transposed activations over padded slot columns (routed) and token columns (shared)
   transpose(dAU, 2LL * F, 0, dAUT, P, 0, 2 * d.F, P, 1, 0, pcol, nullptr, 1, nullptr);

@@ -1,11 +1,15 @@
-// Forward expert GEMMs of the MoE layer in bf16 on gfx950 MFMA: 256 x 256
-// output tiles, one workgroup of 8 waves per CU.
+// Expert GEMMs of the MoE layer in bf16 on gfx950 MFMA: 256 x 256 output
+// tiles, one workgroup of 8 waves per CU.
 //
 // The two forward launches of a bf16 layer run here:
 //   gate/up: routed (grouped over experts, A rows gathered from x through the
 //            dispatch order) + shared (dense), SwiGLU epilogue -> H, Hs
 //   down:    routed (grouped, rows scaled by their routing weight) + shared
-//            (dense, plain store) -> O, S
+//            (dense, two contraction slices, plain store) -> O, S
+// and the two input-gradient launches of the backward:
+//   dH:      routed (A rows of dy gathered, rows scaled by their gate) +
+//            shared, SwiGLU-backward epilogue -> dA|dU, dAs|dUs
+//   dX:      routed + shared, plain store -> dXp, dXs
 // The experts are the SwiGLU FFNs of widths 512 (routed) and 2048 (shared) of
 // the seventnews article "A relay race of rented GPUs trained NanoColibri's
 // 2.7B MoE for $200" (opening section, architecture paragraph).
@@ -121,7 +125,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   // row r now and the gate two K steps before the end (after the wait that
   // drains every stage load, so no stage wait counts it); the scales reach
   // the waves through LDS.
-  const bool scaled = p.gate != nullptr && p.epi == EPI_ROWSCALE;
+  const bool scaled = p.gate != nullptr && (p.epi == EPI_ROWSCALE || p.epi == EPI_SWIGLU_BWD);
   int my_perm = 0;
   if (scaled && tid < BM) my_perm = p.perm[row_base + min(tid, rows - 1)];
 
@@ -325,6 +329,23 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
         }
         store_vec<T, NI>(C + row * p.ldc + n, v);
         if (aux) store_vec<T, NI>(aux + row * p.ldaux + n, raw);
+      } else if (p.epi == EPI_SWIGLU_BWD) {
+        // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u)
+        const float sc = p.gate ? row_scale[lr] : 1.f;
+        const T* au = reinterpret_cast<const T*>(p.aux) + row * p.ldaux;
+        float a[NI], u[NI], da[NI], du[NI];
+        load_vec<T, NI>(au + n, a);
+        load_vec<T, NI>(au + p.N + n, u);
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const float dh = acc[mi][ni][i] * sc;
+          const float sg = sigmoidf_(a[ni]);
+          const float si = a[ni] * sg;
+          da[ni] = dh * u[ni] * (sg * (1.f + a[ni] * (1.f - sg)));
+          du[ni] = dh * si;
+        }
+        store_vec<T, NI>(C + row * p.ldc + n, da);
+        store_vec<T, NI>(C + row * p.ldc + p.N + n, du);
       } else {  // EPI_STORE
         float v[NI];
 #pragma unroll
@@ -343,9 +364,9 @@ int job_chunks(const GemmJob& j) {
 
 }  // namespace
 
-// bf16 forward jobs only: epilogues SwiGLU, row scale or plain store, no
-// per-expert contraction ranges, K / ksplit a multiple of 32 (checked by the
-// caller); a split job's slices each write their own output.
+// bf16 jobs only: epilogues SwiGLU, row scale, SwiGLU backward or plain
+// store, no per-expert contraction ranges, K / ksplit a multiple of 32
+// (checked by the caller); a split job's slices each write their own output.
 void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
   GemmArgs a = in;
   long long total = 0;

@@ -102,8 +102,9 @@ struct GemmArgs {
   GemmJob job[2];
 };
 void launch_gemm(const GemmArgs& a, hipStream_t s);
-// bf16 forward jobs (SwiGLU, row-scale or store epilogue, K % 32 == 0) on
-// 256 x 256 tiles; grouped jobs index the kTileMFwd tile table.
+// bf16 jobs with the SwiGLU, row-scale, SwiGLU-backward or store epilogue
+// (K % 32 == 0) on 256 x 256 tiles; grouped jobs index the kTileMFwd tile
+// table.
 void launch_gemm_fwd256(const GemmArgs& a, hipStream_t s);
 
 // Top-1 serving with int4 routed experts, T <= 64 tokens (decode.hip), built
