@@ -186,6 +186,23 @@ void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void
                         r->counts, r->offsets, tiles, tiles_fwd, r->perm, r->pos, s);
 }
 
+// Column groups of the XCD grid of a dense job with M x K and N x K operands
+// (launch_gemm_fwd256): the gc in {1, 2, 4, 8} with the fewest L2 misses,
+// (M * gc + N * 8 / gc) rows, at most the job's N tiles of 256.
+int dense_xcd_cols(long long M, long long N) {
+  int best = 1;
+  long long best_rows = M + 8 * N;
+  for (int gc = 2; gc <= 8; gc *= 2) {
+    if ((N + 255) / 256 < gc) break;
+    const long long rows = M * gc + N * (8 / gc);
+    if (rows < best_rows) {
+      best = gc;
+      best_rows = rows;
+    }
+  }
+  return best;
+}
+
 moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
 
 // Phase-boundary events registered by moe_set_phase_events (instrumentation).
@@ -391,6 +408,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   sg.max_items = (d.T + tm - 1) / tm;
   sg.C = Hs;
   sg.ldc = Fs;
+  sg.xcd_cols = dense_xcd_cols(d.T, 2LL * Fs);
   sg.aux = training ? at<char>(ws, L.AUs) : nullptr;
   sg.ldaux = 2LL * Fs;
 
@@ -439,6 +457,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   const int nsd = shared_down_slices(d);
   sd.ksplit = nsd;
   sd.c_kstride = (long long)d.T * D;
+  sd.xcd_cols = dense_xcd_cols(d.T, D);
 
   GemmArgs da{};
   da.act = d.act;
@@ -616,6 +635,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hs.max_items = (d.T + tm - 1) / tm;
   hs.C = dAUs;
   hs.ldc = 2LL * Fs;
+  hs.xcd_cols = dense_xcd_cols(d.T, Fs);
   hs.aux = at<char>(ws, L.AUs);
   hs.ldaux = 2LL * Fs;
   GemmArgs g1{};
@@ -652,6 +672,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   xs.C = dXs;
   xs.ldc = D;
   xs.aux = nullptr;
+  xs.xcd_cols = dense_xcd_cols(d.T, D);
   GemmArgs g2{};
   g2.act = act;
   g2.njobs = 2;

@@ -34,12 +34,16 @@
 // rows are XOR-swizzled (swz) and B rows permuted so that each lane's output
 // columns are adjacent, as in gemm.hip.
 //
-// Scheduling: as in gemm.hip.  Items are 256-row tiles (dense: row blocks,
-// times the contraction slices of a split dense job; grouped: the 256-row
-// tile table the router wrote).  Block b runs on XCD
-// b % 8; XCD x gets the contiguous item range [x*q, (x+1)*q); grouped jobs
-// run all N tiles of an item back to back, dense jobs all of the XCD's row
-// blocks for one N tile before the next.
+// Scheduling.  Items are 256-row tiles (dense: row blocks, times the
+// contraction slices of a split dense job; grouped: the 256-row tile table
+// the router wrote).  Block b runs on XCD b % 8.  Grouped jobs: XCD x gets
+// the contiguous item range [x*q, (x+1)*q) and runs all N tiles of an item
+// back to back (an expert's weights are read once).  Dense jobs: the XCDs
+// split the (row block, N tile) grid into an (8 / gc) x gc grid of ranges,
+// gc chosen by the caller so that the L2 misses of the two operands,
+// (M rows x gc + N rows x 8 / gc) x K, are smallest; measured with
+// FETCH_SIZE, gc = 1 on the 4096-token shared gate/up fetched the 8 MiB
+// weight matrix once per XCD.
 #include <type_traits>
 
 #include "gemm_tile.h"
@@ -70,6 +74,10 @@ __device__ __forceinline__ int item_count(const GemmJob& j) {
 inline long long max_item_count(const GemmJob& j) {
   return j.grouped ? j.max_items : (long long)(j.M + BM - 1) / BM * k_slices(j);
 }
+// XCD grid of a dense job: gc column groups (N-tile ranges) x 8 / gc row groups
+__device__ __host__ __forceinline__ int xcd_cols(const GemmJob& j) {
+  return j.xcd_cols == 2 || j.xcd_cols == 4 || j.xcd_cols == 8 ? j.xcd_cols : 1;
+}
 
 template <bool SWIGLU>
 __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
@@ -84,22 +92,28 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   select_job(args, blockIdx.x, jid, bid);
   const GemmJob& p = args.job[jid];
 
-  // ---- work item and N tile
+  // ---- work item and N tile.  Grouped: XCD x takes items [x*q, (x+1)*q),
+  // each with all its N tiles back to back.  Dense: XCD x takes row-item
+  // range xr and N-tile range xc of an (8 / gc) x gc grid, N tiles outer.
   const int count = item_count(p);
-  const int q = (count + 7) >> 3;
   const int nbn = n_tiles(p);
   const int xcd = bid & 7, local = bid >> 3;
-  int pi, nt;
+  int item, nt;
   if (p.grouped) {
-    pi = local / nbn;
+    const int q = (count + 7) >> 3;
+    const int pi = local / nbn;
     nt = local - pi * nbn;
+    if (pi >= q) return;
+    item = xcd * q + pi;
   } else {
-    nt = local / (q > 0 ? q : 1);
-    pi = local - nt * q;
+    const int gc = xcd_cols(p), gr = 8 / gc;
+    const int qr = (count + gr - 1) / gr, qc = (nbn + gc - 1) / gc;
+    const int ntl = local / (qr > 0 ? qr : 1), pi = local - ntl * qr;
+    if (ntl >= qc) return;
+    nt = (xcd % gc) * qc + ntl;
+    item = (xcd / gc) * qr + pi;
     if (nt >= nbn) return;
   }
-  if (pi >= q) return;
-  const int item = xcd * q + pi;
   if (item >= count) return;
   int e = 0, rows, row_base, kz = 0;
   if (p.grouped) {
@@ -356,10 +370,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   }
 }
 
+// chunks of 8 blocks (one per XCD) a job needs: the blocks one XCD runs
 int job_chunks(const GemmJob& j) {
   const int nbn = n_tiles(j);
-  const long long groups = (max_item_count(j) + 7) / 8;
-  return (int)(groups * nbn);
+  if (j.grouped) return (int)((max_item_count(j) + 7) / 8 * nbn);
+  const int gc = xcd_cols(j), gr = 8 / gc;
+  return (int)((max_item_count(j) + gr - 1) / gr * ((nbn + gc - 1) / gc));
 }
 
 }  // namespace

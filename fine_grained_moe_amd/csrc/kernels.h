@@ -84,6 +84,9 @@ struct GemmJob {
   // equal slices (K / ksplit a multiple of 32); slice z writes C + z * c_kstride.
   int ksplit;
   long long c_kstride;
+  // dense jobs of launch_gemm_fwd256: the 8 XCDs take a (8 / xcd_cols) x
+  // xcd_cols grid of (row-block, N-tile) ranges (1, 2, 4 or 8; 0 means 1)
+  int xcd_cols;
   // outputs
   void* C;
   long long ldc;
