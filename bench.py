@@ -64,6 +64,41 @@ def algorithmic_work(T, d, E, F, Fs, k, es=2):
     return w
 
 
+# Hardware byte counters of the dominant kernel (rocprofv3 --pmc FETCH_SIZE,
+# then WRITE_SIZE, on this benchmark), kept under profiles/ with the hash of
+# the sources they were taken on; reported only while those sources are
+# unchanged.
+TRAFFIC_FILE = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                            "layer_t4096_gate_up_traffic.json")
+
+
+def kernel_sources_hash(files):
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(root, f), "rb") as fh:
+            h.update(f.encode() + b"\0" + fh.read() + b"\0")
+    return h.hexdigest()
+
+
+def measured_traffic():
+    """HBM bytes per launch of the gate/up GEMM from the committed counter
+    summary: FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for a plain 1 GiB device copy; None if the
+    summary is missing or the kernel's sources changed since."""
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            t = json.load(fh)
+        if kernel_sources_hash(t["sources"]) != t["sources_sha256"]:
+            return None
+        fetch = t["fetch_kib"] * 1024 * t["copy_bytes"] / (t["copy_fetch_kib"] * 1024)
+        write = t["write_kib"] * 1024 * t["copy_bytes"] / (t["copy_write_kib"] * 1024)
+        return fetch + write
+    except (OSError, KeyError, ValueError, ZeroDivisionError):
+        return None
+
+
 HIP_EVENT_DISABLE_SYSTEM_FENCE = 0x20000000
 
 
@@ -223,6 +258,46 @@ def cpu_baseline(inp, seconds: float):
                        f"{el:.1f} s wall")
 
 
+GATE_UP_KERNEL = "gemm256_kernel<true>"
+TRAFFIC_SOURCES = ["fine_grained_moe_amd/csrc/gemm_fwd.hip", "fine_grained_moe_amd/csrc/gemm_tile.h",
+                   "fine_grained_moe_amd/csrc/common.h", "fine_grained_moe_amd/csrc/kernels.h",
+                   "fine_grained_moe_amd/csrc/api.hip"]
+
+
+def traffic_summary(fetch_csv, write_csv):
+    """Reduce two rocprofv3 --pmc counter files of a `--copy-calibration` run
+    (FETCH_SIZE, then WRITE_SIZE) to the figures bench.py reports: the mean
+    per-dispatch KiB of the gate/up GEMM, and the counter readings of the
+    1 GiB device copy that scale them to bytes."""
+    import csv
+
+    def read(path, counter):
+        gemm, copy = [], []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r["Counter_Name"] != counter:
+                    continue
+                v = float(r["Counter_Value"])
+                if GATE_UP_KERNEL in r["Kernel_Name"]:
+                    gemm.append(v)
+                elif "copyBuffer" in r["Kernel_Name"] and v >= 256 * 1024:   # the 1 GiB copies
+                    copy.append(v)
+        if not gemm or not copy:
+            raise SystemExit(f"{path}: no {counter} readings of the gate/up GEMM or of the 1 GiB copy")
+        return sum(gemm) / len(gemm), len(gemm), max(copy)
+
+    f_kib, nf, f_copy = read(fetch_csv, "FETCH_SIZE")
+    w_kib, nw, w_copy = read(write_csv, "WRITE_SIZE")
+    out = dict(kernel=GATE_UP_KERNEL, workload="layer_t4096", fetch_kib=round(f_kib, 1), write_kib=round(w_kib, 1),
+               dispatches=[nf, nw], copy_bytes=1 << 30, copy_fetch_kib=round(f_copy, 1),
+               copy_write_kib=round(w_copy, 1), sources=TRAFFIC_SOURCES,
+               sources_sha256=kernel_sources_hash(TRAFFIC_SOURCES))
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(out, fh, indent=1)
+        fh.write("\n")
+    print(json.dumps(out))
+
+
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -238,7 +313,12 @@ def main() -> int:
                     help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
+    ap.add_argument("--traffic-summary", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the gate/up GEMM's counter summary from two rocprofv3 --pmc runs and exit")
     args = ap.parse_args()
+    if args.traffic_summary:
+        traffic_summary(*args.traffic_summary)
+        return 0
 
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU only: this build has no multi-GPU path "
@@ -324,7 +404,10 @@ def main() -> int:
     else:
         roof = dict(bound="hbm", achieved=wd["bytes"] / t / 1e9, peak=PEAK_HBM_BPS / 1e9, unit="GB/s")
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = None
+    # hardware HBM bytes per launch of the dominant kernel (the gate/up GEMM)
+    traffic = measured_traffic() if dom == "gate_up" else None
+    roof["traffic"] = None if traffic is None else int(round(traffic))   # bytes per launch
+    roof["algorithmic_bytes"] = wd["bytes"]
     roof["kernel"] = KERNEL_OF_PHASE[dom]
     roof["avg_us"] = phases[dom]
 
