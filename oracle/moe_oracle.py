@@ -21,7 +21,10 @@ Citations below name its sections:
     are int4;
   * "Relay training" section, top-2 paragraph: at top_k=1 the routing weight is
     a constant and the router gets no gradient; two winners competing restore
-    the gradient; serving runs one expert per token.
+    the gradient; serving runs one expert per token; aux-loss-free balancing
+    held, with a low dead-expert fraction;
+  * "Relay training" section, baton paragraph: the read-only training
+    dashboard shows expert balance.
 
 Readings where the article is silent (each is listed with its reason in the
 design notes of the repository):
@@ -38,7 +41,11 @@ design notes of the repository):
       bf16(absmax/7), q = clamp(rne(w/scale), -8, 7), two's-complement
       nibbles, element 2i in the low nibble;
   R11 backward: exact derivatives with the selection held fixed; the router
-      gradient flows only through the normalised gates.
+      gradient flows only through the normalised gates;
+  R19 expert balance of one batch = (dead fraction: experts with zero load
+      over E; max load over the mean load T*k/E; entropy -sum p ln p of the
+      load shares p = load/(T*k), 0 ln 0 = 0; that entropy over ln E, 1 for
+      E = 1); a batch with no assignments reads (1, 0, 0, 0).
 """
 from __future__ import annotations
 
@@ -211,6 +218,27 @@ def bias_update(bias, counts, total_assignments: int, gamma: float) -> np.ndarra
     E = c.size
     sgn = np.sign(np.int64(total_assignments) - np.int64(E) * c).astype(np.float32)
     return (b + np.float32(gamma) * sgn).astype(np.float32)
+
+
+def load_stats(counts, total_assignments: int) -> np.ndarray:
+    """Expert-balance telemetry of one batch (R19): [dead fraction, max/mean
+    load, load entropy in nats, entropy / ln E], from the per-expert loads.
+
+    The article's top-2 paragraph ("Relay training" section) reports that the
+    dead-expert fraction stayed low under aux-loss-free balancing, and its
+    baton paragraph puts expert balance on the training dashboard; it defines
+    neither figure, so these are the plain readings of R19.
+    """
+    c = np.asarray(counts, dtype=f64)
+    E = c.size
+    total = f64(total_assignments)
+    dead = f64(np.count_nonzero(c == 0)) / E
+    if total <= 0:
+        return np.array([1.0, 0.0, 0.0, 0.0], dtype=f64)
+    p = c / total
+    nz = p[p > 0]
+    ent = f64(-np.sum(nz * np.log(nz)))
+    return np.array([dead, c.max() / (total / E), ent, ent / np.log(E) if E > 1 else 1.0], dtype=f64)
 
 
 # --------------------------------------------------------------------------

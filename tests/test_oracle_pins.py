@@ -436,3 +436,39 @@ def test_generator_is_deterministic_and_exact():
     # bf16 rounding: ties to even on hand-picked bit patterns
     v = np.array([0x3F808000, 0x3F818000, 0x3F80C000, 0x3F807FFF], np.uint32).view(np.float32)
     assert (synth.round_to_bf16(v).view(np.uint32) >> 16).tolist() == [0x3F80, 0x3F82, 0x3F81, 0x3F80]
+
+
+# ---------------------------------------------------------------- expert balance (R19)
+
+def test_load_stats_closed_forms():
+    """Balance telemetry ("Relay training" section: a low dead-expert fraction,
+    expert balance on the dashboard) against closed forms: uniform loads,
+    everything on one expert, an even split over two of eight experts."""
+    # uniform: nobody dead, max = mean, entropy ln E
+    s = om.load_stats(np.full(64, 128), 64 * 128)
+    np.testing.assert_allclose(s, [0.0, 1.0, math.log(64.0), 1.0], rtol=1e-15)
+    # one-hot: E - 1 dead, max/mean = E, entropy 0
+    c = np.zeros(64, np.int64)
+    c[17] = 8192
+    np.testing.assert_allclose(om.load_stats(c, 8192), [63 / 64, 64.0, 0.0, 0.0], rtol=1e-15, atol=0)
+    # two of eight experts, 50/50: 6/8 dead, max/mean 4, entropy ln 2 (in nats: 1/3 of ln 8)
+    c = np.array([0, 50, 0, 0, 50, 0, 0, 0])
+    np.testing.assert_allclose(om.load_stats(c, 100), [0.75, 4.0, math.log(2.0), 1 / 3], rtol=1e-15)
+    # one expert: normalised entropy reads 1; an empty batch reads (1, 0, 0, 0)
+    np.testing.assert_allclose(om.load_stats(np.array([9]), 9), [0.0, 1.0, 0.0, 1.0], atol=0)
+    np.testing.assert_array_equal(om.load_stats(np.zeros(8, np.int64), 0), [1.0, 0.0, 0.0, 0.0])
+
+
+def test_load_stats_invariants():
+    """Permuting experts changes nothing; 0 <= H <= ln E; max/mean >= 1; the
+    entropy of a distribution equals ln E minus its KL divergence from uniform."""
+    rng = np.random.default_rng(7)
+    for E in (3, 8, 64):
+        c = rng.multinomial(1000, rng.dirichlet(np.ones(E)))
+        s = om.load_stats(c, 1000)
+        np.testing.assert_allclose(om.load_stats(rng.permutation(c), 1000), s, rtol=1e-14)
+        assert 0.0 <= s[2] <= math.log(E) + 1e-12 and s[1] >= 1.0
+        p = c[c > 0] / 1000.0
+        kl = float(np.sum(p * np.log(p * E)))
+        assert abs(s[2] - (math.log(E) - kl)) < 1e-12
+        assert s[0] == np.count_nonzero(c == 0) / E
