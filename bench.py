@@ -3,10 +3,13 @@
 
 A step is one pass of the whole path over one batch: moe_forward (router,
 top-2, loads and dispatch, routed gate/up + SwiGLU, routed down + gate
-scaling, shared expert, combine) followed by moe_bias_update, on the one-layer
+scaling, shared expert, combine) followed by the bias step (moe_bias_update_stats), on the one-layer
 workload T = 4096 tokens (batch 2 x seq 2048), d = 1024, 64 experts of width
 512, top-2, shared expert 2048, bf16 with fp32 accumulation.  Inputs come from
 the seeded generator and sit in HBM before timing starts.
+
+The bias step of every timed step also writes the batch's expert-balance
+figures (moe_bias_update_stats) to a device buffer, read after timing.
 
 Headline `value`: tokens/s with the expert weights rotated over several
 distinct copies (each step reads its weights from HBM, not from the 256 MB
@@ -365,18 +368,21 @@ def main() -> int:
     ev = HipEvents()
     nph = len(PHASES) + 1
 
+    # expert-balance telemetry of every step, one row each, read after timing
+    stats = torch.zeros(max(args.steps, 1), 4, dtype=torch.float32, device="cuda")
+
     def run(n_sets, steps, warmup):
         bias.copy_(bias0)
         for i in range(warmup):
             moe.moe_forward(dims, x, sets[i % n_sets], bias, y, r, ws)
-            moe.moe_bias_update(E, T * k, r["counts"], GAMMA, bias)
+            moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, stats[0])
         events = [[ev.create() for _ in range(nph)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             moe.moe_set_phase_events(events[i])
             moe.moe_forward(dims, x, sets[(warmup + i) % n_sets], bias, y, r, ws)
-            moe.moe_bias_update(E, T * k, r["counts"], GAMMA, bias)
+            moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, stats[i])
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         moe.moe_set_phase_events(None)
@@ -394,6 +400,8 @@ def main() -> int:
     value = T * args.steps / el
     log(f"cold: {value / 1e6:.2f} M tokens/s, {el / args.steps * 1e6:.1f} us/step; phases (us): "
         + ", ".join(f"{p}={v:.1f}" for p, v in phases.items()))
+    last = stats[args.steps - 1].cpu().tolist()
+    balance = dict(dead_fraction=last[0], max_over_mean=last[1], entropy=last[2], entropy_normalized=last[3])
 
     work = algorithmic_work(T, d, E, F, Fs, k)
     dom = max(phases, key=lambda p: phases[p])
@@ -425,6 +433,7 @@ def main() -> int:
         phase_report[p] = dict(us=round(us, 2), tflops=round(wp["flops"] / (us * 1e-6) / 1e12, 1),
                                gbps=round(wp["bytes"] / (us * 1e-6) / 1e9, 1), bound=wp["bound"])
     out["phases"] = phase_report
+    out["balance"] = balance      # the last timed step's loads (moe_bias_update_stats)
 
     if not args.no_warm:
         el_w, ph_w = run(1, args.steps, args.warmup)

@@ -480,7 +480,19 @@ moe_status moe_bias_update(int32_t E, int64_t total_assignments, const int32_t* 
   if (E > 64) return MOE_E_UNSUPPORTED;
   std::vector<Range> rs = {{counts, (size_t)E * 4, false}, {bias, (size_t)E * 4, true}};
   if (any_alias(rs)) return MOE_E_ALIAS;
-  launch_bias_update(E, (long long)total_assignments, counts, gamma, bias, reinterpret_cast<hipStream_t>(stream));
+  launch_bias_update(E, (long long)total_assignments, counts, gamma, bias, nullptr,
+                     reinterpret_cast<hipStream_t>(stream));
+  return device_status();
+}
+
+moe_status moe_bias_update_stats(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma,
+                                 float* bias, float* stats, void* stream) {
+  if (E < 1 || total_assignments < 0 || !counts || !bias || !stats) return MOE_E_ARG;
+  if (E > 64) return MOE_E_UNSUPPORTED;
+  std::vector<Range> rs = {{counts, (size_t)E * 4, false}, {bias, (size_t)E * 4, true}, {stats, 4 * 4, true}};
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  launch_bias_update(E, (long long)total_assignments, counts, gamma, bias, stats,
+                     reinterpret_cast<hipStream_t>(stream));
   return device_status();
 }
 

@@ -36,7 +36,9 @@ void launch_route_topk(int act, const void* x, const void* w_router, const float
 void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
                            int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
                            int32_t* perm, int32_t* pos, hipStream_t s);
-void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s);
+// stats (may be null): [4] expert-balance figures of the batch
+void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, float* stats,
+                        hipStream_t s);
 
 enum Epilogue {
   EPI_SWIGLU = 0,       // C[row, f] = silu(acc_gate) * acc_up; aux = (gate | up) pre-activations

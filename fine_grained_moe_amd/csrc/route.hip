@@ -371,6 +371,50 @@ __global__ void bias_update_kernel(int E, long long total, const int32_t* __rest
   }
 }
 
+// ---------------------------------------------------------------------------
+// The bias step plus the batch's expert-balance telemetry ("Relay training"
+// section: a low dead-expert fraction, expert balance on the dashboard):
+// stats = [experts with zero load / E, max load * E / total, load entropy
+// -sum p ln p (p = load / total, 0 ln 0 = 0), entropy / ln E (1 for E = 1)];
+// an empty batch reads (1, 0, 0, 0).  One wave, lane e for expert e; the sums
+// and the maximum are butterfly reductions in a fixed order.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void bias_update_stats_kernel(int E, long long total,
+                                                               const int32_t* __restrict__ counts, float gamma,
+                                                               float* __restrict__ bias, float* __restrict__ stats) {
+  const int e = threadIdx.x;
+  const int c = e < E ? counts[e] : 0;
+  if (e < E) {
+    const long long diff = total - (long long)E * (long long)c;
+    const float sg = (float)((diff > 0) - (diff < 0));
+    bias[e] = __fadd_rn(bias[e], gamma * sg);
+  }
+  int dead = (e < E && c == 0) ? 1 : 0;
+  int mx = c;
+  float h = 0.f;
+  if (c > 0 && total > 0) {
+    const float pr = (float)c / (float)total;
+    h = -pr * logf(pr);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    dead += __shfl_xor(dead, off);
+    mx = max(mx, __shfl_xor(mx, off));
+    h += __shfl_xor(h, off);
+  }
+  if (e == 0) {
+    if (total <= 0) {
+      stats[0] = 1.f;
+      stats[1] = stats[2] = stats[3] = 0.f;
+    } else {
+      stats[0] = (float)dead / (float)E;
+      stats[1] = (float)((double)mx * E / (double)total);
+      stats[2] = h;
+      stats[3] = E > 1 ? h / logf((float)E) : 1.f;
+    }
+  }
+}
+
 template <typename A, int K>
 void launch_topk_k(const void* x, const void* w_router, const float* bias, int T, int d, int E, int32_t* idx,
                    float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
@@ -415,8 +459,12 @@ void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, cons
                      counts, offsets, tiles, tiles_fwd, perm, pos);
 }
 
-void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, hipStream_t s) {
-  hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(64), 0, s, E, total, counts, gamma, bias);
+void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, float* stats,
+                        hipStream_t s) {
+  if (stats)
+    hipLaunchKernelGGL(bias_update_stats_kernel, dim3(1), dim3(64), 0, s, E, total, counts, gamma, bias, stats);
+  else
+    hipLaunchKernelGGL(bias_update_kernel, dim3(1), dim3(64), 0, s, E, total, counts, gamma, bias);
 }
 
 }  // namespace fgmoe

@@ -67,6 +67,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_forward.restype = ctypes.c_int
     lib.moe_bias_update.argtypes = [I32, I64, P, ctypes.c_float, P, P]
     lib.moe_bias_update.restype = ctypes.c_int
+    lib.moe_bias_update_stats.argtypes = [I32, I64, P, ctypes.c_float, P, P, P]
+    lib.moe_bias_update_stats.restype = ctypes.c_int
     lib.moe_backward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P, P,
                                  ctypes.POINTER(MoeGrads), P, SZ, P]
     lib.moe_backward.restype = ctypes.c_int
@@ -138,6 +140,12 @@ def moe_forward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y, rou
 def moe_bias_update(E: int, total_assignments: int, counts, gamma: float, bias, stream=None) -> None:
     _check(LIB.moe_bias_update(int(E), int(total_assignments), _ptr(counts), float(gamma), _ptr(bias),
                                _stream(stream)), "moe_bias_update")
+
+
+def moe_bias_update_stats(E: int, total_assignments: int, counts, gamma: float, bias, stats, stream=None) -> None:
+    """stats: a float32 device tensor of (at least) 4 elements, e.g. one row of a [steps, 4] buffer."""
+    _check(LIB.moe_bias_update_stats(int(E), int(total_assignments), _ptr(counts), float(gamma), _ptr(bias),
+                                     _ptr(stats), _stream(stream)), "moe_bias_update_stats")
 
 
 def moe_backward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], routing: Dict[str, torch.Tensor], dy, dx,

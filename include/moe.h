@@ -140,6 +140,23 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
 moe_status moe_bias_update(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma,
                            float* bias, void* stream);
 
+/* The same bias step in the same launch, plus the batch's expert-balance
+ * figures, which the article's "Relay training" section watches (the top-2
+ * paragraph: a low dead-expert fraction under aux-loss-free balancing; the
+ * baton paragraph: expert balance on the training dashboard).  stats: [4]
+ * float32 (device, caller-owned; e.g. row `step` of a [steps, 4] buffer, so a
+ * loop of steps needs no host synchronisation), written as
+ *   stats[0] = (experts with counts[e] == 0) / E,
+ *   stats[1] = max_e counts[e] * E / total_assignments   (max over mean load),
+ *   stats[2] = -sum_e p_e ln p_e, p_e = counts[e] / total_assignments
+ *              (0 ln 0 = 0; nats),
+ *   stats[3] = stats[2] / ln E (1 when E = 1);
+ * total_assignments = 0 gives (1, 0, 0, 0).  fp32, reductions in a fixed
+ * order (run-to-run identical).  Errors as moe_bias_update; stats may not
+ * overlap counts or bias (MOE_E_ALIAS), a null stats is MOE_E_ARG. */
+moe_status moe_bias_update_stats(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma,
+                                 float* bias, float* stats, void* stream);
+
 /* Backward of a training moe_forward with the selection held fixed: dx [T, d]
  * act, and the float32 weight gradients.  The router gradient flows only
  * through the normalised gates (top-2 paragraph of the "Relay training"

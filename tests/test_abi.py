@@ -28,8 +28,8 @@ def lib():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward",
-                                           "moe_bias_update", "moe_backward", "moe_status_str",
-                                           "moe_set_phase_events"])
+                                           "moe_bias_update", "moe_bias_update_stats", "moe_backward",
+                                           "moe_status_str", "moe_set_phase_events"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -92,6 +92,13 @@ def test_host_checks_reject_before_launch(lib):
     assert lib.LIB.moe_bias_update(0, 16, 0x2000, 1e-3, 0x1000, None) == lib.MOE_E_ARG
     assert lib.LIB.moe_bias_update(65, 16, 0x2000, 1e-3, 0x1000, None) == lib.MOE_E_UNSUPPORTED
     assert lib.LIB.moe_bias_update(8, 16, 0x1000, 1e-3, 0x1010, None) == lib.MOE_E_ALIAS
+    # bias step with telemetry: stats must be present and overlap neither input
+    st = lib.LIB.moe_bias_update_stats
+    assert st(8, 16, 0x2000, 1e-3, 0x1000, None, None) == lib.MOE_E_ARG
+    assert st(8, 16, 0x2000, 1e-3, 0x1000, 0x1010, None) == lib.MOE_E_ALIAS
+    assert st(8, 16, 0x2000, 1e-3, 0x1000, 0x2008, None) == lib.MOE_E_ALIAS
+    assert st(65, 16, 0x2000, 1e-3, 0x1000, 0x3000, None) == lib.MOE_E_UNSUPPORTED
+    assert st(8, -1, 0x2000, 1e-3, 0x1000, 0x3000, None) == lib.MOE_E_ARG
 
 
 def test_route_host_checks(lib):
