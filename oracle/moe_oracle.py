@@ -45,7 +45,11 @@ design notes of the repository):
   R19 expert balance of one batch = (dead fraction: experts with zero load
       over E; max load over the mean load T*k/E; entropy -sum p ln p of the
       load shares p = load/(T*k), 0 ln 0 = 0; that entropy over ln E, 1 for
-      E = 1); a batch with no assignments reads (1, 0, 0, 0).
+      E = 1); a batch with no assignments reads (1, 0, 0, 0);
+  R20 the MoE block around the layer (the article's 23 MoE layers of a
+      pre-norm transformer): x = bf16(h / sqrt(mean(h^2) + 1e-6) * gamma)
+      (RMSNorm with a learned per-channel scale gamma, eps as R13), and the
+      block returns h + y, rounded once to the activation dtype.
 """
 from __future__ import annotations
 
@@ -218,6 +222,26 @@ def bias_update(bias, counts, total_assignments: int, gamma: float) -> np.ndarra
     E = c.size
     sgn = np.sign(np.int64(total_assignments) - np.int64(E) * c).astype(np.float32)
     return (b + np.float32(gamma) * sgn).astype(np.float32)
+
+
+RMS_EPS = 1e-6
+
+
+def rms_norm(h, gamma, eps: float = RMS_EPS) -> np.ndarray:
+    """Pre-norm of the MoE block (R20): each token row of h divided by its root
+    mean square (plus eps under the root), times gamma, rounded to bf16."""
+    h = np.asarray(h, dtype=f64)
+    ms = np.mean(h * h, axis=-1, keepdims=True)
+    return to_bf16_nearest(h / np.sqrt(ms + eps) * np.asarray(gamma, dtype=f64))
+
+
+def block_forward(h, gamma, w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down, bias, k: int,
+                  eps: float = RMS_EPS):
+    """The MoE block (R20): h + MoE(rms_norm(h)).  Returns (h_out, x, routing),
+    h_out exact (float64), x the bf16 values the layer reads."""
+    x = rms_norm(h, gamma, eps)
+    y, routing = forward(x, w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down, bias, k)
+    return np.asarray(h, dtype=f64) + y, x, routing
 
 
 def load_stats(counts, total_assignments: int) -> np.ndarray:

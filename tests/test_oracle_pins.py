@@ -472,3 +472,40 @@ def test_load_stats_invariants():
         kl = float(np.sum(p * np.log(p * E)))
         assert abs(s[2] - (math.log(E) - kl)) < 1e-12
         assert s[0] == np.count_nonzero(c == 0) / E
+
+
+# ---------------------------------------------------------------- MoE block (R20)
+
+def test_rms_norm_closed_forms():
+    """RMSNorm of the block: a hand-worked row, constant rows, gamma, and the
+    invariance to a positive scale of the row."""
+    # h = [3, 4]: mean square 12.5, so x = [3, 4] / sqrt(12.5 + 1e-6)
+    x = om.rms_norm(np.array([[3.0, 4.0]]), np.ones(2))
+    r = math.sqrt(12.5 + 1e-6)
+    np.testing.assert_array_equal(x, om.to_bf16_nearest(np.array([[3 / r, 4 / r]])))
+    assert abs(x[0, 0] - 0.84765625) < 1e-12 and abs(x[0, 1] - 1.1328125) < 1e-12   # bf16 of 0.8485, 1.1314
+    # a constant row c maps to sign(c) |c| / sqrt(c^2 + eps) ~ sign(c), times gamma
+    g = np.array([0.5, -2.0, 1.0, 3.0])
+    x = om.rms_norm(np.full((1, 4), -7.0), g)
+    np.testing.assert_array_equal(x, om.to_bf16_nearest(-g * 7 / math.sqrt(49 + 1e-6))[None])
+    # scale invariance (eps negligible against the mean square)
+    rng = np.random.default_rng(2)
+    h = rng.standard_normal((5, 64))
+    np.testing.assert_array_equal(om.rms_norm(h * 8.0, np.ones(64)), om.rms_norm(h, np.ones(64)))
+    # the root mean square of a normalised row is 1 up to bf16 rounding
+    xs = om.rms_norm(h, np.ones(64))
+    np.testing.assert_allclose(np.sqrt(np.mean(xs * xs, axis=1)), 1.0, rtol=4e-3)
+
+
+def test_block_with_silent_experts_is_the_identity():
+    """With every expert's and the shared expert's output rows zero, the block
+    returns its input exactly (the residual path), whatever the routing."""
+    inp = synth.make_layer(T=40, d=128, E=8, F=64, Fs=128, k=2, act="f32", seed=8, rms_norm=False)
+    w_down = np.zeros_like(inp.w_down)
+    w_sh_down = np.zeros_like(inp.w_sh_down)
+    h = inp.x * 3.0
+    h_out, x, r = om.block_forward(h, np.ones(inp.d), inp.w_router, inp.w_gate_up, w_down, inp.w_sh_gate_up,
+                                   w_sh_down, inp.bias, inp.k)
+    np.testing.assert_array_equal(h_out, h.astype(np.float64))
+    # and the layer inside reads the normalised rows
+    np.testing.assert_array_equal(r.idx, om.route(x, inp.w_router, inp.bias, inp.k).idx)
