@@ -22,6 +22,7 @@ size_t act_bytes(int act) { return act == MOE_BF16 ? 2 : 4; }
 // Workspace regions (byte offsets from the workspace base).
 struct Layout {
   size_t block_counts, rank, tile_e, tile_m0, tile_count, tile2_e, tile2_m0, tile2_count;
+  size_t xb;              // moe_forward_block: x = RMSNorm(h)
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
   // backward scratch (training): padded contraction tables and transposed operands
@@ -81,6 +82,7 @@ Layout make_layout(const moe_dims& d, int training) {
   L.tile2_e = take(tiles2 * 4);
   L.tile2_m0 = take(tiles2 * 4);
   L.tile2_count = take(4);
+  L.xb = take((size_t)d.T * d.d * es);           // the MoE block's normalised input
   L.H = take(slots * d.F * es);
   L.Hs = take((size_t)d.T * d.Fs * es);
   if (d.w_routed == MOE_INT4_G128) {
@@ -266,9 +268,14 @@ moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, 
   return device_status();
 }
 
+}  // extern "C"
+
+namespace {
+
 // Top-1 serving with int4 routed experts.
 moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, const float* bias, void* y,
-                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s) {
+                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
+                        const void* resid = nullptr, bool x_in_ws = false) {
   if (training) return MOE_E_UNSUPPORTED;
   const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
   std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
@@ -281,6 +288,8 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
                            {w->w_sh_down, D * Fs * 2, false},
                            {bias, E * 4, false},
                            {y, (size_t)d.T * D * 2, true}};
+  if (resid) rs.push_back({resid, (size_t)d.T * D * 2, false});
+  if (x_in_ws) rs.erase(rs.begin());             // x lives in the workspace (the block's normalised input)
   add_routing_ranges(rs, d, routing);
   if (null_with_size(rs)) return MOE_E_ARG;
   const Layout L = make_layout(d, 0);
@@ -317,19 +326,24 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.H = at<uint16_t>(ws, L.H);
   a.part_sh = at<float>(ws, L.part_sh);
   a.y = (uint16_t*)y;
+  a.resid = (const uint16_t*)resid;
   mark_phase(0, s);
   launch_decode(a, s);
   mark_phase(1, s);
   return device_status();
 }
 
-moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
-                       const moe_routing* routing, int training, void* ws, size_t ws_bytes, void* stream) {
+// The forward of the layer; resid (the MoE block's input h, or null) is
+// added to y in the combine.  x_in_ws: x is the workspace's normalised block
+// input (not checked against the workspace for overlap).
+moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
+                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
+                        const void* resid, bool x_in_ws) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (!w || !routing) return MOE_E_ARG;
   if (dims->w_routed == MOE_INT4_G128)
-    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream));
+    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws);
   const moe_dims& d = *dims;
   if (training && check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
   const size_t es = act_bytes(d.act);
@@ -342,6 +356,8 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
                            {w->w_sh_down, D * Fs * es, false},
                            {bias, E * 4, false},
                            {y, (size_t)d.T * D * es, true}};
+  if (resid) rs.push_back({resid, (size_t)d.T * D * es, false});
+  if (x_in_ws) rs.erase(rs.begin());
   add_routing_ranges(rs, d, routing);
   if (null_with_size(rs)) return MOE_E_ARG;
   const Layout L = make_layout(d, training ? 1 : 0);
@@ -349,7 +365,6 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   rs.push_back({ws, L.total, true});
   if (any_alias(rs)) return MOE_E_ALIAS;
 
-  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   mark_phase(0, s);
   enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
   mark_phase(1, s);
@@ -469,9 +484,40 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
   mark_phase(3, s);
 
   // combine: y[t] = S[t] + sum_j O[pos[t, j]]
-  launch_combine(d.act, S, nsd, O, routing->pos, d.T, d.d, d.k, y, s);
+  launch_combine(d.act, S, nsd, O, routing->pos, d.T, d.d, d.k, resid, y, s);
   mark_phase(4, s);
   return device_status();
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
+                       const moe_routing* routing, int training, void* ws, size_t ws_bytes, void* stream) {
+  return forward_core(dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                      nullptr, false);
+}
+
+moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* norm_weight, float eps,
+                             const moe_weights* w, const float* bias, void* h_out, const moe_routing* routing,
+                             void* ws, size_t ws_bytes, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  const moe_dims& d = *dims;
+  if (d.act != MOE_BF16 || d.d > 8 * 64 * kNormMaxVec) return MOE_E_UNSUPPORTED;
+  if (!(eps >= 0.f) || !w || !routing) return MOE_E_ARG;
+  const size_t n = (size_t)d.T * d.d * 2;
+  std::vector<Range> rs = {{h, n, false}, {norm_weight, (size_t)d.d * 4, false}, {h_out, n, true}};
+  if (null_with_size(rs) || !norm_weight) return MOE_E_ARG;
+  const Layout L = make_layout(d, 0);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* x = at<char>(ws, L.xb);
+  launch_rmsnorm(h, norm_weight, eps, d.T, d.d, x, s);
+  return forward_core(dims, x, w, bias, h_out, routing, 0, ws, ws_bytes, s, h, true);
 }
 
 moe_status moe_bias_update(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma, float* bias,

@@ -1,5 +1,6 @@
 // Weighted combine of the MoE layer (gfx950): y_t = S_t + sum_j O[pos(t, j)].
-// With a contraction-split shared down, S_t arrives as nS slices added in order.
+// With a contraction-split shared down, S_t arrives as nS slices added in order;
+// in the MoE block the residual input h_t is added last.
 //
 // O rows already carry their routing weight (the routed down GEMM scaled
 // them), S is the shared expert's output; the article's proof-of-loop
@@ -33,7 +34,7 @@ template <typename T>
 __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, int nS, long long s_stride,
                                                       const T* __restrict__ O,
                                                       const int32_t* __restrict__ pos, int T_, int d, int k,
-                                                      T* __restrict__ y) {
+                                                      const T* __restrict__ resid, T* __restrict__ y) {
   constexpr int V = 16 / sizeof(T);            // elements per 16-byte vector
   const int vec_per_row = d / V;
   const long long gid = (long long)blockIdx.x * blockDim.x + threadIdx.x;
@@ -48,6 +49,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, i
     const long long slot = pos[(long long)t * k + j];
     add_vec<T>(acc, ld16(O + slot * d + c));
   }
+  if (resid) add_vec<T>(acc, ld16(resid + (long long)t * d + c));
   u32x4_t out;
   if constexpr (sizeof(T) == 2) {
 #pragma unroll
@@ -61,8 +63,8 @@ __global__ __launch_bounds__(256) void combine_kernel(const T* __restrict__ S, i
 
 }  // namespace
 
-void launch_combine(int act, const void* S, int nS, const void* O, const int32_t* pos, int T, int d, int k, void* y,
-                    hipStream_t s) {
+void launch_combine(int act, const void* S, int nS, const void* O, const int32_t* pos, int T, int d, int k,
+                    const void* resid, void* y, hipStream_t s) {
   const long long s_stride = (long long)T * d;
   const int es = act == 1 ? 2 : 4;
   const long long n = (long long)T * (d * es / 16);
@@ -70,10 +72,10 @@ void launch_combine(int act, const void* S, int nS, const void* O, const int32_t
   const unsigned blocks = (unsigned)((n + 255) / 256);
   if (act == 1)
     hipLaunchKernelGGL(combine_kernel<bf16_t>, dim3(blocks), dim3(256), 0, s, (const bf16_t*)S, nS, s_stride, (const bf16_t*)O,
-                       pos, T, d, k, (bf16_t*)y);
+                       pos, T, d, k, (const bf16_t*)resid, (bf16_t*)y);
   else
     hipLaunchKernelGGL(combine_kernel<float>, dim3(blocks), dim3(256), 0, s, (const float*)S, nS, s_stride, (const float*)O, pos,
-                       T, d, k, (float*)y);
+                       T, d, k, (const float*)resid, (float*)y);
 }
 
 }  // namespace fgmoe

@@ -482,9 +482,9 @@ __global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int nt
 // Stage 3, routed down + combine: item i takes active expert a = i / (D/32)
 // and output columns 32 cb .. 32 cb + 31 (cb = i % (D/32)), two 16-row
 // tiles; wave w takes scale group w of the contraction F.  For each of the
-// expert's tokens t (slot s): y[t] = (((sh0 + sh1) + sh2) + sh3)[s] + o,
-// rounded once, where sh_q are the shared-down partials and o the routed row
-// (top-1: gate 1).  Every token belongs to exactly one active expert, so
+// expert's tokens t (slot s): y[t] = (((sh0 + sh1) + sh2) + sh3)[s] + o
+// (+ resid[t] in the MoE block), rounded once, where sh_q are the shared-down
+// partials and o the routed row (top-1: gate 1).  Every token belongs to exactly one active expert, so
 // every y row is written once.  Operands come straight from global memory
 // (as in stage 2).
 // ---------------------------------------------------------------------------
@@ -521,6 +521,7 @@ __global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
     const int m = tid >> 2, c8 = (tid & 3) * 8;
     int tok = 0;
     f32x4_t sh[4][2];
+    u32x4_t rs = {0u, 0u, 0u, 0u};                   // the block's residual input (bf16), if any
     if (tid < 64) {
       const int mc = min(m, nt - 1);
       tok = p.perm[s0 + m0 + mc];
@@ -530,6 +531,7 @@ __global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
         sh[q][0] = *reinterpret_cast<const f32x4_t*>(src);
         sh[q][1] = *reinterpret_cast<const f32x4_t*>(src + 4);
       }
+      if (p.resid) rs = ld16(p.resid + (long long)tok * D + cb * 32 + c8);
     }
 #pragma unroll
     for (int tile = 0; tile < 2; ++tile) {
@@ -547,6 +549,7 @@ __global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
         const float o = sum4(lds + m * 33 + c8 + c, 16 * 33);
         const float s = ((sh[0][c >> 2][c & 3] + sh[1][c >> 2][c & 3]) + sh[2][c >> 2][c & 3]) + sh[3][c >> 2][c & 3];
         v[c] = s + o;
+        if (p.resid) v[c] += bf16_to_f32((bf16_t)((rs[c >> 1] >> (16 * (c & 1))) & 0xFFFF));
       }
       st16(p.y + (long long)tok * D + cb * 32 + c8, pack8(v));
     }

@@ -142,6 +142,7 @@ struct DecodeArgs {
   uint16_t* H;                       // [T*k, F] bf16 (workspace)
   float* part_sh;                    // [4, T, d] fp32 shared down partials (workspace)
   uint16_t* y;                       // [T, d] bf16
+  const uint16_t* resid;             // [T, d] bf16 residual added to y, or null
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);
 
@@ -183,10 +184,17 @@ void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm
 void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, const float* dl, const int32_t* idx,
                    const int32_t* pos, int T, int d, int k, void* dx, hipStream_t s);
 
-// y[t] = S_0[t] + ... + S_{nS-1}[t] + sum_j O[pos[t*k + j]] in that order,
-// rounded once.  The S_z ([T, d] each, consecutive) are the contraction
-// slices of the shared down.
-void launch_combine(int act, const void* S, int nS, const void* O, const int32_t* pos, int T, int d, int k, void* y,
-                    hipStream_t s);
+// y[t] = S_0[t] + ... + S_{nS-1}[t] + sum_j O[pos[t*k + j]] (+ resid[t]) in
+// that order, rounded once.  The S_z ([T, d] each, consecutive) are the
+// contraction slices of the shared down; resid (may be null) is the MoE
+// block's residual input.
+void launch_combine(int act, const void* S, int nS, const void* O, const int32_t* pos, int T, int d, int k,
+                    const void* resid, void* y, hipStream_t s);
+
+// x = bf16(h / sqrt(mean(h^2) + eps) * gamma) per row (block.hip); bf16 h and
+// x [T, d], gamma [d] float32, d a multiple of 8 and at most 8 * 64 *
+// kNormMaxVec.
+constexpr int kNormMaxVec = 16;
+void launch_rmsnorm(const void* h, const float* gamma, float eps, int T, int d, void* x, hipStream_t s);
 
 }  // namespace fgmoe

@@ -6,7 +6,8 @@ this module loads the library and raises if it is missing; there is no other
 implementation to fall back to.
 
 The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
-moe_bias_update, moe_backward, moe_status_str.  Weights, routing buffers and
+moe_forward_block, moe_bias_update, moe_bias_update_stats, moe_backward,
+moe_status_str.  Weights, routing buffers and
 gradients are passed as dicts of torch tensors keyed by the C field names.
 """
 from __future__ import annotations
@@ -65,6 +66,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, P, ctypes.POINTER(MoeRouting),
                                 ctypes.c_int, P, SZ, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_block.argtypes = [dims_p, P, P, ctypes.c_float, ctypes.POINTER(MoeWeights), P, P,
+                                      ctypes.POINTER(MoeRouting), P, SZ, P]
+    lib.moe_forward_block.restype = ctypes.c_int
     lib.moe_bias_update.argtypes = [I32, I64, P, ctypes.c_float, P, P]
     lib.moe_bias_update.restype = ctypes.c_int
     lib.moe_bias_update_stats.argtypes = [I32, I64, P, ctypes.c_float, P, P, P]
@@ -135,6 +139,16 @@ def moe_forward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y, rou
     _check(LIB.moe_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), _ptr(y), ctypes.byref(r),
                            int(bool(training)), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_block(dims: MoeDims, h, norm_weight, eps: float, weights: Dict[str, torch.Tensor], bias, h_out,
+                      routing: Dict[str, torch.Tensor], ws, stream=None) -> None:
+    """h_out = h + MoE(RMSNorm(h) * norm_weight); norm_weight: [d] float32."""
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_forward_block(ctypes.byref(dims), _ptr(h), _ptr(norm_weight), float(eps), ctypes.byref(w),
+                                 _ptr(bias), _ptr(h_out), ctypes.byref(r), _ptr(ws), ws.numel() * ws.element_size(),
+                                 _stream(stream)), "moe_forward_block")
 
 
 def moe_bias_update(E: int, total_assignments: int, counts, gamma: float, bias, stream=None) -> None:

@@ -131,6 +131,21 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
                        void* y, const moe_routing* routing, int training,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* The MoE block around the layer, as the architecture paragraph places the
+ * layer in 23 of the model's 24 transformer layers (pre-norm and residual:
+ * this library's reading):
+ *   x     = bf16(h / sqrt(mean_i h_i^2 + eps) * norm_weight)   (RMSNorm, per token row)
+ *   h_out = h + MoE(x), summed in fp32 with the layer's combine and rounded once.
+ * h, h_out: [T, d] bf16 (device), must not overlap (MOE_E_ALIAS); norm_weight:
+ * [d] float32 (device); eps >= 0.  bf16 activations only, d <= 8192
+ * (MOE_E_UNSUPPORTED otherwise); no training mode.  x is kept in the
+ * workspace (moe_workspace_bytes(dims, 0) bytes); routing and bias as in
+ * moe_forward (the routing of x).  With w_routed = MOE_INT4_G128 this is the
+ * top-1 serving path of moe_forward with the same norm and residual. */
+moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* norm_weight, float eps,
+                             const moe_weights* w, const float* bias, void* h_out, const moe_routing* routing,
+                             void* ws, size_t ws_bytes, void* stream);
+
 /* Aux-loss-free balancing step (architecture paragraph, DeepSeek-V3 recipe):
  * bias[e] <- fl32(bias[e] + gamma * sign(total_assignments - E * counts[e])),
  * i.e. the target load total_assignments/E compared exactly in integers,

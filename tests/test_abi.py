@@ -27,7 +27,7 @@ def lib():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward",
+    assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
                                            "moe_status_str", "moe_set_phase_events"])
 
@@ -124,3 +124,24 @@ def test_library_has_no_undefined_kernel_stubs():
     out = subprocess.run(["nm", "-D", LIBPATH], stdout=subprocess.PIPE, text=True).stdout
     undefined = [l for l in out.splitlines() if " U " in l and "fgmoe" in l]
     assert not undefined, undefined
+
+
+def test_block_host_checks(lib):
+    """moe_forward_block rejects, before any launch: fp32 activations, a null
+    norm scale, a negative eps, a short workspace, h_out overlapping h."""
+    W = lib.MoeWeights(*[0x10000000 + i * 0x1000000 for i in range(7)])
+    R = lib.MoeRouting(*[0x40000000 + i * 0x1000000 for i in range(6)])
+    h, h_out, g, ws = 0x60000000, 0x70000000, 0x5f000000, 0x80000000
+
+    def call(dims, h_, g_, eps, out, ws_bytes):
+        return lib.LIB.moe_forward_block(ctypes.byref(dims), h_, g_, eps, ctypes.byref(W), 0x50000000, out,
+                                         ctypes.byref(R), ws, ws_bytes, None)
+
+    f32 = lib.make_dims(16, 128, 8, 64, 256, 2, "f32")
+    assert call(f32, h, g, 1e-6, h_out, 1 << 30) == lib.MOE_E_UNSUPPORTED
+    dims = lib.make_dims(16, 128, 8, 64, 256, 2, "bf16")
+    need = lib.moe_workspace_bytes(dims)
+    assert call(dims, h, None, 1e-6, h_out, need) == lib.MOE_E_ARG
+    assert call(dims, h, g, -1.0, h_out, need) == lib.MOE_E_ARG
+    assert call(dims, h, g, 1e-6, h_out, need - 1) == lib.MOE_E_WORKSPACE
+    assert call(dims, h, g, 1e-6, h + 64, need) == lib.MOE_E_ALIAS

@@ -1,0 +1,135 @@
+"""GPU parity of the MoE block (moe_forward_block): h_out = h + MoE(x) with
+x = bf16(RMSNorm(h) * gamma), against the oracle's block_forward.
+
+The block input h is an unnormalised bf16 residual stream (N(0,1) rows with a
+per-row scale), gamma a per-channel scale around 1.  Rows whose routing of the
+oracle's x comes within 1e-3 of a top-(k+1) tie are redrawn.  Checked:
+routing bit-exact; h_out within relative Frobenius error 1e-2 (bf16); and the
+block's own contribution: ||h_out - h_ref|| <= 1e-2 ||y_ref|| + 2^-8 ||h_ref||,
+the layer's tolerance plus one bf16 rounding of h_out at the scale of h.
+"""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as om
+from fine_grained_moe_amd import synth
+from tests import _helpers as H
+
+pytestmark = pytest.mark.gpu
+
+NEAR_TIE = 1e-3
+
+
+def _residual_stream(T, d, w_router, k, seed, bias=None):
+    """bf16 h and fp32 gamma with no near-tie rows in the routing of RMSNorm(h)."""
+    rng = np.random.default_rng(seed)
+    gamma = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
+
+    def draw(n):
+        scale = rng.uniform(0.5, 4.0, size=(n, 1))
+        return synth.round_to_bf16((rng.standard_normal((n, d)) * scale).astype(np.float32))
+
+    h = draw(T)
+    b = np.zeros(w_router.shape[0], np.float32) if bias is None else bias
+    for _ in range(20):
+        x = om.rms_norm(h, gamma)
+        v = om.route(x, w_router, b, k).v
+        bad = np.nonzero(om.topk_margin(v, k) < NEAR_TIE)[0]
+        if bad.size == 0:
+            return h, gamma
+        h[bad] = draw(bad.size)
+    raise RuntimeError("near-tie redraw did not converge")
+
+
+def _check(h, h_out, h_ref, what):
+    """h_out within 1e-2 of h_ref (relative Frobenius), and the block's own
+    contribution within the layer's tolerance plus one bf16 rounding of the
+    output: ||h_out - h_ref|| <= 1e-2 ||y_ref|| + 2^-8 ||h_ref|| (round to
+    nearest with 8 significant bits errs by at most 2^-8 of the value)."""
+    y_ref = h_ref - h.astype(np.float64)
+    e1 = H.rel_fro(h_out, h_ref)
+    err = float(np.linalg.norm(h_out - h_ref))
+    bound = 1e-2 * float(np.linalg.norm(y_ref)) + 2.0 ** -8 * float(np.linalg.norm(h_ref))
+    print(f"[{what}] rel_fro(h_out) = {e1:.2e}, ||h_out - h_ref|| / ||y_ref|| = "
+          f"{err / np.linalg.norm(y_ref):.2e} (bound {bound / np.linalg.norm(y_ref):.2e})", flush=True)
+    assert e1 <= 1e-2 and err <= bound, (e1, err, bound)
+
+
+def _bf(a):
+    import torch
+    return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+
+
+def _run_block(dims, h, gamma, w, bias):
+    import torch
+    from fine_grained_moe_amd import moe
+    ht = _bf(h)
+    out = torch.empty_like(ht)
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+    moe.moe_forward_block(dims, ht, torch.from_numpy(gamma).cuda(), 1e-6, w, torch.from_numpy(bias).cuda(), out, r,
+                          ws)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), {k: v.cpu().numpy() for k, v in r.items()}
+
+
+@pytest.mark.parametrize("T", [1, 1000])
+def test_block_bf16(T):
+    from fine_grained_moe_amd import moe
+    inp = synth.make_layer(T=1, d=1024, E=64, F=512, Fs=2048, k=2, act="bf16", seed=21)
+    h, gamma = _residual_stream(T, inp.d, inp.w_router, inp.k, seed=T)
+    w = dict(w_router=_bf(inp.w_router), w_gate_up=_bf(inp.w_gate_up), w_down=_bf(inp.w_down),
+             w_sh_gate_up=_bf(inp.w_sh_gate_up), w_sh_down=_bf(inp.w_sh_down))
+    dims = moe.make_dims(T, inp.d, inp.E, inp.F, inp.Fs, inp.k, "bf16")
+    h_out, rn = _run_block(dims, h, gamma, w, inp.bias)
+    h_ref, x_ref, r_ref = om.block_forward(h, gamma, inp.w_router, inp.w_gate_up, inp.w_down, inp.w_sh_gate_up,
+                                           inp.w_sh_down, inp.bias, inp.k)
+    H.check_routing_exact(rn, r_ref, inp.E)
+    _check(h, h_out, h_ref, f"bf16 block T={T}")
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_block_int4_top1(T):
+    from fine_grained_moe_amd import moe
+    base = synth.make_layer(T=1, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=7)
+    qg, sg = om.quantize_int4(base.w_gate_up)
+    qd, sd = om.quantize_int4(base.w_down)
+    import torch
+    w = dict(w_router=_bf(base.w_router), w_gate_up=torch.from_numpy(qg).cuda(), s_gate_up=_bf(sg),
+             w_down=torch.from_numpy(qd).cuda(), s_down=_bf(sd), w_sh_gate_up=_bf(base.w_sh_gate_up),
+             w_sh_down=_bf(base.w_sh_down))
+    h, gamma = _residual_stream(T, 1024, base.w_router, 1, seed=100 + T)
+    dims = moe.make_dims(T, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+    bias = np.zeros(64, np.float32)
+    h_out, rn = _run_block(dims, h, gamma, w, bias)
+    x = om.rms_norm(h, gamma)
+    y_ref, r_ref = om.forward_int4_top1(x, base.w_router, qg, sg, qd, sd, base.w_sh_gate_up, base.w_sh_down, bias)
+    np.testing.assert_array_equal(rn["idx"].ravel(), r_ref.idx.ravel())
+    _check(h, h_out, h.astype(np.float64) + y_ref, f"int4 top-1 block T={T}")
+
+
+def test_block_stack_of_three_layers():
+    """Three blocks with distinct weights chained through the residual stream,
+    as the model's MoE layers run; each block's input is the previous block's
+    output on the GPU, and the oracle chain runs on the same inputs."""
+    import torch
+    from fine_grained_moe_amd import moe
+    T, d = 300, 1024
+    layers = [synth.make_layer(T=1, d=d, E=64, F=512, Fs=2048, k=2, act="bf16", seed=60 + i) for i in range(3)]
+    h, gamma = _residual_stream(T, d, layers[0].w_router, 2, seed=5)
+    dims = moe.make_dims(T, d, 64, 512, 2048, 2, "bf16")
+    h_gpu = h
+    h_ref = h.astype(np.float64)
+    for i, inp in enumerate(layers):
+        w = dict(w_router=_bf(inp.w_router), w_gate_up=_bf(inp.w_gate_up), w_down=_bf(inp.w_down),
+                 w_sh_gate_up=_bf(inp.w_sh_gate_up), w_sh_down=_bf(inp.w_sh_down))
+        out, rn = _run_block(dims, h_gpu, gamma, w, inp.bias)
+        # the oracle's block on the GPU's input (bf16 values) for this layer
+        ref, _, r_ref = om.block_forward(h_gpu, gamma, inp.w_router, inp.w_gate_up, inp.w_down, inp.w_sh_gate_up,
+                                         inp.w_sh_down, inp.bias, 2)
+        margin = om.topk_margin(om.route(om.rms_norm(h_gpu, gamma), inp.w_router, inp.bias, 2).v, 2)
+        ok = margin >= NEAR_TIE          # a later layer's input is not redrawn: leave its near-tie rows out
+        np.testing.assert_array_equal(rn["idx"].reshape(T, 2)[ok], r_ref.idx.reshape(T, 2)[ok])
+        _check(h_gpu[ok], out[ok], ref[ok], f"stack layer {i} ({int((~ok).sum())} near-tie rows left out)")
+        h_gpu = out.astype(np.float32)
+    torch.cuda.synchronize()
