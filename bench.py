@@ -202,6 +202,94 @@ def bench_decode(moe, synth, torch, np, n_layers=23, iters=46, graph_reps=20):
     return out
 
 
+def bench_stack(moe, synth, torch, np, n_layers=23, reps=10, graph_reps=20):
+    """The model's 23 MoE layers chained through the residual stream with
+    moe_forward_block (RMSNorm in, residual add out), distinct weights per
+    layer so every layer reads its weights from HBM: bf16 at T = 4096 (eager
+    launches), and the int4 top-1 serving path at T = 1, 8, 64 (the 23 blocks
+    captured once in a HIP graph and replayed).  Weights are seeded N(0, 0.02)
+    draws on the device (the same recipe as the one-layer workload; parity is
+    the tests' business)."""
+    E, d, F, Fs = 64, 1024, 512, 2048
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(1234)
+
+    def randn(*shape, std=0.02, dtype=torch.bfloat16):
+        return (torch.randn(*shape, generator=gen, device="cuda", dtype=torch.float32) * std).to(dtype)
+
+    gamma = 1.0 + randn(d, std=0.1, dtype=torch.float32)
+    out = {}
+    # bf16 batch path, T = 4096
+    T, k = 4096, 2
+    layers = [dict(w_router=randn(E, d), w_gate_up=randn(E, 2 * F, d), w_down=randn(E, d, F),
+                   w_sh_gate_up=randn(2 * Fs, d), w_sh_down=randn(d, Fs)) for _ in range(n_layers)]
+    biases = [torch.zeros(E, device="cuda") for _ in range(n_layers)]
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+    h = [randn(T, d, std=1.0), torch.empty(T, d, device="cuda", dtype=torch.bfloat16)]
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+
+    def stack():
+        for i in range(n_layers):
+            moe.moe_forward_block(dims, h[i % 2], gamma, 1e-6, layers[i], biases[i], h[(i + 1) % 2], r, ws)
+
+    for _ in range(2):
+        stack()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        stack()
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / reps
+    out["bf16_t4096"] = dict(us_per_stack=round(el * 1e6, 1), us_per_layer=round(el * 1e6 / n_layers, 2),
+                             tokens_per_s=T / el)
+    log(f"stack bf16 T={T}: {el * 1e3:.3f} ms per {n_layers}-layer stack ({el * 1e6 / n_layers:.1f} us per layer), "
+        f"{T / el / 1e6:.3f} M tokens/s")
+    del layers, h, r, ws
+    torch.cuda.empty_cache()
+    # int4 top-1 serving path, T = 1, 8, 64
+    base = synth.make_layer(T=64, d=d, E=E, F=F, Fs=Fs, k=1, act="bf16", seed=11)
+    qg, sg = synth.random_int4(E, 2 * F, d, seed=11)
+    qd, sd = synth.random_int4(E, d, F, seed=12)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+    w0 = dict(w_router=bf(base.w_router), w_gate_up=torch.from_numpy(qg).cuda(), s_gate_up=bf(sg),
+              w_down=torch.from_numpy(qd).cuda(), s_down=bf(sd), w_sh_gate_up=bf(base.w_sh_gate_up),
+              w_sh_down=bf(base.w_sh_down))
+    qlayers = [w0] + [{n: t.clone() for n, t in w0.items()} for _ in range(n_layers - 1)]
+    bias = torch.zeros(E, device="cuda")
+    out["int4_top1"] = {}
+    for T in (1, 8, 64):
+        dims = moe.make_dims(T, d, E, F, Fs, 1, "bf16", w_routed="int4")
+        h = [randn(T, d, std=1.0), torch.empty(T, d, device="cuda", dtype=torch.bfloat16)]
+        r = moe.alloc_routing(dims)
+        ws = moe.alloc_workspace(dims)
+
+        def qstack():
+            for i in range(n_layers):
+                moe.moe_forward_block(dims, h[i % 2], gamma, 1e-6, qlayers[i], bias, h[(i + 1) % 2], r, ws)
+
+        qstack()
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g):
+            qstack()
+        g.replay()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(graph_reps):
+            g.replay()
+        e1.record()
+        torch.cuda.synchronize()
+        us = e0.elapsed_time(e1) * 1e3 / graph_reps
+        del g
+        out["int4_top1"][f"T{T}"] = dict(us_per_stack=round(us, 1), us_per_layer=round(us / n_layers, 2),
+                                         tokens_per_s=T / (us * 1e-6))
+        log(f"stack int4 top-1 T={T}: {us:.1f} us per {n_layers}-layer stack (graph replay, "
+            f"{us / n_layers:.1f} us per layer), {T / (us * 1e-6):.0f} tokens/s")
+    return out
+
+
 def bench_train(moe, synth, torch, np, steps=10, warmup=3):
     """One training step of the layer at T = 32768 (16 x 2048): forward with
     saved activations, backward (dx and every weight gradient), bias step."""
@@ -312,7 +400,8 @@ def main() -> int:
     ap.add_argument("--no-warm", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true")
-    ap.add_argument("--leg", choices=("decode", "train"),
+    ap.add_argument("--no-stack", action="store_true")
+    ap.add_argument("--leg", choices=("decode", "train", "stack"),
                     help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
@@ -334,7 +423,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.leg is not None:
-        fn = bench_decode if args.leg == "decode" else bench_train
+        fn = {"decode": bench_decode, "train": bench_train, "stack": bench_stack}[args.leg]
         print(json.dumps({args.leg: fn(moe, synth, torch, np)}), flush=True)
         return 0
     inp = synth.make_workload("layer_t4096", seed=0)
@@ -445,6 +534,8 @@ def main() -> int:
         out["decode"] = bench_decode(moe, synth, torch, np)
     if not args.no_train:
         out["train"] = bench_train(moe, synth, torch, np)
+    if not args.no_stack:
+        out["stack"] = bench_stack(moe, synth, torch, np)
 
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
