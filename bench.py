@@ -199,6 +199,24 @@ def bench_decode(moe, synth, torch, np, n_layers=23, iters=46, graph_reps=20):
                             gbps=round(gbps, 1), frac_hbm=round(gbps / (PEAK_HBM_BPS / 1e9), 4))
         log(f"decode T={T}: {us:.1f} us per forward (graph replay; eager {eager_us:.1f} us), {uniq} experts, "
             f"{gbps:.0f} GB/s ({gbps / 8000:.1%} of HBM)")
+    # The floor the three dependent launches of a forward put under it: three
+    # minimal dependent kernels (one-element adds) per forward, 23 forwards,
+    # captured and replayed the same way.
+    z = torch.zeros(1, device="cuda")
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        for _ in range(n_layers * 3):
+            z.add_(1.0)
+    g.replay()
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(graph_reps):
+        g.replay()
+    e1.record()
+    torch.cuda.synchronize()
+    out["launch_floor_us"] = round(e0.elapsed_time(e1) * 1e3 / (graph_reps * n_layers), 2)
+    del g
+    log(f"decode launch floor: {out['launch_floor_us']:.2f} us per forward (3 minimal dependent kernels, graph replay)")
     return out
 
 
@@ -287,6 +305,64 @@ def bench_stack(moe, synth, torch, np, n_layers=23, reps=10, graph_reps=20):
                                          tokens_per_s=T / (us * 1e-6))
         log(f"stack int4 top-1 T={T}: {us:.1f} us per {n_layers}-layer stack (graph replay, "
             f"{us / n_layers:.1f} us per layer), {T / (us * 1e-6):.0f} tokens/s")
+    return out
+
+
+def bench_zipf(moe, synth, torch, np, steps=50, warmup=5, calib=400):
+    """Skewed routing: the layer at T = 16384 with the router bias preset so
+    the expected expert loads follow Zipf(1) over the 64 experts (expert 0
+    hottest, ~21% of assignments; several near-dead experts).  The preset is
+    found with the library's own router: b_e += eta * sign(T*k*p_e - load_e),
+    eta = 0.02 * 2^-(it // 100), 400 iterations on this batch.  Then forward +
+    bias step with telemetry, timed like the headline (8 weight sets)."""
+    inp = synth.make_workload("zipf_t16384", seed=0)
+    T, d, E, F, Fs, k = inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+    base = dict(w_router=bf(inp.w_router), w_gate_up=bf(inp.w_gate_up), w_down=bf(inp.w_down),
+                w_sh_gate_up=bf(inp.w_sh_gate_up), w_sh_down=bf(inp.w_sh_down))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(7)]
+    x = bf(inp.x)
+    y = torch.empty_like(x)
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+    pz = 1.0 / np.arange(1, E + 1)
+    target = T * k * pz / pz.sum()
+    b = np.zeros(E, np.float32)
+    bt = torch.zeros(E, device="cuda")
+    for it in range(calib):
+        bt.copy_(torch.from_numpy(b))
+        moe.moe_route(dims, x, base["w_router"], bt, r, ws)
+        load = r["counts"].cpu().numpy()
+        b = (b + np.float32(0.02 * 2.0 ** -(it // 100)) * np.sign(target - load).astype(np.float32)).astype(np.float32)
+    bt.copy_(torch.from_numpy(b))
+    stats = torch.zeros(steps, 4, device="cuda")
+    bias = bt.clone()
+    for i in range(warmup):
+        moe.moe_forward(dims, x, sets[i % 8], bias, y, r, ws)
+    ev = HipEvents()
+    e_g = [[ev.create() for _ in range(len(PHASES) + 1)] for _ in range(steps)]
+    bias.copy_(bt)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_set_phase_events(e_g[i])
+        moe.moe_forward(dims, x, sets[i % 8], bias, y, r, ws)
+        moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, stats[i])
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    moe.moe_set_phase_events(None)
+    gate_up_us = sum(ev.elapsed_ms(e_g[i][2], e_g[i][3]) for i in range(steps)) / steps * 1e3
+    for row in e_g:
+        for e_ in row:
+            ev.destroy(e_)
+    st0 = stats[0].cpu().tolist()
+    work = algorithmic_work(T, d, E, F, Fs, k)
+    out = dict(T=T, us_per_step=round(el * 1e6, 1), tokens_per_s=T / el, gate_up_us=round(gate_up_us, 1),
+               gate_up_tflops=round(work["gate_up"]["flops"] / (gate_up_us * 1e-6) / 1e12, 1),
+               max_over_mean_load=round(st0[1], 3), dead_fraction=round(st0[0], 4))
+    log(f"zipf T={T}: {el * 1e6:.1f} us/step, {T / el / 1e6:.2f} M tokens/s; gate/up {gate_up_us:.1f} us "
+        f"({out['gate_up_tflops']:.0f} TFLOP/s); hottest expert {st0[1]:.2f} x the mean load")
     return out
 
 
@@ -401,7 +477,8 @@ def main() -> int:
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
-    ap.add_argument("--leg", choices=("decode", "train", "stack"),
+    ap.add_argument("--no-zipf", action="store_true")
+    ap.add_argument("--leg", choices=("decode", "train", "stack", "zipf"),
                     help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
@@ -423,7 +500,7 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.leg is not None:
-        fn = {"decode": bench_decode, "train": bench_train, "stack": bench_stack}[args.leg]
+        fn = {"decode": bench_decode, "train": bench_train, "stack": bench_stack, "zipf": bench_zipf}[args.leg]
         print(json.dumps({args.leg: fn(moe, synth, torch, np)}), flush=True)
         return 0
     inp = synth.make_workload("layer_t4096", seed=0)
@@ -536,6 +613,8 @@ def main() -> int:
         out["train"] = bench_train(moe, synth, torch, np)
     if not args.no_stack:
         out["stack"] = bench_stack(moe, synth, torch, np)
+    if not args.no_zipf:
+        out["zipf"] = bench_zipf(moe, synth, torch, np)
 
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
