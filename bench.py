@@ -352,17 +352,24 @@ def bench_zipf(moe, synth, torch, np, steps=50, warmup=5, calib=400):
     torch.cuda.synchronize()
     el = (time.perf_counter() - t0) / steps
     moe.moe_set_phase_events(None)
-    gate_up_us = sum(ev.elapsed_ms(e_g[i][2], e_g[i][3]) for i in range(steps)) / steps * 1e3
+    # phase j spans events j -> j + 1 (PHASES: route, gate_up, down, combine)
+    ph_us = {p: sum(ev.elapsed_ms(e_g[i][j], e_g[i][j + 1]) for i in range(steps)) / steps * 1e3
+             for j, p in enumerate(PHASES)}
+    gate_up_us = ph_us["gate_up"]
     for row in e_g:
         for e_ in row:
             ev.destroy(e_)
     st0 = stats[0].cpu().tolist()
     work = algorithmic_work(T, d, E, F, Fs, k)
-    out = dict(T=T, us_per_step=round(el * 1e6, 1), tokens_per_s=T / el, gate_up_us=round(gate_up_us, 1),
+    out = dict(T=T, us_per_step=round(el * 1e6, 1), tokens_per_s=T / el,
+               phases_us={p: round(v, 1) for p, v in ph_us.items()}, gate_up_us=round(gate_up_us, 1),
                gate_up_tflops=round(work["gate_up"]["flops"] / (gate_up_us * 1e-6) / 1e12, 1),
+               down_tflops=round(work["down"]["flops"] / (ph_us["down"] * 1e-6) / 1e12, 1),
                max_over_mean_load=round(st0[1], 3), dead_fraction=round(st0[0], 4))
-    log(f"zipf T={T}: {el * 1e6:.1f} us/step, {T / el / 1e6:.2f} M tokens/s; gate/up {gate_up_us:.1f} us "
-        f"({out['gate_up_tflops']:.0f} TFLOP/s); hottest expert {st0[1]:.2f} x the mean load")
+    log(f"zipf T={T}: {el * 1e6:.1f} us/step, {T / el / 1e6:.2f} M tokens/s; phases (us): "
+        + ", ".join(f"{p}={v:.1f}" for p, v in ph_us.items())
+        + f"; gate/up {out['gate_up_tflops']:.0f} TFLOP/s, down {out['down_tflops']:.0f} TFLOP/s; "
+        f"hottest expert {st0[1]:.2f} x the mean load")
     return out
 
 
