@@ -14,7 +14,9 @@
 // dependent steps as the data flow allows):
 //   stage 1  router (one workgroup per 16 tokens: logits on MFMA, top-1,
 //            gate) beside the shared expert's gate/up, which does not
-//            depend on the routing;
+//            depend on the routing (in the MoE block every workgroup first
+//            normalises its 16 rows of h, and the router's first expert
+//            tile writes them for stage 2);
 //   stage 2  one workgroup writes the routing outputs (loads, offsets,
 //            dispatch order, active experts); the shared down in four
 //            contraction quarters (fp32 partials); the routed gate/up of each
@@ -129,6 +131,63 @@ __device__ __forceinline__ void stage_rows(char* dst, const char* base, long lon
   }
 }
 
+// stage_rows<512> for the MoE block: the staged quarter (wave w holds
+// columns 256 w .. 256 w + 255 of the 16 rows) is normalised on the way to
+// LDS, x = bf16(h / sqrt(mean(h^2) + eps) * gamma).  Each wave sums the
+// squares of its quarter per row (lane order, then a butterfly over the 32
+// lanes of a row), the 4 quarters meet in red[4][16] and are added in wave
+// order; every wave of the workgroup calls this (it holds a barrier).  With
+// xn, the normalised rows 0 .. n-1 are also written there.
+__device__ __forceinline__ void stage_rows_norm(char* dst, const char* base, long long stride, int n, int lane,
+                                                int wave, int d, const float* gamma, float eps, float* red,
+                                                uint16_t* xn) {
+  constexpr int PR = 32, NS = 8;                     // 512-byte quarters: 32 pieces per row
+  u32x4_t v[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int pc = i * 64 + lane, r = min(pc / PR, n - 1), c = pc % PR;
+    v[i] = ld16(base + (long long)r * stride + c * 16);
+  }
+  float ps[NS];
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    ps[i] = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_to_f32((bf16_t)(v[i][j] & 0xFFFF)), hi = bf16_to_f32((bf16_t)(v[i][j] >> 16));
+      ps[i] += lo * lo;
+      ps[i] += hi * hi;
+    }
+#pragma unroll
+    for (int off = 1; off < 32; off <<= 1) ps[i] += __shfl_xor(ps[i], off);
+  }
+  // lane 0 holds rows 0, 2, .., 14 of this quarter, lane 32 rows 1, 3, .., 15
+  if ((lane & 31) == 0) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) red[wave * 16 + 2 * i + (lane >> 5)] = ps[i];
+  }
+  __syncthreads();
+  const int c = lane % PR;
+  const float4 g0 = *reinterpret_cast<const float4*>(gamma + wave * 256 + c * 8);
+  const float4 g1 = *reinterpret_cast<const float4*>(gamma + wave * 256 + c * 8 + 4);
+  const float gm[8] = {g0.x, g0.y, g0.z, g0.w, g1.x, g1.y, g1.z, g1.w};
+#pragma unroll
+  for (int i = 0; i < NS; ++i) {
+    const int r = 2 * i + (lane >> 5);
+    const float ss = ((red[r] + red[16 + r]) + red[32 + r]) + red[48 + r];
+    const float rstd = 1.f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float lo = bf16_to_f32((bf16_t)(v[i][j] & 0xFFFF)), hi = bf16_to_f32((bf16_t)(v[i][j] >> 16));
+      v[i][j] = pack_bf16x2(lo * rstd * gm[2 * j], hi * rstd * gm[2 * j + 1]);
+    }
+    if (r < n) {
+      st16(dst + r * 512 + ((c ^ xsw<512>(r)) << 4), v[i]);
+      if (xn) st16(xn + (long long)r * d + wave * 256 + c * 8, v[i]);
+    }
+  }
+}
+
 // Lane fr's operand piece `piece` of activation row fr.  Rows >= n hold stale
 // data; they only feed MFMA output rows that are never stored.
 template <int Q>
@@ -172,14 +231,20 @@ __device__ __forceinline__ void xcd_item(int i, int ntile, int& blk, int& tile) 
 // ---------------------------------------------------------------------------
 constexpr int kS1Wave = 16384;
 
+// write_xn: the MoE block's normalised rows of this token tile go to p.xn.
 template <int D>
-__device__ f32x4_t stage1_tile(const char* wrow, int tt, int T, const DecodeArgs& p, char* wreg) {
+__device__ f32x4_t stage1_tile(const char* wrow, int tt, int T, const DecodeArgs& p, char* wreg, float* red,
+                               bool write_xn) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int fr = lane & 15, g = lane >> 4;
   static_assert(D == 1024, "one contraction quarter is 512 bytes");
   dma_w<8>(wrow + wave * (D / 2), wreg, lane);
-  stage_rows<512>(wreg + 8192, reinterpret_cast<const char*>(p.x) + (long long)tt * 16 * D * 2 + wave * (D / 2),
-                  (long long)D * 2, nullptr, min(16, T - tt * 16), lane);
+  const char* xq = reinterpret_cast<const char*>(p.x) + (long long)tt * 16 * D * 2 + wave * (D / 2);
+  if (p.gamma)
+    stage_rows_norm(wreg + 8192, xq, (long long)D * 2, min(16, T - tt * 16), lane, wave, D, p.gamma, p.eps, red,
+                    write_xn ? p.xn + (long long)tt * 16 * D : nullptr);
+  else
+    stage_rows<512>(wreg + 8192, xq, (long long)D * 2, nullptr, min(16, T - tt * 16), lane);
   wait_all();
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -201,6 +266,7 @@ __device__ __forceinline__ float part_sum(const char* lds, int wave_bytes, int o
 template <int D, int FS>
 __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs p, int ntile) {
   __shared__ __align__(16) char lds[4 * kS1Wave];
+  __shared__ float red[64];                           // the MoE block's per-quarter sums of squares
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   char* wreg = lds + wave * kS1Wave;
   const int n_sh = (FS / 8) * ntile;
@@ -211,7 +277,8 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs p, int nt
     xcd_item(blk, ntile, hb, tt);
     const int f = hb * 8 + (r & 7);
     const int wr = r < 8 ? f : FS + f;
-    stage1_tile<D>(reinterpret_cast<const char*>(p.w_sh_gate_up) + (long long)wr * D * 2, tt, T, p, wreg);
+    stage1_tile<D>(reinterpret_cast<const char*>(p.w_sh_gate_up) + (long long)wr * D * 2, tt, T, p, wreg, red,
+                   false);
     __syncthreads();
     const int t = tt * 16 + tid;
     if (tid < 16 && t < T) {
@@ -226,7 +293,7 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs p, int nt
     const int t = tid >> 4, c = tid & 15, e = et * 16 + c;
     const float b = e < p.E ? p.bias[e] : 0.f;
     stage1_tile<D>(reinterpret_cast<const char*>(p.w_router) + (long long)min(et * 16 + r, p.E - 1) * D * 2, tt, T, p,
-                   wreg);
+                   wreg, red, et == 0);
     __syncthreads();
     const float sc = 1.0f / (1.0f + expf(-part_sum(lds, kS1Wave, 8192, t * 17 + c)));
     uint64_t key = e < p.E ? (((uint64_t)float_key(sc + b) << 32) | (uint32_t)(63 - e)) : 0ull;
@@ -415,7 +482,8 @@ __device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds,
   for (int m0 = 0; m0 < n; m0 += 16) {
     const int nt = min(16, n - m0);
     const int tok = B.perm[s0 + m0 + min(fr, nt - 1)];
-    const char* xr = reinterpret_cast<const char*>(p.x + (long long)tok * D) + wave * (D / 2) + g * 64;
+    const uint16_t* xsrc = p.gamma ? p.xn : p.x;     // the MoE block: the rows stage 1 normalised
+    const char* xr = reinterpret_cast<const char*>(xsrc + (long long)tok * D) + wave * (D / 2) + g * 64;
     u32x4_t xa[2][4];
 #pragma unroll
     for (int grp = 0; grp < 2; ++grp)
