@@ -30,6 +30,7 @@ struct Layout {
       dXs;
   long long P, Tp;        // padded column counts of the routed and shared transposes
   size_t active, n_active, rkey, rscore, part_sh;   // int4 serving path: active experts, router tile maxima, fp32 shared-down partials
+  size_t wdq_gu, wdq_d;   // int4 prefill: the experts' weights dequantised to bf16
   size_t total;
 };
 
@@ -41,8 +42,12 @@ moe_status check_dims(const moe_dims* d) {
   if (d->E > 64 || d->k > d->E || d->k > 8) return MOE_E_UNSUPPORTED;
   if (d->d % 128 || d->F % 64 || d->Fs % 64) return MOE_E_UNSUPPORTED;
   if (d->w_routed == MOE_INT4_G128) {
-    // top-1 serving path: bf16 activations, one expert per token, small batches
-    if (d->act != MOE_BF16 || d->k != 1 || d->T > kDecodeMaxT || !decode_shape_supported(d->d, d->F, d->Fs))
+    // top-1 serving: bf16 activations, one expert per token.  Up to
+    // kDecodeMaxT tokens the decode kernels (built for the NanoColibri
+    // shape); above, the prefill (the active experts dequantised, then the
+    // grouped GEMMs), whose groups of 128 run along d and F.
+    if (d->act != MOE_BF16 || d->k != 1) return MOE_E_UNSUPPORTED;
+    if (d->T <= kDecodeMaxT ? !decode_shape_supported(d->d, d->F, d->Fs) : d->F % 128 != 0)
       return MOE_E_UNSUPPORTED;
   }
   const long long slots = (long long)d->T * d->k;
@@ -85,7 +90,7 @@ Layout make_layout(const moe_dims& d, int training) {
   L.xb = take((size_t)d.T * d.d * es);           // the MoE block's normalised input
   L.H = take(slots * d.F * es);
   L.Hs = take((size_t)d.T * d.Fs * es);
-  if (d.w_routed == MOE_INT4_G128) {
+  if (d.w_routed == MOE_INT4_G128 && d.T <= kDecodeMaxT) {
     L.active = take((size_t)d.E * 3 * 4);
     L.n_active = take(4);
     L.rkey = take(4 * 64 * 8);
@@ -98,6 +103,10 @@ Layout make_layout(const moe_dims& d, int training) {
   // bf16: the shared down is split over contraction slices, each written as
   // its own [T, d] block that the combine adds
   L.S = take((size_t)d.T * d.d * es * shared_down_slices(d));
+  if (d.w_routed == MOE_INT4_G128) {
+    L.wdq_gu = take((size_t)d.E * 2 * d.F * d.d * 2);
+    L.wdq_d = take((size_t)d.E * d.d * d.F * 2);
+  }
   if (training) {
     L.AU = take(slots * 2 * d.F * es);
     L.Ou = take(slots * d.d * es);
@@ -272,109 +281,14 @@ moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, 
 
 namespace {
 
-// Top-1 serving with int4 routed experts.
-// gamma (the MoE block): x is the block input h; stage 1 normalises it.
-moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, const float* bias, void* y,
-                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
-                        const void* resid = nullptr, bool x_in_ws = false, const float* gamma = nullptr,
-                        float eps = 0.f) {
-  if (training) return MOE_E_UNSUPPORTED;
-  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
-  std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
-                           {w->w_router, E * D * 2, false},
-                           {w->w_gate_up, E * 2 * F * D / 2, false},
-                           {w->s_gate_up, E * 2 * F * (D / 128) * 2, false},
-                           {w->w_down, E * D * F / 2, false},
-                           {w->s_down, E * D * (F / 128) * 2, false},
-                           {w->w_sh_gate_up, 2 * Fs * D * 2, false},
-                           {w->w_sh_down, D * Fs * 2, false},
-                           {bias, E * 4, false},
-                           {y, (size_t)d.T * D * 2, true}};
-  if (resid) rs.push_back({resid, (size_t)d.T * D * 2, false});
-  if (x_in_ws) rs.erase(rs.begin());             // x lives in the workspace (the block's normalised input)
-  add_routing_ranges(rs, d, routing);
-  if (null_with_size(rs)) return MOE_E_ARG;
-  const Layout L = make_layout(d, 0);
-  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
-  rs.push_back({ws, L.total, true});
-  if (any_alias(rs)) return MOE_E_ALIAS;
-  DecodeArgs a{};
-  a.T = d.T;
-  a.d = d.d;
-  a.E = d.E;
-  a.F = d.F;
-  a.Fs = d.Fs;
-  a.k = d.k;
-  a.x = (const uint16_t*)x;
-  a.w_router = (const uint16_t*)w->w_router;
-  a.bias = bias;
-  a.w_sh_gate_up = (const uint16_t*)w->w_sh_gate_up;
-  a.w_sh_down = (const uint16_t*)w->w_sh_down;
-  a.q_gate_up = (const uint8_t*)w->w_gate_up;
-  a.s_gate_up = (const uint16_t*)w->s_gate_up;
-  a.q_down = (const uint8_t*)w->w_down;
-  a.s_down = (const uint16_t*)w->s_down;
-  a.idx = routing->idx;
-  a.gate = routing->gate;
-  a.counts = routing->counts;
-  a.offsets = routing->offsets;
-  a.perm = routing->perm;
-  a.pos = routing->pos;
-  a.active = at<int32_t>(ws, L.active);
-  a.n_active = at<int32_t>(ws, L.n_active);
-  a.rkey = at<uint64_t>(ws, L.rkey);
-  a.rscore = at<float>(ws, L.rscore);
-  a.Hs = at<uint16_t>(ws, L.Hs);
-  a.H = at<uint16_t>(ws, L.H);
-  a.part_sh = at<float>(ws, L.part_sh);
-  a.y = (uint16_t*)y;
-  a.resid = (const uint16_t*)resid;
-  a.gamma = gamma;
-  a.eps = eps;
-  a.xn = at<uint16_t>(ws, L.xb);
-  mark_phase(0, s);
-  launch_decode(a, s);
-  mark_phase(1, s);
-  return device_status();
-}
-
-// The forward of the layer; resid (the MoE block's input h, or null) is
-// added to y in the combine.  x_in_ws: x is the workspace's normalised block
-// input (not checked against the workspace for overlap).
-moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
-                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
-                        const void* resid, bool x_in_ws) {
-  moe_status st = check_dims(dims);
-  if (st != MOE_OK) return st;
-  if (!w || !routing) return MOE_E_ARG;
-  if (dims->w_routed == MOE_INT4_G128)
-    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws);
-  const moe_dims& d = *dims;
-  if (training && check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
-  const size_t es = act_bytes(d.act);
-  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
-  std::vector<Range> rs = {{x, (size_t)d.T * D * es, false},
-                           {w->w_router, E * D * es, false},
-                           {w->w_gate_up, E * 2 * F * D * es, false},
-                           {w->w_down, E * D * F * es, false},
-                           {w->w_sh_gate_up, 2 * Fs * D * es, false},
-                           {w->w_sh_down, D * Fs * es, false},
-                           {bias, E * 4, false},
-                           {y, (size_t)d.T * D * es, true}};
-  if (resid) rs.push_back({resid, (size_t)d.T * D * es, false});
-  if (x_in_ws) rs.erase(rs.begin());
-  add_routing_ranges(rs, d, routing);
-  if (null_with_size(rs)) return MOE_E_ARG;
-  const Layout L = make_layout(d, training ? 1 : 0);
-  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
-  rs.push_back({ws, L.total, true});
-  if (any_alias(rs)) return MOE_E_ALIAS;
-
-  mark_phase(0, s);
-  enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
-  mark_phase(1, s);
-  if (d.T == 0) return device_status();
-
+// The expert GEMMs and the combine, once routing (and the dispatch tables)
+// are in place: gate/up (routed + shared), down (routed + shared), combine.
+// w's routed weights are act-typed (the bf16/fp32 layer, or the int4
+// prefill's dequantised copies).
+moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* x, const moe_weights* w, void* y,
+                                const moe_routing* routing, int training, void* ws, hipStream_t s,
+                                const void* resid) {
+  const size_t D = d.d, F = d.F, Fs = d.Fs;
   const long long slots = (long long)d.T * d.k;
   // bf16 runs on the 256 x 256 tiles of gemm_fwd.hip (grouped jobs index the
   // 256-row tile table), fp32 on gemm.hip's 128 x 256 tiles.
@@ -494,6 +408,127 @@ moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* 
   return device_status();
 }
 
+// Top-1 serving with int4 routed experts.
+// gamma (the MoE block): x is the block input h; stage 1 normalises it.
+moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, const float* bias, void* y,
+                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
+                        const void* resid = nullptr, bool x_in_ws = false, const float* gamma = nullptr,
+                        float eps = 0.f) {
+  if (training) return MOE_E_UNSUPPORTED;
+  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
+  std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
+                           {w->w_router, E * D * 2, false},
+                           {w->w_gate_up, E * 2 * F * D / 2, false},
+                           {w->s_gate_up, E * 2 * F * (D / 128) * 2, false},
+                           {w->w_down, E * D * F / 2, false},
+                           {w->s_down, E * D * (F / 128) * 2, false},
+                           {w->w_sh_gate_up, 2 * Fs * D * 2, false},
+                           {w->w_sh_down, D * Fs * 2, false},
+                           {bias, E * 4, false},
+                           {y, (size_t)d.T * D * 2, true}};
+  if (resid) rs.push_back({resid, (size_t)d.T * D * 2, false});
+  if (x_in_ws) rs.erase(rs.begin());             // x lives in the workspace (the block's normalised input)
+  add_routing_ranges(rs, d, routing);
+  if (null_with_size(rs)) return MOE_E_ARG;
+  const Layout L = make_layout(d, 0);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  if (d.T > kDecodeMaxT) {
+    // Prefill: route, dequantise every expert that received tokens into the
+    // workspace (bf16, one rounding of q * scale), then the bf16 expert GEMMs.
+    char* wgu = at<char>(ws, L.wdq_gu);
+    char* wd = at<char>(ws, L.wdq_d);
+    moe_weights wb = *w;
+    wb.w_gate_up = wgu;
+    wb.w_down = wd;
+    mark_phase(0, s);
+    enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
+    launch_dequant_int4(w->w_gate_up, w->s_gate_up, d.E, 2 * d.F, d.d, routing->counts, wgu, s);
+    launch_dequant_int4(w->w_down, w->s_down, d.E, d.d, d.F, routing->counts, wd, s);
+    mark_phase(1, s);
+    return enqueue_expert_gemms(d, L, x, &wb, y, routing, 0, ws, s, resid);
+  }
+  DecodeArgs a{};
+  a.T = d.T;
+  a.d = d.d;
+  a.E = d.E;
+  a.F = d.F;
+  a.Fs = d.Fs;
+  a.k = d.k;
+  a.x = (const uint16_t*)x;
+  a.w_router = (const uint16_t*)w->w_router;
+  a.bias = bias;
+  a.w_sh_gate_up = (const uint16_t*)w->w_sh_gate_up;
+  a.w_sh_down = (const uint16_t*)w->w_sh_down;
+  a.q_gate_up = (const uint8_t*)w->w_gate_up;
+  a.s_gate_up = (const uint16_t*)w->s_gate_up;
+  a.q_down = (const uint8_t*)w->w_down;
+  a.s_down = (const uint16_t*)w->s_down;
+  a.idx = routing->idx;
+  a.gate = routing->gate;
+  a.counts = routing->counts;
+  a.offsets = routing->offsets;
+  a.perm = routing->perm;
+  a.pos = routing->pos;
+  a.active = at<int32_t>(ws, L.active);
+  a.n_active = at<int32_t>(ws, L.n_active);
+  a.rkey = at<uint64_t>(ws, L.rkey);
+  a.rscore = at<float>(ws, L.rscore);
+  a.Hs = at<uint16_t>(ws, L.Hs);
+  a.H = at<uint16_t>(ws, L.H);
+  a.part_sh = at<float>(ws, L.part_sh);
+  a.y = (uint16_t*)y;
+  a.resid = (const uint16_t*)resid;
+  a.gamma = gamma;
+  a.eps = eps;
+  a.xn = at<uint16_t>(ws, L.xb);
+  mark_phase(0, s);
+  launch_decode(a, s);
+  mark_phase(1, s);
+  return device_status();
+}
+
+// The forward of the layer; resid (the MoE block's input h, or null) is
+// added to y in the combine.  x_in_ws: x is the workspace's normalised block
+// input (not checked against the workspace for overlap).
+moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
+                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
+                        const void* resid, bool x_in_ws) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!w || !routing) return MOE_E_ARG;
+  if (dims->w_routed == MOE_INT4_G128)
+    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws);
+  const moe_dims& d = *dims;
+  if (training && check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
+  const size_t es = act_bytes(d.act);
+  const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
+  std::vector<Range> rs = {{x, (size_t)d.T * D * es, false},
+                           {w->w_router, E * D * es, false},
+                           {w->w_gate_up, E * 2 * F * D * es, false},
+                           {w->w_down, E * D * F * es, false},
+                           {w->w_sh_gate_up, 2 * Fs * D * es, false},
+                           {w->w_sh_down, D * Fs * es, false},
+                           {bias, E * 4, false},
+                           {y, (size_t)d.T * D * es, true}};
+  if (resid) rs.push_back({resid, (size_t)d.T * D * es, false});
+  if (x_in_ws) rs.erase(rs.begin());
+  add_routing_ranges(rs, d, routing);
+  if (null_with_size(rs)) return MOE_E_ARG;
+  const Layout L = make_layout(d, training ? 1 : 0);
+  if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
+  rs.push_back({ws, L.total, true});
+  if (any_alias(rs)) return MOE_E_ALIAS;
+
+  mark_phase(0, s);
+  enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
+  mark_phase(1, s);
+  if (d.T == 0) return device_status();
+
+  return enqueue_expert_gemms(d, L, x, w, y, routing, training, ws, s, resid);
+}
+
 }  // namespace
 
 extern "C" {
@@ -552,6 +587,20 @@ moe_status moe_bias_update_stats(int32_t E, int64_t total_assignments, const int
   if (any_alias(rs)) return MOE_E_ALIAS;
   launch_bias_update(E, (long long)total_assignments, counts, gamma, bias, stats,
                      reinterpret_cast<hipStream_t>(stream));
+  return device_status();
+}
+
+moe_status moe_quantize_int4(int32_t dtype, const void* w, int64_t rows, int32_t K, uint8_t* packed, void* scales,
+                             void* stream) {
+  if (rows < 0 || K < 1) return MOE_E_ARG;
+  if (dtype != MOE_BF16 && dtype != MOE_F32) return MOE_E_UNSUPPORTED;
+  if (K % 128 || rows * (K / 128) >= (1LL << 33)) return MOE_E_UNSUPPORTED;
+  if (rows == 0) return MOE_OK;
+  if (!w || !packed || !scales) return MOE_E_ARG;
+  const size_t n = (size_t)rows * (size_t)K;
+  std::vector<Range> rs = {{w, n * act_bytes(dtype), false}, {packed, n / 2, true}, {scales, n / 128 * 2, true}};
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  launch_quant_int4(dtype, w, rows, K, packed, scales, reinterpret_cast<hipStream_t>(stream));
   return device_status();
 }
 

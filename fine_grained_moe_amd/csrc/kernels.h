@@ -173,6 +173,14 @@ struct TransposeArgs {
   const float* scale;        // optional, indexed by the source index before division
 };
 void launch_fill_zero(void* p, size_t bytes, hipStream_t s);   // bytes % 4 == 0
+// int4 export (quant.hip): w [rows, K] (act 1 = bf16, else fp32), K % 128 == 0
+// -> packed [rows, K/2] bytes and bf16 scales [rows, K/128].
+void launch_quant_int4(int act, const void* w, long long rows, int K, uint8_t* packed, void* scales,
+                       hipStream_t s);
+// Inverse for the int4 prefill: packed [E, rows_e, K/2] + scales [E, rows_e,
+// K/128] -> bf16 [E, rows_e, K] for the experts with counts[e] > 0.
+void launch_dequant_int4(const void* packed, const void* scales, int E, int rows_e, int K, const int32_t* counts,
+                         void* out, hipStream_t s);
 void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int S, int step,
                      int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s);
 // Contraction slices of the shared expert's weight gradients (a function of

@@ -7,7 +7,7 @@ implementation to fall back to.
 
 The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
 moe_forward_block, moe_bias_update, moe_bias_update_stats, moe_backward,
-moe_status_str.  Weights, routing buffers and
+moe_quantize_int4, moe_status_str.  Weights, routing buffers and
 gradients are passed as dicts of torch tensors keyed by the C field names.
 """
 from __future__ import annotations
@@ -76,6 +76,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_backward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P, P,
                                  ctypes.POINTER(MoeGrads), P, SZ, P]
     lib.moe_backward.restype = ctypes.c_int
+    lib.moe_quantize_int4.argtypes = [I32, P, I64, I32, P, P, P]
+    lib.moe_quantize_int4.restype = ctypes.c_int
     lib.moe_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     lib.moe_set_phase_events.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -160,6 +162,20 @@ def moe_bias_update_stats(E: int, total_assignments: int, counts, gamma: float, 
     """stats: a float32 device tensor of (at least) 4 elements, e.g. one row of a [steps, 4] buffer."""
     _check(LIB.moe_bias_update_stats(int(E), int(total_assignments), _ptr(counts), float(gamma), _ptr(bias),
                                      _ptr(stats), _stream(stream)), "moe_bias_update_stats")
+
+
+def moe_quantize_int4(w, packed, scales, stream=None) -> None:
+    """w: [..., K] bf16 or float32 device tensor (rows = product of the leading
+    dims); packed: uint8 [..., K/2]; scales: bf16 [..., K/128]."""
+    dt = {torch.bfloat16: MOE_BF16, torch.float32: MOE_F32}.get(w.dtype)
+    if dt is None:
+        raise MoeError(MOE_E_UNSUPPORTED, "moe_quantize_int4")
+    K = int(w.shape[-1])
+    rows = w.numel() // K if K else 0
+    if packed.numel() != rows * (K // 2) or scales.numel() != rows * (K // 128) or not w.is_contiguous():
+        raise MoeError(MOE_E_ARG, "moe_quantize_int4")
+    _check(LIB.moe_quantize_int4(dt, _ptr(w), rows, K, _ptr(packed), _ptr(scales), _stream(stream)),
+           "moe_quantize_int4")
 
 
 def moe_backward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], routing: Dict[str, torch.Tensor], dy, dx,

@@ -181,6 +181,25 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
                         const moe_routing* routing, const void* dy, void* dx, const moe_grads* dw,
                         void* ws, size_t ws_bytes, void* stream);
 
+/* int4 export of expert weights into the container that MOE_INT4_G128 reads
+ * (the article's opening section, proof-of-loop paragraph, says the
+ * containers are int4; the format is this library's reading, as described at
+ * moe_weights): per group of 128 consecutive elements of a row,
+ *   scale = absmax / 7 rounded once to bf16 (ties to even), 0 for an all-zero group,
+ *   q     = clamp(round-half-even(w / scale), -8, 7), a two's-complement nibble,
+ * with both decisions taken in float64 from the exact inputs.
+ *  dtype   MOE_BF16 or MOE_F32 (else MOE_E_UNSUPPORTED)
+ *  w       [rows, K] dtype, row-major (device, read only); K % 128 == 0 (else
+ *          MOE_E_UNSUPPORTED); for a layer: rows = E * 2F, K = d (gate/up) or
+ *          rows = E * d, K = F (down)
+ *  packed  [rows, K/2] uint8 (device, written): element 2i in the low nibble
+ *  scales  [rows, K/128] bf16 (device, written)
+ * rows = 0 does nothing.  Outputs may not overlap w or each other
+ * (MOE_E_ALIAS).  Inputs are finite with absmax / 7 in bf16's normal range
+ * (or zero); other values are not checked. */
+moe_status moe_quantize_int4(int32_t dtype, const void* w, int64_t rows, int32_t K, uint8_t* packed,
+                             void* scales, void* stream);
+
 /* Instrumentation, not part of the layer.  Registers n (0..8) hipEvent_t
  * handles, passed as void*, that every later moe_forward records on its
  * stream at its phase boundaries:

@@ -14,7 +14,7 @@ LIBPATH = os.path.join(ROOT, "fine_grained_moe_amd", "libfgmoe.so")
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(moe_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", text)))
 
 
 @pytest.fixture(scope="module")
@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
-                                           "moe_status_str", "moe_set_phase_events"])
+                                           "moe_quantize_int4", "moe_status_str", "moe_set_phase_events"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -111,10 +111,42 @@ def test_route_host_checks(lib):
                              None) == lib.MOE_E_ARG
 
 
+def test_quantize_int4_host_checks(lib):
+    """moe_quantize_int4 rejects, before any launch: bad sizes, other dtypes, K
+    not a multiple of 128, null pointers and overlapping outputs."""
+    q = lib.LIB.moe_quantize_int4
+    bf, f32 = lib.MOE_BF16, lib.MOE_F32
+    assert q(bf, 0x1000, -1, 128, 0x100000, 0x200000, None) == lib.MOE_E_ARG
+    assert q(bf, 0x1000, 4, 0, 0x100000, 0x200000, None) == lib.MOE_E_ARG
+    assert q(lib.MOE_INT4_G128, 0x1000, 4, 128, 0x100000, 0x200000, None) == lib.MOE_E_UNSUPPORTED
+    assert q(bf, 0x1000, 4, 192, 0x100000, 0x200000, None) == lib.MOE_E_UNSUPPORTED
+    assert q(bf, 0x1000, 0, 128, None, None, None) == lib.MOE_OK          # nothing to do
+    assert q(bf, None, 4, 128, 0x100000, 0x200000, None) == lib.MOE_E_ARG
+    assert q(f32, 0x1000, 4, 128, None, 0x200000, None) == lib.MOE_E_ARG
+    # w is 4 x 128 bf16 = 1 KiB at 0x1000: packed inside it overlaps
+    assert q(bf, 0x1000, 4, 128, 0x1200, 0x200000, None) == lib.MOE_E_ALIAS
+    # packed (256 B) and scales (8 B) overlapping each other
+    assert q(bf, 0x1000, 4, 128, 0x100000, 0x100080, None) == lib.MOE_E_ALIAS
+
+
 def test_int4_requires_top1_bf16(lib):
     for act, k in (("f32", 1), ("bf16", 2)):
         d = lib.make_dims(8, 1024, 64, 512, 2048, k, act, w_routed="int4")
         assert lib.moe_workspace_bytes(d) == 0
+
+
+def test_int4_shapes_decode_and_prefill(lib):
+    """Up to 64 tokens the int4 path is the decode kernels (NanoColibri shape
+    only); above, the prefill takes any shape whose F is a multiple of 128 and
+    needs the dequantised experts in its workspace."""
+    ws = lambda T, d=1024, E=64, F=512, Fs=2048: lib.moe_workspace_bytes(
+        lib.make_dims(T, d, E, F, Fs, 1, "bf16", w_routed="int4"))
+    assert ws(64) > 0 and ws(65) > 0 and ws(4096) > 0
+    assert ws(64, d=256, E=8, F=128, Fs=256) == 0                  # not the decode shape
+    assert ws(65, d=256, E=8, F=128, Fs=256) > 0
+    assert ws(65, F=192) == 0                                       # groups of 128 along F
+    bf16_layer = lib.moe_workspace_bytes(lib.make_dims(4096, 1024, 64, 512, 2048, 1, "bf16"))
+    assert ws(4096) >= bf16_layer + 64 * 3 * 1024 * 512 * 2
 
 
 def test_library_has_no_undefined_kernel_stubs():

@@ -90,7 +90,6 @@ def test_int4_decode_empty_batch(weights):
 
 def test_int4_rejects_unsupported_shapes():
     from fine_grained_moe_amd import moe
-    assert moe.moe_workspace_bytes(moe.make_dims(65, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")) == 0
     assert moe.moe_workspace_bytes(moe.make_dims(8, 1024, 64, 512, 2048, 2, "bf16", w_routed="int4")) == 0
     assert moe.moe_workspace_bytes(moe.make_dims(8, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")) > 0
 
