@@ -373,6 +373,83 @@ def bench_zipf(moe, synth, torch, np, steps=50, warmup=5, calib=400):
     return out
 
 
+def bench_int4(moe, synth, torch, np, reps=20, steps=50, warmup=5, n_sets=8):
+    """int4 export and prefill.  Export: moe_quantize_int4 over one layer's
+    routed weights (bf16 [64, 1024, 1024] gate/up and [64, 1024, 512] down,
+    N(0, 0.02)); algorithmic bytes = 2 read + 0.5 written per element + 2 per
+    128 (scales).  Prefill: the int4 top-1 layer at T = 4096 (x RMS-normalised
+    N(0, 1)) on those exported weights, 8 weight sets rotated (cold), phases
+    from the library's events (the first phase holds routing and the
+    dequantisation of the loaded experts)."""
+    E, d, F, Fs = 64, 1024, 512, 2048
+    inp = synth.make_layer(T=4096, d=d, E=E, F=F, Fs=Fs, k=1, act="bf16", seed=5)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+    wgu, wd = bf(inp.w_gate_up), bf(inp.w_down)
+    pg = torch.empty(E, 2 * F, d // 2, dtype=torch.uint8, device="cuda")
+    sg = torch.empty(E, 2 * F, d // 128, dtype=torch.bfloat16, device="cuda")
+    pd = torch.empty(E, d, F // 2, dtype=torch.uint8, device="cuda")
+    sd = torch.empty(E, d, F // 128, dtype=torch.bfloat16, device="cuda")
+
+    def export():
+        moe.moe_quantize_int4(wgu, pg, sg)
+        moe.moe_quantize_int4(wd, pd, sd)
+
+    for _ in range(3):
+        export()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(reps):
+        export()
+    e1.record()
+    torch.cuda.synchronize()
+    us_x = e0.elapsed_time(e1) * 1e3 / reps
+    n_el = E * 2 * F * d + E * d * F
+    xbytes = n_el * (2 + 0.5) + n_el // 128 * 2
+    out = dict(export=dict(us=round(us_x, 1), gbps=round(xbytes / (us_x * 1e-6) / 1e9, 1),
+                           frac_hbm=round(xbytes / (us_x * 1e-6) / PEAK_HBM_BPS, 3), bytes=int(xbytes)))
+    log(f"int4 export: {us_x:.1f} us for one layer's routed weights ({xbytes / 1e6:.1f} MB), "
+        f"{xbytes / (us_x * 1e-6) / 1e9:.0f} GB/s")
+    del wgu, wd
+    # prefill on the exported weights
+    T = inp.T
+    dims = moe.make_dims(T, d, E, F, Fs, 1, "bf16", w_routed="int4")
+    base = dict(w_router=bf(inp.w_router), w_gate_up=pg, s_gate_up=sg, w_down=pd, s_down=sd,
+                w_sh_gate_up=bf(inp.w_sh_gate_up), w_sh_down=bf(inp.w_sh_down))
+    sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(n_sets - 1)]
+    x = bf(inp.x)
+    y = torch.empty_like(x)
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+    bias = torch.zeros(E, device="cuda")
+    for i in range(warmup):
+        moe.moe_forward(dims, x, sets[i % n_sets], bias, y, r, ws)
+    ev = HipEvents()
+    e_g = [[ev.create() for _ in range(len(PHASES) + 1)] for _ in range(steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        moe.moe_set_phase_events(e_g[i])
+        moe.moe_forward(dims, x, sets[i % n_sets], bias, y, r, ws)
+    torch.cuda.synchronize()
+    el = (time.perf_counter() - t0) / steps
+    moe.moe_set_phase_events(None)
+    ph_us = {p: sum(ev.elapsed_ms(e_g[i][j], e_g[i][j + 1]) for i in range(steps)) / steps * 1e3
+             for j, p in enumerate(PHASES)}
+    for row in e_g:
+        for e_ in row:
+            ev.destroy(e_)
+    active = int(np.count_nonzero(r["counts"].cpu().numpy()))
+    work = algorithmic_work(T, d, E, F, Fs, 1)
+    out["prefill"] = dict(T=T, us_per_forward=round(el * 1e6, 1), tokens_per_s=T / el, active_experts=active,
+                          phases_us={("route_dequant" if p == "route" else p): round(v, 1) for p, v in ph_us.items()},
+                          gate_up_tflops=round(work["gate_up"]["flops"] / (ph_us["gate_up"] * 1e-6) / 1e12, 1))
+    log(f"int4 prefill T={T}: {el * 1e6:.1f} us/forward, {T / el / 1e6:.2f} M tokens/s; phases (us): "
+        + ", ".join(f"{p}={v:.1f}" for p, v in ph_us.items()) + f" (route includes the dequantisation), "
+        f"{active} experts loaded")
+    return out
+
+
 def bench_train(moe, synth, torch, np, steps=10, warmup=3):
     """One training step of the layer at T = 32768 (16 x 2048): forward with
     saved activations, backward (dx and every weight gradient), bias step."""
@@ -485,7 +562,8 @@ def main() -> int:
     ap.add_argument("--no-train", action="store_true")
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-zipf", action="store_true")
-    ap.add_argument("--leg", choices=("decode", "train", "stack", "zipf"),
+    ap.add_argument("--no-int4", action="store_true")
+    ap.add_argument("--leg", choices=("decode", "train", "stack", "zipf", "int4"),
                     help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
@@ -507,7 +585,8 @@ def main() -> int:
 
     torch.cuda.set_device(0)
     if args.leg is not None:
-        fn = {"decode": bench_decode, "train": bench_train, "stack": bench_stack, "zipf": bench_zipf}[args.leg]
+        fn = {"decode": bench_decode, "train": bench_train, "stack": bench_stack, "zipf": bench_zipf,
+              "int4": bench_int4}[args.leg]
         print(json.dumps({args.leg: fn(moe, synth, torch, np)}), flush=True)
         return 0
     inp = synth.make_workload("layer_t4096", seed=0)
@@ -622,6 +701,8 @@ def main() -> int:
         out["stack"] = bench_stack(moe, synth, torch, np)
     if not args.no_zipf:
         out["zipf"] = bench_zipf(moe, synth, torch, np)
+    if not args.no_int4:
+        out["int4"] = bench_int4(moe, synth, torch, np)
 
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")
