@@ -1,15 +1,18 @@
 #!/usr/bin/env python3
 """Throughput of the NanoColibri MoE layer's hot path on one MI355X.
 
-A step is one pass of the whole path over one batch: moe_forward (router,
+A step is one pass of the whole path over one batch: the forward (router,
 top-2, loads and dispatch, routed gate/up + SwiGLU, routed down + gate
-scaling, shared expert, combine) followed by the bias step (moe_bias_update_stats), on the one-layer
+scaling, shared expert, combine) and the bias step with the balance figures,
+in one call (moe_forward_bias_step: the dispatch launch takes the bias step
+once the loads are known; the same bits as moe_forward followed by
+moe_bias_update_stats, one launch fewer), on the one-layer
 workload T = 4096 tokens (batch 2 x seq 2048), d = 1024, 64 experts of width
 512, top-2, shared expert 2048, bf16 with fp32 accumulation.  Inputs come from
 the seeded generator and sit in HBM before timing starts.
 
 The bias step of every timed step also writes the batch's expert-balance
-figures (moe_bias_update_stats) to a device buffer, read after timing.
+figures to a device buffer, read after timing.
 
 Headline `value`: tokens/s with the expert weights rotated over several
 distinct copies (each step reads its weights from HBM, not from the 256 MB
@@ -626,15 +629,13 @@ def main() -> int:
     def run(n_sets, steps, warmup):
         bias.copy_(bias0)
         for i in range(warmup):
-            moe.moe_forward(dims, x, sets[i % n_sets], bias, y, r, ws)
-            moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, stats[0])
+            moe.moe_forward_bias_step(dims, x, sets[i % n_sets], bias, GAMMA, stats[0], y, r, ws)
         events = [[ev.create() for _ in range(nph)] for _ in range(steps)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
             moe.moe_set_phase_events(events[i])
-            moe.moe_forward(dims, x, sets[(warmup + i) % n_sets], bias, y, r, ws)
-            moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, stats[i])
+            moe.moe_forward_bias_step(dims, x, sets[(warmup + i) % n_sets], bias, GAMMA, stats[i], y, r, ws)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
         moe.moe_set_phase_events(None)
@@ -685,7 +686,7 @@ def main() -> int:
         phase_report[p] = dict(us=round(us, 2), tflops=round(wp["flops"] / (us * 1e-6) / 1e12, 1),
                                gbps=round(wp["bytes"] / (us * 1e-6) / 1e9, 1), bound=wp["bound"])
     out["phases"] = phase_report
-    out["balance"] = balance      # the last timed step's loads (moe_bias_update_stats)
+    out["balance"] = balance      # the last timed step's loads (the fused bias step's figures)
 
     if not args.no_warm:
         el_w, ph_w = run(1, args.steps, args.warmup)

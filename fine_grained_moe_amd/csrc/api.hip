@@ -185,16 +185,25 @@ P* at(void* ws, size_t off) {
   return reinterpret_cast<P*>(reinterpret_cast<char*>(ws) + off);
 }
 
+// The bias step fused into a forward (moe_forward_bias_step).
+struct BiasStep {
+  float gamma;
+  float* bias;
+  float* stats;
+};
+
 // Router + loads + dispatch order; the routing outputs are complete afterwards.
+// bs (may be null): the bias step, taken by the dispatch launch.
 void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void* w_router, const float* bias,
-                   const moe_routing* r, void* ws, hipStream_t s) {
+                   const moe_routing* r, void* ws, hipStream_t s, const BiasStep* bs = nullptr) {
   const int nblk = route_blocks(d.T);
   launch_route_topk(d.act, x, w_router, bias, d.T, d.d, d.E, d.k, r->idx, r->gate, at<int32_t>(ws, L.block_counts),
                     at<int32_t>(ws, L.rank), s);
   const TileTable tiles{at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count)};
   const TileTable tiles_fwd{at<int32_t>(ws, L.tile2_e), at<int32_t>(ws, L.tile2_m0), at<int32_t>(ws, L.tile2_count)};
   launch_route_dispatch(at<int32_t>(ws, L.block_counts), r->idx, at<int32_t>(ws, L.rank), nblk, d.T, d.E, d.k,
-                        r->counts, r->offsets, tiles, tiles_fwd, r->perm, r->pos, s);
+                        r->counts, r->offsets, tiles, tiles_fwd, r->perm, r->pos, bs ? bs->gamma : 0.f,
+                        bs ? bs->bias : nullptr, bs ? bs->stats : nullptr, s);
 }
 
 // Column groups of the XCD grid of a dense job with M x K and N x K operands
@@ -413,7 +422,7 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
 moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, const float* bias, void* y,
                         const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
                         const void* resid = nullptr, bool x_in_ws = false, const float* gamma = nullptr,
-                        float eps = 0.f) {
+                        float eps = 0.f, const BiasStep* bs = nullptr) {
   if (training) return MOE_E_UNSUPPORTED;
   const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
   std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
@@ -424,9 +433,10 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
                            {w->s_down, E * D * (F / 128) * 2, false},
                            {w->w_sh_gate_up, 2 * Fs * D * 2, false},
                            {w->w_sh_down, D * Fs * 2, false},
-                           {bias, E * 4, false},
+                           {bias, E * 4, bs != nullptr},
                            {y, (size_t)d.T * D * 2, true}};
   if (resid) rs.push_back({resid, (size_t)d.T * D * 2, false});
+  if (bs && bs->stats) rs.push_back({bs->stats, 4 * 4, true});
   if (x_in_ws) rs.erase(rs.begin());             // x lives in the workspace (the block's normalised input)
   add_routing_ranges(rs, d, routing);
   if (null_with_size(rs)) return MOE_E_ARG;
@@ -443,7 +453,7 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
     wb.w_gate_up = wgu;
     wb.w_down = wd;
     mark_phase(0, s);
-    enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
+    enqueue_route(d, L, x, w->w_router, bias, routing, ws, s, bs);
     launch_dequant_int4(w->w_gate_up, w->s_gate_up, d.E, 2 * d.F, d.d, routing->counts, wgu, s);
     launch_dequant_int4(w->w_down, w->s_down, d.E, d.d, d.F, routing->counts, wd, s);
     mark_phase(1, s);
@@ -485,6 +495,9 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.xn = at<uint16_t>(ws, L.xb);
   mark_phase(0, s);
   launch_decode(a, s);
+  // the decode's launches hold no point where all loads are known before the
+  // bias is no longer read, so the bias step is a launch of its own here
+  if (bs) launch_bias_update(d.E, (long long)d.T * d.k, routing->counts, bs->gamma, bs->bias, bs->stats, s);
   mark_phase(1, s);
   return device_status();
 }
@@ -494,12 +507,12 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
 // input (not checked against the workspace for overlap).
 moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
                         const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
-                        const void* resid, bool x_in_ws) {
+                        const void* resid, bool x_in_ws, const BiasStep* bs = nullptr) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (!w || !routing) return MOE_E_ARG;
   if (dims->w_routed == MOE_INT4_G128)
-    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws);
+    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws, nullptr, 0.f, bs);
   const moe_dims& d = *dims;
   if (training && check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
   const size_t es = act_bytes(d.act);
@@ -510,9 +523,10 @@ moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* 
                            {w->w_down, E * D * F * es, false},
                            {w->w_sh_gate_up, 2 * Fs * D * es, false},
                            {w->w_sh_down, D * Fs * es, false},
-                           {bias, E * 4, false},
+                           {bias, E * 4, bs != nullptr},
                            {y, (size_t)d.T * D * es, true}};
   if (resid) rs.push_back({resid, (size_t)d.T * D * es, false});
+  if (bs && bs->stats) rs.push_back({bs->stats, 4 * 4, true});
   if (x_in_ws) rs.erase(rs.begin());
   add_routing_ranges(rs, d, routing);
   if (null_with_size(rs)) return MOE_E_ARG;
@@ -522,7 +536,7 @@ moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* 
   if (any_alias(rs)) return MOE_E_ALIAS;
 
   mark_phase(0, s);
-  enqueue_route(d, L, x, w->w_router, bias, routing, ws, s);
+  enqueue_route(d, L, x, w->w_router, bias, routing, ws, s, bs);
   mark_phase(1, s);
   if (d.T == 0) return device_status();
 
@@ -537,6 +551,15 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, void* stream) {
   return forward_core(dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
                       nullptr, false);
+}
+
+moe_status moe_forward_bias_step(const moe_dims* dims, const void* x, const moe_weights* w, float* bias, float gamma,
+                                 float* stats, void* y, const moe_routing* routing, int training, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!bias) return MOE_E_ARG;
+  const BiasStep bs{gamma, bias, stats};
+  return forward_core(dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                      nullptr, false, &bs);
 }
 
 moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* norm_weight, float eps,

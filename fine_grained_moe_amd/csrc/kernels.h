@@ -33,9 +33,12 @@ struct TileTable {
 void launch_route_topk(int act, const void* x, const void* w_router, const float* bias, int T, int d, int E,
                        int k, int32_t* idx, float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s);
 // tiles: kTileM rows per entry; tiles_fwd: kTileMFwd rows (may be null).
+// bias (may be null): once the loads are known, the bias step with gamma on
+// bias (in place) and, if stats is not null, the balance figures (as
+// launch_bias_update with total T * k).
 void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
                            int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
-                           int32_t* perm, int32_t* pos, hipStream_t s);
+                           int32_t* perm, int32_t* pos, float gamma, float* bias, float* stats, hipStream_t s);
 // stats (may be null): [4] expert-balance figures of the batch
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, float* stats,
                         hipStream_t s);

@@ -281,6 +281,49 @@ __device__ __forceinline__ void write_tiles(TileTable t, int tm, int cnt, int e)
   }
   if (e == 63) *t.count = tincl;
 }
+// The bias step of one wave, lane e holding expert e's load c (0 for e >= E):
+// bias[e] <- fl32(bias[e] + gamma * sign(total - E * c)), and with stats the
+// batch's balance figures, stats = [experts with zero load / E, max load * E /
+// total, load entropy -sum p ln p (p = load / total, 0 ln 0 = 0), entropy /
+// ln E (1 for E = 1)]; an empty batch reads (1, 0, 0, 0).  ("Relay training"
+// section: a low dead-expert fraction under aux-loss-free balancing, expert
+// balance on the dashboard.)  The sums and the maximum are butterfly
+// reductions in a fixed order.  Used by the bias kernel and by the dispatch
+// kernel's fused step, so both give the same bits.
+__device__ __forceinline__ void bias_step_wave(int e, int E, long long total, int c, float gamma,
+                                               float* __restrict__ bias, float* __restrict__ stats) {
+  if (e < E) {
+    const long long diff = total - (long long)E * (long long)c;
+    const float sg = (float)((diff > 0) - (diff < 0));
+    bias[e] = __fadd_rn(bias[e], gamma * sg);
+  }
+  if (!stats) return;
+  int dead = (e < E && c == 0) ? 1 : 0;
+  int mx = c;
+  float h = 0.f;
+  if (c > 0 && total > 0) {
+    const float pr = (float)c / (float)total;
+    h = -pr * logf(pr);
+  }
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    dead += __shfl_xor(dead, off);
+    mx = max(mx, __shfl_xor(mx, off));
+    h += __shfl_xor(h, off);
+  }
+  if (e == 0) {
+    if (total <= 0) {
+      stats[0] = 1.f;
+      stats[1] = stats[2] = stats[3] = 0.f;
+    } else {
+      stats[0] = (float)dead / (float)E;
+      stats[1] = (float)((double)mx * E / (double)total);
+      stats[2] = h;
+      stats[3] = E > 1 ? h / logf((float)E) : 1.f;
+    }
+  }
+}
+
 constexpr int kDispatchBatch = 16;   // count loads a thread keeps in flight
 __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __restrict__ block_counts,
                                                               const int32_t* __restrict__ idx,
@@ -288,7 +331,9 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
                                                               int E, int k, int32_t* __restrict__ counts,
                                                               int32_t* __restrict__ offsets,
                                                               TileTable tiles, TileTable tiles_fwd,
-                                                              int32_t* __restrict__ perm, int32_t* __restrict__ pos) {
+                                                              int32_t* __restrict__ perm, int32_t* __restrict__ pos,
+                                                              float gamma, float* __restrict__ bias,
+                                                              float* __restrict__ stats) {
   __shared__ int part_tot[16][64];
   __shared__ int part_pre[16][64];
   __shared__ int sub_cnt[kDispatchSub][64];
@@ -344,6 +389,8 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
       if (e == E - 1) offsets[E] = incl;
       write_tiles(tiles, kTileM, cnt, e);
       if (tiles_fwd.e) write_tiles(tiles_fwd, kTileMFwd, cnt, e);
+      // the fused bias step: the router has read the bias (it ran before this launch)
+      if (bias) bias_step_wave(e, E, (long long)T_ * k, cnt, gamma, bias, stats);
     }
   }
   __syncthreads();
@@ -372,47 +419,14 @@ __global__ void bias_update_kernel(int E, long long total, const int32_t* __rest
 }
 
 // ---------------------------------------------------------------------------
-// The bias step plus the batch's expert-balance telemetry ("Relay training"
-// section: a low dead-expert fraction, expert balance on the dashboard):
-// stats = [experts with zero load / E, max load * E / total, load entropy
-// -sum p ln p (p = load / total, 0 ln 0 = 0), entropy / ln E (1 for E = 1)];
-// an empty batch reads (1, 0, 0, 0).  One wave, lane e for expert e; the sums
-// and the maximum are butterfly reductions in a fixed order.
+// The bias step plus the batch's expert-balance telemetry (bias_step_wave).
+// One wave, lane e for expert e.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(64) void bias_update_stats_kernel(int E, long long total,
                                                                const int32_t* __restrict__ counts, float gamma,
                                                                float* __restrict__ bias, float* __restrict__ stats) {
   const int e = threadIdx.x;
-  const int c = e < E ? counts[e] : 0;
-  if (e < E) {
-    const long long diff = total - (long long)E * (long long)c;
-    const float sg = (float)((diff > 0) - (diff < 0));
-    bias[e] = __fadd_rn(bias[e], gamma * sg);
-  }
-  int dead = (e < E && c == 0) ? 1 : 0;
-  int mx = c;
-  float h = 0.f;
-  if (c > 0 && total > 0) {
-    const float pr = (float)c / (float)total;
-    h = -pr * logf(pr);
-  }
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    dead += __shfl_xor(dead, off);
-    mx = max(mx, __shfl_xor(mx, off));
-    h += __shfl_xor(h, off);
-  }
-  if (e == 0) {
-    if (total <= 0) {
-      stats[0] = 1.f;
-      stats[1] = stats[2] = stats[3] = 0.f;
-    } else {
-      stats[0] = (float)dead / (float)E;
-      stats[1] = (float)((double)mx * E / (double)total);
-      stats[2] = h;
-      stats[3] = E > 1 ? h / logf((float)E) : 1.f;
-    }
-  }
+  bias_step_wave(e, E, total, e < E ? counts[e] : 0, gamma, bias, stats);
 }
 
 template <typename A, int K>
@@ -453,10 +467,10 @@ void launch_route_topk(int act, const void* x, const void* w_router, const float
 
 void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
                            int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
-                           int32_t* perm, int32_t* pos, hipStream_t s) {
+                           int32_t* perm, int32_t* pos, float gamma, float* bias, float* stats, hipStream_t s) {
   const int grid = nblk > 0 ? (nblk + kDispatchSub - 1) / kDispatchSub : 1;   // block 0 runs even for T = 0
   hipLaunchKernelGGL(route_dispatch_kernel, dim3(grid), dim3(1024), 0, s, block_counts, idx, rank, nblk, T, E, k,
-                     counts, offsets, tiles, tiles_fwd, perm, pos);
+                     counts, offsets, tiles, tiles_fwd, perm, pos, gamma, bias, stats);
 }
 
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, float* stats,

@@ -6,8 +6,8 @@ this module loads the library and raises if it is missing; there is no other
 implementation to fall back to.
 
 The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
-moe_forward_block, moe_bias_update, moe_bias_update_stats, moe_backward,
-moe_quantize_int4, moe_status_str.  Weights, routing buffers and
+moe_forward_bias_step, moe_forward_block, moe_bias_update, moe_bias_update_stats,
+moe_backward, moe_quantize_int4, moe_status_str.  Weights, routing buffers and
 gradients are passed as dicts of torch tensors keyed by the C field names.
 """
 from __future__ import annotations
@@ -76,6 +76,9 @@ def _load() -> ctypes.CDLL:
     lib.moe_backward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeRouting), P, P,
                                  ctypes.POINTER(MoeGrads), P, SZ, P]
     lib.moe_backward.restype = ctypes.c_int
+    lib.moe_forward_bias_step.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, ctypes.c_float, P, P,
+                                          ctypes.POINTER(MoeRouting), ctypes.c_int, P, SZ, P]
+    lib.moe_forward_bias_step.restype = ctypes.c_int
     lib.moe_quantize_int4.argtypes = [I32, P, I64, I32, P, P, P]
     lib.moe_quantize_int4.restype = ctypes.c_int
     lib.moe_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
@@ -141,6 +144,17 @@ def moe_forward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y, rou
     _check(LIB.moe_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), _ptr(y), ctypes.byref(r),
                            int(bool(training)), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_bias_step(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, gamma: float, stats, y,
+                          routing: Dict[str, torch.Tensor], ws, training: bool = False, stream=None) -> None:
+    """moe_forward with bias, then the bias step on bias (in place) and, with a
+    stats tensor (float32, >= 4 elements; None skips it), the balance figures."""
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_forward_bias_step(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), float(gamma),
+                                     _ptr(stats), _ptr(y), ctypes.byref(r), int(bool(training)), _ptr(ws),
+                                     ws.numel() * ws.element_size(), _stream(stream)), "moe_forward_bias_step")
 
 
 def moe_forward_block(dims: MoeDims, h, norm_weight, eps: float, weights: Dict[str, torch.Tensor], bias, h_out,

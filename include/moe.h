@@ -131,6 +131,25 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
                        void* y, const moe_routing* routing, int training,
                        void* ws, size_t ws_bytes, void* stream);
 
+/* One training step's forward and bias step in one call (architecture
+ * paragraph: the expert bias is nudged after each batch; the "Relay
+ * training" section's top-2 paragraph watches the dead-expert fraction):
+ * moe_forward with the current bias, then
+ *   bias[e] <- fl32(bias[e] + gamma * sign(T*k - E * counts[e]))
+ * and, when stats is not NULL, stats[0..3] = the balance figures of
+ * moe_bias_update_stats.  The same results, bit for bit, as moe_forward
+ * followed by moe_bias_update_stats (moe_bias_update when stats is NULL),
+ * with one launch fewer where routing has a dispatch launch (every path but
+ * the int4 decode, where the bias step stays a launch of its own).
+ *  bias   [E] float32 (device), read by the router, then updated in place;
+ *         must not be NULL (MOE_E_ARG)
+ *  stats  [4] float32 (device, written) or NULL
+ * bias and stats may overlap no other argument (MOE_E_ALIAS).  The other
+ * arguments, shapes and statuses are moe_forward's. */
+moe_status moe_forward_bias_step(const moe_dims* dims, const void* x, const moe_weights* w, float* bias,
+                                 float gamma, float* stats, void* y, const moe_routing* routing, int training,
+                                 void* ws, size_t ws_bytes, void* stream);
+
 /* The MoE block around the layer, as the architecture paragraph places the
  * layer in 23 of the model's 24 transformer layers (pre-norm and residual:
  * this library's reading):

@@ -29,7 +29,8 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
-                                           "moe_quantize_int4", "moe_status_str", "moe_set_phase_events"])
+                                           "moe_quantize_int4", "moe_forward_bias_step", "moe_status_str",
+                                           "moe_set_phase_events"])
 
 
 def test_library_exports_every_declared_symbol(lib):
@@ -109,6 +110,26 @@ def test_route_host_checks(lib):
                              need - 1, None) == lib.MOE_E_WORKSPACE
     assert lib.LIB.moe_route(ctypes.byref(dims), 0x1000, 0x20000, 0x30000, None, 0x90000000, need,
                              None) == lib.MOE_E_ARG
+
+
+def test_forward_bias_step_host_checks(lib):
+    """moe_forward_bias_step rejects a null bias, and a bias or stats that
+    overlaps another argument, before any launch."""
+    dims = lib.make_dims(16, 128, 8, 64, 256, 2, "bf16")
+    need = lib.moe_workspace_bytes(dims)
+    W = lib.MoeWeights(0x100000, 0x200000, 0x300000, None, None, 0x400000, 0x500000)
+    R = lib.MoeRouting(*[0x40000000 + i * 0x1000000 for i in range(6)])
+    f = lib.LIB.moe_forward_bias_step
+    x, y, ws = 0x1000, 0x8000, 0x90000000
+    ok = (ctypes.byref(dims), x, ctypes.byref(W))
+    assert f(*ok, None, 1e-3, None, y, ctypes.byref(R), 0, ws, need, None) == lib.MOE_E_ARG
+    # the bias inside x (x is 16 x 128 bf16 = 4 KiB from 0x1000)
+    assert f(*ok, 0x1100, 1e-3, None, y, ctypes.byref(R), 0, ws, need, None) == lib.MOE_E_ALIAS
+    # stats inside the bias
+    assert f(*ok, 0x20000, 1e-3, 0x20004, y, ctypes.byref(R), 0, ws, need, None) == lib.MOE_E_ALIAS
+    # stats inside the workspace
+    assert f(*ok, 0x20000, 1e-3, ws + 64, y, ctypes.byref(R), 0, ws, need, None) == lib.MOE_E_ALIAS
+    assert f(*ok, 0x20000, 1e-3, None, y, ctypes.byref(R), 0, ws, need - 1, None) == lib.MOE_E_WORKSPACE
 
 
 def test_quantize_int4_host_checks(lib):

@@ -108,3 +108,71 @@ def test_ten_step_balancing_loop_without_host_sync():
         _check_stats(got[step], counts, total)
     print(f"zipf balance, step 0: {got[0].tolist()}, step 9: {got[9].tolist()}", flush=True)
     assert got[0][1] > 10.0            # the hottest expert holds ~20% of assignments: ~13x the mean
+
+
+def _fused_vs_separate(dims, x, w, b0, with_stats=True):
+    """moe_forward + moe_bias_update_stats against moe_forward_bias_step from
+    the same bias: y, routing, the new bias and the figures bit for bit."""
+    import torch
+    from fine_grained_moe_amd import moe
+    T, E, k = dims.T, dims.E, dims.k
+    outs = []
+    for fused in (False, True):
+        bias = b0.clone()
+        y = torch.empty_like(x)
+        r = moe.alloc_routing(dims)
+        ws = moe.alloc_workspace(dims)
+        st = torch.full((4,), -7.0, device="cuda") if with_stats else None
+        if fused:
+            moe.moe_forward_bias_step(dims, x, w, bias, GAMMA, st, y, r, ws)
+        else:
+            moe.moe_forward(dims, x, w, bias, y, r, ws)
+            if with_stats:
+                moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, st)
+            else:
+                moe.moe_bias_update(E, T * k, r["counts"], GAMMA, bias)
+        torch.cuda.synchronize()
+        outs.append((y, r, bias, st))
+    (y0, r0, b_0, s0), (y1, r1, b_1, s1) = outs
+    assert torch.equal(y0, y1)
+    for n in r0:
+        assert torch.equal(r0[n], r1[n]), n
+    assert torch.equal(b_0.view(torch.int32), b_1.view(torch.int32))
+    assert not torch.equal(b_1, b0) or T == 0
+    if with_stats:
+        assert torch.equal(s0.view(torch.int32), s1.view(torch.int32))
+        _check_stats(s1.cpu().numpy(), r1["counts"].cpu().numpy(), T * k)
+    return r1
+
+
+@pytest.mark.parametrize("case", ["layer_t4096", "tiny_f32", "empty", "no_stats"])
+def test_fused_bias_step_bitwise(case):
+    import torch
+    from fine_grained_moe_amd import moe
+    name = "tiny_f32" if case == "tiny_f32" else "layer_t4096"
+    T = 0 if case == "empty" else (1500 if case == "no_stats" else None)
+    inp = synth.make_workload(name, T=T) if T is not None else synth.make_workload(name)
+    x, w = H.to_gpu(inp)
+    dims = moe.make_dims(inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k, inp.act)
+    b0 = torch.from_numpy(np.linspace(-0.01, 0.01, inp.E).astype(np.float32)).cuda()
+    _fused_vs_separate(dims, x, w, b0, with_stats=case != "no_stats")
+
+
+@pytest.mark.parametrize("T", [8, 300])
+def test_fused_bias_step_int4(T):
+    """The int4 top-1 layer: the decode (T <= 64: the bias step stays a launch
+    of its own) and the prefill (the dispatch launch takes it)."""
+    import torch
+    from fine_grained_moe_amd import moe
+    base = synth.make_layer(T=T, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=77)
+    qg, sg = om.quantize_int4(base.w_gate_up)
+    qd, sd = om.quantize_int4(base.w_down)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+
+    w = dict(w_router=bf(base.w_router), w_gate_up=torch.from_numpy(qg).cuda(), s_gate_up=bf(sg),
+             w_down=torch.from_numpy(qd).cuda(), s_down=bf(sd), w_sh_gate_up=bf(base.w_sh_gate_up),
+             w_sh_down=bf(base.w_sh_down))
+    dims = moe.make_dims(T, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+    _fused_vs_separate(dims, bf(base.x), w, torch.zeros(64, device="cuda"))
