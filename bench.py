@@ -453,6 +453,84 @@ def bench_int4(moe, synth, torch, np, reps=20, steps=50, warmup=5, n_sets=8):
     return out
 
 
+def bench_stream(moe, synth, torch, np, steps=200, warmup=30):
+    """Expert streaming for int4 top-1 serving: the LRU expert cache over a few
+    HBM slots, filled from pinned host memory, against all experts resident.
+    A step serves one batch of fresh tokens: moe_route, the loads copied to the
+    host, moe_cache_prepare (the misses' int4 arrays copied host -> slot), then
+    moe_forward_cached; eager launches, timed on the host clock.  Routing:
+    uniform (no bias) and skewed (bias_e = -0.1 ln(1 + e), favouring the low
+    experts).  Weights: N(0, 0.02) draws, int4-encoded by the library."""
+    E, d, F, Fs = 64, 1024, 512, 2048
+    inp = synth.make_layer(T=1, d=d, E=E, F=F, Fs=Fs, k=1, act="bf16", seed=9)
+    bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
+    wgu, wd = bf(inp.w_gate_up), bf(inp.w_down)
+    full = dict(w_router=bf(inp.w_router), w_sh_gate_up=bf(inp.w_sh_gate_up), w_sh_down=bf(inp.w_sh_down),
+                w_gate_up=torch.empty(E, 2 * F, d // 2, dtype=torch.uint8, device="cuda"),
+                s_gate_up=torch.empty(E, 2 * F, d // 128, dtype=torch.bfloat16, device="cuda"),
+                w_down=torch.empty(E, d, F // 2, dtype=torch.uint8, device="cuda"),
+                s_down=torch.empty(E, d, F // 128, dtype=torch.bfloat16, device="cuda"))
+    moe.moe_quantize_int4(wgu, full["w_gate_up"], full["s_gate_up"])
+    moe.moe_quantize_int4(wd, full["w_down"], full["s_down"])
+    del wgu, wd
+    int4 = ("w_gate_up", "s_gate_up", "w_down", "s_down")
+    pinned = {n: full[n].cpu().pin_memory() for n in int4}
+    per_expert = sum(pinned[n][0].numel() * pinned[n].element_size() for n in int4)
+    out = dict(bytes_per_expert=per_expert, cases=[])
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(77)
+    for T in (1, 8):
+        dims = moe.make_dims(T, d, E, F, Fs, 1, "bf16", w_routed="int4")
+        xs = (torch.randn(warmup + steps, T, d, generator=gen, device="cuda")).to(torch.bfloat16)
+        r = moe.alloc_routing(dims)
+        ws = moe.alloc_workspace(dims)
+        y = torch.empty(T, d, dtype=torch.bfloat16, device="cuda")
+        for skew in (0.0, 0.1):
+            bias = (-skew * torch.log1p(torch.arange(E, dtype=torch.float32, device="cuda"))).contiguous()
+            # all experts resident
+            for i in range(warmup):
+                moe.moe_forward(dims, xs[i], full, bias, y, r, ws)
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for i in range(steps):
+                moe.moe_forward(dims, xs[warmup + i], full, bias, y, r, ws)
+            torch.cuda.synchronize()
+            us_res = (time.perf_counter() - t0) / steps * 1e6
+            for n_slots in (8, 16, 32, 64):
+                dev = {n: torch.zeros((n_slots,) + tuple(pinned[n].shape[1:]), dtype=pinned[n].dtype,
+                                      device="cuda") for n in int4}
+                slot = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+                cache = moe.ExpertCache(dims, n_slots, host=pinned, dev=dev, slot=slot)
+                cache.state()
+                out["fill"] = "one launch reading the pinned host copy" if cache.zero_copy else "hipMemcpyAsync per array"
+                w = dict(full)
+                w.update(dev)
+                nmiss, active = 0, 0
+                t0 = 0.0
+                for i in range(warmup + steps):
+                    if i == warmup:
+                        torch.cuda.synchronize()
+                        t0 = time.perf_counter()
+                        nmiss, active = 0, 0
+                    moe.moe_route(dims, xs[i], full["w_router"], bias, r, ws)
+                    counts = r["counts"].cpu().numpy()
+                    nmiss += cache.prepare(counts)
+                    active += int(np.count_nonzero(counts))
+                    moe.moe_forward_cached(dims, xs[i], w, slot, n_slots, bias, y, r, ws)
+                torch.cuda.synchronize()
+                us = (time.perf_counter() - t0) / steps * 1e6
+                cache.close()
+                case = dict(T=T, skew=skew, n_slots=n_slots, us_per_step=round(us, 1), us_all_resident=round(us_res, 1),
+                            misses_per_step=round(nmiss / steps, 3), miss_rate=round(nmiss / max(active, 1), 4),
+                            h2d_mb_per_step=round(nmiss * per_expert / steps / 1e6, 3), tokens_per_s=T / (us * 1e-6))
+                out["cases"].append(case)
+                log(f"stream T={T} skew={skew} slots={n_slots}: {us:.1f} us/step (all resident {us_res:.1f}), "
+                    f"{nmiss / steps:.2f} misses/step ({100 * nmiss / max(active, 1):.1f}% of active experts), "
+                    f"{nmiss * per_expert / steps / 1e6:.2f} MB/step host->device")
+                del dev, slot, w
+    return out
+
+
 def bench_train(moe, synth, torch, np, steps=10, warmup=3):
     """One training step of the layer at T = 32768 (16 x 2048): forward with
     saved activations, backward (dx and every weight gradient), bias step."""
@@ -566,7 +644,8 @@ def main() -> int:
     ap.add_argument("--no-stack", action="store_true")
     ap.add_argument("--no-zipf", action="store_true")
     ap.add_argument("--no-int4", action="store_true")
-    ap.add_argument("--leg", choices=("decode", "train", "stack", "zipf", "int4"),
+    ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--leg", choices=("decode", "train", "stack", "zipf", "int4", "stream"),
                     help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (for scaling hardware byte counters)")
@@ -589,7 +668,7 @@ def main() -> int:
     torch.cuda.set_device(0)
     if args.leg is not None:
         fn = {"decode": bench_decode, "train": bench_train, "stack": bench_stack, "zipf": bench_zipf,
-              "int4": bench_int4}[args.leg]
+              "int4": bench_int4, "stream": bench_stream}[args.leg]
         print(json.dumps({args.leg: fn(moe, synth, torch, np)}), flush=True)
         return 0
     inp = synth.make_workload("layer_t4096", seed=0)
@@ -704,6 +783,8 @@ def main() -> int:
         out["zipf"] = bench_zipf(moe, synth, torch, np)
     if not args.no_int4:
         out["int4"] = bench_int4(moe, synth, torch, np)
+    if not args.no_stream:
+        out["stream"] = bench_stream(moe, synth, torch, np)
 
     if not args.no_cpu_baseline:
         log(f"CPU oracle baseline (~{args.cpu_seconds:.0f} s)")

@@ -422,21 +422,26 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
 moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, const float* bias, void* y,
                         const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
                         const void* resid = nullptr, bool x_in_ws = false, const float* gamma = nullptr,
-                        float eps = 0.f, const BiasStep* bs = nullptr) {
+                        float eps = 0.f, const BiasStep* bs = nullptr, const int32_t* slot = nullptr,
+                        int n_slots = 0) {
   if (training) return MOE_E_UNSUPPORTED;
+  // expert streaming (slot table): the decode path only
+  if (slot && d.T > kDecodeMaxT) return MOE_E_UNSUPPORTED;
   const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
+  const size_t EW = slot ? (size_t)n_slots : E;   // expert weight blocks held
   std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
                            {w->w_router, E * D * 2, false},
-                           {w->w_gate_up, E * 2 * F * D / 2, false},
-                           {w->s_gate_up, E * 2 * F * (D / 128) * 2, false},
-                           {w->w_down, E * D * F / 2, false},
-                           {w->s_down, E * D * (F / 128) * 2, false},
+                           {w->w_gate_up, EW * 2 * F * D / 2, false},
+                           {w->s_gate_up, EW * 2 * F * (D / 128) * 2, false},
+                           {w->w_down, EW * D * F / 2, false},
+                           {w->s_down, EW * D * (F / 128) * 2, false},
                            {w->w_sh_gate_up, 2 * Fs * D * 2, false},
                            {w->w_sh_down, D * Fs * 2, false},
                            {bias, E * 4, bs != nullptr},
                            {y, (size_t)d.T * D * 2, true}};
   if (resid) rs.push_back({resid, (size_t)d.T * D * 2, false});
   if (bs && bs->stats) rs.push_back({bs->stats, 4 * 4, true});
+  if (slot) rs.push_back({slot, E * 4, false});
   if (x_in_ws) rs.erase(rs.begin());             // x lives in the workspace (the block's normalised input)
   add_routing_ranges(rs, d, routing);
   if (null_with_size(rs)) return MOE_E_ARG;
@@ -493,6 +498,8 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.gamma = gamma;
   a.eps = eps;
   a.xn = at<uint16_t>(ws, L.xb);
+  a.slot = slot;
+  a.n_slots = n_slots;
   mark_phase(0, s);
   launch_decode(a, s);
   // the decode's launches hold no point where all loads are known before the
@@ -560,6 +567,18 @@ moe_status moe_forward_bias_step(const moe_dims* dims, const void* x, const moe_
   const BiasStep bs{gamma, bias, stats};
   return forward_core(dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
                       nullptr, false, &bs);
+}
+
+moe_status moe_forward_cached(const moe_dims* dims, const void* x, const moe_weights* w, const int32_t* slot,
+                              int32_t n_slots, const float* bias, void* y, const moe_routing* routing, void* ws,
+                              size_t ws_bytes, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  if (!w || !routing || !slot) return MOE_E_ARG;
+  if (n_slots < 1 || n_slots > dims->E) return MOE_E_ARG;
+  if (dims->w_routed != MOE_INT4_G128 || dims->T > kDecodeMaxT) return MOE_E_UNSUPPORTED;
+  return forward_int4(*dims, x, w, bias, y, routing, 0, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                      nullptr, false, nullptr, 0.f, nullptr, slot, n_slots);
 }
 
 moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* norm_weight, float eps,

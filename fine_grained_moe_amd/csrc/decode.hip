@@ -460,6 +460,15 @@ __device__ void decode_shared_down(const DecodeArgs& p, int j, int tt, float* ld
   }
 }
 
+// Where expert e's int4 weights sit: its own index, or with expert
+// streaming the slot the cache gave it (clamped, so a stale table cannot
+// address outside the slots).
+__device__ __forceinline__ int weight_slot(const DecodeArgs& p, int e) {
+  if (!p.slot) return e;
+  const int s = p.slot[e];
+  return s < 0 ? 0 : (s >= p.n_slots ? p.n_slots - 1 : s);
+}
+
 template <int D, int FR>
 __device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds, Book& B) {
   decode_book(p, B);
@@ -469,7 +478,7 @@ __device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds,
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
   const int e = B.act_e[a], s0 = B.act_s0[a], n = B.act_n[a];
-  const long long rg = (long long)e * 2 * FR + fb * 16 + fr, ru = rg + FR;
+  const long long rg = (long long)weight_slot(p, e) * 2 * FR + fb * 16 + fr, ru = rg + FR;
   const int qofs = wave * (D / 8) + g * 16;          // bytes into a packed row
   u32x4_t wg[2], wu[2];
 #pragma unroll
@@ -572,7 +581,7 @@ __global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
   float sc[2];
 #pragma unroll
   for (int tile = 0; tile < 2; ++tile) {
-    const long long r = (long long)e * D + cb * 32 + tile * 16 + fr;
+    const long long r = (long long)weight_slot(p, e) * D + cb * 32 + tile * 16 + fr;
     wq[tile] = ld16(p.q_down + r * (FR / 2) + wave * 64 + g * 16);
     sc[tile] = bf16_to_f32(p.s_down[r * (FR / kGroup) + wave]);
   }

@@ -152,6 +152,10 @@ struct DecodeArgs {
   const float* gamma;                // [d] float32, or null
   float eps;
   uint16_t* xn;                      // [T, d] bf16 (workspace)
+  // Expert streaming: the routed weights above hold n_slots slots, and expert
+  // e's weights sit in slot slot[e] (clamped to the slots), or null: slot e.
+  const int32_t* slot;               // [E] int32, or null
+  int n_slots;
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);
 

@@ -7,7 +7,8 @@ implementation to fall back to.
 
 The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
 moe_forward_bias_step, moe_forward_block, moe_bias_update, moe_bias_update_stats,
-moe_backward, moe_quantize_int4, moe_status_str.  Weights, routing buffers and
+moe_backward, moe_quantize_int4, moe_forward_cached, moe_cache_create, moe_cache_prepare,
+moe_cache_state, moe_cache_destroy, moe_status_str.  Weights, routing buffers and
 gradients are passed as dicts of torch tensors keyed by the C field names.
 """
 from __future__ import annotations
@@ -79,6 +80,18 @@ def _load() -> ctypes.CDLL:
     lib.moe_forward_bias_step.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, ctypes.c_float, P, P,
                                           ctypes.POINTER(MoeRouting), ctypes.c_int, P, SZ, P]
     lib.moe_forward_bias_step.restype = ctypes.c_int
+    lib.moe_forward_cached.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, I32, P, P,
+                                       ctypes.POINTER(MoeRouting), P, SZ, P]
+    lib.moe_forward_cached.restype = ctypes.c_int
+    lib.moe_cache_create.argtypes = [dims_p, I32, ctypes.POINTER(MoeWeights), ctypes.POINTER(MoeWeights), P, I32,
+                                     ctypes.POINTER(ctypes.c_void_p)]
+    lib.moe_cache_create.restype = ctypes.c_int
+    lib.moe_cache_prepare.argtypes = [P, P, P, ctypes.POINTER(I32)]
+    lib.moe_cache_prepare.restype = ctypes.c_int
+    lib.moe_cache_state.argtypes = [P, P, P]
+    lib.moe_cache_state.restype = ctypes.c_int
+    lib.moe_cache_destroy.argtypes = [P]
+    lib.moe_cache_destroy.restype = None
     lib.moe_quantize_int4.argtypes = [I32, P, I64, I32, P, P, P]
     lib.moe_quantize_int4.restype = ctypes.c_int
     lib.moe_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
@@ -116,6 +129,15 @@ def _stream(stream) -> int:
     if stream is None:
         stream = torch.cuda.current_stream()
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+def _host_ptr(t) -> Optional[int]:
+    """A pinned host tensor (the expert cache's source of copies)."""
+    if t is None:
+        return None
+    if not isinstance(t, torch.Tensor) or t.device.type != "cpu" or not t.is_contiguous() or not t.is_pinned():
+        raise ValueError("the expert cache's host copy must be contiguous pinned CPU tensors")
+    return t.data_ptr()
 
 
 def _struct(cls, fields, tensors: Dict[str, torch.Tensor]):
@@ -190,6 +212,61 @@ def moe_quantize_int4(w, packed, scales, stream=None) -> None:
         raise MoeError(MOE_E_ARG, "moe_quantize_int4")
     _check(LIB.moe_quantize_int4(dt, _ptr(w), rows, K, _ptr(packed), _ptr(scales), _stream(stream)),
            "moe_quantize_int4")
+
+
+def moe_forward_cached(dims: MoeDims, x, weights: Dict[str, torch.Tensor], slot, n_slots: int, bias, y,
+                       routing: Dict[str, torch.Tensor], ws, stream=None) -> None:
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_forward_cached(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(slot), int(n_slots), _ptr(bias),
+                                  _ptr(y), ctypes.byref(r), _ptr(ws), ws.numel() * ws.element_size(),
+                                  _stream(stream)), "moe_forward_cached")
+
+
+class ExpertCache:
+    """The library's LRU expert cache (moe_cache_*).  host: dict of pinned CPU
+    tensors (int4 fields of all E experts); dev: dict of device tensors of
+    n_slots slots; slot: [E] int32 device tensor.  dry_run keeps only the
+    bookkeeping.  The tensors must outlive the cache."""
+
+    def __init__(self, dims: MoeDims, n_slots: int, host=None, dev=None, slot=None, dry_run: bool = False):
+        self._keep = (host, dev, slot)
+        self.dry = bool(dry_run)
+        hw = MoeWeights(*[_host_ptr((host or {}).get(f)) for f in WEIGHT_FIELDS])
+        dw = _struct(MoeWeights, WEIGHT_FIELDS, dev or {})
+        h = ctypes.c_void_p()
+        _check(LIB.moe_cache_create(ctypes.byref(dims), int(n_slots), ctypes.byref(hw), ctypes.byref(dw),
+                                    _ptr(slot) if slot is not None else None, int(bool(dry_run)), ctypes.byref(h)),
+               "moe_cache_create")
+        self.handle = h
+        self.E = dims.E
+
+    def prepare(self, counts_host, stream=None) -> int:
+        import numpy as np
+        c = np.ascontiguousarray(np.asarray(counts_host, dtype=np.int32))
+        m = ctypes.c_int32(0)
+        _check(LIB.moe_cache_prepare(self.handle, c.ctypes.data, 0 if self.dry else _stream(stream), ctypes.byref(m)),
+               "moe_cache_prepare")
+        return m.value
+
+    def state(self):
+        import numpy as np
+        so = np.zeros(self.E, np.int32)
+        hm = np.zeros(3, np.int64)
+        _check(LIB.moe_cache_state(self.handle, so.ctypes.data, hm.ctypes.data), "moe_cache_state")
+        self.zero_copy = bool(hm[2])
+        return so, int(hm[0]), int(hm[1])
+
+    def close(self) -> None:
+        if self.handle:
+            LIB.moe_cache_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def moe_backward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], routing: Dict[str, torch.Tensor], dy, dx,

@@ -13,7 +13,9 @@
  *    `stream` has finished.
  *  - `stream` is a hipStream_t passed as void*; NULL is the default stream.
  *    Every call only enqueues work on it and returns: no synchronisation, no
- *    allocation, no host<->device copies.
+ *    allocation, no host<->device copies.  The one exception is the expert
+ *    cache (moe_cache_*), which keeps its own host bookkeeping and enqueues
+ *    host -> device fills of the experts it streams.
  *  - Arguments are checked on the host before anything is enqueued.  A failed
  *    check returns an error status and enqueues nothing.  MOE_E_DEVICE means a
  *    launch was rejected by the runtime (hipGetLastError after enqueueing).
@@ -124,9 +126,12 @@ moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, 
  * bias: [E] float32, read only (moe_bias_update changes it).  routing: filled
  * as by moe_route.  training = 1 stores in ws what moe_backward needs.
  * With w_routed = MOE_INT4_G128 this is the top-1 serving path (k = 1,
- * gate = 1, int4 experts dequantised inside the kernels), built for the
- * NanoColibri shape (d = 1024, F = 512, Fs = 2048) and T <= 64; other shapes
- * return MOE_E_UNSUPPORTED. */
+ * gate = 1).  Up to 64 tokens the int4 experts are dequantised inside the
+ * decode kernels, built for the NanoColibri shape (d = 1024, F = 512,
+ * Fs = 2048); above 64 tokens (the prefill) the experts that received tokens
+ * are dequantised to bf16 in the workspace (one rounding of q * scale) and
+ * run through the grouped GEMMs, for any shape with F % 128 == 0.  Other int4
+ * requests return MOE_E_UNSUPPORTED. */
 moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias,
                        void* y, const moe_routing* routing, int training,
                        void* ws, size_t ws_bytes, void* stream);
@@ -149,6 +154,56 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
 moe_status moe_forward_bias_step(const moe_dims* dims, const void* x, const moe_weights* w, float* bias,
                                  float gamma, float* stats, void* y, const moe_routing* routing, int training,
                                  void* ws, size_t ws_bytes, void* stream);
+
+/* Expert streaming (the opening section's proof-of-loop paragraph: a token
+ * touches the resident shared expert plus a couple of small routed experts
+ * streamed from larger storage).  moe_forward on the int4 top-1 decode path
+ * (w_routed = MOE_INT4_G128, T <= 64; else MOE_E_UNSUPPORTED) with the routed
+ * weights held in n_slots slots: w->w_gate_up, s_gate_up, w_down, s_down are
+ * [n_slots, ...] arrays in the moe_weights int4 layout, and expert e's
+ * weights are in slot slot[e].
+ *  slot     [E] int32 (device, read): every expert the batch routes to must
+ *           have its weights in the slot named (moe_cache_prepare arranges
+ *           it); entries are clamped to [0, n_slots), so a stale table gives
+ *           wrong rows, never an out-of-range read
+ *  n_slots  1 .. E (else MOE_E_ARG)
+ * Everything else is moe_forward's (no training). */
+moe_status moe_forward_cached(const moe_dims* dims, const void* x, const moe_weights* w, const int32_t* slot,
+                              int32_t n_slots, const float* bias, void* y, const moe_routing* routing,
+                              void* ws, size_t ws_bytes, void* stream);
+
+/* (host) The expert cache that fills those slots: least-recently-used
+ * replacement over n_slots slots, filled from a pinned host copy of all E
+ * experts.  Per step: moe_route, copy counts to the host, moe_cache_prepare,
+ * then moe_forward_cached on the same stream.
+ *  moe_cache_create: dims of the layer (int4 routed, E <= 64, d and F
+ *    multiples of 128); host: the int4 fields (w_gate_up, s_gate_up, w_down,
+ *    s_down) point to pinned host arrays of all E experts; dev: the same
+ *    fields point to device arrays of n_slots slots; dev_slot: [E] int32
+ *    device.  The caller owns all of them and keeps them alive.  dry_run = 1
+ *    keeps the bookkeeping only (no copies, no launches; pointers may be
+ *    NULL).  Starts empty.
+ *  moe_cache_prepare: host_counts [E] (host) = the batch's loads.  Experts
+ *    with a load that are resident are kept; each other one (in ascending
+ *    order) takes a free slot, else the slot whose last use is oldest among
+ *    those the batch does not need (lowest slot first among equals); its four
+ *    arrays are copied host -> slot on stream (one launch for all misses, or
+ *    hipMemcpyAsync calls: moe_cache_state), then the slot table is rewritten
+ *    by one small launch.  *misses (may be NULL) =
+ *    this step's misses.  More experts with a load than slots:
+ *    MOE_E_UNSUPPORTED, nothing changed.
+ *  moe_cache_state: slot_of [E] (host, may be NULL) = each expert's slot or
+ *    -1; hits_misses [3] (host, may be NULL) = hits and misses since
+ *    creation, then 1 if misses are filled by one launch that reads the host
+ *    copy in place (the runtime maps it at the same address on the device),
+ *    0 if by hipMemcpyAsync calls.
+ *  moe_cache_destroy: frees the bookkeeping (not the caller's buffers). */
+typedef struct moe_expert_cache moe_expert_cache;
+moe_status moe_cache_create(const moe_dims* dims, int32_t n_slots, const moe_weights* host, const moe_weights* dev,
+                            int32_t* dev_slot, int32_t dry_run, moe_expert_cache** out);
+moe_status moe_cache_prepare(moe_expert_cache* cache, const int32_t* host_counts, void* stream, int32_t* misses);
+moe_status moe_cache_state(const moe_expert_cache* cache, int32_t* slot_of, int64_t* hits_misses);
+void moe_cache_destroy(moe_expert_cache* cache);
 
 /* The MoE block around the layer, as the architecture paragraph places the
  * layer in 23 of the model's 24 transformer layers (pre-norm and residual:

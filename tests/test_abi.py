@@ -30,7 +30,8 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
                                            "moe_quantize_int4", "moe_forward_bias_step", "moe_status_str",
-                                           "moe_set_phase_events"])
+                                           "moe_set_phase_events", "moe_forward_cached", "moe_cache_create",
+                                           "moe_cache_prepare", "moe_cache_state", "moe_cache_destroy"])
 
 
 def test_library_exports_every_declared_symbol(lib):

@@ -1,0 +1,131 @@
+"""GPU parity of expert streaming (int4 top-1 serving): moe_forward_cached,
+which reads expert e's int4 weights from slot slot[e], gives the bits of
+moe_forward on the full expert arrays; and the LRU expert cache
+(moe_cache_prepare), filling a few slots from pinned host memory step by
+step, keeps those bits at every step of a stream of fresh batches.
+moe_forward itself is checked against the oracle in test_gpu_decode.py."""
+import numpy as np
+import pytest
+
+import oracle.moe_oracle as om
+from fine_grained_moe_amd import synth
+
+pytestmark = pytest.mark.gpu
+
+E, D, F, FS = 64, 1024, 512, 2048
+INT4 = ("w_gate_up", "s_gate_up", "w_down", "s_down")
+
+
+@pytest.fixture(scope="module")
+def layer():
+    import torch
+    base = synth.make_layer(T=1, d=D, E=E, F=F, Fs=FS, k=1, act="bf16", seed=61)
+    qg, sg = om.quantize_int4(base.w_gate_up)
+    qd, sd = om.quantize_int4(base.w_down)
+
+    def bf(a):
+        return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(dtype=torch.bfloat16)
+
+    host = dict(w_gate_up=torch.from_numpy(qg), s_gate_up=bf(sg), w_down=torch.from_numpy(qd), s_down=bf(sd))
+    full = {n: t.cuda() for n, t in host.items()}
+    full.update(w_router=bf(base.w_router).cuda(), w_sh_gate_up=bf(base.w_sh_gate_up).cuda(),
+                w_sh_down=bf(base.w_sh_down).cuda())
+    return base, host, full
+
+
+def _x(T, seed):
+    import torch
+    rng = np.random.default_rng(seed)
+    x = rng.standard_normal((T, D)).astype(np.float32)
+    x /= np.sqrt((x.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6).astype(np.float32)
+    return torch.from_numpy(synth.round_to_bf16(x)).to(device="cuda", dtype=torch.bfloat16)
+
+
+def _reference(dims, x, full, bias):
+    import torch
+    from fine_grained_moe_amd import moe
+    y = torch.empty_like(x)
+    r = moe.alloc_routing(dims)
+    moe.moe_forward(dims, x, full, bias, y, r, moe.alloc_workspace(dims))
+    return y, r
+
+
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_permuted_slots_give_the_same_bits(layer, T):
+    import torch
+    from fine_grained_moe_amd import moe
+    _, host, full = layer
+    dims = moe.make_dims(T, D, E, F, FS, 1, "bf16", w_routed="int4")
+    perm = np.random.default_rng(T).permutation(E).astype(np.int32)       # expert e -> slot perm[e]
+    slotted = dict(full)
+    for n in INT4:
+        t = torch.empty_like(full[n])
+        t[torch.from_numpy(perm).long().cuda()] = full[n]
+        slotted[n] = t
+    slot = torch.from_numpy(perm).cuda()
+    x = _x(T, 100 + T)
+    bias = torch.zeros(E, device="cuda")
+    y_ref, r_ref = _reference(dims, x, full, bias)
+    y = torch.empty_like(x)
+    r = moe.alloc_routing(dims)
+    moe.moe_forward_cached(dims, x, slotted, slot, E, bias, y, r, moe.alloc_workspace(dims))
+    torch.cuda.synchronize()
+    assert torch.equal(y, y_ref)
+    for n in r:
+        assert torch.equal(r[n], r_ref[n]), n
+
+
+def test_lru_stream_matches_the_full_layer(layer):
+    """12 slots for 64 experts, 8 tokens per step, 12 steps of fresh tokens."""
+    import torch
+    from fine_grained_moe_amd import moe
+    _, host, full = layer
+    T, n_slots = 8, 12
+    dims = moe.make_dims(T, D, E, F, FS, 1, "bf16", w_routed="int4")
+    pinned = {n: t.contiguous().pin_memory() for n, t in host.items()}
+    dev = {n: torch.empty((n_slots,) + tuple(t.shape[1:]), dtype=t.dtype, device="cuda") for n, t in host.items()}
+    for t in dev.values():
+        t.fill_(0)
+    slot = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    cache = moe.ExpertCache(dims, n_slots, host=pinned, dev=dev, slot=slot)
+    w = dict(full)
+    w.update(dev)
+    bias = torch.zeros(E, device="cuda")
+    ws = moe.alloc_workspace(dims)
+    r = moe.alloc_routing(dims)
+    total_misses = 0
+    for step in range(12):
+        x = _x(T, 500 + step)
+        moe.moe_route(dims, x, full["w_router"], bias, r, ws)
+        counts = r["counts"].cpu().numpy()
+        misses = cache.prepare(counts)
+        assert 0 <= misses <= np.count_nonzero(counts)
+        total_misses += misses
+        y = torch.empty_like(x)
+        r2 = moe.alloc_routing(dims)
+        moe.moe_forward_cached(dims, x, w, slot, n_slots, bias, y, r2, ws)
+        y_ref, r_ref = _reference(dims, x, full, bias)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), step
+        assert torch.equal(r2["idx"], r_ref["idx"]), step
+    so, hits, misses_all = cache.state()
+    assert misses_all == total_misses and hits + misses_all >= 12
+    print(f"lru stream: {misses_all} misses, {hits} hits over 12 steps with {n_slots} slots", flush=True)
+    cache.close()
+
+
+def test_more_experts_than_slots_is_refused(layer):
+    import torch
+    from fine_grained_moe_amd import moe
+    _, host, full = layer
+    T = 8
+    dims = moe.make_dims(T, D, E, F, FS, 1, "bf16", w_routed="int4")
+    pinned = {n: t.contiguous().pin_memory() for n, t in host.items()}
+    dev = {n: torch.zeros((2,) + tuple(t.shape[1:]), dtype=t.dtype, device="cuda") for n, t in host.items()}
+    slot = torch.full((E,), -1, dtype=torch.int32, device="cuda")
+    cache = moe.ExpertCache(dims, 2, host=pinned, dev=dev, slot=slot)
+    counts = np.zeros(E, np.int32)
+    counts[[1, 5, 9]] = 1
+    with pytest.raises(moe.MoeError):
+        cache.prepare(counts)
+    cache.close()
