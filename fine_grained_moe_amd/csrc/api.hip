@@ -853,6 +853,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   transpose(at<char>(ws, L.Hs), Fs, 0, HsT, Tp, 0, d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
 
   // 7. weight gradients, contracting over each expert's padded slot range
+  // (bf16: gemm_fwd.hip's 256 x 256 tiles with an fp32 store; fp32: gemm.hip)
   auto kjob = [&](const void* A, long long lda, const void* B, long long ldb, int M, int N, int nexp,
                   const int32_t* ko, const int32_t* kl, void* C, long long ldc, long long cstride) {
     GemmJob j{};
@@ -868,7 +869,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
     j.nexp = nexp;
     j.kofs = ko;
     j.klen = kl;
-    j.max_items = nexp * ((M + kTileM - 1) / kTileM);
+    j.max_items = nexp * ((M + tm - 1) / tm);
     j.C = C;
     j.ldc = ldc;
     j.c_estride = cstride;
@@ -882,7 +883,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   float* dwpart = at<float>(ws, L.dwpart);
   g3.job[1] = kjob(dAUsT, Tp, xT, Tp, 2 * d.Fs, d.d, S, ksh, ksh + S, S > 1 ? (void*)dwpart : dw->dw_sh_gate_up, D,
                    2LL * Fs * D);
-  launch_gemm(g3, s);
+  gemm_in(g3, s);
   if (S > 1) launch_splitk_reduce(dwpart, 2LL * Fs * D, S, (float*)dw->dw_sh_gate_up, s);
   GemmArgs g4{};
   g4.act = act;
@@ -890,7 +891,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   g4.job[0] = kjob(dOT, P, HT, P, d.d, d.F, d.E, kofs, klen, dw->dw_down, F, (long long)D * F);
   g4.job[1] = kjob(dyT, Tp, HsT, Tp, d.d, d.Fs, S, ksh, ksh + S, S > 1 ? (void*)dwpart : dw->dw_sh_down, Fs,
                    (long long)D * Fs);
-  launch_gemm(g4, s);
+  gemm_in(g4, s);
   if (S > 1) launch_splitk_reduce(dwpart, (long long)D * Fs, S, (float*)dw->dw_sh_down, s);
 
   // 8. router weight gradient and the input gradient

@@ -68,10 +68,14 @@ __device__ __host__ __forceinline__ int n_tiles(const GemmJob& j) {
 }
 // contraction slices of a dense job
 __device__ __host__ __forceinline__ int k_slices(const GemmJob& j) { return j.ksplit > 1 ? j.ksplit : 1; }
+// items: grouped jobs the router's tile table; per-expert-contraction jobs
+// (kgroup) every (expert, row block); dense jobs row blocks x contraction slices
 __device__ __forceinline__ int item_count(const GemmJob& j) {
+  if (j.kgroup) return j.nexp * ((j.M + BM - 1) / BM);
   return j.grouped ? *j.tile_count : (j.M + BM - 1) / BM * k_slices(j);
 }
 inline long long max_item_count(const GemmJob& j) {
+  if (j.kgroup) return (long long)j.nexp * ((j.M + BM - 1) / BM);
   return j.grouped ? j.max_items : (long long)(j.M + BM - 1) / BM * k_slices(j);
 }
 // XCD grid of a dense job: gc column groups (N-tile ranges) x 8 / gc row groups
@@ -99,7 +103,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   const int nbn = n_tiles(p);
   const int xcd = bid & 7, local = bid >> 3;
   int item, nt;
-  if (p.grouped) {
+  if (p.grouped || p.kgroup) {
     const int q = (count + 7) >> 3;
     const int pi = local / nbn;
     nt = local - pi * nbn;
@@ -121,6 +125,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     const int m0 = p.tile_m0[item];
     rows = p.counts[e] - m0;
     row_base = p.offsets[e] + m0;
+  } else if (p.kgroup) {
+    // (expert, row block): dense rows, the expert's own contraction range
+    const int nrb = (p.M + BM - 1) / BM;
+    e = item / nrb;
+    const int m0 = (item - e * nrb) * BM;
+    rows = p.M - m0;
+    row_base = m0;
   } else {
     // dense items: row blocks of contraction slice 0, then of slice 1, ...
     const int nrb = (p.M + BM - 1) / BM;
@@ -129,8 +140,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     rows = p.M - m0;
     row_base = m0;
   }
-  const int klen = p.K / k_slices(p);
-  const long long kofs = (long long)kz * klen;
+  const int klen = p.kgroup ? p.klen[e] : p.K / k_slices(p);
+  const long long kofs = p.kgroup ? (long long)p.kofs[e] : (long long)kz * klen;
   rows = rows < BM ? rows : BM;
   // this wave's 64-row band holds rows of the item
   const bool active = wm * WM < rows;
@@ -293,8 +304,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     }
     compute(s, fa0, fa1, A{}, std::false_type{}, std::false_type{});
   };
-  if (active) run(std::true_type{});
-  else run(std::false_type{});
+  // an expert with an empty contraction range (no tokens) stores zeros
+  if (nk > 0) {
+    if (active) run(std::true_type{});
+    else run(std::false_type{});
+  }
 
   // Row scales, staged in ring buffer 0 once every wave is past its last
   // read of the ring.
@@ -309,6 +323,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   // column, past the wave's base, is 8f + ni (f = lane % 16); for SwiGLU,
   // blocks ni < 4 are gate columns 4f + ni and ni >= 4 the matching up.
   T* C = reinterpret_cast<T*>(p.C) + kz * p.c_kstride;
+  float* const Cf = reinterpret_cast<float*>(p.C) + (long long)e * p.c_estride;   // EPI_STORE_F32 (kgroup)
   T* aux = reinterpret_cast<T*>(p.aux);
   const int n = nt * BN + wn * WN + NI * fr;               // first column of this lane (not SwiGLU)
   const int fh = nt * (BN / 2) + wn * (WN / 2) + HN * fr;  // first h column of this lane (SwiGLU)
@@ -360,6 +375,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
         }
         store_vec<T, NI>(C + row * p.ldc + n, da);
         store_vec<T, NI>(C + row * p.ldc + p.N + n, du);
+      } else if (p.epi == EPI_STORE_F32) {
+        float v[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) v[ni] = acc[mi][ni][i];
+        store_vec<float, NI>(Cf + row * p.ldc + n, v);
       } else {  // EPI_STORE
         float v[NI];
 #pragma unroll
@@ -373,16 +393,18 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
 // chunks of 8 blocks (one per XCD) a job needs: the blocks one XCD runs
 int job_chunks(const GemmJob& j) {
   const int nbn = n_tiles(j);
-  if (j.grouped) return (int)((max_item_count(j) + 7) / 8 * nbn);
+  if (j.grouped || j.kgroup) return (int)((max_item_count(j) + 7) / 8 * nbn);
   const int gc = xcd_cols(j), gr = 8 / gc;
   return (int)((max_item_count(j) + gr - 1) / gr * ((nbn + gc - 1) / gc));
 }
 
 }  // namespace
 
-// bf16 jobs only: epilogues SwiGLU, row scale, SwiGLU backward or plain
-// store, no per-expert contraction ranges, K / ksplit a multiple of 32
-// (checked by the caller); a split job's slices each write their own output.
+// bf16 operands only: epilogues SwiGLU, row scale, SwiGLU backward, plain
+// store (bf16) or fp32 store (the weight gradients, with per-expert
+// contraction ranges: klen[e] a multiple of 32, possibly 0); K / ksplit a
+// multiple of 32 (checked by the caller); a split job's slices each write
+// their own output.
 void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
   GemmArgs a = in;
   long long total = 0;

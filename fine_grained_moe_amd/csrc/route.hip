@@ -29,7 +29,6 @@ namespace fgmoe {
 // the dispatch kernel turns into the slot.
 // ---------------------------------------------------------------------------
 constexpr int kRouteWaves = 8;
-constexpr int kRouteMaxK = 8;
 
 __device__ __forceinline__ uint64_t route_key(float v, int e) {
   return ((uint64_t)float_key(v) << 32) | (uint32_t)(63 - e);
