@@ -9,7 +9,9 @@ once the loads are known; the same bits as moe_forward followed by
 moe_bias_update_stats, one launch fewer), on the one-layer
 workload T = 4096 tokens (batch 2 x seq 2048), d = 1024, 64 experts of width
 512, top-2, shared expert 2048, bf16 with fp32 accumulation.  Inputs come from
-the seeded generator and sit in HBM before timing starts.
+the seeded generator and sit in HBM before timing starts; the routed expert
+weights are packed into the stage-major layout (moe_pack_routed_bf16) once,
+before timing, as a server does when it loads the model.
 
 The bias step of every timed step also writes the batch's expert-balance
 figures to a device buffer, read after timing.
@@ -635,6 +637,8 @@ def main() -> int:
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--routed-layout", choices=("staged", "row-major"), default="staged",
+                    help="layout of the routed expert weights in the headline step")
     ap.add_argument("--weight-sets", type=int, default=8, help="distinct expert-weight copies rotated per step")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -674,13 +678,19 @@ def main() -> int:
     inp = synth.make_workload("layer_t4096", seed=0)
     T, d, E, F, Fs, k = inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k
     log(f"workload layer_t4096: T={T} d={d} E={E} F={F} Fs={Fs} k={k} bf16")
-    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+    # routed weights in the stage-major layout (packed once, as at model load)
+    staged = args.routed_layout == "staged"
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16", w_routed="bf16_staged" if staged else None)
 
     def up(a):
         return torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
 
     base = dict(w_router=up(inp.w_router), w_gate_up=up(inp.w_gate_up), w_down=up(inp.w_down),
                 w_sh_gate_up=up(inp.w_sh_gate_up), w_sh_down=up(inp.w_sh_down))
+    if staged:
+        packed_gu, packed_d = torch.empty_like(base["w_gate_up"]), torch.empty_like(base["w_down"])
+        moe.moe_pack_routed_bf16(dims, base["w_gate_up"], base["w_down"], packed_gu, packed_d)
+        base["w_gate_up"], base["w_down"] = packed_gu, packed_d
     sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(max(0, args.weight_sets - 1))]
     x = up(inp.x)
     y = torch.empty_like(x)
@@ -756,7 +766,9 @@ def main() -> int:
         "warmup": args.warmup, "ms_per_step": el / args.steps * 1e3, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "layer_t4096", "T": T, "d": d, "E": E, "F": F, "Fs": Fs, "k": k,
-                   "weight_sets": args.weight_sets, "bias_update_every_step": True},
+                   "weight_sets": args.weight_sets, "bias_update_every_step": True,
+                   "routed_weights": ("bf16, stage-major (packed once before timing)" if staged
+                                      else "bf16, row-major")},
         "roofline": roof,
     }
     phase_report = {}

@@ -38,7 +38,11 @@ moe_status check_dims(const moe_dims* d) {
   if (!d) return MOE_E_ARG;
   if (d->T < 0 || d->d < 1 || d->E < 1 || d->F < 1 || d->Fs < 1 || d->k < 1) return MOE_E_ARG;
   if (d->act != MOE_F32 && d->act != MOE_BF16) return MOE_E_UNSUPPORTED;
-  if (d->w_routed != d->act && d->w_routed != MOE_INT4_G128) return MOE_E_UNSUPPORTED;
+  if (d->w_routed != d->act && d->w_routed != MOE_INT4_G128 && d->w_routed != MOE_BF16_STAGED)
+    return MOE_E_UNSUPPORTED;
+  // stage-major bf16 routed weights: whole 256-row tiles of the gate/up and
+  // down launches
+  if (d->w_routed == MOE_BF16_STAGED && (d->act != MOE_BF16 || d->d % 256 || d->F % 128)) return MOE_E_UNSUPPORTED;
   if (d->E > 64 || d->k > d->E || d->k > 8) return MOE_E_UNSUPPORTED;
   if (d->d % 128 || d->F % 64 || d->Fs % 64) return MOE_E_UNSUPPORTED;
   if (d->w_routed == MOE_INT4_G128) {
@@ -60,7 +64,8 @@ moe_status check_dims(const moe_dims* d) {
 // Training needs the backward GEMM tiles (128 output columns over F and Fs)
 // and the bf16/fp32 routed experts.
 moe_status check_training(const moe_dims& d) {
-  if (d.w_routed == MOE_INT4_G128 || d.F % 128 || d.Fs % 128) return MOE_E_UNSUPPORTED;
+  if (d.w_routed == MOE_INT4_G128 || d.w_routed == MOE_BF16_STAGED || d.F % 128 || d.Fs % 128)
+    return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
 
@@ -321,6 +326,7 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   g.B = w->w_gate_up;
   g.ldb = D;
   g.b_estride = 2LL * F * D;
+  g.b_staged = d.w_routed == MOE_BF16_STAGED;
   g.K = d.d;
   g.N = d.F;
   g.up_off = d.F;
@@ -629,6 +635,22 @@ moe_status moe_bias_update_stats(int32_t E, int64_t total_assignments, const int
   if (any_alias(rs)) return MOE_E_ALIAS;
   launch_bias_update(E, (long long)total_assignments, counts, gamma, bias, stats,
                      reinterpret_cast<hipStream_t>(stream));
+  return device_status();
+}
+
+moe_status moe_pack_routed_bf16(const moe_dims* dims, const void* w_gate_up, const void* w_down, void* out_gate_up,
+                                void* out_down, void* stream) {
+  if (!dims) return MOE_E_ARG;
+  moe_dims d = *dims;
+  d.w_routed = MOE_BF16_STAGED;
+  d.T = 0;
+  moe_status st = check_dims(&d);
+  if (st != MOE_OK) return st;
+  const size_t gu = (size_t)d.E * 2 * d.F * d.d * 2, dn = (size_t)d.E * d.d * d.F * 2;
+  std::vector<Range> rs = {{w_gate_up, gu, false}, {w_down, dn, false}, {out_gate_up, gu, true}, {out_down, dn, true}};
+  if (null_with_size(rs)) return MOE_E_ARG;
+  if (any_alias(rs)) return MOE_E_ALIAS;
+  launch_pack_routed(w_gate_up, w_down, d.E, d.d, d.F, out_gate_up, out_down, reinterpret_cast<hipStream_t>(stream));
   return device_status();
 }
 

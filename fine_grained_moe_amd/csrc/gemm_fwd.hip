@@ -44,6 +44,7 @@
 // (M rows x gc + N rows x 8 / gc) x K, are smallest; measured with
 // FETCH_SIZE, gc = 1 on the 4096-token shared gate/up fetched the 8 MiB
 // weight matrix once per XCD.
+#include <algorithm>
 #include <type_traits>
 
 #include "gemm_tile.h"
@@ -65,6 +66,20 @@ static_assert(BM == 256, "the wave layout covers 256 rows");
 __device__ __host__ __forceinline__ int n_tiles(const GemmJob& j) {
   const int w = j.epi == EPI_SWIGLU ? BN / 2 : BN;
   return (j.N + w - 1) / w;
+}
+// The weight row that LDS B row R of N tile nt holds (before clamping to the
+// last row): SwiGLU tiles put 128 gate rows, then the matching 128 up rows,
+// ordered so that each lane's output columns are adjacent; other tiles 256
+// rows in the same interleaved order.  The stage-major layout stores rows in
+// this LDS order.
+__device__ __host__ __forceinline__ long long b_tile_row(bool swiglu, int R, int nt, int up_off) {
+  if (swiglu) {
+    const int half = R >> 7, h = R & 127;
+    const int w = h >> 6, ni = (h >> 4) & 3, f = h & 15;
+    return (long long)(half ? up_off : 0) + nt * (BN / 2) + w * 64 + 4 * f + ni;
+  }
+  const int w = R >> 7, ni = (R >> 4) & 7, f = R & 15;
+  return (long long)nt * BN + w * 128 + 8 * f + ni;
 }
 // contraction slices of a dense job
 __device__ __host__ __forceinline__ int k_slices(const GemmJob& j) { return j.ksplit > 1 ? j.ksplit : 1; }
@@ -176,18 +191,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   for (int j = 0; j < NDB; ++j) {
     const int R = wave * (BN / 8) + j * 16 + (lane >> 2);
     const int c = swz_piece(R, lane & 3);
-    long long brow;
-    if (SWIGLU) {
-      const int half = R >> 7, h = R & 127;
-      const int w = h >> 6, ni = (h >> 4) & 3, f = h & 15;
-      const int col = min(nt * (BN / 2) + w * 64 + 4 * f + ni, p.N - 1);
-      brow = (long long)(half ? p.up_off : 0) + col;
+    if (p.b_staged) {
+      // stage s of this tile: 256 rows x 64 bytes, contiguous, in LDS row order
+      b_src[j] = bbase + (long long)nt * p.K * BN * (long long)sizeof(T) + R * kRowB + c * 16;
     } else {
-      const int w = R >> 7, ni = (R >> 4) & 7, f = R & 15;
-      brow = min(nt * BN + w * 128 + 8 * f + ni, p.N - 1);
+      long long brow;
+      if (SWIGLU) {
+        const long long col = min(b_tile_row(true, R, nt, 0), (long long)p.N - 1);
+        brow = (R >> 7 ? p.up_off : 0) + col;
+      } else {
+        brow = min(b_tile_row(false, R, nt, 0), (long long)p.N - 1);
+      }
+      b_src[j] = bbase + (brow * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
     }
-    b_src[j] = bbase + (brow * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
   }
+  const long long b_step = p.b_staged ? (long long)BN * kRowB : (long long)kRowB;
   const int nk = (int)((long long)klen * sizeof(T) / kRowB);
   auto issue_one = [&](int s, int j) {
     char* st = lds + (s % kStages) * kStageBytes;
@@ -195,7 +213,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     if (j < NDA)
       __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(st + wave * (BM / 8) * kRowB + j * 1024), 16, 0, 0);
     else
-      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + off,
+      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
                                        (lds_ptr_t)(st + ATILE + wave * (BN / 8) * kRowB + (j - NDA) * 1024), 16, 0, 0);
   };
   auto issue = [&](int s) {
@@ -398,7 +416,43 @@ int job_chunks(const GemmJob& j) {
   return (int)((max_item_count(j) + gr - 1) / gr * ((nbn + gc - 1) / gc));
 }
 
+// One 16-byte piece per thread: piece u of the stage-major array is piece
+// (u % 4) of the 64-byte chunk s of weight row b_tile_row(R, nt), where
+// u / 4 = ((e * ntiles + nt) * nstages + s) * 256 + R.
+__global__ __launch_bounds__(256) void pack_routed_kernel(const char* __restrict__ w, char* __restrict__ out,
+                                                          long long units, int K, int ntiles, int up_off,
+                                                          int swiglu) {
+  const int nstages = K * 2 / kRowB;
+  for (long long u = (long long)blockIdx.x * 256 + threadIdx.x; u < units; u += (long long)gridDim.x * 256) {
+    const int piece = (int)(u & 3);
+    const long long rowu = u >> 2;
+    const int R = (int)(rowu % BN);
+    const long long t = rowu / BN;
+    const int st = (int)(t % nstages);
+    const long long en = t / nstages;
+    const int nt = (int)(en % ntiles);
+    const long long e = en / ntiles;
+    const long long row = b_tile_row(swiglu != 0, R, nt, up_off);
+    const long long rows_e = (long long)ntiles * BN;
+    const char* src = w + ((e * rows_e + row) * K) * 2 + st * kRowB + piece * 16;
+    *reinterpret_cast<uint4*>(out + u * 16) = *reinterpret_cast<const uint4*>(src);
+  }
+}
+
 }  // namespace
+
+void launch_pack_routed(const void* w_gate_up, const void* w_down, int E, int d, int F, void* out_gate_up,
+                        void* out_down, hipStream_t s) {
+  // gate/up: [E, 2F, d] in tiles of 128 h columns (256 rows); down: [E, d, F]
+  // in tiles of 256 output columns
+  const long long u_gu = (long long)E * 2 * F * d * 2 / 16, u_d = (long long)E * d * F * 2 / 16;
+  if (u_gu > 0)
+    hipLaunchKernelGGL(pack_routed_kernel, dim3((unsigned)std::min<long long>((u_gu + 255) / 256, 16384)), dim3(256),
+                       0, s, (const char*)w_gate_up, (char*)out_gate_up, u_gu, d, F / (BN / 2), F, 1);
+  if (u_d > 0)
+    hipLaunchKernelGGL(pack_routed_kernel, dim3((unsigned)std::min<long long>((u_d + 255) / 256, 16384)), dim3(256),
+                       0, s, (const char*)w_down, (char*)out_down, u_d, F, d / BN, 0, 0);
+}
 
 // bf16 operands only: epilogues SwiGLU, row scale, SwiGLU backward, plain
 // store (bf16) or fp32 store (the weight gradients, with per-expert

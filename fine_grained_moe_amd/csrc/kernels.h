@@ -65,6 +65,9 @@ struct GemmJob {
   const void* B;
   long long ldb;
   long long b_estride;
+  // launch_gemm_fwd256 only: B in the stage-major layout of
+  // launch_pack_routed (whole 256-row tiles; ldb unused)
+  int b_staged;
   int K;
   int N;                   // output columns (SwiGLU: h columns; B then has gate rows 0..N-1 and up rows up_off..)
   int up_off;
@@ -114,6 +117,11 @@ void launch_gemm(const GemmArgs& a, hipStream_t s);
 // (K % 32 == 0) on 256 x 256 tiles; grouped jobs index the kTileMFwd tile
 // table.
 void launch_gemm_fwd256(const GemmArgs& a, hipStream_t s);
+// Routed bf16 weights into the stage-major layout that launch_gemm_fwd256
+// reads with b_staged: gate/up [E, 2F, d] (F % 128 == 0) and down [E, d, F]
+// (d % 256 == 0) to arrays of the same sizes.
+void launch_pack_routed(const void* w_gate_up, const void* w_down, int E, int d, int F, void* out_gate_up,
+                        void* out_down, hipStream_t s);
 
 // Top-1 serving with int4 routed experts, T <= 64 tokens (decode.hip), built
 // for the NanoColibri layer shape.

@@ -7,7 +7,7 @@ implementation to fall back to.
 
 The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
 moe_forward_bias_step, moe_forward_block, moe_bias_update, moe_bias_update_stats,
-moe_backward, moe_quantize_int4, moe_forward_cached, moe_cache_create, moe_cache_prepare,
+moe_backward, moe_quantize_int4, moe_pack_routed_bf16, moe_forward_cached, moe_cache_create, moe_cache_prepare,
 moe_cache_state, moe_cache_destroy, moe_status_str.  Weights, routing buffers and
 gradients are passed as dicts of torch tensors keyed by the C field names.
 """
@@ -22,9 +22,9 @@ import torch  # first: the library binds to the HIP runtime torch has loaded
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfgmoe.so")
 
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_ALIAS, MOE_E_DEVICE = range(6)
-MOE_F32, MOE_BF16, MOE_INT4_G128 = 0, 1, 2
+MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_BF16_STAGED = 0, 1, 2, 3
 
-DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128}
+DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "bf16_staged": MOE_BF16_STAGED}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
 
 WEIGHT_FIELDS = ("w_router", "w_gate_up", "w_down", "s_gate_up", "s_down", "w_sh_gate_up", "w_sh_down")
@@ -94,6 +94,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_cache_destroy.restype = None
     lib.moe_quantize_int4.argtypes = [I32, P, I64, I32, P, P, P]
     lib.moe_quantize_int4.restype = ctypes.c_int
+    lib.moe_pack_routed_bf16.argtypes = [ctypes.POINTER(MoeDims), P, P, P, P, P]
+    lib.moe_pack_routed_bf16.restype = ctypes.c_int
     lib.moe_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
     lib.moe_set_phase_events.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
@@ -198,6 +200,15 @@ def moe_bias_update_stats(E: int, total_assignments: int, counts, gamma: float, 
     """stats: a float32 device tensor of (at least) 4 elements, e.g. one row of a [steps, 4] buffer."""
     _check(LIB.moe_bias_update_stats(int(E), int(total_assignments), _ptr(counts), float(gamma), _ptr(bias),
                                      _ptr(stats), _stream(stream)), "moe_bias_update_stats")
+
+
+def moe_pack_routed_bf16(dims: MoeDims, w_gate_up, w_down, out_gate_up, out_down, stream=None) -> None:
+    """Routed bf16 weights into the stage-major layout that w_routed = "bf16_staged" reads."""
+    for a, b in ((w_gate_up, out_gate_up), (w_down, out_down)):
+        if a.dtype != torch.bfloat16 or b.dtype != torch.bfloat16 or a.numel() != b.numel():
+            raise MoeError(MOE_E_ARG, "moe_pack_routed_bf16")
+    _check(LIB.moe_pack_routed_bf16(ctypes.byref(dims), _ptr(w_gate_up), _ptr(w_down), _ptr(out_gate_up),
+                                    _ptr(out_down), _stream(stream)), "moe_pack_routed_bf16")
 
 
 def moe_quantize_int4(w, packed, scales, stream=None) -> None:

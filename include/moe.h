@@ -45,12 +45,16 @@ typedef enum {
   MOE_E_DEVICE = 5        /* the HIP runtime rejected a launch                  */
 } moe_status;
 
-typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2 } moe_dtype;
+typedef enum { MOE_F32 = 0, MOE_BF16 = 1, MOE_INT4_G128 = 2, MOE_BF16_STAGED = 3 } moe_dtype;
 
 /* (host) Layer sizes.  T tokens, d hidden, E routed experts of width F, one
  * shared expert of width Fs, top-k.  act: dtype of x, y, the router and the
  * shared expert.  w_routed: dtype of the routed expert weights, equal to act,
- * or MOE_INT4_G128 (requires act = MOE_BF16 and k = 1: top-1 serving). */
+ * or MOE_INT4_G128 (requires act = MOE_BF16 and k = 1: top-1 serving), or
+ * MOE_BF16_STAGED: bf16 routed weights in the stage-major layout written by
+ * moe_pack_routed_bf16 (requires act = MOE_BF16, d % 256 == 0, F % 128 == 0;
+ * inference only: moe_backward and training forwards return
+ * MOE_E_UNSUPPORTED). */
 typedef struct {
   int32_t T, d, E, F, Fs, k;
   int32_t act;
@@ -273,6 +277,25 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
  * (or zero); other values are not checked. */
 moe_status moe_quantize_int4(int32_t dtype, const void* w, int64_t rows, int32_t K, uint8_t* packed,
                              void* scales, void* stream);
+
+/* Routed bf16 expert weights into the stage-major layout that w_routed =
+ * MOE_BF16_STAGED reads (a storage order of the same matrices, for the
+ * routed experts of the article's layer; the values are copied unchanged).
+ * The grouped GEMM streams each 256-row weight tile in contraction chunks of
+ * 32 elements; in row-major order such a chunk is 64 bytes from each of 256
+ * rows 2 KiB or 1 KiB apart, which HBM serves less efficiently than one
+ * contiguous 16 KiB block.  The packed arrays hold, per expert, per 256-row
+ * tile, per chunk, the tile's 256 row pieces in the order the kernel places
+ * them in LDS.  Pack once when the weights are loaded.
+ *  dims         act = MOE_BF16, d % 256 == 0, F % 128 == 0 (else
+ *               MOE_E_UNSUPPORTED); T and w_routed are ignored
+ *  w_gate_up    [E, 2F, d] bf16 row-major, as moe_weights (device, read only)
+ *  w_down       [E, d, F]  bf16 row-major (device, read only)
+ *  out_gate_up  E * 2F * d bf16 (device, written): pass it as w_gate_up
+ *  out_down     E * d * F  bf16 (device, written): pass it as w_down
+ * Outputs may not overlap the inputs or each other (MOE_E_ALIAS). */
+moe_status moe_pack_routed_bf16(const moe_dims* dims, const void* w_gate_up, const void* w_down, void* out_gate_up,
+                                void* out_down, void* stream);
 
 /* Instrumentation, not part of the layer.  Registers n (0..8) hipEvent_t
  * handles, passed as void*, that every later moe_forward records on its

@@ -29,7 +29,7 @@ def lib():
 def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
-                                           "moe_quantize_int4", "moe_forward_bias_step", "moe_status_str",
+                                           "moe_quantize_int4", "moe_pack_routed_bf16", "moe_forward_bias_step", "moe_status_str",
                                            "moe_set_phase_events", "moe_forward_cached", "moe_cache_create",
                                            "moe_cache_prepare", "moe_cache_state", "moe_cache_destroy"])
 
@@ -199,3 +199,23 @@ def test_block_host_checks(lib):
     assert call(dims, h, g, -1.0, h_out, need) == lib.MOE_E_ARG
     assert call(dims, h, g, 1e-6, h_out, need - 1) == lib.MOE_E_WORKSPACE
     assert call(dims, h, g, 1e-6, h + 64, need) == lib.MOE_E_ALIAS
+
+
+def test_pack_routed_host_checks(lib):
+    moe = lib
+    import ctypes
+    f = moe.LIB.moe_pack_routed_bf16
+    d = moe.make_dims(0, 1024, 64, 512, 2048, 2, "bf16")
+    gu, dn = 0x10000000, 0x20000000
+    assert f(ctypes.byref(d), None, dn, 0x30000000, 0x40000000, None) == moe.MOE_E_ARG
+    assert f(ctypes.byref(d), gu, dn, gu, 0x40000000, None) == moe.MOE_E_ALIAS          # output over its input
+    assert f(ctypes.byref(moe.make_dims(0, 1024, 64, 512, 2048, 2, "f32")), gu, dn, 0x30000000, 0x40000000,
+             None) == moe.MOE_E_UNSUPPORTED
+    assert f(ctypes.byref(moe.make_dims(0, 384, 64, 512, 2048, 2, "bf16")), gu, dn, 0x30000000, 0x40000000,
+             None) == moe.MOE_E_UNSUPPORTED                                               # d % 256
+    assert f(ctypes.byref(moe.make_dims(0, 1024, 64, 192, 2048, 2, "bf16")), gu, dn, 0x30000000, 0x40000000,
+             None) == moe.MOE_E_UNSUPPORTED                                               # F % 128
+    staged = moe.make_dims(4096, 1024, 64, 512, 2048, 2, "bf16", w_routed="bf16_staged")
+    assert moe.moe_workspace_bytes(staged) > 0
+    assert moe.moe_workspace_bytes(staged, training=True) == 0                           # inference only
+    assert moe.moe_workspace_bytes(moe.make_dims(4096, 1024, 64, 512, 2048, 2, "f32", w_routed="bf16_staged")) == 0
