@@ -225,12 +225,21 @@ def bench_decode(moe, synth, torch, np, n_layers=23, iters=46, graph_reps=20):
     return out
 
 
+def _pack_routed(moe, torch, dims, w):
+    """w with its routed weights replaced by stage-major copies (moe_pack_routed_bf16)."""
+    out = dict(w)
+    out["w_gate_up"], out["w_down"] = torch.empty_like(w["w_gate_up"]), torch.empty_like(w["w_down"])
+    moe.moe_pack_routed_bf16(dims, w["w_gate_up"], w["w_down"], out["w_gate_up"], out["w_down"])
+    return out
+
+
 def bench_stack(moe, synth, torch, np, n_layers=23, reps=10, graph_reps=20):
     """The model's 23 MoE layers chained through the residual stream with
     moe_forward_block (RMSNorm in, residual add out), distinct weights per
     layer so every layer reads its weights from HBM: bf16 at T = 4096 (eager
     launches), and the int4 top-1 serving path at T = 1, 8, 64 (the 23 blocks
-    captured once in a HIP graph and replayed).  Weights are seeded N(0, 0.02)
+    captured once in a HIP graph and replayed; the bf16 routed weights
+    stage-major, packed before timing).  Weights are seeded N(0, 0.02)
     draws on the device (the same recipe as the one-layer workload; parity is
     the tests' business)."""
     E, d, F, Fs = 64, 1024, 512, 2048
@@ -244,10 +253,11 @@ def bench_stack(moe, synth, torch, np, n_layers=23, reps=10, graph_reps=20):
     out = {}
     # bf16 batch path, T = 4096
     T, k = 4096, 2
-    layers = [dict(w_router=randn(E, d), w_gate_up=randn(E, 2 * F, d), w_down=randn(E, d, F),
-                   w_sh_gate_up=randn(2 * Fs, d), w_sh_down=randn(d, Fs)) for _ in range(n_layers)]
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16", w_routed="bf16_staged")   # routed weights stage-major
+    layers = [_pack_routed(moe, torch, dims, dict(w_router=randn(E, d), w_gate_up=randn(E, 2 * F, d),
+                                                  w_down=randn(E, d, F), w_sh_gate_up=randn(2 * Fs, d),
+                                                  w_sh_down=randn(d, Fs))) for _ in range(n_layers)]
     biases = [torch.zeros(E, device="cuda") for _ in range(n_layers)]
-    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
     h = [randn(T, d, std=1.0), torch.empty(T, d, device="cuda", dtype=torch.bfloat16)]
     r = moe.alloc_routing(dims)
     ws = moe.alloc_workspace(dims)
@@ -322,10 +332,11 @@ def bench_zipf(moe, synth, torch, np, steps=50, warmup=5, calib=400):
     bias step with telemetry, timed like the headline (8 weight sets)."""
     inp = synth.make_workload("zipf_t16384", seed=0)
     T, d, E, F, Fs, k = inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k
-    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+    dims = moe.make_dims(T, d, E, F, Fs, k, "bf16", w_routed="bf16_staged")   # routed weights stage-major
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
-    base = dict(w_router=bf(inp.w_router), w_gate_up=bf(inp.w_gate_up), w_down=bf(inp.w_down),
-                w_sh_gate_up=bf(inp.w_sh_gate_up), w_sh_down=bf(inp.w_sh_down))
+    base = _pack_routed(moe, torch, dims, dict(w_router=bf(inp.w_router), w_gate_up=bf(inp.w_gate_up),
+                                               w_down=bf(inp.w_down), w_sh_gate_up=bf(inp.w_sh_gate_up),
+                                               w_sh_down=bf(inp.w_sh_down)))
     sets = [base] + [{n: t.clone() for n, t in base.items()} for _ in range(7)]
     x = bf(inp.x)
     y = torch.empty_like(x)
