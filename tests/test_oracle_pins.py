@@ -509,3 +509,60 @@ def test_block_with_silent_experts_is_the_identity():
     np.testing.assert_array_equal(h_out, h.astype(np.float64))
     # and the layer inside reads the normalised rows
     np.testing.assert_array_equal(r.idx, om.route(x, inp.w_router, inp.bias, inp.k).idx)
+
+
+def test_block_residual_hand_worked():
+    """The block's residual adds the layer output (R20): a hand-worked token
+    with one expert (so k = 1 and the gate is 1).  h = [1, 1] has mean square
+    1, so x = bf16([1, 1] / sqrt(1 + 1e-6)) = [1, 1] exactly (the quotient
+    0.9999995 is within half a bf16 step of 1).  Routed expert: a = x . [L/2,
+    L/2] = L, u = x . [1, 0] = 1, h_e = silu(L) = 3L/4, out = [1, 2] * 3L/4.
+    Shared expert: a = x . [-L/2, -L/2] = -L, u = x . [0, 1] = 1, h_s =
+    silu(-L) = -L/4, out = [4, 0] * (-L/4).  So y = [3L/4 - L, 3L/2] and
+    h_out = [1 - L/4, 1 + 3L/2] (h - y would give [1 + L/4, 1 - 3L/2])."""
+    h = np.array([[1.0, 1.0]])
+    w_router = np.array([[0.3, -0.2]])
+    w_gate_up = np.array([[[L / 2, L / 2], [1.0, 0.0]]])       # [E=1, 2F=2, d=2]
+    w_down = np.array([[[1.0], [2.0]]])                           # [E=1, d=2, F=1]
+    w_sh_gate_up = np.array([[-L / 2, -L / 2], [0.0, 1.0]])       # [2Fs=2, d=2]
+    w_sh_down = np.array([[4.0], [0.0]])                          # [d=2, Fs=1]
+    h_out, x, r = om.block_forward(h, np.ones(2), w_router, w_gate_up, w_down, w_sh_gate_up, w_sh_down,
+                                   np.zeros(1, np.float32), 1)
+    np.testing.assert_array_equal(x, [[1.0, 1.0]])
+    assert r.idx.tolist() == [[0]] and r.gate.tolist() == [[1.0]]
+    np.testing.assert_allclose(h_out, [[1.0 - L / 4, 1.0 + 1.5 * L]], rtol=0, atol=1e-14)
+
+
+def test_dispatch_order_hand_listed():
+    """Dispatch order (R18): slots grouped by expert, ascending t*k + j inside
+    each expert.  idx = [[2, 0], [0, 1], [2, 1]] flattens to experts
+    [2, 0, 0, 1, 2, 1] at t*k + j = 0..5, so expert 0 holds assignments 1, 2;
+    expert 1 holds 3, 5; expert 2 holds 0, 4."""
+    idx = np.array([[2, 0], [0, 1], [2, 1]])
+    perm, pos = om.dispatch_order(idx, 3)
+    assert perm.tolist() == [1, 2, 3, 5, 0, 4]
+    assert pos.tolist() == [[4, 0], [1, 2], [5, 3]]
+    np.testing.assert_array_equal(om.expert_offsets(om.expert_counts(idx, 3)), [0, 2, 4, 6])
+
+
+def test_bf16_rounding_ties_to_even():
+    """bf16 keeps 8 significant bits.  1 + 2^-8 lies exactly halfway between
+    1 and 1 + 2^-7 and goes to the even significand, 1; 1 + 3 * 2^-8 lies
+    halfway between 1 + 2^-7 (odd) and 1 + 2^-6 (even) and goes up.  The same
+    holds for negative values and in other binades; values off the midpoint
+    go to the nearer neighbour."""
+    cases = {1 + 2 ** -8: 1.0, 1 + 3 * 2 ** -8: 1 + 2 ** -6, -(1 + 2 ** -8): -1.0,
+             -(1 + 3 * 2 ** -8): -(1 + 2 ** -6), 4 * (1 + 5 * 2 ** -8): 4 * (1 + 2 ** -6),
+             2 ** -10 * (1 + 7 * 2 ** -8): 2 ** -10 * (1 + 2 ** -5), 1 + 2 ** -8 + 2 ** -30: 1 + 2 ** -7,
+             1 + 2 ** -8 - 2 ** -30: 1.0, 0.75: 0.75}
+    got = om.to_bf16_nearest(np.array(list(cases)))
+    np.testing.assert_array_equal(got, np.array(list(cases.values())))
+    # the int4 scale of a group whose absmax is 7 (1 + 2^-8): absmax / 7 is the
+    # exact tie 1 + 2^-8, so the scale is 1 and the largest code 7
+    w = np.zeros((1, 128))
+    w[0, 5] = 7 * (1 + 2 ** -8)
+    w[0, 9] = -3.5
+    packed, scale = om.quantize_int4(w)
+    assert scale.tolist() == [[1.0]]
+    q = om.unpack_int4(packed)
+    assert q[0, 5] == 7 and q[0, 9] == -4 and np.count_nonzero(q) == 2    # -3.5 is a tie: to even, -4
