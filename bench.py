@@ -123,6 +123,7 @@ class HipEvents:
         self.hip.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(ctypes.c_void_p), ctypes.c_uint]
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
 
     def create(self):
         ev = ctypes.c_void_p()
@@ -140,6 +141,49 @@ class HipEvents:
 
     def destroy(self, e):
         self.hip.hipEventDestroy(ctypes.c_void_p(e))
+
+    def record(self, e, stream):
+        rc = self.hip.hipEventRecord(ctypes.c_void_p(e), ctypes.c_void_p(stream))
+        if rc != 0:
+            raise RuntimeError(f"hipEventRecord failed ({rc})")
+
+
+def percentiles(us):
+    """median / p10 / p90 of a list of per-step times (microseconds)."""
+    import numpy as np
+    a = np.asarray(us, dtype=np.float64)
+    return dict(median=round(float(np.median(a)), 2), p10=round(float(np.percentile(a, 10)), 2),
+                p90=round(float(np.percentile(a, 90)), 2), n=int(a.size))
+
+
+def measured_peaks(torch):
+    """Second denominators for the rooflines, measured on this GPU: the HBM
+    rate of a plain 1 GiB device copy (read + write bytes over time) and the
+    bf16 rate of the vendor GEMM library (torch.matmul -> hipBLASLt) on an
+    8192^3 product, each the median of 10 event-timed runs."""
+    import numpy as np
+    out = {}
+    src = torch.empty(1 << 30, dtype=torch.uint8, device="cuda").fill_(1)
+    dst = torch.empty_like(src)
+    a = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    b = torch.randn(8192, 8192, device="cuda", dtype=torch.bfloat16)
+    for name, fn, work in (("hbm_copy_gbps", lambda: dst.copy_(src), 2.0 * (1 << 30) / 1e9),
+                           ("bf16_gemm_tflops", lambda: torch.matmul(a, b), 2.0 * 8192 ** 3 / 1e12)):
+        for _ in range(3):
+            fn()
+        ts = []
+        for _ in range(10):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            fn()
+            e1.record()
+            torch.cuda.synchronize()
+            ts.append(e0.elapsed_time(e1) * 1e-3)
+        out[name] = round(work / float(np.median(ts)), 1)
+    del src, dst, a, b
+    out["how"] = ("hbm_copy_gbps: 1 GiB device-to-device copy, bytes read + written over time; "
+                  "bf16_gemm_tflops: torch.matmul (hipBLASLt) 8192^3 bf16; medians of 10 runs")
+    return out
 
 
 def decode_bytes(T, d, E, F, Fs, unique_experts):
@@ -362,12 +406,10 @@ def bench_zipf(moe, synth, torch, np, steps=50, warmup=5, calib=400):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_set_phase_events(e_g[i])
-        moe.moe_forward(dims, x, sets[i % 8], bias, y, r, ws)
-        moe.moe_bias_update_stats(E, T * k, r["counts"], GAMMA, bias, stats[i])
+        moe.moe_forward_events(dims, x, sets[i % 8], bias, y, r, ws, e_g[i], bias_step=True, gamma=GAMMA,
+                               stats=stats[i])
     torch.cuda.synchronize()
     el = (time.perf_counter() - t0) / steps
-    moe.moe_set_phase_events(None)
     # phase j spans events j -> j + 1 (PHASES: route, gate_up, down, combine)
     ph_us = {p: sum(ev.elapsed_ms(e_g[i][j], e_g[i][j + 1]) for i in range(steps)) / steps * 1e3
              for j, p in enumerate(PHASES)}
@@ -445,11 +487,9 @@ def bench_int4(moe, synth, torch, np, reps=20, steps=50, warmup=5, n_sets=8):
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(steps):
-        moe.moe_set_phase_events(e_g[i])
-        moe.moe_forward(dims, x, sets[i % n_sets], bias, y, r, ws)
+        moe.moe_forward_events(dims, x, sets[i % n_sets], bias, y, r, ws, e_g[i])
     torch.cuda.synchronize()
     el = (time.perf_counter() - t0) / steps
-    moe.moe_set_phase_events(None)
     ph_us = {p: sum(ev.elapsed_ms(e_g[i][j], e_g[i][j + 1]) for i in range(steps)) / steps * 1e3
              for j, p in enumerate(PHASES)}
     for row in e_g:
@@ -585,11 +625,21 @@ def cpu_baseline(inp, seconds: float):
     whole copies of the benchmark batch until `seconds` have passed."""
     import numpy as np
     from oracle import moe_oracle as om
+    cores = len(os.sched_getaffinity(0))          # the host cores this process may run on
     try:
         from threadpoolctl import threadpool_info
-        cores = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
+        threads = max((i.get("num_threads", 1) for i in threadpool_info()), default=1)
     except Exception:
-        cores = os.cpu_count() or 1
+        threads = None
+    model = None
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     t0 = time.perf_counter()
     n = 0
     while True:
@@ -599,6 +649,7 @@ def cpu_baseline(inp, seconds: float):
         if el >= seconds:
             break
     return dict(value=n * inp.T / el, unit="tokens/s", cores=int(cores), kind="oracle",
+                impl="NumPy float64, BLAS matmuls as steps", blas_threads=threads, cpu_model=model,
                 sample=f"{n} x the {inp.T}-token benchmark batch (float64 oracle forward incl. routing), "
                        f"{el:.1f} s wall")
 
@@ -660,6 +711,7 @@ def main() -> int:
     ap.add_argument("--no-zipf", action="store_true")
     ap.add_argument("--no-int4", action="store_true")
     ap.add_argument("--no-stream", action="store_true")
+    ap.add_argument("--no-row-major", action="store_true")
     ap.add_argument("--leg", choices=("decode", "train", "stack", "zipf", "int4", "stream"),
                     help="run only this extra leg and print its result (for kernel traces of it)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -722,38 +774,65 @@ def main() -> int:
 
     ev = HipEvents()
     nph = len(PHASES) + 1
+    stream = torch.cuda.current_stream().cuda_stream
 
     # expert-balance telemetry of every step, one row each, read after timing
-    stats = torch.zeros(max(args.steps, 1), 4, dtype=torch.float32, device="cuda")
+    stats = torch.zeros(max(args.steps, 100, 1), 4, dtype=torch.float32, device="cuda")
 
-    def run(n_sets, steps, warmup):
+    def run(wsets, steps, warmup):
+        """`steps` timed steps on the host clock, bracketed by synchronisations;
+        one HIP event between consecutive steps gives each step's GPU time."""
+        n_sets = len(wsets)
         bias.copy_(bias0)
         for i in range(warmup):
-            moe.moe_forward_bias_step(dims, x, sets[i % n_sets], bias, GAMMA, stats[0], y, r, ws)
-        events = [[ev.create() for _ in range(nph)] for _ in range(steps)]
+            moe.moe_forward_bias_step(dims, x, wsets[i % n_sets], bias, GAMMA, stats[0], y, r, ws)
+        marks = [ev.create() for _ in range(steps + 1)]
         torch.cuda.synchronize()
         t0 = time.perf_counter()
         for i in range(steps):
-            moe.moe_set_phase_events(events[i])
-            moe.moe_forward_bias_step(dims, x, sets[(warmup + i) % n_sets], bias, GAMMA, stats[i], y, r, ws)
+            ev.record(marks[i], stream)
+            moe.moe_forward_bias_step(dims, x, wsets[(warmup + i) % n_sets], bias, GAMMA, stats[i], y, r, ws)
+        ev.record(marks[steps], stream)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        moe.moe_set_phase_events(None)
-        ph = {p: 0.0 for p in PHASES}
+        step_us = [ev.elapsed_ms(marks[i], marks[i + 1]) * 1e3 for i in range(steps)]
+        for e_ in marks:
+            ev.destroy(e_)
+        return el, step_us
+
+    def run_phases(wsets, steps, warmup):
+        """The phase split, from a run of its own: the instrumented entry point
+        records an event at every phase boundary of every step."""
+        n_sets = len(wsets)
+        bias.copy_(bias0)
+        for i in range(warmup):
+            moe.moe_forward_bias_step(dims, x, wsets[i % n_sets], bias, GAMMA, stats[0], y, r, ws)
+        events = [[ev.create() for _ in range(nph)] for _ in range(steps)]
+        torch.cuda.synchronize()
         for i in range(steps):
-            for j, p in enumerate(PHASES):
-                ph[p] += ev.elapsed_ms(events[i][j], events[i][j + 1])
+            moe.moe_forward_events(dims, x, wsets[(warmup + i) % n_sets], bias, y, r, ws, events[i],
+                                   bias_step=True, gamma=GAMMA, stats=stats[i])
+        torch.cuda.synchronize()
+        ph = {p: [ev.elapsed_ms(events[i][j], events[i][j + 1]) * 1e3 for i in range(steps)]
+              for j, p in enumerate(PHASES)}
         for row in events:
             for e_ in row:
                 ev.destroy(e_)
-        return el, {p: v / steps * 1e3 for p, v in ph.items()}   # seconds, microseconds per launch
+        return {p: sum(v) / len(v) for p, v in ph.items()}, {p: percentiles(v) for p, v in ph.items()}
 
+    n_dist = max(args.steps, 100)
     log(f"timing {args.steps} steps (+{args.warmup} warm-up) over {args.weight_sets} weight sets")
-    el, phases = run(args.weight_sets, args.steps, args.warmup)
+    el, step_us = run(sets, args.steps, args.warmup)
     value = T * args.steps / el
-    log(f"cold: {value / 1e6:.2f} M tokens/s, {el / args.steps * 1e6:.1f} us/step; phases (us): "
-        + ", ".join(f"{p}={v:.1f}" for p, v in phases.items()))
     last = stats[args.steps - 1].cpu().tolist()
+    if n_dist > args.steps:
+        log(f"per-step distribution: {n_dist} more steps")
+        _, step_us = run(sets, n_dist, args.warmup)
+    dist = percentiles(step_us)
+    phases, phase_dist = run_phases(sets, n_dist, args.warmup)
+    log(f"cold: {value / 1e6:.2f} M tokens/s, {el / args.steps * 1e6:.1f} us/step (host clock); per-step GPU "
+        f"median {dist['median']} us (p10 {dist['p10']}, p90 {dist['p90']}); phases (us, mean): "
+        + ", ".join(f"{p}={v:.1f}" for p, v in phases.items()))
     balance = dict(dead_fraction=last[0], max_over_mean=last[1], entropy=last[2], entropy_normalized=last[3])
 
     work = algorithmic_work(T, d, E, F, Fs, k)
@@ -769,8 +848,11 @@ def main() -> int:
     traffic = measured_traffic() if dom == "gate_up" else None
     roof["traffic"] = None if traffic is None else int(round(traffic))   # bytes per launch
     roof["algorithmic_bytes"] = wd["bytes"]
+    roof["algorithmic_flops"] = wd["flops"]
     roof["kernel"] = KERNEL_OF_PHASE[dom]
     roof["avg_us"] = phases[dom]
+    roof["mfma_frac"] = wd["flops"] / t / PEAK_BF16_FLOPS
+    roof["hbm_frac"] = wd["bytes"] / t / PEAK_HBM_BPS
 
     out = {
         "metric": METRIC, "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -781,20 +863,41 @@ def main() -> int:
                    "routed_weights": ("bf16, stage-major (packed once before timing)" if staged
                                       else "bf16, row-major")},
         "roofline": roof,
+        "step_us": dist,
     }
     phase_report = {}
     for p, us in phases.items():
         wp = work[p]
         phase_report[p] = dict(us=round(us, 2), tflops=round(wp["flops"] / (us * 1e-6) / 1e12, 1),
-                               gbps=round(wp["bytes"] / (us * 1e-6) / 1e9, 1), bound=wp["bound"])
+                               gbps=round(wp["bytes"] / (us * 1e-6) / 1e9, 1), bound=wp["bound"],
+                               dist_us=phase_dist[p])
     out["phases"] = phase_report
     out["balance"] = balance      # the last timed step's loads (the fused bias step's figures)
 
     if not args.no_warm:
-        el_w, ph_w = run(1, args.steps, args.warmup)
-        out["warm"] = dict(value=T * args.steps / el_w, ms_per_step=el_w / args.steps * 1e3,
-                           phases_us={p: round(v, 2) for p, v in ph_w.items()})
-        log(f"warm: {out['warm']['value'] / 1e6:.2f} M tokens/s")
+        el_w, us_w = run(sets[:1], n_dist, args.warmup)
+        out["warm"] = dict(value=T * n_dist / el_w, ms_per_step=el_w / n_dist * 1e3, step_us=percentiles(us_w))
+        log(f"warm: {out['warm']['value'] / 1e6:.2f} M tokens/s, per-step median {out['warm']['step_us']['median']} us")
+
+    if staged and not args.no_row_major:
+        # the same step on row-major routed weights (what a training forward reads)
+        dims_rm = moe.make_dims(T, d, E, F, Fs, k, "bf16")
+        rm = dict(base)
+        rm["w_gate_up"], rm["w_down"] = up(inp.w_gate_up), up(inp.w_down)
+        sets_rm = [rm] + [{n: t.clone() for n, t in rm.items()} for _ in range(max(0, args.weight_sets - 1))]
+        dims_save, dims = dims, dims_rm
+        el_r, us_r = run(sets_rm, n_dist, args.warmup)
+        dims = dims_save
+        out["row_major"] = dict(value=T * n_dist / el_r, ms_per_step=el_r / n_dist * 1e3, step_us=percentiles(us_r))
+        log(f"row-major routed weights: {out['row_major']['value'] / 1e6:.2f} M tokens/s, per-step median "
+            f"{out['row_major']['step_us']['median']} us")
+        del sets_rm, rm
+
+    out["measured_peaks"] = measured_peaks(torch)
+    mp = out["measured_peaks"]
+    roof["frac_of_measured"] = (wd["flops"] / t / 1e12 / mp["bf16_gemm_tflops"] if roof["bound"] == "mfma"
+                                else wd["bytes"] / t / 1e9 / mp["hbm_copy_gbps"])
+    log(f"measured peaks: copy {mp['hbm_copy_gbps']} GB/s, hipBLASLt bf16 {mp['bf16_gemm_tflops']} TFLOP/s")
 
     if not args.no_decode:
         out["decode"] = bench_decode(moe, synth, torch, np)

@@ -230,27 +230,22 @@ int dense_xcd_cols(long long M, long long N) {
 
 moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
 
-// Phase-boundary events registered by moe_set_phase_events (instrumentation).
+// Phase-boundary events of one instrumented call (moe_forward_events): the
+// caller's hipEvent_t handles, recorded on the call's stream.  Held for the
+// duration of the call only; null for every other entry point.
 constexpr int kMaxPhaseEvents = 8;
-hipEvent_t g_phase_events[kMaxPhaseEvents];
-int g_n_phase_events = 0;
+struct Phases {
+  hipEvent_t ev[kMaxPhaseEvents];
+  int n;
+};
 
-void mark_phase(int i, hipStream_t s) {
-  if (i < g_n_phase_events) (void)hipEventRecord(g_phase_events[i], s);
+void mark_phase(const Phases* ph, int i, hipStream_t s) {
+  if (ph && i < ph->n) (void)hipEventRecord(ph->ev[i], s);
 }
 
 }  // namespace
 
 extern "C" {
-
-moe_status moe_set_phase_events(void* const* events, int32_t n) {
-  if (n < 0 || n > kMaxPhaseEvents || (n > 0 && !events)) return MOE_E_ARG;
-  for (int i = 0; i < n; ++i)
-    if (!events[i]) return MOE_E_ARG;
-  for (int i = 0; i < n; ++i) g_phase_events[i] = reinterpret_cast<hipEvent_t>(events[i]);
-  g_n_phase_events = events ? n : 0;
-  return MOE_OK;
-}
 
 const char* moe_status_str(moe_status s) {
   switch (s) {
@@ -301,7 +296,7 @@ namespace {
 // prefill's dequantised copies).
 moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* x, const moe_weights* w, void* y,
                                 const moe_routing* routing, int training, void* ws, hipStream_t s,
-                                const void* resid) {
+                                const void* resid, const Phases* ph) {
   const size_t D = d.d, F = d.F, Fs = d.Fs;
   const long long slots = (long long)d.T * d.k;
   // bf16 runs on the 256 x 256 tiles of gemm_fwd.hip (grouped jobs index the
@@ -368,7 +363,7 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   ga.job[0] = g;
   ga.job[1] = sg;
   gemm(ga, s);
-  mark_phase(2, s);
+  mark_phase(ph, 2, s);
 
   // Launch 2: routed down, rows scaled by their routing weight
   // (O[slot] = g * (H[slot] Wd^T)), and shared down (S = Hs Wsd^T).
@@ -415,11 +410,11 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   da.job[0] = dn;
   da.job[1] = sd;
   gemm(da, s);
-  mark_phase(3, s);
+  mark_phase(ph, 3, s);
 
   // combine: y[t] = S[t] + sum_j O[pos[t, j]]
   launch_combine(d.act, S, nsd, O, routing->pos, d.T, d.d, d.k, resid, y, s);
-  mark_phase(4, s);
+  mark_phase(ph, 4, s);
   return device_status();
 }
 
@@ -429,7 +424,7 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
                         const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
                         const void* resid = nullptr, bool x_in_ws = false, const float* gamma = nullptr,
                         float eps = 0.f, const BiasStep* bs = nullptr, const int32_t* slot = nullptr,
-                        int n_slots = 0) {
+                        int n_slots = 0, const Phases* ph = nullptr) {
   if (training) return MOE_E_UNSUPPORTED;
   // expert streaming (slot table): the decode path only
   if (slot && d.T > kDecodeMaxT) return MOE_E_UNSUPPORTED;
@@ -463,12 +458,12 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
     moe_weights wb = *w;
     wb.w_gate_up = wgu;
     wb.w_down = wd;
-    mark_phase(0, s);
+    mark_phase(ph, 0, s);
     enqueue_route(d, L, x, w->w_router, bias, routing, ws, s, bs);
     launch_dequant_int4(w->w_gate_up, w->s_gate_up, d.E, 2 * d.F, d.d, routing->counts, wgu, s);
     launch_dequant_int4(w->w_down, w->s_down, d.E, d.d, d.F, routing->counts, wd, s);
-    mark_phase(1, s);
-    return enqueue_expert_gemms(d, L, x, &wb, y, routing, 0, ws, s, resid);
+    mark_phase(ph, 1, s);
+    return enqueue_expert_gemms(d, L, x, &wb, y, routing, 0, ws, s, resid, ph);
   }
   DecodeArgs a{};
   a.T = d.T;
@@ -506,12 +501,12 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.xn = at<uint16_t>(ws, L.xb);
   a.slot = slot;
   a.n_slots = n_slots;
-  mark_phase(0, s);
+  mark_phase(ph, 0, s);
   launch_decode(a, s);
   // the decode's launches hold no point where all loads are known before the
   // bias is no longer read, so the bias step is a launch of its own here
   if (bs) launch_bias_update(d.E, (long long)d.T * d.k, routing->counts, bs->gamma, bs->bias, bs->stats, s);
-  mark_phase(1, s);
+  mark_phase(ph, 1, s);
   return device_status();
 }
 
@@ -520,12 +515,14 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
 // input (not checked against the workspace for overlap).
 moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
                         const moe_routing* routing, int training, void* ws, size_t ws_bytes, hipStream_t s,
-                        const void* resid, bool x_in_ws, const BiasStep* bs = nullptr) {
+                        const void* resid, bool x_in_ws, const BiasStep* bs = nullptr,
+                        const Phases* ph = nullptr) {
   moe_status st = check_dims(dims);
   if (st != MOE_OK) return st;
   if (!w || !routing) return MOE_E_ARG;
   if (dims->w_routed == MOE_INT4_G128)
-    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws, nullptr, 0.f, bs);
+    return forward_int4(*dims, x, w, bias, y, routing, training, ws, ws_bytes, s, resid, x_in_ws, nullptr, 0.f, bs,
+                        nullptr, 0, ph);
   const moe_dims& d = *dims;
   if (training && check_training(d) != MOE_OK) return MOE_E_UNSUPPORTED;
   const size_t es = act_bytes(d.act);
@@ -548,12 +545,12 @@ moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* 
   rs.push_back({ws, L.total, true});
   if (any_alias(rs)) return MOE_E_ALIAS;
 
-  mark_phase(0, s);
+  mark_phase(ph, 0, s);
   enqueue_route(d, L, x, w->w_router, bias, routing, ws, s, bs);
-  mark_phase(1, s);
+  mark_phase(ph, 1, s);
   if (d.T == 0) return device_status();
 
-  return enqueue_expert_gemms(d, L, x, w, y, routing, training, ws, s, resid);
+  return enqueue_expert_gemms(d, L, x, w, y, routing, training, ws, s, resid, ph);
 }
 
 }  // namespace
@@ -573,6 +570,23 @@ moe_status moe_forward_bias_step(const moe_dims* dims, const void* x, const moe_
   const BiasStep bs{gamma, bias, stats};
   return forward_core(dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
                       nullptr, false, &bs);
+}
+
+moe_status moe_forward_events(const moe_dims* dims, const void* x, const moe_weights* w, float* bias, int32_t bias_step,
+                              float gamma, float* stats, void* y, const moe_routing* routing, int training, void* ws,
+                              size_t ws_bytes, void* stream, void* const* events, int32_t n_events) {
+  if (n_events < 0 || n_events > kMaxPhaseEvents || (n_events > 0 && !events)) return MOE_E_ARG;
+  if (bias_step != 0 && bias_step != 1) return MOE_E_ARG;
+  Phases ph{};
+  ph.n = n_events;
+  for (int i = 0; i < n_events; ++i) {
+    if (!events[i]) return MOE_E_ARG;
+    ph.ev[i] = reinterpret_cast<hipEvent_t>(events[i]);
+  }
+  if (bias_step && !bias) return MOE_E_ARG;
+  const BiasStep bs{gamma, bias, stats};
+  return forward_core(dims, x, w, bias, y, routing, training, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
+                      nullptr, false, bias_step ? &bs : nullptr, &ph);
 }
 
 moe_status moe_forward_cached(const moe_dims* dims, const void* x, const moe_weights* w, const int32_t* slot,
@@ -613,7 +627,7 @@ moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* n
   launch_rmsnorm(h, norm_weight, eps, d.T, d.d, x, s);
   if (d.w_routed == MOE_INT4_G128)
     return forward_int4(d, x, w, bias, h_out, routing, 0, ws, ws_bytes, s, h, true);
-  return forward_core(dims, x, w, bias, h_out, routing, 0, ws, ws_bytes, s, h, true);
+  return forward_core(dims, x, w, bias, h_out, routing, 0, ws, ws_bytes, s, h, true, nullptr, nullptr);
 }
 
 moe_status moe_bias_update(int32_t E, int64_t total_assignments, const int32_t* counts, float gamma, float* bias,
@@ -737,7 +751,6 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   void* HsT = at<char>(ws, L.HsT);
   void* dXs = at<char>(ws, L.dXs);
 
-  mark_phase(0, s);
   // 1. padded per-expert contraction ranges
   const int S = splitk_count(Tp), step = (int)splitk_step(Tp);
   launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, S, step, kofs, klen, ksh, pcol, s);
@@ -920,7 +933,6 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   launch_bwd_dwr(act, x, dl, routing->perm, pcol, P, kofs, klen, d.E, d.d, d.k, at<float>(ws, L.dwr_part),
                  dw->dw_router, s);
   launch_bwd_dx(act, dXs, dXp, w->w_router, dl, routing->idx, routing->pos, d.T, d.d, d.k, dx, s);
-  mark_phase(1, s);
   return device_status();
 }
 

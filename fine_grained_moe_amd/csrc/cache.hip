@@ -85,13 +85,15 @@ struct moe_expert_cache {
 extern "C" {
 
 moe_status moe_cache_create(const moe_dims* dims, int32_t n_slots, const moe_weights* host, const moe_weights* dev,
-                            int32_t* dev_slot, int32_t dry_run, moe_expert_cache** out) {
+                            int32_t* dev_slot, int32_t flags, moe_expert_cache** out) {
   if (!dims || !out) return MOE_E_ARG;
   *out = nullptr;
   const moe_dims& d = *dims;
   if (d.E < 1 || d.E > 64 || d.d < 128 || d.d % 128 || d.F < 128 || d.F % 128) return MOE_E_UNSUPPORTED;
   if (d.w_routed != MOE_INT4_G128) return MOE_E_UNSUPPORTED;
   if (n_slots < 1 || n_slots > d.E) return MOE_E_ARG;
+  if (flags & ~(MOE_CACHE_DRY_RUN | MOE_CACHE_COPY_FILLS)) return MOE_E_ARG;
+  const bool dry_run = (flags & MOE_CACHE_DRY_RUN) != 0;
   if (!dry_run) {
     if (!host || !dev || !dev_slot) return MOE_E_ARG;
     if (!host->w_gate_up || !host->s_gate_up || !host->w_down || !host->s_down || !dev->w_gate_up ||
@@ -102,7 +104,7 @@ moe_status moe_cache_create(const moe_dims* dims, int32_t n_slots, const moe_wei
   if (!c) return MOE_E_ARG;
   c->E = d.E;
   c->n_slots = n_slots;
-  c->dry = dry_run != 0;
+  c->dry = dry_run;
   const size_t D = d.d, F = d.F;
   c->bytes[0] = 2 * F * D / 2;               // [2F, d/2] packed
   c->bytes[1] = 2 * F * (D / 128) * 2;       // [2F, d/128] bf16
@@ -116,8 +118,8 @@ moe_status moe_cache_create(const moe_dims* dims, int32_t n_slots, const moe_wei
       c->dev[i] = static_cast<char*>(const_cast<void*>(v[i]));
     }
     c->dev_slot = dev_slot;
-    c->zero_copy = true;
-    for (int i = 0; i < 4; ++i) {
+    c->zero_copy = (flags & MOE_CACHE_COPY_FILLS) == 0;
+    for (int i = 0; i < 4 && c->zero_copy; ++i) {
       hipPointerAttribute_t at;
       memset(&at, 0, sizeof(at));
       if (hipPointerGetAttributes(&at, h[i]) != hipSuccess || at.type != hipMemoryTypeHost ||

@@ -8,7 +8,7 @@ implementation to fall back to.
 The functions carry the C names: moe_workspace_bytes, moe_route, moe_forward,
 moe_forward_bias_step, moe_forward_block, moe_bias_update, moe_bias_update_stats,
 moe_backward, moe_quantize_int4, moe_pack_routed_bf16, moe_forward_cached, moe_cache_create, moe_cache_prepare,
-moe_cache_state, moe_cache_destroy, moe_status_str.  Weights, routing buffers and
+moe_cache_state, moe_cache_destroy, moe_forward_events (instrumentation), moe_status_str.  Weights, routing buffers and
 gradients are passed as dicts of torch tensors keyed by the C field names.
 """
 from __future__ import annotations
@@ -23,6 +23,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfgmoe.so
 
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_ALIAS, MOE_E_DEVICE = range(6)
 MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_BF16_STAGED = 0, 1, 2, 3
+MOE_CACHE_DRY_RUN, MOE_CACHE_COPY_FILLS = 1, 2
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "bf16_staged": MOE_BF16_STAGED}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
@@ -96,8 +97,10 @@ def _load() -> ctypes.CDLL:
     lib.moe_quantize_int4.restype = ctypes.c_int
     lib.moe_pack_routed_bf16.argtypes = [ctypes.POINTER(MoeDims), P, P, P, P, P]
     lib.moe_pack_routed_bf16.restype = ctypes.c_int
-    lib.moe_set_phase_events.argtypes = [ctypes.POINTER(ctypes.c_void_p), I32]
-    lib.moe_set_phase_events.restype = ctypes.c_int
+    lib.moe_forward_events.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, I32, ctypes.c_float, P, P,
+                                       ctypes.POINTER(MoeRouting), ctypes.c_int, P, SZ, P,
+                                       ctypes.POINTER(ctypes.c_void_p), I32]
+    lib.moe_forward_events.restype = ctypes.c_int
     lib.moe_status_str.argtypes = [ctypes.c_int]
     lib.moe_status_str.restype = ctypes.c_char_p
     return lib
@@ -238,16 +241,21 @@ class ExpertCache:
     """The library's LRU expert cache (moe_cache_*).  host: dict of pinned CPU
     tensors (int4 fields of all E experts); dev: dict of device tensors of
     n_slots slots; slot: [E] int32 device tensor.  dry_run keeps only the
-    bookkeeping.  The tensors must outlive the cache."""
+    bookkeeping; copy_fills fills misses with hipMemcpyAsync calls instead
+    of one launch reading the host copy in place.  The tensors must outlive
+    the cache."""
 
-    def __init__(self, dims: MoeDims, n_slots: int, host=None, dev=None, slot=None, dry_run: bool = False):
+    def __init__(self, dims: MoeDims, n_slots: int, host=None, dev=None, slot=None, dry_run: bool = False,
+                 copy_fills: bool = False):
         self._keep = (host, dev, slot)
         self.dry = bool(dry_run)
         hw = MoeWeights(*[_host_ptr((host or {}).get(f)) for f in WEIGHT_FIELDS])
         dw = _struct(MoeWeights, WEIGHT_FIELDS, dev or {})
         h = ctypes.c_void_p()
         _check(LIB.moe_cache_create(ctypes.byref(dims), int(n_slots), ctypes.byref(hw), ctypes.byref(dw),
-                                    _ptr(slot) if slot is not None else None, int(bool(dry_run)), ctypes.byref(h)),
+                                    _ptr(slot) if slot is not None else None,
+                                    (MOE_CACHE_DRY_RUN if dry_run else 0) | (MOE_CACHE_COPY_FILLS if copy_fills else 0),
+                                    ctypes.byref(h)),
                "moe_cache_create")
         self.handle = h
         self.E = dims.E
@@ -290,13 +298,20 @@ def moe_backward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], routing: Di
            "moe_backward")
 
 
-def moe_set_phase_events(events) -> None:
-    """events: sequence of raw hipEvent_t handles (ints), or None to stop recording."""
-    if not events:
-        _check(LIB.moe_set_phase_events(None, 0), "moe_set_phase_events")
-        return
-    arr = (ctypes.c_void_p * len(events))(*[int(e) for e in events])
-    _check(LIB.moe_set_phase_events(arr, len(events)), "moe_set_phase_events")
+def moe_forward_events(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y, routing: Dict[str, torch.Tensor],
+                       ws, events, bias_step: bool = False, gamma: float = 0.0, stats=None, training: bool = False,
+                       stream=None) -> None:
+    """Instrumentation: moe_forward (bias_step False) or moe_forward_bias_step
+    (True) recording the raw hipEvent_t handles `events` (ints, at most 8) at
+    the phase boundaries."""
+    events = list(events or [])
+    arr = (ctypes.c_void_p * max(1, len(events)))(*[int(e) for e in events])
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_forward_events(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), int(bool(bias_step)),
+                                  float(gamma), _ptr(stats), _ptr(y), ctypes.byref(r), int(bool(training)), _ptr(ws),
+                                  ws.numel() * ws.element_size(), _stream(stream), arr, len(events)),
+           "moe_forward_events")
 
 
 # ---------------------------------------------------------------- allocation helpers

@@ -184,9 +184,11 @@ moe_status moe_forward_cached(const moe_dims* dims, const void* x, const moe_wei
  *    multiples of 128); host: the int4 fields (w_gate_up, s_gate_up, w_down,
  *    s_down) point to pinned host arrays of all E experts; dev: the same
  *    fields point to device arrays of n_slots slots; dev_slot: [E] int32
- *    device.  The caller owns all of them and keeps them alive.  dry_run = 1
- *    keeps the bookkeeping only (no copies, no launches; pointers may be
- *    NULL).  Starts empty.
+ *    device.  The caller owns all of them and keeps them alive.  flags: 0, or
+ *    MOE_CACHE_DRY_RUN (bookkeeping only: no copies, no launches; pointers
+ *    may be NULL), or MOE_CACHE_COPY_FILLS (fill misses with hipMemcpyAsync
+ *    even where one launch could read the host copy in place); other bits
+ *    are MOE_E_ARG.  Starts empty.
  *  moe_cache_prepare: host_counts [E] (host) = the batch's loads.  Experts
  *    with a load that are resident are kept; each other one (in ascending
  *    order) takes a free slot, else the slot whose last use is oldest among
@@ -203,8 +205,9 @@ moe_status moe_forward_cached(const moe_dims* dims, const void* x, const moe_wei
  *    0 if by hipMemcpyAsync calls.
  *  moe_cache_destroy: frees the bookkeeping (not the caller's buffers). */
 typedef struct moe_expert_cache moe_expert_cache;
+enum { MOE_CACHE_DRY_RUN = 1, MOE_CACHE_COPY_FILLS = 2 };
 moe_status moe_cache_create(const moe_dims* dims, int32_t n_slots, const moe_weights* host, const moe_weights* dev,
-                            int32_t* dev_slot, int32_t dry_run, moe_expert_cache** out);
+                            int32_t* dev_slot, int32_t flags, moe_expert_cache** out);
 moe_status moe_cache_prepare(moe_expert_cache* cache, const int32_t* host_counts, void* stream, int32_t* misses);
 moe_status moe_cache_state(const moe_expert_cache* cache, int32_t* slot_of, int64_t* hits_misses);
 void moe_cache_destroy(moe_expert_cache* cache);
@@ -297,16 +300,22 @@ moe_status moe_quantize_int4(int32_t dtype, const void* w, int64_t rows, int32_t
 moe_status moe_pack_routed_bf16(const moe_dims* dims, const void* w_gate_up, const void* w_down, void* out_gate_up,
                                 void* out_down, void* stream);
 
-/* Instrumentation, not part of the layer.  Registers n (0..8) hipEvent_t
- * handles, passed as void*, that every later moe_forward records on its
- * stream at its phase boundaries:
- *   0 before the router, 1 after routing and dispatch bookkeeping,
+/* Instrumentation, not part of the layer.  moe_forward (bias_step = 0; gamma
+ * and stats ignored) or moe_forward_bias_step (bias_step = 1) that also
+ * records the caller's hipEvent_t handles events[0 .. n_events-1] (passed
+ * as void*, n_events 0..8) on `stream` at its phase boundaries:
+ *   0 before the router, 1 after routing and dispatch bookkeeping (the int4
+ *   decode: after the whole forward and its bias step),
  *   2 after the gate/up launch (routed and shared experts together),
  *   3 after the down launch (routed and shared together), 4 after the combine.
- * Boundaries beyond n are not recorded; n = 0 (or events = NULL) turns the
- * recording off.  The registration is process-wide: do not change it while
- * another thread is inside moe_forward.  The caller owns the events. */
-moe_status moe_set_phase_events(void* const* events, int32_t n);
+ * Boundaries beyond n_events are not recorded.  Nothing is kept after the
+ * call returns (no process-wide state); the caller owns the events.  A null
+ * entry among the first n_events, n_events outside 0..8, or bias_step not 0
+ * or 1 is MOE_E_ARG; otherwise the statuses of the call it instruments. */
+moe_status moe_forward_events(const moe_dims* dims, const void* x, const moe_weights* w, float* bias,
+                              int32_t bias_step, float gamma, float* stats, void* y, const moe_routing* routing,
+                              int training, void* ws, size_t ws_bytes, void* stream, void* const* events,
+                              int32_t n_events);
 
 /* Static, NUL-terminated description of a status code. */
 const char* moe_status_str(moe_status s);

@@ -21,6 +21,37 @@ def rel_fro(a, b) -> float:
     return float(np.linalg.norm(a - b) / (nb if nb > 0 else 1.0))
 
 
+def row_rel_max(a, b) -> float:
+    """Largest per-row relative error max_t ||a_t - b_t|| / ||b_t|| over the
+    token rows (the last axis is the row); a row whose reference is zero must
+    be zero.  A localised fault (one wrong MFMA tile, one wrong column band of
+    a ragged tile) that the whole-tensor norm would average away shows here."""
+    a = np.asarray(a, dtype=np.float64)
+    b = np.asarray(b, dtype=np.float64)
+    a = a.reshape(-1, a.shape[-1])
+    b = b.reshape(-1, b.shape[-1])
+    if a.shape[0] == 0:
+        return 0.0
+    num = np.linalg.norm(a - b, axis=1)
+    den = np.linalg.norm(b, axis=1)
+    zero = den == 0
+    r = np.where(zero, np.where(num == 0, 0.0, np.inf), num / np.where(zero, 1.0, den))
+    return float(r.max())
+
+
+def check_close(a, b, act: str, what: str = "", tol=None) -> float:
+    """The output bar: relative Frobenius error over the whole tensor within
+    the layer's tolerance (1e-2 bf16, 1e-4 fp32), and every token row within
+    three times that.  Returns the whole-tensor error."""
+    tol = {"f32": 1e-4, "bf16": 1e-2}[act] if tol is None else tol
+    err = rel_fro(a, b)
+    row = row_rel_max(a, b)
+    print(f"{what} rel_fro = {err:.3e}, worst row {row:.3e}", flush=True)
+    assert err <= tol, (what, err)
+    assert row <= 3 * tol, (what, "worst row", row)
+    return err
+
+
 def scores(inp: synth.LayerInputs) -> np.ndarray:
     """Sigmoid scores of every (token, expert) from the oracle's router."""
     return om.route(inp.x, inp.w_router, np.zeros(inp.E, np.float32), inp.k).scores

@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
                                            "moe_quantize_int4", "moe_pack_routed_bf16", "moe_forward_bias_step", "moe_status_str",
-                                           "moe_set_phase_events", "moe_forward_cached", "moe_cache_create",
+                                           "moe_forward_events", "moe_forward_cached", "moe_cache_create",
                                            "moe_cache_prepare", "moe_cache_state", "moe_cache_destroy"])
 
 
@@ -131,6 +131,31 @@ def test_forward_bias_step_host_checks(lib):
     # stats inside the workspace
     assert f(*ok, 0x20000, 1e-3, ws + 64, y, ctypes.byref(R), 0, ws, need, None) == lib.MOE_E_ALIAS
     assert f(*ok, 0x20000, 1e-3, None, y, ctypes.byref(R), 0, ws, need - 1, None) == lib.MOE_E_WORKSPACE
+
+
+def test_forward_events_host_checks(lib):
+    """The instrumented forward checks its own arguments (event count 0..8,
+    no null event among them, bias_step 0 or 1) and otherwise reports the
+    statuses of the call it instruments, before any launch."""
+    dims = lib.make_dims(16, 128, 8, 64, 256, 2, "bf16")
+    need = lib.moe_workspace_bytes(dims)
+    W = lib.MoeWeights(0x100000, 0x200000, 0x300000, None, None, 0x400000, 0x500000)
+    R = lib.MoeRouting(*[0x40000000 + i * 0x1000000 for i in range(6)])
+    f = lib.LIB.moe_forward_events
+    x, y, ws, b = 0x1000, 0x8000, 0x90000000, 0x20000
+    ev9 = (ctypes.c_void_p * 9)(*([0x123] * 9))
+    ev_null = (ctypes.c_void_p * 2)(0x123, None)
+    head = (ctypes.byref(dims), x, ctypes.byref(W), b)
+    tail = (y, ctypes.byref(R), 0, ws, need, None)
+    assert f(*head, 0, 0.0, None, *tail, ev9, 9) == lib.MOE_E_ARG
+    assert f(*head, 0, 0.0, None, *tail, ev9, -1) == lib.MOE_E_ARG
+    assert f(*head, 0, 0.0, None, *tail, None, 2) == lib.MOE_E_ARG
+    assert f(*head, 0, 0.0, None, *tail, ev_null, 2) == lib.MOE_E_ARG
+    assert f(*head, 2, 0.0, None, *tail, ev9, 0) == lib.MOE_E_ARG
+    assert f(ctypes.byref(dims), x, ctypes.byref(W), None, 1, 1e-3, None, *tail, ev9, 0) == lib.MOE_E_ARG
+    # the instrumented call's own checks: workspace, aliasing
+    assert f(*head, 0, 0.0, None, y, ctypes.byref(R), 0, ws, need - 1, None, ev9, 0) == lib.MOE_E_WORKSPACE
+    assert f(*head, 1, 1e-3, 0x20004, *tail, ev9, 0) == lib.MOE_E_ALIAS
 
 
 def test_quantize_int4_host_checks(lib):

@@ -132,3 +132,19 @@ def test_forward_cached_host_checks(moe):
     assert f(*args(0xA000, 8, big)) == moe.MOE_E_UNSUPPORTED
     bf = moe.make_dims(8, 1024, 64, 512, 2048, 1, "bf16")
     assert f(*args(0xA000, 8, bf)) == moe.MOE_E_UNSUPPORTED
+
+
+def test_cache_create_rejects_unknown_flags(moe):
+    """moe_cache_create takes MOE_CACHE_DRY_RUN and MOE_CACHE_COPY_FILLS; any
+    other bit is an argument error, before anything is created."""
+    import ctypes
+    dims = moe.make_dims(8, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+    h = ctypes.c_void_p()
+    w = moe.MoeWeights()
+    for flags in (4, 8, 1 << 30, -1):
+        assert moe.LIB.moe_cache_create(ctypes.byref(dims), 4, ctypes.byref(w), ctypes.byref(w), None, flags,
+                                        ctypes.byref(h)) == moe.MOE_E_ARG
+    code = moe.LIB.moe_cache_create(ctypes.byref(dims), 4, ctypes.byref(w), ctypes.byref(w), None,
+                                    moe.MOE_CACHE_DRY_RUN | moe.MOE_CACHE_COPY_FILLS, ctypes.byref(h))
+    assert code == moe.MOE_OK and h.value
+    moe.LIB.moe_cache_destroy(h)

@@ -56,6 +56,9 @@ def _check(inp, tol):
     print(f"[{inp.act} T={inp.T} E={inp.E} k={inp.k}] " + ", ".join(f"{n}={e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= tol, (n, e)
+    row = H.row_rel_max(got["dx"], gref.dx)              # every token row of dx within 3x the tolerance
+    print(f"  worst dx row {row:.2e}", flush=True)
+    assert row <= 3 * tol, ("dx worst row", row)
     return got, gref, rn
 
 

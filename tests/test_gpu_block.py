@@ -53,6 +53,10 @@ def _check(h, h_out, h_ref, what):
     print(f"[{what}] rel_fro(h_out) = {e1:.2e}, ||h_out - h_ref|| / ||y_ref|| = "
           f"{err / np.linalg.norm(y_ref):.2e} (bound {bound / np.linalg.norm(y_ref):.2e})", flush=True)
     assert e1 <= 1e-2 and err <= bound, (e1, err, bound)
+    # every token row: three times the layer's tolerance plus one rounding
+    rerr = np.linalg.norm(h_out - h_ref, axis=-1)
+    rbound = 3e-2 * np.linalg.norm(y_ref, axis=-1) + 2.0 ** -8 * np.linalg.norm(h_ref, axis=-1)
+    assert np.all(rerr <= rbound), ("worst row", float((rerr / rbound).max()))
 
 
 def _bf(a):

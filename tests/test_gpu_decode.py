@@ -61,9 +61,7 @@ def test_int4_top1_decode(weights, T):
     y, rn, y_ref, ref = _run(weights, T, seed=100 + T)
     H.check_routing_exact(rn, ref, 64)
     assert np.all(rn["gate"] == 1.0)
-    err = H.rel_fro(y, y_ref)
-    print(f"decode T={T}: rel_fro(y) = {err:.3e}, active experts {np.count_nonzero(rn['counts'])}", flush=True)
-    assert err <= 1e-2
+    H.check_close(y, y_ref, "bf16", f"decode T={T} ({np.count_nonzero(rn['counts'])} active experts) y:")
 
 
 def test_int4_decode_all_tokens_one_expert(weights):

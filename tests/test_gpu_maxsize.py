@@ -19,6 +19,7 @@ import pytest
 
 import oracle.moe_oracle as om
 from fine_grained_moe_amd import synth
+from tests import _helpers as H
 
 pytestmark = pytest.mark.gpu
 
@@ -103,3 +104,6 @@ def test_largest_accepted_batch():
     print(f"max batch: {clear.sum()} of {len(sample)} sampled tokens clear of ties, rel_fro(y) = {err:.3e}",
           flush=True)
     assert err <= 1e-2
+    row = H.row_rel_max(ys[clear], y_ref[clear])
+    print(f"  worst sampled row {row:.3e}", flush=True)
+    assert row <= 3e-2

@@ -65,10 +65,8 @@ def _check(inp, b, q, y, rn, what):
     y_ref, ref = om.forward_int4_top1(inp.x, inp.w_router, qg, sg, qd, sd, inp.w_sh_gate_up, inp.w_sh_down, b)
     H.check_routing_exact(rn, ref, inp.E)
     assert np.all(rn["gate"] == 1.0)
-    err = H.rel_fro(y, y_ref)
-    print(f"[{what}] prefill T={inp.T}: rel_fro(y) = {err:.3e}, active experts "
-          f"{np.count_nonzero(rn['counts'])}", flush=True)
-    assert err <= 1e-2
+    err = H.check_close(y, y_ref, "bf16",
+                        f"[{what}] prefill T={inp.T} ({np.count_nonzero(rn['counts'])} active experts) y:")
     return err
 
 
@@ -148,3 +146,6 @@ def test_int4_prefill_block():
     bound = 1e-2 * float(np.linalg.norm(y_ref)) + 2.0 ** -8 * float(np.linalg.norm(h_ref))
     print(f"[block] prefill T={T}: ||h_out - h_ref|| / ||y_ref|| = {err / np.linalg.norm(y_ref):.2e}", flush=True)
     assert H.rel_fro(h_out, h_ref) <= 1e-2 and err <= bound
+    rerr = np.linalg.norm(h_out - h_ref, axis=-1)
+    rbound = 3e-2 * np.linalg.norm(y_ref, axis=-1) + 2.0 ** -8 * np.linalg.norm(h_ref, axis=-1)
+    assert np.all(rerr <= rbound), ("worst row", float((rerr / rbound).max()))

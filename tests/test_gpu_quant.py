@@ -80,6 +80,13 @@ def _edge_groups():
     g = synth.round_to_bf16(np.geomspace(1e-4, 50.0, 128).astype(np.float32))
     g[::3] *= -1
     rows.append(g)                                          # six decades in one group
+    g = z.copy()
+    g[5] = 7 * (1 + 2 ** -8)                                # absmax / 7 = 1 + 2^-8, a bf16 tie: scale 1 (even)
+    g[9] = -3.5                                             # q tie: to even, -4
+    rows.append(g)
+    g = z.copy()
+    g[40] = -7 * (1 + 3 * 2 ** -8)                          # absmax / 7 = 1 + 3 * 2^-8: scale rounds up to 1 + 2^-6
+    rows.append(g)
     return np.stack(rows)
 
 
@@ -128,6 +135,4 @@ def test_exported_weights_serve_the_int4_path():
                                       np.zeros(64, np.float32))
     rn = {k: v.cpu().numpy() for k, v in r.items()}
     H.check_routing_exact(rn, ref, 64)
-    err = H.rel_fro(y.float().cpu().numpy(), y_ref)
-    print(f"export -> serve T={T}: rel_fro(y) = {err:.3e}", flush=True)
-    assert err <= 1e-2
+    H.check_close(y.float().cpu().numpy(), y_ref, "bf16", f"export -> serve T={T} y:")

@@ -114,6 +114,4 @@ def test_staged_other_shape_against_oracle():
     H.remove_near_ties(inp)
     y = _compare(inp).float().cpu().numpy().astype(np.float64)
     y_ref, _ = H.oracle_forward(inp)
-    err = H.rel_fro(y, y_ref)
-    print(f"staged d=256 E=8 k=3: rel_fro(y) = {err:.3e}", flush=True)
-    assert err <= 1e-2
+    H.check_close(y, y_ref, "bf16", "staged d=256 E=8 k=3 y:")

@@ -1,9 +1,14 @@
-"""GPU parity of expert streaming (int4 top-1 serving): moe_forward_cached,
-which reads expert e's int4 weights from slot slot[e], gives the bits of
-moe_forward on the full expert arrays; and the LRU expert cache
-(moe_cache_prepare), filling a few slots from pinned host memory step by
-step, keeps those bits at every step of a stream of fresh batches.
-moe_forward itself is checked against the oracle in test_gpu_decode.py."""
+"""GPU parity of expert streaming (int4 top-1 serving) against the oracle.
+
+moe_forward_cached reads expert e's int4 weights from slot slot[e]; the LRU
+expert cache (moe_cache_prepare) fills a few slots from pinned host memory
+step by step.  At every step the streamed forward's routing must equal the
+oracle's exactly and y must be within the bf16 tolerance of
+om.forward_int4_top1 on the same packed bytes (whole tensor 1e-2, every token
+row 3e-2); it must also give the bits of moe_forward on the full expert
+arrays.  The stream runs once with misses filled by one launch that reads the
+host copy in place and once with hipMemcpyAsync fills.  Token rows that come
+within 1e-3 of a top-1/top-2 tie are redrawn (the oracle decides which)."""
 import numpy as np
 import pytest
 
@@ -30,15 +35,39 @@ def layer():
     full = {n: t.cuda() for n, t in host.items()}
     full.update(w_router=bf(base.w_router).cuda(), w_sh_gate_up=bf(base.w_sh_gate_up).cuda(),
                 w_sh_down=bf(base.w_sh_down).cuda())
-    return base, host, full
+    return base, host, full, (qg, sg, qd, sd)
 
 
-def _x(T, seed):
+def _x(T, seed, base):
+    """RMS-normalised bf16 token rows clear of top-1 near ties; returns the
+    numpy values and the device tensor."""
     import torch
+    from tests import _helpers as H
     rng = np.random.default_rng(seed)
-    x = rng.standard_normal((T, D)).astype(np.float32)
-    x /= np.sqrt((x.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6).astype(np.float32)
-    return torch.from_numpy(synth.round_to_bf16(x)).to(device="cuda", dtype=torch.bfloat16)
+
+    def draw(n):
+        x = rng.standard_normal((n, D)).astype(np.float32)
+        x /= np.sqrt((x.astype(np.float64) ** 2).mean(axis=1, keepdims=True) + 1e-6).astype(np.float32)
+        return synth.round_to_bf16(x)
+    x = draw(T)
+    for _ in range(20):
+        v = om.route(x, base.w_router, np.zeros(E, np.float32), 1).v
+        bad = np.nonzero(om.topk_margin(v, 1) < H.NEAR_TIE)[0]
+        if bad.size == 0:
+            return x, torch.from_numpy(x).to(device="cuda", dtype=torch.bfloat16)
+        x[bad] = draw(bad.size)
+    raise RuntimeError("near-tie redraw did not converge")
+
+
+def _oracle(base, q, x_np, rn):
+    """Routing exact and y within the bf16 bar of the oracle on the packed bytes."""
+    from tests import _helpers as H
+    qg, sg, qd, sd = q
+    y_ref, ref = om.forward_int4_top1(x_np, base.w_router, qg, sg, qd, sd, base.w_sh_gate_up, base.w_sh_down,
+                                      np.zeros(E, np.float32))
+    H.check_routing_exact(rn, ref, E)
+    assert np.all(rn["gate"] == 1.0)
+    return y_ref
 
 
 def _reference(dims, x, full, bias):
@@ -54,7 +83,7 @@ def _reference(dims, x, full, bias):
 def test_permuted_slots_give_the_same_bits(layer, T):
     import torch
     from fine_grained_moe_amd import moe
-    _, host, full = layer
+    base, host, full, q = layer
     dims = moe.make_dims(T, D, E, F, FS, 1, "bf16", w_routed="int4")
     perm = np.random.default_rng(T).permutation(E).astype(np.int32)       # expert e -> slot perm[e]
     slotted = dict(full)
@@ -63,23 +92,28 @@ def test_permuted_slots_give_the_same_bits(layer, T):
         t[torch.from_numpy(perm).long().cuda()] = full[n]
         slotted[n] = t
     slot = torch.from_numpy(perm).cuda()
-    x = _x(T, 100 + T)
+    from tests import _helpers as H
+    x_np, x = _x(T, 100 + T, base)
     bias = torch.zeros(E, device="cuda")
-    y_ref, r_ref = _reference(dims, x, full, bias)
+    y_full, r_full = _reference(dims, x, full, bias)
     y = torch.empty_like(x)
     r = moe.alloc_routing(dims)
     moe.moe_forward_cached(dims, x, slotted, slot, E, bias, y, r, moe.alloc_workspace(dims))
     torch.cuda.synchronize()
-    assert torch.equal(y, y_ref)
+    y_ref = _oracle(base, q, x_np, {k: v.cpu().numpy() for k, v in r.items()})
+    H.check_close(y.float().cpu().numpy(), y_ref, "bf16", f"cached T={T}, permuted slots, y:")
+    assert torch.equal(y, y_full)
     for n in r:
-        assert torch.equal(r[n], r_ref[n]), n
+        assert torch.equal(r[n], r_full[n]), n
 
 
-def test_lru_stream_matches_the_full_layer(layer):
+@pytest.mark.parametrize("copy_fills", [False, True])
+def test_lru_stream_matches_the_oracle(layer, copy_fills):
     """12 slots for 64 experts, 8 tokens per step, 12 steps of fresh tokens."""
     import torch
     from fine_grained_moe_amd import moe
-    _, host, full = layer
+    from tests import _helpers as H
+    base, host, full, q = layer
     T, n_slots = 8, 12
     dims = moe.make_dims(T, D, E, F, FS, 1, "bf16", w_routed="int4")
     pinned = {n: t.contiguous().pin_memory() for n, t in host.items()}
@@ -87,7 +121,9 @@ def test_lru_stream_matches_the_full_layer(layer):
     for t in dev.values():
         t.fill_(0)
     slot = torch.full((E,), -1, dtype=torch.int32, device="cuda")
-    cache = moe.ExpertCache(dims, n_slots, host=pinned, dev=dev, slot=slot)
+    cache = moe.ExpertCache(dims, n_slots, host=pinned, dev=dev, slot=slot, copy_fills=copy_fills)
+    cache.state()
+    assert not (copy_fills and cache.zero_copy)
     w = dict(full)
     w.update(dev)
     bias = torch.zeros(E, device="cuda")
@@ -95,7 +131,7 @@ def test_lru_stream_matches_the_full_layer(layer):
     r = moe.alloc_routing(dims)
     total_misses = 0
     for step in range(12):
-        x = _x(T, 500 + step)
+        x_np, x = _x(T, 500 + step, base)
         moe.moe_route(dims, x, full["w_router"], bias, r, ws)
         counts = r["counts"].cpu().numpy()
         misses = cache.prepare(counts)
@@ -104,20 +140,23 @@ def test_lru_stream_matches_the_full_layer(layer):
         y = torch.empty_like(x)
         r2 = moe.alloc_routing(dims)
         moe.moe_forward_cached(dims, x, w, slot, n_slots, bias, y, r2, ws)
-        y_ref, r_ref = _reference(dims, x, full, bias)
+        y_full, r_full = _reference(dims, x, full, bias)
         torch.cuda.synchronize()
-        assert torch.equal(y, y_ref), step
-        assert torch.equal(r2["idx"], r_ref["idx"]), step
+        y_ref = _oracle(base, q, x_np, {k: v.cpu().numpy() for k, v in r2.items()})
+        H.check_close(y.float().cpu().numpy(), y_ref, "bf16", f"stream step {step} ({misses} misses) y:")
+        assert torch.equal(y, y_full), step
+        assert torch.equal(r2["idx"], r_full["idx"]), step
     so, hits, misses_all = cache.state()
     assert misses_all == total_misses and hits + misses_all >= 12
-    print(f"lru stream: {misses_all} misses, {hits} hits over 12 steps with {n_slots} slots", flush=True)
+    print(f"lru stream ({'hipMemcpyAsync' if not cache.zero_copy else 'one launch'} fills): {misses_all} misses, "
+          f"{hits} hits over 12 steps with {n_slots} slots", flush=True)
     cache.close()
 
 
 def test_more_experts_than_slots_is_refused(layer):
     import torch
     from fine_grained_moe_amd import moe
-    _, host, full = layer
+    _, host, full, _ = layer
     T = 8
     dims = moe.make_dims(T, D, E, F, FS, 1, "bf16", w_routed="int4")
     pinned = {n: t.contiguous().pin_memory() for n, t in host.items()}
