@@ -5,6 +5,7 @@
 #include <stdint.h>
 
 #include <algorithm>
+#include <mutex>
 #include <vector>
 
 #include "kernels.h"
@@ -556,6 +557,54 @@ moe_status forward_core(const moe_dims* dims, const void* x, const moe_weights* 
 }  // namespace
 
 extern "C" {
+
+}  // extern "C"
+
+namespace {
+
+// The workspace of moe_forward_noalloc: a static device array, one copy per
+// GPU the library runs on, held until the process ends.  In host code the
+// array's name is only a host-side stand-in: its device address on the
+// current GPU comes from hipGetSymbolAddress, taken once per device on the
+// first call there and kept in scratch_dev.
+constexpr size_t kNoAllocScratchBytes = (size_t)MOE_NOALLOC_SCRATCH_BYTES;
+__device__ __align__(256) char scratch[kNoAllocScratchBytes];
+
+constexpr int kMaxDevices = 64;
+std::mutex scratch_mu;
+void* scratch_dev[kMaxDevices];
+
+// This GPU's address of `scratch`, or null if the runtime refuses it.
+void* scratch_on_current_device() {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lock(scratch_mu);
+  if (!scratch_dev[dev]) {
+    void* p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+      (void)hipGetLastError();
+      return nullptr;
+    }
+    scratch_dev[dev] = p;
+  }
+  return scratch_dev[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+moe_status moe_forward_noalloc(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
+                               const moe_routing* routing, void* stream) {
+  moe_status st = check_dims(dims);
+  if (st != MOE_OK) return st;
+  // the size check comes first: a refused request touches no device state
+  if (make_layout(*dims, 0).total > kNoAllocScratchBytes) return MOE_E_WORKSPACE;
+  void* ws = scratch_on_current_device();
+  if (!ws) return MOE_E_DEVICE;
+  return forward_core(dims, x, w, bias, y, routing, 0, ws, kNoAllocScratchBytes,
+                      reinterpret_cast<hipStream_t>(stream), nullptr, false);
+}
 
 moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias, void* y,
                        const moe_routing* routing, int training, void* ws, size_t ws_bytes, void* stream) {

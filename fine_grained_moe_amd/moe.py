@@ -24,6 +24,7 @@ LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libfgmoe.so
 MOE_OK, MOE_E_ARG, MOE_E_UNSUPPORTED, MOE_E_WORKSPACE, MOE_E_ALIAS, MOE_E_DEVICE = range(6)
 MOE_F32, MOE_BF16, MOE_INT4_G128, MOE_BF16_STAGED = 0, 1, 2, 3
 MOE_CACHE_DRY_RUN, MOE_CACHE_COPY_FILLS = 1, 2
+MOE_NOALLOC_SCRATCH_BYTES = 8 << 20      # the static workspace of moe_forward_noalloc
 
 DTYPES = {"f32": MOE_F32, "bf16": MOE_BF16, "int4": MOE_INT4_G128, "bf16_staged": MOE_BF16_STAGED}
 TORCH_DTYPE = {MOE_F32: torch.float32, MOE_BF16: torch.bfloat16}
@@ -68,6 +69,8 @@ def _load() -> ctypes.CDLL:
     lib.moe_forward.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, P, ctypes.POINTER(MoeRouting),
                                 ctypes.c_int, P, SZ, P]
     lib.moe_forward.restype = ctypes.c_int
+    lib.moe_forward_noalloc.argtypes = [dims_p, P, ctypes.POINTER(MoeWeights), P, P, ctypes.POINTER(MoeRouting), P]
+    lib.moe_forward_noalloc.restype = ctypes.c_int
     lib.moe_forward_block.argtypes = [dims_p, P, P, ctypes.c_float, ctypes.POINTER(MoeWeights), P, P,
                                       ctypes.POINTER(MoeRouting), P, SZ, P]
     lib.moe_forward_block.restype = ctypes.c_int
@@ -171,6 +174,16 @@ def moe_forward(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y, rou
     _check(LIB.moe_forward(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), _ptr(y), ctypes.byref(r),
                            int(bool(training)), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_forward")
+
+
+def moe_forward_noalloc(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, y,
+                        routing: Dict[str, torch.Tensor], stream=None) -> None:
+    """moe_forward on the library's static device workspace (no workspace
+    argument, nothing allocated; inference only)."""
+    w = _struct(MoeWeights, WEIGHT_FIELDS, weights)
+    r = _struct(MoeRouting, ROUTING_FIELDS, routing)
+    _check(LIB.moe_forward_noalloc(ctypes.byref(dims), _ptr(x), ctypes.byref(w), _ptr(bias), _ptr(y),
+                                   ctypes.byref(r), _stream(stream)), "moe_forward_noalloc")
 
 
 def moe_forward_bias_step(dims: MoeDims, x, weights: Dict[str, torch.Tensor], bias, gamma: float, stats, y,

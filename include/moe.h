@@ -159,6 +159,23 @@ moe_status moe_forward_bias_step(const moe_dims* dims, const void* x, const moe_
                                  float gamma, float* stats, void* y, const moe_routing* routing, int training,
                                  void* ws, size_t ws_bytes, void* stream);
 
+/* moe_forward for callers that cannot allocate device memory: code under HIP
+ * graph capture, tight serving loops, harnesses that forbid hipMalloc.  There
+ * is no workspace argument; the workspace is a static device array of
+ * MOE_NOALLOC_SCRATCH_BYTES (8 MiB) that the library holds on every GPU it
+ * runs on until the process ends.  No hipMalloc, hipFree or other allocating
+ * call is made.  Inference only (training = 0).  Dims whose
+ * moe_workspace_bytes(dims, 0) exceeds the array return MOE_E_WORKSPACE
+ * before anything is enqueued (at the NanoColibri shape: the bf16 layer up to
+ * 512 tokens, the int4 top-1 serving path up to 64 tokens).  Every call on a
+ * GPU uses that GPU's one array: calls that overlap on one GPU (two streams,
+ * two threads) race and give wrong results, so serialise them.  Nothing the
+ * forward reads from the array is left over from an earlier call.  The other
+ * arguments, outputs and statuses are moe_forward's. */
+#define MOE_NOALLOC_SCRATCH_BYTES (8u << 20)
+moe_status moe_forward_noalloc(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias,
+                               void* y, const moe_routing* routing, void* stream);
+
 /* Expert streaming (the opening section's proof-of-loop paragraph: a token
  * touches the resident shared expert plus a couple of small routed experts
  * streamed from larger storage).  moe_forward on the int4 top-1 decode path

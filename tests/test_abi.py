@@ -30,7 +30,7 @@ def test_header_declares_the_entry_points():
     assert declared_functions() == sorted(["moe_workspace_bytes", "moe_route", "moe_forward", "moe_forward_block",
                                            "moe_bias_update", "moe_bias_update_stats", "moe_backward",
                                            "moe_quantize_int4", "moe_pack_routed_bf16", "moe_forward_bias_step", "moe_status_str",
-                                           "moe_forward_events", "moe_forward_cached", "moe_cache_create",
+                                           "moe_forward_events", "moe_forward_noalloc", "moe_forward_cached", "moe_cache_create",
                                            "moe_cache_prepare", "moe_cache_state", "moe_cache_destroy"])
 
 
@@ -244,3 +244,19 @@ def test_pack_routed_host_checks(lib):
     assert moe.moe_workspace_bytes(staged) > 0
     assert moe.moe_workspace_bytes(staged, training=True) == 0                           # inference only
     assert moe.moe_workspace_bytes(moe.make_dims(4096, 1024, 64, 512, 2048, 2, "f32", w_routed="bf16_staged")) == 0
+
+
+def test_noalloc_refuses_what_does_not_fit(lib):
+    """moe_forward_noalloc checks the dims and the size of their workspace
+    against its static array before it touches any device state, so these
+    refusals need no GPU."""
+    f = lib.LIB.moe_forward_noalloc
+    W = lib.MoeWeights(0x100000, 0x200000, 0x300000, None, None, 0x400000, 0x500000)
+    R = lib.MoeRouting(*[0x40000000 + i * 0x1000000 for i in range(6)])
+    big = lib.make_dims(4096, 1024, 64, 512, 2048, 2, "bf16")
+    assert lib.moe_workspace_bytes(big) > lib.MOE_NOALLOC_SCRATCH_BYTES
+    assert f(ctypes.byref(big), 0x1000, ctypes.byref(W), 0x2000, 0x3000, ctypes.byref(R), None) == lib.MOE_E_WORKSPACE
+    bad = lib.make_dims(16, 1024, 65, 512, 2048, 2, "bf16")
+    assert f(ctypes.byref(bad), 0x1000, ctypes.byref(W), 0x2000, 0x3000, ctypes.byref(R), None) == lib.MOE_E_UNSUPPORTED
+    fits = lib.make_dims(500, 1024, 64, 512, 2048, 2, "bf16")
+    assert lib.moe_workspace_bytes(fits) <= lib.MOE_NOALLOC_SCRATCH_BYTES
