@@ -502,11 +502,13 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.xn = at<uint16_t>(ws, L.xb);
   a.slot = slot;
   a.n_slots = n_slots;
+  // the bias step: stage 2's first workgroup takes it once the loads are
+  // known (the router in stage 1 is the bias's only reader)
+  a.step_bias = bs ? bs->bias : nullptr;
+  a.step_gamma = bs ? bs->gamma : 0.f;
+  a.step_stats = bs ? bs->stats : nullptr;
   mark_phase(ph, 0, s);
   launch_decode(a, s);
-  // the decode's launches hold no point where all loads are known before the
-  // bias is no longer read, so the bias step is a launch of its own here
-  if (bs) launch_bias_update(d.E, (long long)d.T * d.k, routing->counts, bs->gamma, bs->bias, bs->stats, s);
   mark_phase(ph, 1, s);
   return device_status();
 }

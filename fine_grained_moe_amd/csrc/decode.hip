@@ -18,7 +18,8 @@
 //            normalises its 16 rows of h, and the router's first expert
 //            tile writes them for stage 2);
 //   stage 2  one workgroup writes the routing outputs (loads, offsets,
-//            dispatch order, active experts); the shared down in four
+//            dispatch order, active experts) and takes the bias step of
+//            moe_forward_bias_step; the shared down in four
 //            contraction quarters (fp32 partials); the routed gate/up of each
 //            active expert over its own tokens (int4 dequantised in
 //            registers);
@@ -43,6 +44,7 @@
 // 128-element group is multiplied on MFMA into a fresh accumulator and then
 // scaled once in fp32 (w = q * scale is never rounded to bf16).
 // The path is HBM-bound: every weight byte is read once per call.
+#include "balance.h"
 #include "common.h"
 #include "kernels.h"
 
@@ -534,9 +536,10 @@ __device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds,
   }
 }
 
-// Block 0 writes the routing; then the shared down (256 items x token
-// tiles); then the routed gate/up (items of experts past the active count
-// exit after the bookkeeping).
+// Block 0 writes the routing (and takes the bias step of
+// moe_forward_bias_step); then the shared down (256 items x token tiles);
+// then the routed gate/up (items of experts past the active count exit after
+// the bookkeeping).
 template <int D, int FR, int FS>
 __global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int ntile) {
   __shared__ float lds[4 * 16 * 33];
@@ -546,6 +549,12 @@ __global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int nt
   if (blk == 0) {
     decode_book(p, B);
     decode_write_routing(p, B);
+    // the bias step (stage 1's router was the bias's only reader)
+    if (p.step_bias && threadIdx.x < 64) {
+      const int e = threadIdx.x;
+      bias_step_wave(e, p.E, (long long)p.T * p.k, e < p.E ? (int)__popcll(B.mask[e]) : 0, p.step_gamma,
+                     p.step_bias, p.step_stats);
+    }
   } else if (blk <= n_sd) {
     int j, tt;
     xcd_item(blk - 1, ntile, j, tt);

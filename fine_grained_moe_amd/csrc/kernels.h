@@ -164,6 +164,10 @@ struct DecodeArgs {
   // e's weights sit in slot slot[e] (clamped to the slots), or null: slot e.
   const int32_t* slot;               // [E] int32, or null
   int n_slots;
+  // the bias step, taken by stage 2 once the loads are known (null: none)
+  float* step_bias;                  // [E] in/out (the bias the router read)
+  float step_gamma;
+  float* step_stats;                 // [4] balance figures, or null
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);
 

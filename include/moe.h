@@ -148,8 +148,7 @@ moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w
  * and, when stats is not NULL, stats[0..3] = the balance figures of
  * moe_bias_update_stats.  The same results, bit for bit, as moe_forward
  * followed by moe_bias_update_stats (moe_bias_update when stats is NULL),
- * with one launch fewer where routing has a dispatch launch (every path but
- * the int4 decode, where the bias step stays a launch of its own).
+ * with one launch fewer (the launch that knows the loads takes the step).
  *  bias   [E] float32 (device), read by the router, then updated in place;
  *         must not be NULL (MOE_E_ARG)
  *  stats  [4] float32 (device, written) or NULL
