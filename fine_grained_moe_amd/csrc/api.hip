@@ -70,6 +70,12 @@ moe_status check_training(const moe_dims& d) {
   return MOE_OK;
 }
 
+// The int4 prefill reads the packed experts straight into the grouped GEMMs
+// (dequantised per operand fragment) when a tile's scales fit in LDS;
+// otherwise the experts that received tokens are dequantised to bf16 in the
+// workspace first.
+bool int4_prefill_fused(const moe_dims& d) { return d.d / 128 <= kInt4MaxGroups && d.F / 128 <= kInt4MaxGroups; }
+
 // Contraction slices of the shared down GEMM (bf16 forward): 256 x 256
 // tiles over the whole 2048-long contraction would be 64 tiles holding a
 // quarter of the chip for the whole launch.  Two halves measured best on
@@ -109,7 +115,7 @@ Layout make_layout(const moe_dims& d, int training) {
   // bf16: the shared down is split over contraction slices, each written as
   // its own [T, d] block that the combine adds
   L.S = take((size_t)d.T * d.d * es * shared_down_slices(d));
-  if (d.w_routed == MOE_INT4_G128) {
+  if (d.w_routed == MOE_INT4_G128 && !int4_prefill_fused(d)) {
     L.wdq_gu = take((size_t)d.E * 2 * d.F * d.d * 2);
     L.wdq_d = take((size_t)d.E * d.d * d.F * 2);
   }
@@ -295,9 +301,11 @@ namespace {
 // are in place: gate/up (routed + shared), down (routed + shared), combine.
 // w's routed weights are act-typed (the bf16/fp32 layer, or the int4
 // prefill's dequantised copies).
+// routed_int4: w's routed weights are the packed int4 experts with their
+// scales (the int4 prefill), read by the GEMMs directly.
 moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* x, const moe_weights* w, void* y,
                                 const moe_routing* routing, int training, void* ws, hipStream_t s,
-                                const void* resid, const Phases* ph) {
+                                const void* resid, const Phases* ph, bool routed_int4 = false) {
   const size_t D = d.d, F = d.F, Fs = d.Fs;
   const long long slots = (long long)d.T * d.k;
   // bf16 runs on the 256 x 256 tiles of gemm_fwd.hip (grouped jobs index the
@@ -337,6 +345,14 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   g.ldc = F;
   g.aux = training ? at<char>(ws, L.AU) : nullptr;
   g.ldaux = 2LL * F;
+  if (routed_int4) {
+    g.b_int4 = 1;
+    g.b_staged = 0;
+    g.ldb = D / 2;                                   // bytes per packed row
+    g.b_estride = 2LL * F * (D / 2);                 // bytes per expert
+    g.b_scales = w->s_gate_up;
+    g.b_sestride = 2LL * F * (D / 128);              // scales per expert
+  }
 
   GemmJob sg{};
   sg.epi = EPI_SWIGLU;
@@ -386,6 +402,12 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   dn.ldaux = D;
   dn.gate = routing->gate;
   dn.perm = routing->perm;
+  if (routed_int4) {
+    dn.ldb = F / 2;
+    dn.b_estride = (long long)D * (F / 2);
+    dn.b_scales = w->s_down;
+    dn.b_sestride = (long long)D * (F / 128);
+  }
 
   GemmJob sd = sg;
   sd.epi = EPI_STORE;
@@ -451,9 +473,18 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
   rs.push_back({ws, L.total, true});
   if (any_alias(rs)) return MOE_E_ALIAS;
+  if (d.T > kDecodeMaxT && int4_prefill_fused(d)) {
+    // Prefill: route, then the grouped GEMMs read the int4 experts directly
+    // (each operand fragment expanded to bf16(q * scale) in registers).
+    mark_phase(ph, 0, s);
+    enqueue_route(d, L, x, w->w_router, bias, routing, ws, s, bs);
+    mark_phase(ph, 1, s);
+    return enqueue_expert_gemms(d, L, x, w, y, routing, 0, ws, s, resid, ph, true);
+  }
   if (d.T > kDecodeMaxT) {
-    // Prefill: route, dequantise every expert that received tokens into the
-    // workspace (bf16, one rounding of q * scale), then the bf16 expert GEMMs.
+    // Prefill with contractions too long for a tile's scales in LDS: route,
+    // dequantise every expert that received tokens into the workspace (bf16,
+    // one rounding of q * scale), then the bf16 expert GEMMs.
     char* wgu = at<char>(ws, L.wdq_gu);
     char* wd = at<char>(ws, L.wdq_d);
     moe_weights wb = *w;

@@ -81,6 +81,19 @@ __device__ __host__ __forceinline__ long long b_tile_row(bool swiglu, int R, int
   const int w = R >> 7, ni = (R >> 4) & 7, f = R & 15;
   return (long long)nt * BN + w * 128 + 8 * f + ni;
 }
+// 8 int4 codes (one 32-bit word, element 2i in the low nibble of byte i),
+// each times its row's scale and rounded once to bf16, in MFMA operand order:
+// the same bits as the int4 prefill's separate dequantisation.
+__device__ __forceinline__ u32x4_t dq_int4x8(uint32_t w, float sc) {
+  u32x4_t r;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const float lo = (float)(((int)(w << (28 - 8 * j))) >> 28);
+    const float hi = (float)(((int)(w << (24 - 8 * j))) >> 28);
+    r[j] = pack_bf16x2(lo * sc, hi * sc);
+  }
+  return r;
+}
 // contraction slices of a dense job
 __device__ __host__ __forceinline__ int k_slices(const GemmJob& j) { return j.ksplit > 1 ? j.ksplit : 1; }
 // items: grouped jobs the router's tile table; per-expert-contraction jobs
@@ -98,7 +111,9 @@ __device__ __host__ __forceinline__ int xcd_cols(const GemmJob& j) {
   return j.xcd_cols == 2 || j.xcd_cols == 4 || j.xcd_cols == 8 ? j.xcd_cols : 1;
 }
 
-template <bool SWIGLU>
+// I4: the launch has a job with int4 B (the int4 prefill); the bf16-only
+// instantiations carry none of that code.
+template <bool SWIGLU, bool I4>
 __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   typedef bf16_t T;
   // The ring; after the main loop its first buffer holds the row scales.
@@ -176,9 +191,23 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   // wn*128 + ni*16 + f holds output column (tile base) + wn*128 + 8f + ni; for
   // SwiGLU the first 128 B rows are gate rows and the next 128 the matching
   // up rows, with h column (tile base) + wn*64 + 4f + ni.
+  // int4 B (routed experts of the int4 prefill): a stage of B row r is its
+  // 16 bytes (32 nibbles) at LDS byte 16 r, fetched as four 4-byte pieces by
+  // four consecutive lanes, so a wave instruction still covers 16 rows and
+  // every wave issues the same loads per stage as on the bf16 path.
+  const bool b4 = I4 && p.b_int4 != 0;
   const char* a_src[NDA];
   const char* b_src[NDB];
-  const char* bbase = reinterpret_cast<const char*>(p.B) + (long long)e * p.b_estride * (long long)sizeof(T);
+  const char* bbase = reinterpret_cast<const char*>(p.B) +
+                      (long long)e * p.b_estride * (b4 ? 1LL : (long long)sizeof(T));
+  // the weight row that LDS B row R of this tile holds
+  auto b_row = [&](int R) -> long long {
+    if (SWIGLU) {
+      const long long col = min(b_tile_row(true, R, nt, 0), (long long)p.N - 1);
+      return (R >> 7 ? p.up_off : 0) + col;
+    }
+    return min(b_tile_row(false, R, nt, 0), (long long)p.N - 1);
+  };
 #pragma unroll
   for (int j = 0; j < NDA; ++j) {
     const int R = wave * (BM / 8) + j * 16 + (lane >> 2);
@@ -191,27 +220,25 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   for (int j = 0; j < NDB; ++j) {
     const int R = wave * (BN / 8) + j * 16 + (lane >> 2);
     const int c = swz_piece(R, lane & 3);
-    if (p.b_staged) {
+    if (b4) {
+      b_src[j] = bbase + b_row(R) * p.ldb + kofs / 2 + (lane & 3) * 4;
+    } else if (p.b_staged) {
       // stage s of this tile: 256 rows x 64 bytes, contiguous, in LDS row order
       b_src[j] = bbase + (long long)nt * p.K * BN * (long long)sizeof(T) + R * kRowB + c * 16;
     } else {
-      long long brow;
-      if (SWIGLU) {
-        const long long col = min(b_tile_row(true, R, nt, 0), (long long)p.N - 1);
-        brow = (R >> 7 ? p.up_off : 0) + col;
-      } else {
-        brow = min(b_tile_row(false, R, nt, 0), (long long)p.N - 1);
-      }
-      b_src[j] = bbase + (brow * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
+      b_src[j] = bbase + (b_row(R) * p.ldb + kofs) * (long long)sizeof(T) + c * 16;
     }
   }
-  const long long b_step = p.b_staged ? (long long)BN * kRowB : (long long)kRowB;
+  const long long b_step = b4 ? 16LL : p.b_staged ? (long long)BN * kRowB : (long long)kRowB;
   const int nk = (int)((long long)klen * sizeof(T) / kRowB);
   auto issue_one = [&](int s, int j) {
     char* st = lds + (s % kStages) * kStageBytes;
     const long long off = (long long)s * kRowB;
     if (j < NDA)
       __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(st + wave * (BM / 8) * kRowB + j * 1024), 16, 0, 0);
+    else if (b4)
+      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
+                                       (lds_ptr_t)(st + ATILE + wave * (BN / 8) * 16 + (j - NDA) * 256), 4, 0, 0);
     else
       __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
                                        (lds_ptr_t)(st + ATILE + wave * (BN / 8) * kRowB + (j - NDA) * 1024), 16, 0, 0);
@@ -236,40 +263,80 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
+  // int4 B: the tile's bf16 scales, [K / 128 groups][256 LDS rows], in ring
+  // buffer 0's B space past the 4 KiB its int4 stage uses (never a load
+  // target), filled before the ring and made visible by a barrier.
+  const uint16_t* scl = reinterpret_cast<const uint16_t*>(lds + ATILE + 4096);
+  if (b4) {
+    const int G = p.K / 128;
+    const uint16_t* sg = reinterpret_cast<const uint16_t*>(p.b_scales) + (long long)e * p.b_sestride;
+    uint16_t* dst = reinterpret_cast<uint16_t*>(lds + ATILE + 4096);
+    for (int i = tid; i < G * BN; i += NTHR) {
+      const int gi = i / BN, R = i - gi * BN;
+      dst[i] = sg[b_row(R) * G + gi];
+    }
+    __syncthreads();
+  }
+  // Lane (fr, g)'s int4 operand of LDS B row r: the 8 nibbles of elements
+  // 8g .. 8g + 7 of the stage, and the row's scale for stage s's group.
+  auto qword = [&](const char* Bs, int r) { return *reinterpret_cast<const uint32_t*>(Bs + r * 16 + 4 * g); };
+  auto qscale = [&](int s, int r) { return bf16_to_f32(scl[(s >> 2) * BN + r]); };
+
   // Operands of one stage: lane group g owns 16-byte piece g of each 64-byte
   // row chunk.  The MFMAs of stage s run from registers (fa, fb) while the
   // operands of stage s + 1 are read from LDS behind them: fb[ni] is reloaded
   // as soon as the four MFMAs that use it are issued, the A pieces go to a
   // second set (fa of the next stage).  This wave's global loads of stage
   // s + kStages - 1 go between the MFMAs (after blocks ni = 1, 3, 5, 7).
+  // int4 B: the raw code word and scale of each B fragment (expanded to
+  // bf16 right before its MFMAs)
   u32x4_t fa0[4], fa1[4], fb[NI];
+  uint32_t qb[NI];
+  float qs[NI];
   auto read_a = [&](int s, u32x4_t (&fa)[4]) {
     const char* As = lds + (s % kStages) * kStageBytes;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) fa[mi] = ld16(As + swz(arow_l[mi], g));
   };
-  auto read_b = [&](int s) {
+  auto read_b = [&](int s, auto b4c) {
     const char* Bs = lds + (s % kStages) * kStageBytes + ATILE;
 #pragma unroll
-    for (int ni = 0; ni < NI; ++ni) fb[ni] = ld16(Bs + swz(brow_l[ni], g));
+    for (int ni = 0; ni < NI; ++ni) {
+      if constexpr (decltype(b4c)::value) {
+        qb[ni] = qword(Bs, brow_l[ni]);
+        qs[ni] = qscale(s, brow_l[ni]);
+      } else {
+        fb[ni] = ld16(Bs + swz(brow_l[ni], g));
+      }
+    }
   };
   // stage s from (fa, fb); prefetch: read stage s + 1 into (fn, fb); loads:
   // issue stage s + kStages - 1
   // ACT: this wave's row band holds rows (compile-time, so the loop below is
-  // instantiated once per case and its LDS waits stay exact).
-  auto compute = [&](int s, u32x4_t (&fa)[4], u32x4_t (&fn)[4], auto act, auto prefetch, auto with_loads) {
+  // instantiated once per case and its LDS waits stay exact).  B4: int4 B.
+  auto compute = [&](int s, u32x4_t (&fa)[4], u32x4_t (&fn)[4], auto act, auto prefetch, auto with_loads,
+                     auto b4c) {
     if constexpr (!decltype(act)::value) {
       if constexpr (decltype(with_loads)::value) issue(s + kStages - 1);
       return;
     }
+    constexpr bool B4 = decltype(b4c)::value;
     const char* An = lds + ((s + 1) % kStages) * kStageBytes;
     const char* Bn = An + ATILE;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
+      u32x4_t bv;
+      if constexpr (B4) bv = dq_int4x8(qb[ni], qs[ni]);
+      else bv = fb[ni];
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = Mma<T>::run1(fa[mi], fb[ni], acc[mi][ni]);
+      for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = Mma<T>::run1(fa[mi], bv, acc[mi][ni]);
       if constexpr (decltype(prefetch)::value) {
-        fb[ni] = ld16(Bn + swz(brow_l[ni], g));
+        if constexpr (B4) {
+          qb[ni] = qword(Bn, brow_l[ni]);
+          qs[ni] = qscale(s + 1, brow_l[ni]);
+        } else {
+          fb[ni] = ld16(Bn + swz(brow_l[ni], g));
+        }
         if (ni < 4) fn[ni] = ld16(An + swz(arow_l[ni], g));
       }
       if constexpr (decltype(with_loads)::value) {
@@ -292,11 +359,12 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   else wait_vmcnt<0>();
   block_barrier();
   float my_gate = 0.f;
-  auto run = [&](auto act) {
+  auto run = [&](auto act, auto b4c) {
     using A = decltype(act);
+    using B4 = decltype(b4c);
     if constexpr (A::value) {
       read_a(0, fa0);
-      read_b(0);
+      read_b(0, B4{});
     }
     // Stages issued before iteration s: min(nk, s + 4); in flight after stage
     // s + 1: that minus s + 2.  Two K steps per trip, so the two A sets swap
@@ -306,7 +374,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     for (; s + kStages - 1 < nk; ++s) {
       wait_vmcnt<2 * kLoads>();
       block_barrier();
-      compute(s, fa0, fa1, A{}, std::true_type{}, std::true_type{});
+      compute(s, fa0, fa1, A{}, std::true_type{}, std::true_type{}, B4{});
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
     }
@@ -316,16 +384,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       else wait_vmcnt<0>();
       block_barrier();
       if (scaled && s == nk - 2 && tid < BM) my_gate = p.gate[my_perm];
-      compute(s, fa0, fa1, A{}, std::true_type{}, std::false_type{});
+      compute(s, fa0, fa1, A{}, std::true_type{}, std::false_type{}, B4{});
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
     }
-    compute(s, fa0, fa1, A{}, std::false_type{}, std::false_type{});
+    compute(s, fa0, fa1, A{}, std::false_type{}, std::false_type{}, B4{});
   };
   // an expert with an empty contraction range (no tokens) stores zeros
   if (nk > 0) {
-    if (active) run(std::true_type{});
-    else run(std::false_type{});
+    if (!active) run(std::false_type{}, std::false_type{});   // loads only (issue_one picks the B form)
+    else if constexpr (I4) {
+      if (b4) run(std::true_type{}, std::true_type{});
+      else run(std::true_type{}, std::false_type{});
+    } else {
+      run(std::true_type{}, std::false_type{});
+    }
   }
 
   // Row scales, staged in ring buffer 0 once every wave is past its last
@@ -468,10 +541,14 @@ void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
   }
   if (total == 0) return;
   const dim3 grid((unsigned)(total * 8));
-  if (a.job[0].epi == EPI_SWIGLU)
-    hipLaunchKernelGGL((gemm256_kernel<true>), grid, dim3(NTHR), 0, s, a);
-  else
-    hipLaunchKernelGGL((gemm256_kernel<false>), grid, dim3(NTHR), 0, s, a);
+  const bool i4 = a.job[0].b_int4 || (a.njobs > 1 && a.job[1].b_int4);
+  if (a.job[0].epi == EPI_SWIGLU) {
+    if (i4) hipLaunchKernelGGL((gemm256_kernel<true, true>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((gemm256_kernel<true, false>), grid, dim3(NTHR), 0, s, a);
+  } else {
+    if (i4) hipLaunchKernelGGL((gemm256_kernel<false, true>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((gemm256_kernel<false, false>), grid, dim3(NTHR), 0, s, a);
+  }
 }
 
 }  // namespace fgmoe

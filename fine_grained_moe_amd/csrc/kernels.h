@@ -68,6 +68,14 @@ struct GemmJob {
   // launch_gemm_fwd256 only: B in the stage-major layout of
   // launch_pack_routed (whole 256-row tiles; ldb unused)
   int b_staged;
+  // launch_gemm_fwd256 only, grouped jobs: B holds int4 rows (two nibbles
+  // per byte, element 2i in the low nibble; ldb and b_estride in bytes) with
+  // one bf16 scale per 128 elements of a row in b_scales (row r of expert e
+  // at b_scales + e * b_sestride + r * K / 128); the operand is bf16(q *
+  // scale).  K / 128 <= kInt4MaxGroups.
+  int b_int4;
+  const void* b_scales;
+  long long b_sestride;
   int K;
   int N;                   // output columns (SwiGLU: h columns; B then has gate rows 0..N-1 and up rows up_off..)
   int up_off;
@@ -117,6 +125,9 @@ void launch_gemm(const GemmArgs& a, hipStream_t s);
 // (K % 32 == 0) on 256 x 256 tiles; grouped jobs index the kTileMFwd tile
 // table.
 void launch_gemm_fwd256(const GemmArgs& a, hipStream_t s);
+// Scale groups of an int4 B operand that a launch_gemm_fwd256 tile keeps in
+// LDS (K / 128 of them): K up to 3072.
+constexpr int kInt4MaxGroups = 24;
 // Routed bf16 weights into the stage-major layout that launch_gemm_fwd256
 // reads with b_staged: gate/up [E, 2F, d] (F % 128 == 0) and down [E, d, F]
 // (d % 256 == 0) to arrays of the same sizes.

@@ -49,3 +49,13 @@ def test_traffic_is_null_once_the_kernel_changes(tmp_path, monkeypatch):
     out.write_text(json.dumps(t))
     assert bench.measured_traffic() is not None
 
+
+
+def test_step_time_percentiles():
+    """The per-step distribution the benchmark reports: median, p10, p90 and
+    the count, from the event-timed step times."""
+    import bench
+    d = bench.percentiles([float(v) for v in range(1, 102)])     # 1 .. 101
+    assert d == dict(median=51.0, p10=11.0, p90=91.0, n=101)
+    d = bench.percentiles([5.0] * 7)
+    assert d["median"] == d["p10"] == d["p90"] == 5.0 and d["n"] == 7

@@ -1,7 +1,8 @@
 """GPU parity of the int4 top-1 prefill (w_routed = int4, more than 64 tokens):
-routing, dequantisation of the loaded experts and the grouped bf16 GEMMs,
-against the oracle's layer on the exactly dequantised weights
-(forward_int4_top1).
+routing and the grouped GEMMs reading the packed experts (each operand
+fragment expanded to bf16(q * scale) in registers; for contractions longer
+than 3072, dequantised bf16 copies of the loaded experts), against the
+oracle's layer on the exactly dequantised weights (forward_int4_top1).
 
 The routed weights are N(0, 0.02) draws encoded by the oracle's int4 encoder;
 both sides read the same bytes and scales.  Routing is compared bit-exactly
@@ -149,3 +150,35 @@ def test_int4_prefill_block():
     rerr = np.linalg.norm(h_out - h_ref, axis=-1)
     rbound = 3e-2 * np.linalg.norm(y_ref, axis=-1) + 2.0 ** -8 * np.linalg.norm(h_ref, axis=-1)
     assert np.all(rerr <= rbound), ("worst row", float((rerr / rbound).max()))
+
+
+def test_int4_prefill_fused_equals_bf16_path_bitwise():
+    """The prefill's GEMMs expand each int4 operand fragment to bf16(q *
+    scale) in registers.  Fed the same values as bf16 weights (the host's
+    exact q * scale, rounded once to bf16), the bf16 layer (k = 1) runs the
+    same products in the same order: the outputs must be the same bits."""
+    import torch
+    from fine_grained_moe_amd import moe
+    inp, b, q = _int4_layer(300, seed=23)
+    qg, sg, qd, sd = q
+    y4, rn4 = _run(inp, b, q)
+    dims = moe.make_dims(inp.T, inp.d, inp.E, inp.F, inp.Fs, 1, "bf16")
+    w = dict(w_router=_bf(inp.w_router), w_gate_up=_bf(synth.round_to_bf16(om.dequantize_int4(qg, sg).astype(np.float32))),
+             w_down=_bf(synth.round_to_bf16(om.dequantize_int4(qd, sd).astype(np.float32))),
+             w_sh_gate_up=_bf(inp.w_sh_gate_up), w_sh_down=_bf(inp.w_sh_down))
+    x = _bf(inp.x)
+    y = torch.empty_like(x)
+    r = moe.alloc_routing(dims)
+    moe.moe_forward(dims, x, w, torch.from_numpy(b).cuda(), y, r, moe.alloc_workspace(dims))
+    torch.cuda.synchronize()
+    for n in ("idx", "counts", "perm", "pos"):
+        np.testing.assert_array_equal(r[n].cpu().numpy(), rn4[n], err_msg=n)
+    np.testing.assert_array_equal(y.float().cpu().numpy(), y4)
+
+
+def test_int4_prefill_long_contraction():
+    """d = 3200 (25 scale groups per row, more than a GEMM tile keeps in LDS):
+    the prefill dequantises the loaded experts to bf16 copies first."""
+    inp, b, q = _int4_layer(100, seed=29, d=3200, E=8, F=128, Fs=256)
+    y, rn = _run(inp, b, q)
+    _check(inp, b, q, y, rn, "d3200")
