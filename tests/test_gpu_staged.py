@@ -115,3 +115,32 @@ def test_staged_other_shape_against_oracle():
     y = _compare(inp).float().cpu().numpy().astype(np.float64)
     y_ref, _ = H.oracle_forward(inp)
     H.check_close(y, y_ref, "bf16", "staged d=256 E=8 k=3 y:")
+
+
+def test_staged_block_bitwise_equal_row_major():
+    """The MoE block (RMSNorm in, residual out) on stage-major routed weights,
+    as the 23-layer stack leg runs it, gives the bits of the block on the
+    row-major weights (itself checked against the oracle in
+    test_gpu_block.py)."""
+    import torch
+    from fine_grained_moe_amd import moe
+    T, d, E, F, Fs = 600, 1024, 64, 512, 2048
+    inp = synth.make_layer(T=T, d=d, E=E, F=F, Fs=Fs, k=2, act="bf16", seed=33)
+    x, w = H.to_gpu(inp)
+    rng = np.random.default_rng(33)
+    h = torch.from_numpy(synth.round_to_bf16((rng.standard_normal((T, d)) * 2.0).astype(np.float32))).to(
+        device="cuda", dtype=torch.bfloat16)
+    gamma = torch.from_numpy((1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)).cuda()
+    bias = torch.zeros(E, device="cuda")
+    dims = moe.make_dims(T, d, E, F, Fs, 2, "bf16")
+    dims_s = moe.make_dims(T, d, E, F, Fs, 2, "bf16", w_routed="bf16_staged")
+    outs = []
+    for dm, ww in ((dims, w), (dims_s, _staged(w, dims_s))):
+        out = torch.empty_like(h)
+        r = moe.alloc_routing(dm)
+        moe.moe_forward_block(dm, h, gamma, 1e-6, ww, bias, out, r, moe.alloc_workspace(dm))
+        torch.cuda.synchronize()
+        outs.append((out, r))
+    assert torch.equal(outs[0][0], outs[1][0])
+    for n in outs[0][1]:
+        assert torch.equal(outs[0][1][n], outs[1][1][n]), n
