@@ -26,9 +26,11 @@ struct Layout {
   size_t xb;              // moe_forward_block: x = RMSNorm(h)
   size_t H, O, Hs, S;     // forward intermediates
   size_t AU, Ou, AUs;     // training: routed pre-activations, ungated expert rows, shared pre-activations
-  // backward scratch (training): padded contraction tables and transposed operands
+  // backward scratch (training): padded contraction tables and transposed
+  // operands (fp32; bf16 reads the activations K-major: the token of each
+  // dispatch-order row, a zero row and the gate-scaled routed activations)
   size_t kofs, klen, ksh, pcol, dwr_part, dwpart, dl, dAU, dAUT, XpT, dOT, HT, dXp, WdT, WguT, WsdT, WsguT, dAUs, dAUsT, xT, dyT, HsT,
-      dXs;
+      dXs, krow, zrow, Hg;
   long long P, Tp;        // padded column counts of the routed and shared transposes
   size_t active, n_active, rkey, rscore, part_sh;   // int4 serving path: active experts, router tile maxima, fp32 shared-down partials
   size_t wdq_gu, wdq_d;   // int4 prefill: the experts' weights dequantised to bf16
@@ -135,22 +137,29 @@ Layout make_layout(const moe_dims& d, int training) {
     const int S = splitk_count((long long)Tp);
     L.dwpart = take(S > 1 ? (size_t)S * std::max(2 * Fs * D, D * Fs) * 4 : 0);
     L.dl = take(slots * 4);
+    const bool kmaj = d.act == MOE_BF16;
     L.dAU = take(slots * 2 * F * es);
-    L.dAUT = take(2 * F * P * es);
-    L.XpT = take(D * P * es);
-    L.dOT = take(D * P * es);
-    L.HT = take(F * P * es);
     L.dXp = take(slots * D * es);
     L.WdT = take(E * F * D * es);
     L.WguT = take(E * D * 2 * F * es);
     L.WsdT = take(Fs * D * es);
     L.WsguT = take(D * 2 * Fs * es);
     L.dAUs = take(T * 2 * Fs * es);
-    L.dAUsT = take(2 * Fs * Tp * es);
-    L.xT = take(D * Tp * es);
-    L.dyT = take(D * Tp * es);
-    L.HsT = take(Fs * Tp * es);
     L.dXs = take(T * D * es);
+    if (kmaj) {
+      L.krow = take((slots + 32) * 4);
+      L.zrow = take(512);
+      L.Hg = take(slots * F * es);
+    } else {
+      L.dAUT = take(2 * F * P * es);
+      L.XpT = take(D * P * es);
+      L.dOT = take(D * P * es);
+      L.HT = take(F * P * es);
+      L.dAUsT = take(2 * Fs * Tp * es);
+      L.xT = take(D * Tp * es);
+      L.dyT = take(D * Tp * es);
+      L.HsT = take(Fs * Tp * es);
+    }
   }
   L.total = o;
   return L;
@@ -833,9 +842,16 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   void* HsT = at<char>(ws, L.HsT);
   void* dXs = at<char>(ws, L.dXs);
 
+  // bf16: the weight gradients read the activations K-major (no transposes)
+  const bool kmaj = act == MOE_BF16;
+  int32_t* krow = kmaj ? at<int32_t>(ws, L.krow) : nullptr;
+  void* Hg = kmaj ? at<char>(ws, L.Hg) : nullptr;
+  const long long slots = (long long)d.T * d.k;
+
   // 1. padded per-expert contraction ranges
   const int S = splitk_count(Tp), step = (int)splitk_step(Tp);
-  launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, S, step, kofs, klen, ksh, pcol, s);
+  launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, S, step, kofs, klen, ksh, pcol,
+                  kmaj ? krow + slots : nullptr, kmaj ? at<int32_t>(ws, L.zrow) : nullptr, s);
 
   // 2. transposed weights: W_d^T [E][F][d], W_gu^T [E][d][2F], W_sd^T [Fs][d], W_sgu^T [d][2Fs]
   auto transpose = [&](const void* src, long long ld_src, long long sb, void* dst, long long ld_dst, long long db, int R,
@@ -867,9 +883,8 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
 
   // 3. router and gate gradients
   launch_bwd_gate(act, dy, at<char>(ws, L.Ou), x, w->w_router, routing->idx, routing->gate, routing->pos, d.T, d.d, d.k,
-                  dl, s);
+                  dl, krow, s);
 
-  const long long slots = (long long)d.T * d.k;
   // bf16: the input-gradient launches run on gemm_fwd.hip's 256 x 256 tiles
   // (grouped jobs over the 256-row tile table), fp32 on gemm.hip.
   const bool big = act == MOE_BF16;
@@ -901,6 +916,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hr.ldaux = 2LL * F;
   hr.gate = routing->gate;
   hr.perm = routing->perm;
+  hr.hg = Hg;   // K-major dW_d: the gate-scaled activations g * silu(a) * u
   GemmJob hs{};
   hs.epi = EPI_SWIGLU_BWD;
   hs.A = dy;
@@ -940,6 +956,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   xr.ldc = D;
   xr.aux = nullptr;
   xr.gate = nullptr;
+  xr.hg = nullptr;
   GemmJob xs = hs;
   xs.epi = EPI_STORE;
   xs.A = dAUs;
@@ -959,55 +976,94 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   g2.job[1] = xs;
   gemm_in(g2, s);
 
-  // 6. transposed activations over padded slot columns (routed) and token columns (shared)
-  transpose(dAU, 2LL * F, 0, dAUT, P, 0, 2 * d.F, P, 1, 0, pcol, nullptr, 1, nullptr);
-  transpose(x, D, 0, XpT, P, 0, d.d, P, 1, 0, pcol, routing->perm, d.k, nullptr);
-  transpose(dy, D, 0, dOT, P, 0, d.d, P, 1, 0, pcol, routing->perm, d.k, routing->gate);
-  transpose(at<char>(ws, L.H), F, 0, HT, P, 0, d.F, P, 1, 0, pcol, nullptr, 1, nullptr);
-  transpose(dAUs, 2LL * Fs, 0, dAUsT, Tp, 0, 2 * d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
-  transpose(x, D, 0, xT, Tp, 0, d.d, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
-  transpose(dy, D, 0, dyT, Tp, 0, d.d, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
-  transpose(at<char>(ws, L.Hs), Fs, 0, HsT, Tp, 0, d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
-
-  // 7. weight gradients, contracting over each expert's padded slot range
-  // (bf16: gemm_fwd.hip's 256 x 256 tiles with an fp32 store; fp32: gemm.hip)
-  auto kjob = [&](const void* A, long long lda, const void* B, long long ldb, int M, int N, int nexp,
-                  const int32_t* ko, const int32_t* kl, void* C, long long ldc, long long cstride) {
-    GemmJob j{};
-    j.epi = EPI_STORE_F32;
-    j.A = A;
-    j.lda = lda;
-    j.a_div = 1;
-    j.B = B;
-    j.ldb = ldb;
-    j.N = N;
-    j.M = M;
-    j.kgroup = 1;
-    j.nexp = nexp;
-    j.kofs = ko;
-    j.klen = kl;
-    j.max_items = nexp * ((M + tm - 1) / tm);
-    j.C = C;
-    j.ldc = ldc;
-    j.c_estride = cstride;
-    return j;
-  };
-  GemmArgs g3{};
-  g3.act = act;
-  g3.njobs = 2;
-  g3.job[0] = kjob(dAUT, P, XpT, P, 2 * d.F, d.d, d.E, kofs, klen, dw->dw_gate_up, D, 2LL * F * D);
-  // shared expert: S contraction slices into fp32 partials, then added in order
+  // 6-7. weight gradients, contracting over each expert's rows (routed) and
+  // the tokens (shared, in S slices into fp32 partials, then added in order).
+  // bf16: gemm_fwd.hip's 256 x 256 tiles reading the activations K-major in
+  // place (x and dy through the token of each dispatch-order row; dW_d from
+  // the gate-scaled activations the dH launch wrote) with an fp32 store.
+  // fp32: the activations transposed over padded slot columns (routed) and
+  // token columns (shared) for gemm.hip.
   float* dwpart = at<float>(ws, L.dwpart);
-  g3.job[1] = kjob(dAUsT, Tp, xT, Tp, 2 * d.Fs, d.d, S, ksh, ksh + S, S > 1 ? (void*)dwpart : dw->dw_sh_gate_up, D,
-                   2LL * Fs * D);
+  float* dsgu = S > 1 ? dwpart : (float*)dw->dw_sh_gate_up;
+  float* dsd = S > 1 ? dwpart : (float*)dw->dw_sh_down;
+  GemmArgs g3{}, g4{};
+  g3.act = g4.act = act;
+  g3.njobs = g4.njobs = 2;
+  if (kmaj) {
+    const void* zr = at<char>(ws, L.zrow);
+    // C[e] (M x N) = sum over expert e's rows r of A[r, :]^T B[r, :]
+    auto mjob = [&](const void* A, long long lda, const int32_t* amap, const void* B, long long ldb,
+                    const int32_t* bmap, int M, int N, int nexp, const int32_t* ko, const int32_t* kl, int K, void* C,
+                    long long ldc, long long cstride) {
+      GemmJob j{};
+      j.epi = EPI_STORE_F32;
+      j.kmaj = 1;
+      j.A = A;
+      j.lda = lda;
+      j.a_krow = amap;
+      j.B = B;
+      j.ldb = ldb;
+      j.b_krow = bmap;
+      j.zrow = zr;
+      j.K = K;
+      j.N = N;
+      j.M = M;
+      j.kgroup = 1;
+      j.nexp = nexp;
+      j.kofs = ko;
+      j.klen = kl;
+      j.max_items = nexp * ((M + tm - 1) / tm);
+      j.C = C;
+      j.ldc = ldc;
+      j.c_estride = cstride;
+      return j;
+    };
+    const int sl = (int)slots;
+    g3.job[0] = mjob(dAU, 2LL * F, nullptr, x, D, krow, 2 * d.F, d.d, d.E, routing->offsets, routing->counts, sl,
+                     dw->dw_gate_up, D, 2LL * F * D);
+    g3.job[1] = mjob(dAUs, 2LL * Fs, nullptr, x, D, nullptr, 2 * d.Fs, d.d, S, ksh, ksh + S, d.T, dsgu, D,
+                     2LL * Fs * D);
+    g4.job[0] = mjob(dy, D, krow, Hg, F, nullptr, d.d, d.F, d.E, routing->offsets, routing->counts, sl, dw->dw_down, F,
+                     (long long)D * F);
+    g4.job[1] = mjob(dy, D, nullptr, at<char>(ws, L.Hs), Fs, nullptr, d.d, d.Fs, S, ksh, ksh + S, d.T, dsd, Fs,
+                     (long long)D * Fs);
+  } else {
+    transpose(dAU, 2LL * F, 0, dAUT, P, 0, 2 * d.F, P, 1, 0, pcol, nullptr, 1, nullptr);
+    transpose(x, D, 0, XpT, P, 0, d.d, P, 1, 0, pcol, routing->perm, d.k, nullptr);
+    transpose(dy, D, 0, dOT, P, 0, d.d, P, 1, 0, pcol, routing->perm, d.k, routing->gate);
+    transpose(at<char>(ws, L.H), F, 0, HT, P, 0, d.F, P, 1, 0, pcol, nullptr, 1, nullptr);
+    transpose(dAUs, 2LL * Fs, 0, dAUsT, Tp, 0, 2 * d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+    transpose(x, D, 0, xT, Tp, 0, d.d, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+    transpose(dy, D, 0, dyT, Tp, 0, d.d, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+    transpose(at<char>(ws, L.Hs), Fs, 0, HsT, Tp, 0, d.Fs, Tp, 1, d.T, nullptr, nullptr, 1, nullptr);
+    auto kjob = [&](const void* A, long long lda, const void* B, long long ldb, int M, int N, int nexp,
+                    const int32_t* ko, const int32_t* kl, void* C, long long ldc, long long cstride) {
+      GemmJob j{};
+      j.epi = EPI_STORE_F32;
+      j.A = A;
+      j.lda = lda;
+      j.a_div = 1;
+      j.B = B;
+      j.ldb = ldb;
+      j.N = N;
+      j.M = M;
+      j.kgroup = 1;
+      j.nexp = nexp;
+      j.kofs = ko;
+      j.klen = kl;
+      j.max_items = nexp * ((M + tm - 1) / tm);
+      j.C = C;
+      j.ldc = ldc;
+      j.c_estride = cstride;
+      return j;
+    };
+    g3.job[0] = kjob(dAUT, P, XpT, P, 2 * d.F, d.d, d.E, kofs, klen, dw->dw_gate_up, D, 2LL * F * D);
+    g3.job[1] = kjob(dAUsT, Tp, xT, Tp, 2 * d.Fs, d.d, S, ksh, ksh + S, dsgu, D, 2LL * Fs * D);
+    g4.job[0] = kjob(dOT, P, HT, P, d.d, d.F, d.E, kofs, klen, dw->dw_down, F, (long long)D * F);
+    g4.job[1] = kjob(dyT, Tp, HsT, Tp, d.d, d.Fs, S, ksh, ksh + S, dsd, Fs, (long long)D * Fs);
+  }
   gemm_in(g3, s);
   if (S > 1) launch_splitk_reduce(dwpart, 2LL * Fs * D, S, (float*)dw->dw_sh_gate_up, s);
-  GemmArgs g4{};
-  g4.act = act;
-  g4.njobs = 2;
-  g4.job[0] = kjob(dOT, P, HT, P, d.d, d.F, d.E, kofs, klen, dw->dw_down, F, (long long)D * F);
-  g4.job[1] = kjob(dyT, Tp, HsT, Tp, d.d, d.Fs, S, ksh, ksh + S, S > 1 ? (void*)dwpart : dw->dw_sh_down, Fs,
-                   (long long)D * Fs);
   gemm_in(g4, s);
   if (S > 1) launch_splitk_reduce(dwpart, (long long)D * Fs, S, (float*)dw->dw_sh_down, s);
 

@@ -34,9 +34,13 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int32_t* __restric
                                                         const int32_t* __restrict__ offsets, int E, int Pmax, int Tp,
                                                         int S, int step, int32_t* __restrict__ kofs,
                                                         int32_t* __restrict__ klen, int32_t* __restrict__ ksh,
-                                                        int32_t* __restrict__ pcol) {
+                                                        int32_t* __restrict__ pcol, int32_t* __restrict__ krow_pad,
+                                                        int32_t* __restrict__ zrow) {
   __shared__ int s_kofs[64], s_klen[64];
   const int tid = threadIdx.x;
+  // K-major weight gradients: the token map's readable tail and the zero row
+  if (krow_pad && tid < 32) krow_pad[tid] = 0;
+  if (zrow && tid < 128) zrow[tid] = 0;
   if (tid < 64) {
     const int c = tid < E ? counts[tid] : 0;
     const int kl = (c + kPadK - 1) / kPadK * kPadK;
@@ -161,7 +165,7 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
                                                        const T* __restrict__ x, const T* __restrict__ wr,
                                                        const int32_t* __restrict__ idx, const float* __restrict__ gate,
                                                        const int32_t* __restrict__ pos, int T_, int d, int k,
-                                                       float* __restrict__ dl) {
+                                                       float* __restrict__ dl, int32_t* __restrict__ krow) {
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
@@ -172,6 +176,8 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
     if (j < k) {
       e[j] = idx[(long long)t * k + j];
       slot[j] = pos[(long long)t * k + j];
+      // the token of each dispatch-order row (K-major weight gradients)
+      if (krow && lane == j) krow[slot[j]] = t;
     }
   float dga[8], sb[8];
 #pragma unroll
@@ -367,9 +373,10 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 }
 
 void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int S, int step,
-                     int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s) {
+                     int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, int32_t* krow_pad, int32_t* zrow,
+                     hipStream_t s) {
   hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, Pmax, Tp, S, step, kofs, klen, ksh,
-                     pcol);
+                     pcol, krow_pad, zrow);
 }
 
 void launch_splitk_reduce(const float* part, long long n, int S, float* out, hipStream_t s) {
@@ -383,15 +390,16 @@ void launch_transpose(int act, const TransposeArgs& a, hipStream_t s) {
 }
 
 void launch_bwd_gate(int act, const void* dy, const void* ou, const void* x, const void* wr, const int32_t* idx,
-                     const float* gate, const int32_t* pos, int T, int d, int k, float* dl, hipStream_t s) {
+                     const float* gate, const int32_t* pos, int T, int d, int k, float* dl, int32_t* krow,
+                     hipStream_t s) {
   if (T == 0) return;
   const dim3 grid((T + 3) / 4);
   if (act == 1)
     hipLaunchKernelGGL(bwd_gate_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dy, (const bf16_t*)ou,
-                       (const bf16_t*)x, (const bf16_t*)wr, idx, gate, pos, T, d, k, dl);
+                       (const bf16_t*)x, (const bf16_t*)wr, idx, gate, pos, T, d, k, dl, krow);
   else
     hipLaunchKernelGGL(bwd_gate_kernel<float>, grid, dim3(256), 0, s, (const float*)dy, (const float*)ou,
-                       (const float*)x, (const float*)wr, idx, gate, pos, T, d, k, dl);
+                       (const float*)x, (const float*)wr, idx, gate, pos, T, d, k, dl, krow);
 }
 
 void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* pcol, int P,

@@ -94,6 +94,56 @@ __device__ __forceinline__ u32x4_t dq_int4x8(uint32_t w, float sc) {
   }
   return r;
 }
+// Segment swizzle of K-major stage rows (see the K-major loader).
+__device__ __forceinline__ int ksw(int r) { return (((r >> 3) & 3) << 2) | (r & 3); }
+typedef int i32x4_t __attribute__((ext_vector_type(4)));
+// Four consecutive int32 at a wave-uniform address, loaded through the
+// scalar cache (a read); the values may be used only after sload_wait.
+__device__ __forceinline__ i32x4_t sload4(const int32_t* q) {
+  const unsigned long long a = (unsigned long long)q;
+  const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a), hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
+  const unsigned long long u = ((unsigned long long)hi << 32) | lo;
+  i32x4_t v{0, 0, 0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only parses (its assembler has no such operands)
+  asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(v) : "s"(u));
+#endif
+  return v;
+}
+// Waits for every outstanding scalar-cache and LDS access; the values pass
+// through, so no use of them is scheduled before the wait.
+__device__ __forceinline__ void sload_wait(i32x4_t& a, i32x4_t& b) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(a), "+s"(b));
+#endif
+}
+// One K-major MFMA fragment: two transposing 8-byte LDS reads, 4 K rows
+// apart.  Issued as inline asm: the compiler's builtin for this read makes
+// it wait for every direct-to-LDS load in flight first (it cannot tell them
+// apart), which would drain the load pipeline at each fragment.  The
+// compiler does not see these reads either, so the results are used only
+// after lds_wait_frags.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u32x4_t ds_read_tr_frag(const char* p) {
+  const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
+  u32x2_t lo{0, 0}, hi{0, 0};
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b64_tr_b16 %0, %1" : "=v"(lo) : "v"(a));
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:2048" : "=v"(hi) : "v"(a));
+#endif
+  return u32x4_t{lo[0], lo[1], hi[0], hi[1]};
+}
+// Waits for every LDS and scalar-cache access in flight; the fragments pass
+// through, so nothing reads them before the wait.
+template <int NA, int NB>
+__device__ __forceinline__ void lds_wait_frags(u32x4_t (&a)[NA], u32x4_t (&b)[NB]) {
+  static_assert(NA == 4 && NB == 8, "one wave's fragments");
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)"
+               : "+v"(a[0]), "+v"(a[1]), "+v"(a[2]), "+v"(a[3]), "+v"(b[0]), "+v"(b[1]), "+v"(b[2]), "+v"(b[3]),
+                 "+v"(b[4]), "+v"(b[5]), "+v"(b[6]), "+v"(b[7]));
+#endif
+}
+
 // contraction slices of a dense job
 __device__ __host__ __forceinline__ int k_slices(const GemmJob& j) { return j.ksplit > 1 ? j.ksplit : 1; }
 // items: grouped jobs the router's tile table; per-expert-contraction jobs
@@ -112,8 +162,9 @@ __device__ __host__ __forceinline__ int xcd_cols(const GemmJob& j) {
 }
 
 // I4: the launch has a job with int4 B (the int4 prefill); the bf16-only
-// instantiations carry none of that code.
-template <bool SWIGLU, bool I4>
+// instantiations carry none of that code.  KM: every job has K-major
+// operands (the weight gradients).
+template <bool SWIGLU, bool I4, bool KM>
 __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   typedef bf16_t T;
   // The ring; after the main loop its first buffer holds the row scales.
@@ -172,6 +223,8 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   }
   const int klen = p.kgroup ? p.klen[e] : p.K / k_slices(p);
   const long long kofs = p.kgroup ? (long long)p.kofs[e] : (long long)kz * klen;
+  // K-major: the expert's rows that exist (the rest of its last stage reads zeros)
+  const int kcnt = KM ? max(0, min(klen, p.K - (int)kofs)) : 0;
   rows = rows < BM ? rows : BM;
   // this wave's 64-row band holds rows of the item
   const bool active = wm * WM < rows;
@@ -230,18 +283,69 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     }
   }
   const long long b_step = b4 ? 16LL : p.b_staged ? (long long)BN * kRowB : (long long)kRowB;
-  const int nk = (int)((long long)klen * sizeof(T) / kRowB);
+  const int nk = KM ? (kcnt + 31) >> 5 : (int)((long long)klen * sizeof(T) / kRowB);
+
+  // ---- K-major operands (KM).  A stage holds 32 K rows of 256 columns
+  // (512 bytes) of each operand; load j of wave w fills K rows 4w + 2j + h,
+  // h = lane / 32, 16 bytes per lane.  The 32-byte segment q of K row r sits
+  // at segment q ^ ksw(r), which spreads the 16 rows x 32 bytes of one
+  // transposing fragment read over all the banks.  A lane's piece is clamped
+  // into the tile's columns (the extra columns feed only outputs that are
+  // not stored); rows past the expert's count read zeros.  A gathered
+  // operand's K rows come from its token map, four entries per wave and
+  // stage, fetched by a scalar load one main-loop trip ahead (the vector
+  // memory counter, which the stage waits use, never counts them).
+  int km_col[NDA + NDB];   // byte offset of the lane's piece in its operand row
+  const int kh = lane >> 5, kp = lane & 31;
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const char* const km_base[2] = {reinterpret_cast<const char*>(p.A), reinterpret_cast<const char*>(p.B)};
+  const long long km_ld2[2] = {p.lda * 2, p.ldb * 2};
+  const int32_t* const km_map[2] = {p.a_krow, p.b_krow};
+  const char* const km_zero = reinterpret_cast<const char*>(p.zrow) + 16 * kp;
+  const int km_ofs = (int)kofs;
+  if constexpr (KM) {
+    const int ncols = min(p.N - nt * BN, BN);
+#pragma unroll
+    for (int j = 0; j < NDA + NDB; ++j) {
+      const int r = 4 * wave + 2 * (j & 1) + kh;
+      const int lp = ((((kp >> 1) ^ ksw(r)) << 1) | (kp & 1)) * 8;
+      km_col[j] = j < NDA ? (row_base + min(lp, rows - 8)) * 2 : (nt * BN + min(lp, ncols - 8)) * 2;
+    }
+  }
+  // the map entries of the stage being issued, per operand
+  i32x4_t km_rows[2] = {i32x4_t{0, 0, 0, 0}, i32x4_t{0, 0, 0, 0}};
+  auto km_fetch = [&](int s) {   // start the scalar loads of stage s's map entries
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+      if (km_map[op]) km_rows[op] = sload4(km_map[op] + km_ofs + 32 * s + 4 * wave_u);
+  };
+  auto km_sync = [&]() {         // wait for them
+    if (km_map[0] || km_map[1]) sload_wait(km_rows[0], km_rows[1]);
+  };
+  auto km_src = [&](int s, int j) -> const char* {
+    const int op = j < NDA ? 0 : 1, jj = j & 1;
+    const int kk = 32 * s + 4 * wave + 2 * jj + kh;
+    const int row = km_map[op] ? (kh ? km_rows[op][2 * jj + 1] : km_rows[op][2 * jj]) : km_ofs + kk;
+    return kk < kcnt ? km_base[op] + (long long)row * km_ld2[op] + km_col[j] : km_zero;
+  };
   auto issue_one = [&](int s, int j) {
     char* st = lds + (s % kStages) * kStageBytes;
     const long long off = (long long)s * kRowB;
-    if (j < NDA)
-      __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(st + wave * (BM / 8) * kRowB + j * 1024), 16, 0, 0);
-    else if (b4)
-      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
-                                       (lds_ptr_t)(st + ATILE + wave * (BN / 8) * 16 + (j - NDA) * 256), 4, 0, 0);
-    else
-      __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
-                                       (lds_ptr_t)(st + ATILE + wave * (BN / 8) * kRowB + (j - NDA) * 1024), 16, 0, 0);
+    if constexpr (KM) {
+      const char* src = km_src(s, j);
+      __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + (j < NDA ? 0 : ATILE) + (wave * 2 + (j & 1)) * 1024), 16, 0,
+                                       0);
+    } else {
+      if (j < NDA)
+        __builtin_amdgcn_global_load_lds(a_src[j] + off, (lds_ptr_t)(st + wave * (BM / 8) * kRowB + j * 1024), 16, 0, 0);
+      else if (b4)
+        __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
+                                         (lds_ptr_t)(st + ATILE + wave * (BN / 8) * 16 + (j - NDA) * 256), 4, 0, 0);
+      else
+        __builtin_amdgcn_global_load_lds(b_src[j - NDA] + (long long)s * b_step,
+                                         (lds_ptr_t)(st + ATILE + wave * (BN / 8) * kRowB + (j - NDA) * 1024), 16, 0,
+                                         0);
+    }
   };
   auto issue = [&](int s) {
 #pragma unroll
@@ -293,16 +397,31 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   u32x4_t fa0[4], fa1[4], fb[NI];
   uint32_t qb[NI];
   float qs[NI];
+  // K-major fragment at tile column 16 c16: lane (fr, g) needs K rows 8g ..
+  // 8g + 7 of column 16 c16 + fr.  A transposing read gives lane i of each
+  // 16-lane group the four values at column c0 + i of four consecutive rows
+  // when lane j of the group points at row (first) + j / 4, columns c0 +
+  // 4 (j % 4) .. + 3; two reads (rows 8g and 8g + 4) make the fragment.
+  const int km_lane = (8 * g + (fr >> 2)) * 512 + 8 * (fr & 3);
+  const int km_f = (g << 2) | (fr >> 2);   // ksw of every row this lane reads
+  auto km_frag = [&](const char* X, int c16) -> u32x4_t {
+    return ds_read_tr_frag(X + km_lane + 32 * (c16 ^ km_f));
+  };
   auto read_a = [&](int s, u32x4_t (&fa)[4]) {
     const char* As = lds + (s % kStages) * kStageBytes;
 #pragma unroll
-    for (int mi = 0; mi < 4; ++mi) fa[mi] = ld16(As + swz(arow_l[mi], g));
+    for (int mi = 0; mi < 4; ++mi) {
+      if constexpr (KM) fa[mi] = km_frag(As, 4 * wm + mi);
+      else fa[mi] = ld16(As + swz(arow_l[mi], g));
+    }
   };
   auto read_b = [&](int s, auto b4c) {
     const char* Bs = lds + (s % kStages) * kStageBytes + ATILE;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      if constexpr (decltype(b4c)::value) {
+      if constexpr (KM) {
+        fb[ni] = km_frag(Bs, 8 * wn + ni);
+      } else if constexpr (decltype(b4c)::value) {
         qb[ni] = qword(Bs, brow_l[ni]);
         qs[ni] = qscale(s, brow_l[ni]);
       } else {
@@ -328,22 +447,33 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       u32x4_t bv;
       if constexpr (B4) bv = dq_int4x8(qb[ni], qs[ni]);
       else bv = fb[ni];
+      // K-major: the N fragment is the MFMA's first operand, so a lane's four
+      // results are four adjacent output columns of one output row
 #pragma unroll
-      for (int mi = 0; mi < 4; ++mi) acc[mi][ni] = Mma<T>::run1(fa[mi], bv, acc[mi][ni]);
+      for (int mi = 0; mi < 4; ++mi) {
+        if constexpr (KM) acc[mi][ni] = Mma<T>::run1(bv, fa[mi], acc[mi][ni]);
+        else acc[mi][ni] = Mma<T>::run1(fa[mi], bv, acc[mi][ni]);
+      }
       if constexpr (decltype(prefetch)::value) {
-        if constexpr (B4) {
-          qb[ni] = qword(Bn, brow_l[ni]);
-          qs[ni] = qscale(s + 1, brow_l[ni]);
+        if constexpr (KM) {
+          fb[ni] = km_frag(Bn, 8 * wn + ni);
+          if (ni < 4) fn[ni] = km_frag(An, 4 * wm + ni);
         } else {
-          fb[ni] = ld16(Bn + swz(brow_l[ni], g));
+          if constexpr (B4) {
+            qb[ni] = qword(Bn, brow_l[ni]);
+            qs[ni] = qscale(s + 1, brow_l[ni]);
+          } else {
+            fb[ni] = ld16(Bn + swz(brow_l[ni], g));
+          }
+          if (ni < 4) fn[ni] = ld16(An + swz(arow_l[ni], g));
         }
-        if (ni < 4) fn[ni] = ld16(An + swz(arow_l[ni], g));
       }
       if constexpr (decltype(with_loads)::value) {
         if (ni & 1) issue_one(s + kStages - 1, ni >> 1);
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the reads and loads spread out
     }
+    if constexpr (KM && decltype(prefetch)::value) lds_wait_frags(fn, fb);
   };
 
   // ---- main loop.  Iteration s waits for stage s + 1 (its loads went out
@@ -352,7 +482,14 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   // s - 1, whose operands it read in iteration s - 2: buffer (s - 1) % 5 is
   // free for the loads of stage s + 4.
   static_assert(kStages == 5, "the waits below assume a 5-deep ring");
-  for (int s = 0; s < kStages - 1 && s < nk; ++s) issue(s);
+  for (int s = 0; s < kStages - 1 && s < nk; ++s) {
+    if constexpr (KM) {
+      km_fetch(s);
+      km_sync();
+    }
+    issue(s);
+  }
+  if (KM && kStages - 1 < nk) km_fetch(kStages - 1);
   if (nk >= 4) wait_vmcnt<3 * kLoads>();
   else if (nk == 3) wait_vmcnt<2 * kLoads>();
   else if (nk == 2) wait_vmcnt<kLoads>();
@@ -365,6 +502,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     if constexpr (A::value) {
       read_a(0, fa0);
       read_b(0, B4{});
+      if constexpr (KM) lds_wait_frags(fa0, fb);
     }
     // Stages issued before iteration s: min(nk, s + 4); in flight after stage
     // s + 1: that minus s + 2.  Two K steps per trip, so the two A sets swap
@@ -374,7 +512,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     for (; s + kStages - 1 < nk; ++s) {
       wait_vmcnt<2 * kLoads>();
       block_barrier();
+      if constexpr (KM) km_sync();
       compute(s, fa0, fa1, A{}, std::true_type{}, std::true_type{}, B4{});
+      if (KM && s + kStages < nk) km_fetch(s + kStages);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
     }
@@ -410,6 +550,22 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     __syncthreads();
   }
   if (!active) return;
+  if constexpr (KM) {
+    // acc[mi][ni][i]: tile row wm*64 + 16 mi + fr, column wn*128 + 16 ni + 4g + i
+    float* const Ck = reinterpret_cast<float*>(p.C) + (long long)e * p.c_estride;
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      const int lr = wm * WM + 16 * mi + fr;
+      if (lr >= rows) continue;
+#pragma unroll
+      for (int ni = 0; ni < NI; ++ni) {
+        const int n = nt * BN + wn * WN + 16 * ni + 4 * g;
+        if (n < p.N)
+          *reinterpret_cast<f32x4_t*>(Ck + (long long)(row_base + lr) * p.ldc + n) = acc[mi][ni];
+      }
+    }
+    return;
+  }
   // ---- epilogue.  acc[mi][ni][i] is tile row wm*64 + mi*16 + 4g + i.  Its
   // column, past the wave's base, is 8f + ni (f = lane % 16); for SwiGLU,
   // blocks ni < 4 are gate columns 4f + ni and ni >= 4 the matching up.
@@ -453,7 +609,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
         // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u)
         const float sc = p.gate ? row_scale[lr] : 1.f;
         const T* au = reinterpret_cast<const T*>(p.aux) + row * p.ldaux;
-        float a[NI], u[NI], da[NI], du[NI];
+        float a[NI], u[NI], da[NI], du[NI], hs[NI];
         load_vec<T, NI>(au + n, a);
         load_vec<T, NI>(au + p.N + n, u);
 #pragma unroll
@@ -463,9 +619,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
           const float si = a[ni] * sg;
           da[ni] = dh * u[ni] * (sg * (1.f + a[ni] * (1.f - sg)));
           du[ni] = dh * si;
+          hs[ni] = sc * (si * u[ni]);
         }
         store_vec<T, NI>(C + row * p.ldc + n, da);
         store_vec<T, NI>(C + row * p.ldc + p.N + n, du);
+        if (p.hg) store_vec<T, NI>(reinterpret_cast<T*>(p.hg) + row * p.N + n, hs);
       } else if (p.epi == EPI_STORE_F32) {
         float v[NI];
 #pragma unroll
@@ -529,9 +687,9 @@ void launch_pack_routed(const void* w_gate_up, const void* w_down, int E, int d,
 
 // bf16 operands only: epilogues SwiGLU, row scale, SwiGLU backward, plain
 // store (bf16) or fp32 store (the weight gradients, with per-expert
-// contraction ranges: klen[e] a multiple of 32, possibly 0); K / ksplit a
-// multiple of 32 (checked by the caller); a split job's slices each write
-// their own output.
+// contraction ranges: klen[e] a multiple of 32, possibly 0, or K-major
+// operands, both jobs then); K / ksplit a multiple of 32 (checked by the
+// caller); a split job's slices each write their own output.
 void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
   GemmArgs a = in;
   long long total = 0;
@@ -542,12 +700,14 @@ void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
   if (total == 0) return;
   const dim3 grid((unsigned)(total * 8));
   const bool i4 = a.job[0].b_int4 || (a.njobs > 1 && a.job[1].b_int4);
-  if (a.job[0].epi == EPI_SWIGLU) {
-    if (i4) hipLaunchKernelGGL((gemm256_kernel<true, true>), grid, dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((gemm256_kernel<true, false>), grid, dim3(NTHR), 0, s, a);
+  if (a.job[0].kmaj) {
+    hipLaunchKernelGGL((gemm256_kernel<false, false, true>), grid, dim3(NTHR), 0, s, a);
+  } else if (a.job[0].epi == EPI_SWIGLU) {
+    if (i4) hipLaunchKernelGGL((gemm256_kernel<true, true, false>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((gemm256_kernel<true, false, false>), grid, dim3(NTHR), 0, s, a);
   } else {
-    if (i4) hipLaunchKernelGGL((gemm256_kernel<false, true>), grid, dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((gemm256_kernel<false, false>), grid, dim3(NTHR), 0, s, a);
+    if (i4) hipLaunchKernelGGL((gemm256_kernel<false, true, false>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((gemm256_kernel<false, false, false>), grid, dim3(NTHR), 0, s, a);
   }
 }
 

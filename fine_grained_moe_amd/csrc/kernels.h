@@ -96,6 +96,17 @@ struct GemmJob {
   const int32_t* kofs;
   const int32_t* klen;
   long long c_estride;
+  // launch_gemm_fwd256 only, kgroup jobs with the fp32 store (the weight
+  // gradients): A and B are K-major, element (m, k) of A at A[krow(k) * lda +
+  // m] and (n, k) of B at B[krow(k) * ldb + n], krow(k) = a_krow ? a_krow[k] :
+  // k (b_krow likewise), over expert e's rows kofs[e] + [0, min(klen[e], K -
+  // kofs[e])) (klen[e] any count).  The maps are readable 32 entries past
+  // every range, zrow points at 512 zero bytes, M and N are multiples of 8 and
+  // lda, ldb multiples of 8 elements.
+  int kmaj;
+  const int32_t* a_krow;
+  const int32_t* b_krow;
+  const void* zrow;
   // dense jobs of launch_gemm_fwd256: the contraction is cut into ksplit
   // equal slices (K / ksplit a multiple of 32); slice z writes C + z * c_kstride.
   int ksplit;
@@ -110,6 +121,9 @@ struct GemmJob {
   long long ldaux;
   const float* gate;       // ROWSCALE: row scale gate[perm[slot]]
   const int32_t* perm;
+  // launch_gemm_fwd256, SwiGLU-backward epilogue: also the row-scaled
+  // activation s * silu(a) * u, [rows, N] (unused when null)
+  void* hg;
 };
 
 // A launch: one or two jobs sharing the dtype.
@@ -212,7 +226,8 @@ void launch_quant_int4(int act, const void* w, long long rows, int K, uint8_t* p
 void launch_dequant_int4(const void* packed, const void* scales, int E, int rows_e, int K, const int32_t* counts,
                          void* out, hipStream_t s);
 void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int S, int step,
-                     int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, hipStream_t s);
+                     int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, int32_t* krow_pad, int32_t* zrow,
+                     hipStream_t s);
 // Contraction slices of the shared expert's weight gradients (a function of
 // the padded token count Tp): S slices of `step` columns, step % kPadK == 0.
 constexpr int kMaxSplitK = 8;
@@ -221,7 +236,8 @@ inline long long splitk_step(long long Tp) { return pad_k((Tp + splitk_count(Tp)
 void launch_splitk_reduce(const float* part, long long n, int S, float* out, hipStream_t s);   // n % 4 == 0
 void launch_transpose(int act, const TransposeArgs& a, hipStream_t s);
 void launch_bwd_gate(int act, const void* dy, const void* ou, const void* x, const void* wr, const int32_t* idx,
-                     const float* gate, const int32_t* pos, int T, int d, int k, float* dl, hipStream_t s);
+                     const float* gate, const int32_t* pos, int T, int d, int k, float* dl, int32_t* krow,
+                     hipStream_t s);
 void launch_bwd_dwr(int act, const void* x, const float* dl, const int32_t* perm, const int32_t* pcol, int P,
                     const int32_t* kofs, const int32_t* klen, int E, int d, int k, float* part, float* dwr,
                     hipStream_t s);
