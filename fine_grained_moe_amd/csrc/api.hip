@@ -936,6 +936,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   GemmArgs g1{};
   g1.act = act;
   g1.njobs = 2;
+  g1.order = 1;   // routed tiles first (even with the other orders, measured)
   g1.job[0] = hr;
   g1.job[1] = hs;
   gemm_in(g1, s);
@@ -972,6 +973,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   GemmArgs g2{};
   g2.act = act;
   g2.njobs = 2;
+  g2.order = 2;   // shared tiles first: four times the contraction of a routed tile
   g2.job[0] = xr;
   g2.job[1] = xs;
   gemm_in(g2, s);
@@ -989,6 +991,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   GemmArgs g3{}, g4{};
   g3.act = g4.act = act;
   g3.njobs = g4.njobs = 2;
+  g3.order = g4.order = 2;   // shared slices first: four times the contraction of a routed tile
   if (kmaj) {
     const void* zr = at<char>(ws, L.zrow);
     // C[e] (M x N) = sum over expert e's rows r of A[r, :]^T B[r, :]

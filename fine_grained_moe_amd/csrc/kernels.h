@@ -230,7 +230,7 @@ void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int P
                      hipStream_t s);
 // Contraction slices of the shared expert's weight gradients (a function of
 // the padded token count Tp): S slices of `step` columns, step % kPadK == 0.
-constexpr int kMaxSplitK = 8;
+constexpr int kMaxSplitK = 4;
 inline int splitk_count(long long Tp) { return (int)std::max(1LL, std::min<long long>(kMaxSplitK, Tp / 4096)); }
 inline long long splitk_step(long long Tp) { return pad_k((Tp + splitk_count(Tp) - 1) / splitk_count(Tp)); }
 void launch_splitk_reduce(const float* part, long long n, int S, float* out, hipStream_t s);   // n % 4 == 0
