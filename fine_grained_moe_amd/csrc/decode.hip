@@ -432,32 +432,39 @@ __device__ void decode_write_routing(const DecodeArgs& p, const Book& B) {
 // condition would be waited for at the end of their branch) and are not
 // stored.
 // ---------------------------------------------------------------------------
-template <int D, int FS>
-__device__ void decode_shared_down(const DecodeArgs& p, int j, int tt, float* lds, Book& B) {
+template <int D, int FS, int NT>
+__device__ void decode_shared_down(const DecodeArgs& p, int j, int tt0, float* lds, Book& B) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
   constexpr int J = FS / 16 / 32;                    // MFMA K-steps per wave (4)
   const int cb = j >> 2, quarter = j & 3, T = p.T;
   const int kofs = quarter * (FS / 2) + wave * (FS / 8) + g * 16;   // bytes into a row
   const char* wr = reinterpret_cast<const char*>(p.w_sh_down + (long long)(cb * 16 + fr) * FS) + kofs;
-  const char* hr = reinterpret_cast<const char*>(p.Hs + (long long)min(tt * 16 + fr, T - 1) * FS) + kofs;
-  u32x4_t wv[J], ha[J];
+  u32x4_t wv[J], ha[NT][J];
 #pragma unroll
-  for (int i = 0; i < J; ++i) {
-    wv[i] = ld16(wr + i * 64);
-    ha[i] = ld16(hr + i * 64);
+  for (int i = 0; i < J; ++i) wv[i] = ld16(wr + i * 64);
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    const char* hr = reinterpret_cast<const char*>(p.Hs + (long long)min((tt0 + tt) * 16 + fr, T - 1) * FS) + kofs;
+#pragma unroll
+    for (int i = 0; i < J; ++i) ha[tt][i] = ld16(hr + i * 64);
   }
-  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  // partial tiles: lds[token tile][wave][16][17]
 #pragma unroll
-  for (int i = 0; i < J; ++i) acc = Mma<bf16_t>::run1(ha[i], wv[i], acc);
+  for (int tt = 0; tt < NT; ++tt) {
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-  for (int i = 0; i < 4; ++i) lds[(wave * 16 + 4 * g + i) * 17 + fr] = acc[i];
+    for (int i = 0; i < J; ++i) acc = Mma<bf16_t>::run1(ha[tt][i], wv[i], acc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lds[((tt * 4 + wave) * 16 + 4 * g + i) * 17 + fr] = acc[i];
+  }
   decode_book(p, B);                                 // its loads follow the operand loads; it ends with a barrier
-  const int m = tid >> 2, c4 = (tid & 3) * 4, t = tt * 16 + m;
-  if (tid < 64 && t < T) {
+  const int tt = tid >> 6, m = (tid >> 2) & 15, c4 = (tid & 3) * 4, t = (tt0 + tt) * 16 + m;
+  if (tt < NT && t < T) {
+    const float* q = lds + (tt * 4 * 16 + m) * 17 + c4;
     f32x4_t v;
 #pragma unroll
-    for (int c = 0; c < 4; ++c) v[c] = sum4(lds + m * 17 + c4 + c, 16 * 17);
+    for (int c = 0; c < 4; ++c) v[c] = sum4(q + c, 16 * 17);
     *reinterpret_cast<f32x4_t*>(p.part_sh + ((long long)quarter * T + B.pos[t]) * D + cb * 16 + c4) = v;
   }
 }
@@ -471,25 +478,29 @@ __device__ __forceinline__ int weight_slot(const DecodeArgs& p, int e) {
   return s < 0 ? 0 : (s >= p.n_slots ? p.n_slots - 1 : s);
 }
 
-template <int D, int FR>
+template <int D, int FR, int FBN>
 __device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds, Book& B) {
   decode_book(p, B);
-  constexpr int nfb = FR / 16;
-  const int a = item / nfb, fb = item - a * nfb;
+  constexpr int nfb = FR / 16 / FBN;                 // items per active expert
+  const int a = item / nfb, fb0 = (item - a * nfb) * FBN;
   if (a >= B.n_active) return;                       // uniform over the workgroup
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
   const int e = B.act_e[a], s0 = B.act_s0[a], n = B.act_n[a];
-  const long long rg = (long long)weight_slot(p, e) * 2 * FR + fb * 16 + fr, ru = rg + FR;
   const int qofs = wave * (D / 8) + g * 16;          // bytes into a packed row
-  u32x4_t wg[2], wu[2];
+  u32x4_t wg[FBN][2], wu[FBN][2];
+  uint32_t sg[FBN], su[FBN];
 #pragma unroll
-  for (int grp = 0; grp < 2; ++grp) {
-    wg[grp] = ld16(p.q_gate_up + rg * (D / 2) + qofs + grp * 64);
-    wu[grp] = ld16(p.q_gate_up + ru * (D / 2) + qofs + grp * 64);
+  for (int f = 0; f < FBN; ++f) {
+    const long long rg = (long long)weight_slot(p, e) * 2 * FR + (fb0 + f) * 16 + fr, ru = rg + FR;
+#pragma unroll
+    for (int grp = 0; grp < 2; ++grp) {
+      wg[f][grp] = ld16(p.q_gate_up + rg * (D / 2) + qofs + grp * 64);
+      wu[f][grp] = ld16(p.q_gate_up + ru * (D / 2) + qofs + grp * 64);
+    }
+    sg[f] = *reinterpret_cast<const uint32_t*>(p.s_gate_up + rg * (D / kGroup) + wave * 2);
+    su[f] = *reinterpret_cast<const uint32_t*>(p.s_gate_up + ru * (D / kGroup) + wave * 2);
   }
-  const uint32_t sg = *reinterpret_cast<const uint32_t*>(p.s_gate_up + rg * (D / kGroup) + wave * 2);
-  const uint32_t su = *reinterpret_cast<const uint32_t*>(p.s_gate_up + ru * (D / kGroup) + wave * 2);
   for (int m0 = 0; m0 < n; m0 += 16) {
     const int nt = min(16, n - m0);
     const int tok = B.perm[s0 + m0 + min(fr, nt - 1)];
@@ -500,51 +511,61 @@ __device__ void decode_routed_gate_up(const DecodeArgs& p, int item, float* lds,
     for (int grp = 0; grp < 2; ++grp)
 #pragma unroll
       for (int j = 0; j < 4; ++j) xa[grp][j] = ld16(xr + grp * 256 + j * 16);
-    f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int grp = 0; grp < 2; ++grp) {
-      f32x4_t tg = {0.f, 0.f, 0.f, 0.f}, tu = {0.f, 0.f, 0.f, 0.f};
+    for (int f = 0; f < FBN; ++f) {
+      f32x4_t ag = {0.f, 0.f, 0.f, 0.f}, au = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        tg = Mma<bf16_t>::run1(xa[grp][j], int4x8_to_bf16(wg[grp][j]), tg);
-        tu = Mma<bf16_t>::run1(xa[grp][j], int4x8_to_bf16(wu[grp][j]), tu);
+      for (int grp = 0; grp < 2; ++grp) {
+        f32x4_t tg = {0.f, 0.f, 0.f, 0.f}, tu = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          tg = Mma<bf16_t>::run1(xa[grp][j], int4x8_to_bf16(wg[f][grp][j]), tg);
+          tu = Mma<bf16_t>::run1(xa[grp][j], int4x8_to_bf16(wu[f][grp][j]), tu);
+        }
+        const float scg = bf16_to_f32((bf16_t)(grp ? sg[f] >> 16 : sg[f] & 0xFFFFu));
+        const float scu = bf16_to_f32((bf16_t)(grp ? su[f] >> 16 : su[f] & 0xFFFFu));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          ag[i] += tg[i] * scg;
+          au[i] += tu[i] * scu;
+        }
       }
-      const float scg = bf16_to_f32((bf16_t)(grp ? sg >> 16 : sg & 0xFFFFu));
-      const float scu = bf16_to_f32((bf16_t)(grp ? su >> 16 : su & 0xFFFFu));
+      // lds: [column block][wave][token][column], row stride 33 (gate columns 0-15, up 16-31)
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        ag[i] += tg[i] * scg;
-        au[i] += tu[i] * scu;
+        lds[((f * 4 + wave) * 16 + 4 * g + i) * 33 + fr] = ag[i];
+        lds[((f * 4 + wave) * 16 + 4 * g + i) * 33 + 16 + fr] = au[i];
       }
     }
-    // lds: [wave][token][column], row stride 33 (gate columns 0-15, up 16-31)
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      lds[(wave * 16 + 4 * g + i) * 33 + fr] = ag[i];
-      lds[(wave * 16 + 4 * g + i) * 33 + 16 + fr] = au[i];
-    }
     __syncthreads();
-    if (tid < 2 * nt) {
-      const int m = tid >> 1, c8 = (tid & 1) * 8;
+    if (tid < 2 * nt * FBN) {
+      const int f = tid / (2 * nt), r = tid - f * 2 * nt, m = r >> 1, c8 = (r & 1) * 8;
+      const float* q = lds + (f * 4 * 16 + m) * 33 + c8;
       float h[8];
 #pragma unroll
-      for (int c = 0; c < 8; ++c)
-        h[c] = siluf_(sum4(lds + m * 33 + c8 + c, 16 * 33)) * sum4(lds + m * 33 + 16 + c8 + c, 16 * 33);
-      st16(p.H + (long long)(s0 + m0 + m) * FR + fb * 16 + c8, pack8(h));
+      for (int c = 0; c < 8; ++c) h[c] = siluf_(sum4(q + c, 16 * 33)) * sum4(q + 16 + c, 16 * 33);
+      st16(p.H + (long long)(s0 + m0 + m) * FR + (fb0 + f) * 16 + c8, pack8(h));
     }
     __syncthreads();                                 // before the next tile reuses the partials
   }
 }
 
 // Block 0 writes the routing (and takes the bias step of
-// moe_forward_bias_step); then the shared down (256 items x token tiles);
-// then the routed gate/up (items of experts past the active count exit after
-// the bookkeeping).
-template <int D, int FR, int FS>
-__global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int ntile) {
-  __shared__ float lds[4 * 16 * 33];
+// moe_forward_bias_step); then the shared down; then the routed gate/up
+// (items of experts past the active count exit after the bookkeeping).
+// NT = 1: one shared-down item per weight block and token tile (256 x the
+// token tiles).  Above 16 tokens (NT = 2 or 4) a shared-down item takes
+// every token tile of its weight block (the weights are read once), so that
+// fewer rounds of the workgroups a CU holds at once (four, by registers)
+// cover the grid: at 64 tokens 2305 workgroups became 1537.  FBN = 2 (32 h
+// columns per routed item) would halve the routed items but needs more than
+// the 128 registers of four waves per SIMD (it spilled).
+template <int D, int FR, int FS, int NT, int FBN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void decode_stage2_kernel(DecodeArgs p, int ntile) {
+  constexpr int kSd = NT * 4 * 16 * 17, kGu = FBN * 4 * 16 * 33;
+  __shared__ float lds[kSd > kGu ? kSd : kGu];
   __shared__ Book B;
-  const int n_sd = 4 * (D / 16) * ntile;
+  const int n_sd = NT == 1 ? 4 * (D / 16) * ntile : 4 * (D / 16);
   const int blk = blockIdx.x;
   if (blk == 0) {
     decode_book(p, B);
@@ -556,11 +577,15 @@ __global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int nt
                      p.step_bias, p.step_stats);
     }
   } else if (blk <= n_sd) {
-    int j, tt;
-    xcd_item(blk - 1, ntile, j, tt);
-    decode_shared_down<D, FS>(p, j, tt, lds, B);
+    if constexpr (NT == 1) {
+      int j, tt;
+      xcd_item(blk - 1, ntile, j, tt);
+      decode_shared_down<D, FS, 1>(p, j, tt, lds, B);
+    } else {
+      decode_shared_down<D, FS, NT>(p, blk - 1, 0, lds, B);
+    }
   } else {
-    decode_routed_gate_up<D, FR>(p, blk - 1 - n_sd, lds, B);
+    decode_routed_gate_up<D, FR, FBN>(p, blk - 1 - n_sd, lds, B);
   }
 }
 
@@ -574,11 +599,12 @@ __global__ __launch_bounds__(256) void decode_stage2_kernel(DecodeArgs p, int nt
 // every y row is written once.  Operands come straight from global memory
 // (as in stage 2).
 // ---------------------------------------------------------------------------
-template <int D, int FR>
-__global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
-  __shared__ float lds[4 * 16 * 33];
+template <int D, int FR, int CBN>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CBN == 1 ? 4 : 3))) void decode_stage3_kernel(DecodeArgs p) {
+  constexpr int W = 32 * CBN, LS = W + 1;            // output columns per item, LDS row stride
+  __shared__ float lds[4 * 16 * LS];
   static_assert(FR / kGroup == 4, "one scale group per wave");
-  constexpr int ncb = D / 32;
+  constexpr int ncb = D / W, NTL = W / 16, TPT = W / 8;   // 16-column tiles, threads per token
   const int a = blockIdx.x / ncb, cb = blockIdx.x - a * ncb;
   // the active entry is read together with the count; a < E keeps it in bounds
   const int na = *p.n_active;
@@ -586,11 +612,11 @@ __global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
   if (a >= na) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int fr = lane & 15, g = lane >> 4;
-  u32x4_t wq[2];
-  float sc[2];
+  u32x4_t wq[NTL];
+  float sc[NTL];
 #pragma unroll
-  for (int tile = 0; tile < 2; ++tile) {
-    const long long r = (long long)weight_slot(p, e) * D + cb * 32 + tile * 16 + fr;
+  for (int tile = 0; tile < NTL; ++tile) {
+    const long long r = (long long)weight_slot(p, e) * D + cb * W + tile * 16 + fr;
     wq[tile] = ld16(p.q_down + r * (FR / 2) + wave * 64 + g * 16);
     sc[tile] = bf16_to_f32(p.s_down[r * (FR / kGroup) + wave]);
   }
@@ -601,43 +627,44 @@ __global__ __launch_bounds__(256) void decode_stage3_kernel(DecodeArgs p) {
     u32x4_t ha[4];
 #pragma unroll
     for (int j = 0; j < 4; ++j) ha[j] = ld16(hr + j * 16);
-    // combine operands of this thread's output piece (4 nt <= 64 threads, all
-    // in the first wave), requested after the operands, before the products
-    const bool out = tid < 4 * nt;
-    const int m = tid >> 2, c8 = (tid & 3) * 8;
+    // combine operands of this thread's output piece (TPT nt <= 16 TPT
+    // threads, the first CBN waves), requested after the operands, before
+    // the products
+    const bool out = tid < TPT * nt;
+    const int m = tid / TPT, c8 = (tid - m * TPT) * 8;
     int tok = 0;
     f32x4_t sh[4][2];
     u32x4_t rs = {0u, 0u, 0u, 0u};                   // the block's residual input (bf16), if any
-    if (tid < 64) {
+    if (tid < 16 * TPT) {
       const int mc = min(m, nt - 1);
       tok = p.perm[s0 + m0 + mc];
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        const float* src = p.part_sh + q * q1 + (long long)(s0 + m0 + mc) * D + cb * 32 + c8;
+        const float* src = p.part_sh + q * q1 + (long long)(s0 + m0 + mc) * D + cb * W + c8;
         sh[q][0] = *reinterpret_cast<const f32x4_t*>(src);
         sh[q][1] = *reinterpret_cast<const f32x4_t*>(src + 4);
       }
-      if (p.resid) rs = ld16(p.resid + (long long)tok * D + cb * 32 + c8);
+      if (p.resid) rs = ld16(p.resid + (long long)tok * D + cb * W + c8);
     }
 #pragma unroll
-    for (int tile = 0; tile < 2; ++tile) {
+    for (int tile = 0; tile < NTL; ++tile) {
       f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int j = 0; j < 4; ++j) acc = Mma<bf16_t>::run1(ha[j], int4x8_to_bf16(wq[tile][j]), acc);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) lds[(wave * 16 + 4 * g + i) * 33 + tile * 16 + fr] = acc[i] * sc[tile];
+      for (int i = 0; i < 4; ++i) lds[(wave * 16 + 4 * g + i) * LS + tile * 16 + fr] = acc[i] * sc[tile];
     }
     __syncthreads();
     if (out) {
       float v[8];
 #pragma unroll
       for (int c = 0; c < 8; ++c) {
-        const float o = sum4(lds + m * 33 + c8 + c, 16 * 33);
+        const float o = sum4(lds + m * LS + c8 + c, 16 * LS);
         const float s = ((sh[0][c >> 2][c & 3] + sh[1][c >> 2][c & 3]) + sh[2][c >> 2][c & 3]) + sh[3][c >> 2][c & 3];
         v[c] = s + o;
         if (p.resid) v[c] += bf16_to_f32((bf16_t)((rs[c >> 1] >> (16 * (c & 1))) & 0xFFFF));
       }
-      st16(p.y + (long long)tok * D + cb * 32 + c8, pack8(v));
+      st16(p.y + (long long)tok * D + cb * W + c8, pack8(v));
     }
     __syncthreads();                                 // before the next tile reuses the partials
   }
@@ -652,14 +679,26 @@ void launch_decode(const DecodeArgs& a, hipStream_t s) {
   static_assert((FS / 8) % 8 == 0 && (4 * (D / 16)) % 8 == 0, "token-tiled items need weight blocks in eights");
   const int ntile = (a.T + 15) / 16;
   if (a.T == 0) {   // only the (empty) routing outputs
-    hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS>), dim3(1), dim3(256), 0, s, a, 0);
+    hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS, 1, 1>), dim3(1), dim3(256), 0, s, a, 0);
     return;
   }
   const int max_active = a.T * a.k < a.E ? a.T * a.k : a.E;
   hipLaunchKernelGGL((decode_stage1_kernel<D, FS>), dim3((FS / 8) * ntile + 4 * ntile), dim3(256), 0, s, a, ntile);
-  hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS>), dim3(1 + 4 * (D / 16) * ntile + max_active * (FR / 16)),
-                     dim3(256), 0, s, a, ntile);
-  hipLaunchKernelGGL((decode_stage3_kernel<D, FR>), dim3(max_active * (D / 32)), dim3(256), 0, s, a);
+  // stage 2 and 3 grids sized to one round of resident workgroups (see the kernels)
+  if (ntile == 1) {
+    hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS, 1, 1>), dim3(1 + 4 * (D / 16) + max_active * (FR / 16)),
+                       dim3(256), 0, s, a, ntile);
+  } else if (ntile == 2) {
+    hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS, 2, 1>), dim3(1 + 4 * (D / 16) + max_active * (FR / 16)),
+                       dim3(256), 0, s, a, ntile);
+  } else {
+    hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS, 4, 1>), dim3(1 + 4 * (D / 16) + max_active * (FR / 16)),
+                       dim3(256), 0, s, a, ntile);
+  }
+  if (a.T <= 32)
+    hipLaunchKernelGGL((decode_stage3_kernel<D, FR, 1>), dim3(max_active * (D / 32)), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_stage3_kernel<D, FR, 2>), dim3(max_active * (D / 64)), dim3(256), 0, s, a);
 }
 
 }  // namespace fgmoe
