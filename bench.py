@@ -654,7 +654,7 @@ def cpu_baseline(inp, seconds: float):
                        f"{el:.1f} s wall")
 
 
-GATE_UP_KERNEL = "gemm256_kernel<true>"
+GATE_UP_KERNEL = "gemm256_kernel<true, false, false>"   # the bf16 gate/up instantiation
 TRAFFIC_SOURCES = ["fine_grained_moe_amd/csrc/gemm_fwd.hip", "fine_grained_moe_amd/csrc/gemm_tile.h",
                    "fine_grained_moe_amd/csrc/common.h", "fine_grained_moe_amd/csrc/kernels.h",
                    "fine_grained_moe_amd/csrc/api.hip"]
