@@ -437,8 +437,8 @@ def bench_int4(moe, synth, torch, np, reps=20, steps=50, warmup=5, n_sets=8):
     N(0, 0.02)); algorithmic bytes = 2 read + 0.5 written per element + 2 per
     128 (scales).  Prefill: the int4 top-1 layer at T = 4096 (x RMS-normalised
     N(0, 1)) on those exported weights, 8 weight sets rotated (cold), phases
-    from the library's events (the first phase holds routing and the
-    dequantisation of the loaded experts)."""
+    from the library's events (the grouped GEMMs read the packed experts
+    directly, so the phases are those of the bf16 layer)."""
     E, d, F, Fs = 64, 1024, 512, 2048
     inp = synth.make_layer(T=4096, d=d, E=E, F=F, Fs=Fs, k=1, act="bf16", seed=5)
     bf = lambda a: torch.from_numpy(np.ascontiguousarray(a, np.float32)).to(device="cuda", dtype=torch.bfloat16)
@@ -498,10 +498,10 @@ def bench_int4(moe, synth, torch, np, reps=20, steps=50, warmup=5, n_sets=8):
     active = int(np.count_nonzero(r["counts"].cpu().numpy()))
     work = algorithmic_work(T, d, E, F, Fs, 1)
     out["prefill"] = dict(T=T, us_per_forward=round(el * 1e6, 1), tokens_per_s=T / el, active_experts=active,
-                          phases_us={("route_dequant" if p == "route" else p): round(v, 1) for p, v in ph_us.items()},
+                          phases_us={p: round(v, 1) for p, v in ph_us.items()},
                           gate_up_tflops=round(work["gate_up"]["flops"] / (ph_us["gate_up"] * 1e-6) / 1e12, 1))
     log(f"int4 prefill T={T}: {el * 1e6:.1f} us/forward, {T / el / 1e6:.2f} M tokens/s; phases (us): "
-        + ", ".join(f"{p}={v:.1f}" for p, v in ph_us.items()) + f" (route includes the dequantisation), "
+        + ", ".join(f"{p}={v:.1f}" for p, v in ph_us.items()) + ", "
         f"{active} experts loaded")
     return out
 
