@@ -40,7 +40,7 @@ GAMMA = 1e-3
 PHASES = ("route", "gate_up", "down", "combine")
 KERNEL_OF_PHASE = {
     "route": "route_topk + route_dispatch",
-    "gate_up": "gemm256_kernel<SwiGLU> (routed + shared gate/up, one launch)",
+    "gate_up": "gemm256_kernel<true, false, false> (routed + shared gate/up, one launch)",
     "down": "gemm256_kernel<store> (routed down with gate scaling + shared down in two contraction halves, one launch)",
     "combine": "combine_kernel<bf16>",
 }
