@@ -97,25 +97,16 @@ __device__ __forceinline__ u32x4_t dq_int4x8(uint32_t w, float sc) {
 // Segment swizzle of K-major stage rows (see the K-major loader).
 __device__ __forceinline__ int ksw(int r) { return (((r >> 3) & 3) << 2) | (r & 3); }
 typedef int i32x4_t __attribute__((ext_vector_type(4)));
-// Four consecutive int32 at a wave-uniform address, loaded through the
-// scalar cache (a read); the values may be used only after sload_wait.
+// Four consecutive int32 of a read-only table at a wave-uniform address:
+// through the constant address space the compiler emits a scalar load and
+// tracks its completion itself.
+typedef const __attribute__((address_space(4))) i32x4_t __attribute__((aligned(4)))* const_i32x4_ptr;
 __device__ __forceinline__ i32x4_t sload4(const int32_t* q) {
   const unsigned long long a = (unsigned long long)q;
   const unsigned lo = __builtin_amdgcn_readfirstlane((unsigned)a), hi = __builtin_amdgcn_readfirstlane((unsigned)(a >> 32));
-  const unsigned long long u = ((unsigned long long)hi << 32) | lo;
-  i32x4_t v{0, 0, 0, 0};
-#if defined(__HIP_DEVICE_COMPILE__)   // the host pass only parses (its assembler has no such operands)
-  asm volatile("s_load_dwordx4 %0, %1, 0x0" : "=s"(v) : "s"(u));
-#endif
-  return v;
+  return *reinterpret_cast<const_i32x4_ptr>(((unsigned long long)hi << 32) | lo);
 }
-// Waits for every outstanding scalar-cache and LDS access; the values pass
-// through, so no use of them is scheduled before the wait.
-__device__ __forceinline__ void sload_wait(i32x4_t& a, i32x4_t& b) {
-#if defined(__HIP_DEVICE_COMPILE__)
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+s"(a), "+s"(b));
-#endif
-}
+
 // One K-major MFMA fragment: two transposing 8-byte LDS reads, 4 K rows
 // apart.  Issued as inline asm: the compiler's builtin for this read makes
 // it wait for every direct-to-LDS load in flight first (it cannot tell them
@@ -312,21 +303,30 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       km_col[j] = j < NDA ? (row_base + min(lp, rows - 8)) * 2 : (nt * BN + min(lp, ncols - 8)) * 2;
     }
   }
-  // the map entries of the stage being issued, per operand
+  // The map entries of the next stage to issue, per operand (scalar loads
+  // started one main-loop trip ahead), and this lane's K rows of the stage
+  // being issued (km_sel, at the top of a trip, right after the barrier:
+  // no LDS read is in flight there, so the wait for the scalar loads that the
+  // compiler puts before their first use costs only what is left of them).
   i32x4_t km_rows[2] = {i32x4_t{0, 0, 0, 0}, i32x4_t{0, 0, 0, 0}};
-  auto km_fetch = [&](int s) {   // start the scalar loads of stage s's map entries
+  int km_r[2][2] = {{0, 0}, {0, 0}};
+  auto km_fetch = [&](int s) {
 #pragma unroll
     for (int op = 0; op < 2; ++op)
       if (km_map[op]) km_rows[op] = sload4(km_map[op] + km_ofs + 32 * s + 4 * wave_u);
   };
-  auto km_sync = [&]() {         // wait for them
-    if (km_map[0] || km_map[1]) sload_wait(km_rows[0], km_rows[1]);
+  auto km_sel = [&](int s) {
+#pragma unroll
+    for (int op = 0; op < 2; ++op)
+#pragma unroll
+      for (int jj = 0; jj < 2; ++jj)
+        km_r[op][jj] = km_map[op] ? (kh ? km_rows[op][2 * jj + 1] : km_rows[op][2 * jj])
+                                  : km_ofs + 32 * s + 4 * wave + 2 * jj + kh;
   };
   auto km_src = [&](int s, int j) -> const char* {
     const int op = j < NDA ? 0 : 1, jj = j & 1;
     const int kk = 32 * s + 4 * wave + 2 * jj + kh;
-    const int row = km_map[op] ? (kh ? km_rows[op][2 * jj + 1] : km_rows[op][2 * jj]) : km_ofs + kk;
-    return kk < kcnt ? km_base[op] + (long long)row * km_ld2[op] + km_col[j] : km_zero;
+    return kk < kcnt ? km_base[op] + (long long)km_r[op][jj] * km_ld2[op] + km_col[j] : km_zero;
   };
   auto issue_one = [&](int s, int j) {
     char* st = lds + (s % kStages) * kStageBytes;
@@ -485,7 +485,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   for (int s = 0; s < kStages - 1 && s < nk; ++s) {
     if constexpr (KM) {
       km_fetch(s);
-      km_sync();
+      km_sel(s);
     }
     issue(s);
   }
@@ -512,7 +512,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     for (; s + kStages - 1 < nk; ++s) {
       wait_vmcnt<2 * kLoads>();
       block_barrier();
-      if constexpr (KM) km_sync();
+      if constexpr (KM) km_sel(s + kStages - 1);
       compute(s, fa0, fa1, A{}, std::true_type{}, std::true_type{}, B4{});
       if (KM && s + kStages < nk) km_fetch(s + kStages);
 #pragma unroll

@@ -21,7 +21,7 @@ def _counter_csv(path, counter, rows):
 
 
 def test_traffic_summary_scales_by_the_copy(tmp_path, monkeypatch):
-    gemm = "void fgmoe::(anonymous namespace)::gemm256_kernel<true>(fgmoe::GemmArgs)"
+    gemm = f"void fgmoe::(anonymous namespace)::{bench.GATE_UP_KERNEL}(fgmoe::GemmArgs)"
     f = tmp_path / "f.csv"
     w = tmp_path / "w.csv"
     # FETCH reads half the copy's bytes, WRITE all of them; other kernels are ignored
