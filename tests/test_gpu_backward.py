@@ -74,6 +74,18 @@ def test_backward_ragged_many_tiles_bf16():
     _check(_case(1100, 256, 16, 128, 384, 3, "bf16", seed=3), 1e-2)
 
 
+def test_backward_shared_contraction_slices_ragged_bf16():
+    """T = 9000: the shared expert's weight gradients contract in two token
+    slices (4544 + 4456 tokens), the last one ending inside a 32-row stage,
+    so its rows past the last token read zeros; the routed experts' ranges
+    are ragged too."""
+    _check(_case(9000, 256, 8, 128, 256, 2, "bf16", seed=6), 1e-2)
+
+
+def test_backward_shared_contraction_slices_ragged_f32():
+    _check(_case(9000, 256, 8, 128, 256, 2, "f32", seed=7), 1e-4)
+
+
 def test_backward_top1_router_gradient_is_zero():
     """Top-2 paragraph of the "Relay training" section: with top_k = 1 the
     routing weight is a constant, so the router gets no gradient."""
