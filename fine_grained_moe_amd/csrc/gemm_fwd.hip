@@ -112,7 +112,10 @@ __device__ __forceinline__ i32x4_t sload4(const int32_t* q) {
 // it wait for every direct-to-LDS load in flight first (it cannot tell them
 // apart), which would drain the load pipeline at each fragment.  The
 // compiler does not see these reads either, so the results are used only
-// after lds_wait_frags.
+// after lds_wait_frags, and this relies on each read writing straight into
+// the fragment's registers: a copy the compiler placed between a read and
+// the wait would take the registers before the data arrives (the backward
+// parity tests, which run this path, would show it).
 typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ u32x4_t ds_read_tr_frag(const char* p) {
   const uint32_t a = (uint32_t)(uintptr_t)(lds_ptr_t)p;
