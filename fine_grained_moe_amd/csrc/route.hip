@@ -297,6 +297,20 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
   __shared__ int base[kDispatchSub][64];
   const int tid = threadIdx.x, e = tid & 63, part = tid >> 6;
   const int first = blockIdx.x * kDispatchSub;   // first router block of this dispatch block
+  // This block's assignments (at most kDispatchSub * 16 tokens x 8 = 2048,
+  // two per thread): their experts and ranks are requested first, beside the
+  // loads below, so the scatter at the end waits for no further round trip.
+  const long long a0 = (long long)first * kRouteTokensPerBlock * k;
+  const int ntok = max(0, min(kDispatchSub * kRouteTokensPerBlock, T_ - first * kRouteTokensPerBlock));
+  const int na = ntok * k, per = kRouteTokensPerBlock * k;
+  static_assert(kDispatchSub * kRouteTokensPerBlock * 8 <= 2 * 1024, "two assignments per thread");
+  int my_e[2], my_r[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int a = min(tid + 1024 * i, max(na - 1, 0));   // rows past na re-read the last one; not used
+    my_e[i] = na > 0 ? idx[a0 + a] : 0;
+    my_r[i] = na > 0 ? rank[a0 + a] : 0;
+  }
 
   // loads of every router block: thread (part, e) takes blocks part, part + 16, ...;
   // the prefix counts only blocks before `first`
@@ -352,13 +366,14 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
   }
   __syncthreads();
 
-  const long long a0 = (long long)first * kRouteTokensPerBlock * k;
-  const int ntok = max(0, min(kDispatchSub * kRouteTokensPerBlock, T_ - first * kRouteTokensPerBlock));
-  const int na = ntok * k, per = kRouteTokensPerBlock * k;
-  for (int a = tid; a < na; a += 1024) {
-    const int slot = base[a / per][idx[a0 + a]] + rank[a0 + a];
-    perm[slot] = (int32_t)(a0 + a);
-    pos[a0 + a] = slot;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int a = tid + 1024 * i;
+    if (a < na) {
+      const int slot = base[a / per][my_e[i]] + my_r[i];
+      perm[slot] = (int32_t)(a0 + a);
+      pos[a0 + a] = slot;
+    }
   }
 }
 
