@@ -140,10 +140,12 @@ Layout make_layout(const moe_dims& d, int training) {
     const bool kmaj = d.act == MOE_BF16;
     L.dAU = take(slots * 2 * F * es);
     L.dXp = take(slots * D * es);
-    L.WdT = take(E * F * D * es);
-    L.WguT = take(E * D * 2 * F * es);
-    L.WsdT = take(Fs * D * es);
-    L.WsguT = take(D * 2 * Fs * es);
+    if (!kmaj) {
+      L.WdT = take(E * F * D * es);
+      L.WguT = take(E * D * 2 * F * es);
+      L.WsdT = take(Fs * D * es);
+      L.WsguT = take(D * 2 * Fs * es);
+    }
     L.dAUs = take(T * 2 * Fs * es);
     L.dXs = take(T * D * es);
     if (kmaj) {
@@ -853,7 +855,8 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   launch_bwd_prep(routing->counts, routing->offsets, d.E, P, Tp, S, step, kofs, klen, ksh, pcol,
                   kmaj ? krow + slots : nullptr, kmaj ? at<int32_t>(ws, L.zrow) : nullptr, s);
 
-  // 2. transposed weights: W_d^T [E][F][d], W_gu^T [E][d][2F], W_sd^T [Fs][d], W_sgu^T [d][2Fs]
+  // 2. fp32: transposed weights W_d^T [E][F][d], W_gu^T [E][d][2F], W_sd^T
+  // [Fs][d], W_sgu^T [d][2Fs] (bf16 reads the weights as stored, K-major)
   auto transpose = [&](const void* src, long long ld_src, long long sb, void* dst, long long ld_dst, long long db, int R,
                        int C, int batch, int n_in, const int32_t* map1, const int32_t* map2, int div,
                        const float* scale) {
@@ -874,12 +877,14 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
     t.scale = scale;
     launch_transpose(act, t, s);
   };
-  transpose(w->w_down, d.F, (long long)D * F, WdT, d.d, (long long)F * D, d.F, d.d, d.E, d.d, nullptr, nullptr, 1,
-            nullptr);
-  transpose(w->w_gate_up, d.d, 2LL * F * D, WguT, 2 * d.F, 2LL * F * D, d.d, 2 * d.F, d.E, 2 * d.F, nullptr, nullptr, 1,
-            nullptr);
-  transpose(w->w_sh_down, d.Fs, 0, WsdT, d.d, 0, d.Fs, d.d, 1, d.d, nullptr, nullptr, 1, nullptr);
-  transpose(w->w_sh_gate_up, d.d, 0, WsguT, 2 * d.Fs, 0, d.d, 2 * d.Fs, 1, 2 * d.Fs, nullptr, nullptr, 1, nullptr);
+  if (!kmaj) {
+    transpose(w->w_down, d.F, (long long)D * F, WdT, d.d, (long long)F * D, d.F, d.d, d.E, d.d, nullptr, nullptr, 1,
+              nullptr);
+    transpose(w->w_gate_up, d.d, 2LL * F * D, WguT, 2 * d.F, 2LL * F * D, d.d, 2 * d.F, d.E, 2 * d.F, nullptr, nullptr,
+              1, nullptr);
+    transpose(w->w_sh_down, d.Fs, 0, WsdT, d.d, 0, d.Fs, d.d, 1, d.d, nullptr, nullptr, 1, nullptr);
+    transpose(w->w_sh_gate_up, d.d, 0, WsguT, 2 * d.Fs, 0, d.d, 2 * d.Fs, 1, 2 * d.Fs, nullptr, nullptr, 1, nullptr);
+  }
 
   // 3. router and gate gradients
   launch_bwd_gate(act, dy, at<char>(ws, L.Ou), x, w->w_router, routing->idx, routing->gate, routing->pos, d.T, d.d, d.k,
@@ -898,9 +903,11 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hr.lda = D;
   hr.a_rows = routing->perm;
   hr.a_div = d.k;
-  hr.B = WdT;
-  hr.ldb = D;
+  // B: W_d as stored ([d][F] per expert, K-major over d) for bf16, W_d^T for fp32
+  hr.B = kmaj ? w->w_down : WdT;
+  hr.ldb = kmaj ? F : D;
   hr.b_estride = (long long)F * D;
+  hr.kmaj = kmaj ? 2 : 0;
   hr.K = d.d;
   hr.N = d.F;
   hr.grouped = 1;
@@ -922,8 +929,9 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hs.A = dy;
   hs.lda = D;
   hs.a_div = 1;
-  hs.B = WsdT;
-  hs.ldb = D;
+  hs.B = kmaj ? w->w_sh_down : WsdT;
+  hs.ldb = kmaj ? Fs : D;
+  hs.kmaj = kmaj ? 2 : 0;
   hs.K = d.d;
   hs.N = d.Fs;
   hs.M = d.T;
@@ -948,8 +956,8 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   xr.lda = 2LL * F;
   xr.a_rows = nullptr;
   xr.a_div = 1;
-  xr.B = WguT;
-  xr.ldb = 2LL * F;
+  xr.B = kmaj ? w->w_gate_up : WguT;   // W_gu as stored: [2F][d] per expert, K-major over 2F
+  xr.ldb = kmaj ? D : 2LL * F;
   xr.b_estride = 2LL * F * D;
   xr.K = 2 * d.F;
   xr.N = d.d;
@@ -962,8 +970,8 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   xs.epi = EPI_STORE;
   xs.A = dAUs;
   xs.lda = 2LL * Fs;
-  xs.B = WsguT;
-  xs.ldb = 2LL * Fs;
+  xs.B = kmaj ? w->w_sh_gate_up : WsguT;
+  xs.ldb = kmaj ? D : 2LL * Fs;
   xs.K = 2 * d.Fs;
   xs.N = d.d;
   xs.C = dXs;

@@ -156,9 +156,10 @@ __device__ __host__ __forceinline__ int xcd_cols(const GemmJob& j) {
 }
 
 // I4: the launch has a job with int4 B (the int4 prefill); the bf16-only
-// instantiations carry none of that code.  KM: every job has K-major
-// operands (the weight gradients).
-template <bool SWIGLU, bool I4, bool KM>
+// instantiations carry none of that code.  KM: 1 every job has both
+// operands K-major (the weight gradients), 2 every job has a row-major A and
+// a K-major B (the input gradients, B the weights as stored), 0 neither.
+template <bool SWIGLU, bool I4, int KM>
 __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   typedef bf16_t T;
   // The ring; after the main loop its first buffer holds the row scales.
@@ -170,6 +171,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   int jid, bid;
   select_job(args, blockIdx.x, jid, bid);
   const GemmJob& p = args.job[jid];
+  constexpr bool KA = KM == 1, KB = KM != 0;   // A, B K-major (KB: transposing B reads, N fragment first)
 
   // ---- work item and N tile.  Grouped: XCD x takes items [x*q, (x+1)*q),
   // each with all its N tiles back to back.  Dense: XCD x takes row-item
@@ -218,7 +220,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   const int klen = p.kgroup ? p.klen[e] : p.K / k_slices(p);
   const long long kofs = p.kgroup ? (long long)p.kofs[e] : (long long)kz * klen;
   // K-major: the expert's rows that exist (the rest of its last stage reads zeros)
-  const int kcnt = KM ? max(0, min(klen, p.K - (int)kofs)) : 0;
+  const int kcnt = KA ? max(0, min(klen, p.K - (int)kofs)) : klen;
   rows = rows < BM ? rows : BM;
   // this wave's 64-row band holds rows of the item
   const bool active = wm * WM < rows;
@@ -277,10 +279,11 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     }
   }
   const long long b_step = b4 ? 16LL : p.b_staged ? (long long)BN * kRowB : (long long)kRowB;
-  const int nk = KM ? (kcnt + 31) >> 5 : (int)((long long)klen * sizeof(T) / kRowB);
+  const int nk = KA ? (kcnt + 31) >> 5 : (int)((long long)klen * sizeof(T) / kRowB);
 
-  // ---- K-major operands (KM).  A stage holds 32 K rows of 256 columns
-  // (512 bytes) of each operand; load j of wave w fills K rows 4w + 2j + h,
+  // ---- K-major operands (KM = 1: both, KM = 2: B only, A row-major as
+  // above).  A stage holds 32 K rows of 256 columns (512 bytes) of each
+  // K-major operand; load j of wave w fills K rows 4w + 2j + h,
   // h = lane / 32, 16 bytes per lane.  The 32-byte segment q of K row r sits
   // at segment q ^ ksw(r), which spreads the 16 rows x 32 bytes of one
   // transposing fragment read over all the banks.  A lane's piece is clamped
@@ -292,15 +295,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   int km_col[NDA + NDB];   // byte offset of the lane's piece in its operand row
   const int kh = lane >> 5, kp = lane & 31;
   const int wave_u = __builtin_amdgcn_readfirstlane(wave);
-  const char* const km_base[2] = {reinterpret_cast<const char*>(p.A), reinterpret_cast<const char*>(p.B)};
+  const char* const km_base[2] = {reinterpret_cast<const char*>(p.A),
+                                  reinterpret_cast<const char*>(p.B) + (long long)e * p.b_estride * 2};
   const long long km_ld2[2] = {p.lda * 2, p.ldb * 2};
   const int32_t* const km_map[2] = {p.a_krow, p.b_krow};
   const char* const km_zero = reinterpret_cast<const char*>(p.zrow) + 16 * kp;
   const int km_ofs = (int)kofs;
-  if constexpr (KM) {
+  if constexpr (KB) {
     const int ncols = min(p.N - nt * BN, BN);
 #pragma unroll
-    for (int j = 0; j < NDA + NDB; ++j) {
+    for (int j = KA ? 0 : NDA; j < NDA + NDB; ++j) {
       const int r = 4 * wave + 2 * (j & 1) + kh;
       const int lp = ((((kp >> 1) ^ ksw(r)) << 1) | (kp & 1)) * 8;
       km_col[j] = j < NDA ? (row_base + min(lp, rows - 8)) * 2 : (nt * BN + min(lp, ncols - 8)) * 2;
@@ -326,15 +330,27 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
         km_r[op][jj] = km_map[op] ? (kh ? km_rows[op][2 * jj + 1] : km_rows[op][2 * jj])
                                   : km_ofs + 32 * s + 4 * wave + 2 * jj + kh;
   };
+  // KM = 2: B has every K row (K a multiple of 32) and no map, so its source
+  // is a fixed pointer advanced by 32 rows per stage, as in the row-major path
+  const char* kb_src[NDB];
+  if constexpr (KM == 2) {
+#pragma unroll
+    for (int j = 0; j < NDB; ++j)
+      kb_src[j] = km_base[1] + (long long)(km_ofs + 4 * wave + 2 * j + kh) * km_ld2[1] + km_col[NDA + j];
+  }
   auto km_src = [&](int s, int j) -> const char* {
-    const int op = j < NDA ? 0 : 1, jj = j & 1;
-    const int kk = 32 * s + 4 * wave + 2 * jj + kh;
-    return kk < kcnt ? km_base[op] + (long long)km_r[op][jj] * km_ld2[op] + km_col[j] : km_zero;
+    if constexpr (KM == 2) {
+      return kb_src[j - NDA] + (long long)s * 32 * km_ld2[1];
+    } else {
+      const int op = j < NDA ? 0 : 1, jj = j & 1;
+      const int kk = 32 * s + 4 * wave + 2 * jj + kh;
+      return kk < kcnt ? km_base[op] + (long long)km_r[op][jj] * km_ld2[op] + km_col[j] : km_zero;
+    }
   };
   auto issue_one = [&](int s, int j) {
     char* st = lds + (s % kStages) * kStageBytes;
     const long long off = (long long)s * kRowB;
-    if constexpr (KM) {
+    if (KA || (KB && j >= NDA)) {
       const char* src = km_src(s, j);
       __builtin_amdgcn_global_load_lds(src, (lds_ptr_t)(st + (j < NDA ? 0 : ATILE) + (wave * 2 + (j & 1)) * 1024), 16, 0,
                                        0);
@@ -414,7 +430,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     const char* As = lds + (s % kStages) * kStageBytes;
 #pragma unroll
     for (int mi = 0; mi < 4; ++mi) {
-      if constexpr (KM) fa[mi] = km_frag(As, 4 * wm + mi);
+      if constexpr (KA) fa[mi] = km_frag(As, 4 * wm + mi);
       else fa[mi] = ld16(As + swz(arow_l[mi], g));
     }
   };
@@ -422,7 +438,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     const char* Bs = lds + (s % kStages) * kStageBytes + ATILE;
 #pragma unroll
     for (int ni = 0; ni < NI; ++ni) {
-      if constexpr (KM) {
+      if constexpr (KB) {
         fb[ni] = km_frag(Bs, 8 * wn + ni);
       } else if constexpr (decltype(b4c)::value) {
         qb[ni] = qword(Bs, brow_l[ni]);
@@ -454,13 +470,16 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       // results are four adjacent output columns of one output row
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) {
-        if constexpr (KM) acc[mi][ni] = Mma<T>::run1(bv, fa[mi], acc[mi][ni]);
+        if constexpr (KB) acc[mi][ni] = Mma<T>::run1(bv, fa[mi], acc[mi][ni]);
         else acc[mi][ni] = Mma<T>::run1(fa[mi], bv, acc[mi][ni]);
       }
       if constexpr (decltype(prefetch)::value) {
-        if constexpr (KM) {
+        if constexpr (KB) {
           fb[ni] = km_frag(Bn, 8 * wn + ni);
-          if (ni < 4) fn[ni] = km_frag(An, 4 * wm + ni);
+          if (ni < 4) {
+            if constexpr (KA) fn[ni] = km_frag(An, 4 * wm + ni);
+            else fn[ni] = ld16(An + swz(arow_l[ni], g));
+          }
         } else {
           if constexpr (B4) {
             qb[ni] = qword(Bn, brow_l[ni]);
@@ -476,7 +495,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the reads and loads spread out
     }
-    if constexpr (KM && decltype(prefetch)::value) lds_wait_frags(fn, fb);
+    if constexpr (KB && decltype(prefetch)::value) lds_wait_frags(fn, fb);
   };
 
   // ---- main loop.  Iteration s waits for stage s + 1 (its loads went out
@@ -486,13 +505,13 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   // free for the loads of stage s + 4.
   static_assert(kStages == 5, "the waits below assume a 5-deep ring");
   for (int s = 0; s < kStages - 1 && s < nk; ++s) {
-    if constexpr (KM) {
+    if constexpr (KA) {
       km_fetch(s);
       km_sel(s);
     }
     issue(s);
   }
-  if (KM && kStages - 1 < nk) km_fetch(kStages - 1);
+  if (KA && kStages - 1 < nk) km_fetch(kStages - 1);
   if (nk >= 4) wait_vmcnt<3 * kLoads>();
   else if (nk == 3) wait_vmcnt<2 * kLoads>();
   else if (nk == 2) wait_vmcnt<kLoads>();
@@ -505,7 +524,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     if constexpr (A::value) {
       read_a(0, fa0);
       read_b(0, B4{});
-      if constexpr (KM) lds_wait_frags(fa0, fb);
+      if constexpr (KB) lds_wait_frags(fa0, fb);
     }
     // Stages issued before iteration s: min(nk, s + 4); in flight after stage
     // s + 1: that minus s + 2.  Two K steps per trip, so the two A sets swap
@@ -515,9 +534,9 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     for (; s + kStages - 1 < nk; ++s) {
       wait_vmcnt<2 * kLoads>();
       block_barrier();
-      if constexpr (KM) km_sel(s + kStages - 1);
+      if constexpr (KA) km_sel(s + kStages - 1);
       compute(s, fa0, fa1, A{}, std::true_type{}, std::true_type{}, B4{});
-      if (KM && s + kStages < nk) km_fetch(s + kStages);
+      if (KA && s + kStages < nk) km_fetch(s + kStages);
 #pragma unroll
       for (int mi = 0; mi < 4; ++mi) fa0[mi] = fa1[mi];
     }
@@ -552,8 +571,38 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     if (tid < BM) row_scale[tid] = nk >= 2 ? my_gate : p.gate[my_perm];
     __syncthreads();
   }
+  if constexpr (KM == 2) __syncthreads();            // the ring is reused below
   if (!active) return;
-  if constexpr (KM) {
+  if constexpr (KM == 2) {
+    // acc[mi][ni][i] is tile row wm*64 + 16 mi + fr, column wn*128 + 16 ni +
+    // 4g + i.  Re-laid through LDS (this wave's 32 x 144 fp32 block, past the
+    // row scales), two 16-row blocks at a time, into the layout of the
+    // row-major mode (row wm*64 + 16 mi + 4g + i, column wn*128 + 8 fr + ni),
+    // so that the epilogue below stores 8 adjacent columns per lane.  Rows
+    // 144 floats apart put both directions at two cycles per 1 KiB access.
+    constexpr int XS = 144;
+    float* const xb = reinterpret_cast<float*>(lds + 4096) + wave * (32 * XS);
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni)
+          *reinterpret_cast<f32x4_t*>(xb + (16 * m2 + fr) * XS + 16 * ni + 4 * g) = acc[2 * half + m2][ni];
+#pragma unroll
+      for (int m2 = 0; m2 < 2; ++m2)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float* src = xb + (16 * m2 + 4 * g + i) * XS + 8 * fr;
+          const f32x4_t lo = *reinterpret_cast<const f32x4_t*>(src), hi = *reinterpret_cast<const f32x4_t*>(src + 4);
+#pragma unroll
+          for (int c = 0; c < 4; ++c) {
+            acc[2 * half + m2][c][i] = lo[c];
+            acc[2 * half + m2][c + 4][i] = hi[c];
+          }
+        }
+    }
+  } else if constexpr (KM == 1) {
     // acc[mi][ni][i]: tile row wm*64 + 16 mi + fr, column wn*128 + 16 ni + 4g + i
     float* const Ck = reinterpret_cast<float*>(p.C) + (long long)e * p.c_estride;
 #pragma unroll
@@ -703,14 +752,16 @@ void launch_gemm_fwd256(const GemmArgs& in, hipStream_t s) {
   if (total == 0) return;
   const dim3 grid((unsigned)(total * 8));
   const bool i4 = a.job[0].b_int4 || (a.njobs > 1 && a.job[1].b_int4);
-  if (a.job[0].kmaj) {
-    hipLaunchKernelGGL((gemm256_kernel<false, false, true>), grid, dim3(NTHR), 0, s, a);
+  if (a.job[0].kmaj == 1) {
+    hipLaunchKernelGGL((gemm256_kernel<false, false, 1>), grid, dim3(NTHR), 0, s, a);
+  } else if (a.job[0].kmaj == 2) {
+    hipLaunchKernelGGL((gemm256_kernel<false, false, 2>), grid, dim3(NTHR), 0, s, a);
   } else if (a.job[0].epi == EPI_SWIGLU) {
-    if (i4) hipLaunchKernelGGL((gemm256_kernel<true, true, false>), grid, dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((gemm256_kernel<true, false, false>), grid, dim3(NTHR), 0, s, a);
+    if (i4) hipLaunchKernelGGL((gemm256_kernel<true, true, 0>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((gemm256_kernel<true, false, 0>), grid, dim3(NTHR), 0, s, a);
   } else {
-    if (i4) hipLaunchKernelGGL((gemm256_kernel<false, true, false>), grid, dim3(NTHR), 0, s, a);
-    else hipLaunchKernelGGL((gemm256_kernel<false, false, false>), grid, dim3(NTHR), 0, s, a);
+    if (i4) hipLaunchKernelGGL((gemm256_kernel<false, true, 0>), grid, dim3(NTHR), 0, s, a);
+    else hipLaunchKernelGGL((gemm256_kernel<false, false, 0>), grid, dim3(NTHR), 0, s, a);
   }
 }
 

@@ -96,13 +96,17 @@ struct GemmJob {
   const int32_t* kofs;
   const int32_t* klen;
   long long c_estride;
-  // launch_gemm_fwd256 only, kgroup jobs with the fp32 store (the weight
-  // gradients): A and B are K-major, element (m, k) of A at A[krow(k) * lda +
-  // m] and (n, k) of B at B[krow(k) * ldb + n], krow(k) = a_krow ? a_krow[k] :
-  // k (b_krow likewise), over expert e's rows kofs[e] + [0, min(klen[e], K -
-  // kofs[e])) (klen[e] any count).  The maps are readable 32 entries past
-  // every range, zrow points at 512 zero bytes, M and N are multiples of 8 and
-  // lda, ldb multiples of 8 elements.
+  // launch_gemm_fwd256 only.  kmaj = 1, kgroup jobs with the fp32 store (the
+  // weight gradients): A and B are K-major, element (m, k) of A at
+  // A[krow(k) * lda + m] and (n, k) of B at B[krow(k) * ldb + n], krow(k) =
+  // a_krow ? a_krow[k] : k (b_krow likewise), over expert e's rows kofs[e] +
+  // [0, min(klen[e], K - kofs[e])) (klen[e] any count).  The maps are readable
+  // 32 entries past every range, zrow points at 512 zero bytes, M and N are
+  // multiples of 8 and lda, ldb multiples of 8 elements.  kmaj = 2, grouped
+  // or dense jobs with the plain store or the SwiGLU-backward epilogue (the
+  // input gradients): A as usual, B K-major, (n, k) of expert e at B +
+  // e * b_estride + k * ldb + n; K a multiple of 32, N of 8.  Both jobs of a
+  // launch have the same kmaj.
   int kmaj;
   const int32_t* a_krow;
   const int32_t* b_krow;
