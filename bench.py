@@ -40,7 +40,7 @@ GAMMA = 1e-3
 PHASES = ("route", "gate_up", "down", "combine")
 KERNEL_OF_PHASE = {
     "route": "route_topk + route_dispatch",
-    "gate_up": "gemm256_kernel<true, false, false> (routed + shared gate/up, one launch)",
+    "gate_up": "gemm256_kernel<true, false, 0> (routed + shared gate/up, one launch)",
     "down": "gemm256_kernel<store> (routed down with gate scaling + shared down in two contraction halves, one launch)",
     "combine": "combine_kernel<bf16>",
 }
@@ -654,7 +654,7 @@ def cpu_baseline(inp, seconds: float):
                        f"{el:.1f} s wall")
 
 
-GATE_UP_KERNEL = "gemm256_kernel<true, false, false>"   # the bf16 gate/up instantiation
+GATE_UP_KERNEL = "gemm256_kernel<true, false, 0>"   # the bf16 gate/up instantiation
 TRAFFIC_SOURCES = ["fine_grained_moe_amd/csrc/gemm_fwd.hip", "fine_grained_moe_amd/csrc/gemm_tile.h",
                    "fine_grained_moe_amd/csrc/common.h", "fine_grained_moe_amd/csrc/kernels.h",
                    "fine_grained_moe_amd/csrc/api.hip"]
