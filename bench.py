@@ -41,7 +41,7 @@ PHASES = ("route", "gate_up", "down", "combine")
 KERNEL_OF_PHASE = {
     "route": "route_topk + route_dispatch",
     "gate_up": "gemm256_kernel<true, false, 0> (routed + shared gate/up, one launch)",
-    "down": "gemm256_kernel<store> (routed down with gate scaling + shared down in two contraction halves, one launch)",
+    "down": "gemm256_kernel<false, false, 0> (routed down with gate scaling + shared down in two contraction halves, one launch)",
     "combine": "combine_kernel<bf16>",
 }
 
