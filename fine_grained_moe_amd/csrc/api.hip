@@ -246,6 +246,16 @@ int dense_xcd_cols(long long M, long long N) {
   return best;
 }
 
+// From 16384 rows a dense job whose B fits an XCD's L2 runs each row item's
+// N tiles back to back on one XCD (as grouped jobs do): one XCD's share of
+// the A rows no longer fits its 4 MB L2, so taking the N tiles outer re-read
+// them once per N tile.  Measured: the training step (32768 tokens, shared
+// down, dH and dX shared jobs) 2.67 -> 2.62 ms; the skewed-routing step's
+// shared down (16384) 145 -> 138 us.  The shared gate/up (8 MB of weights)
+// keeps the grid (216 against 209 us), as does the 4096-token layer (no
+// gain).
+int dense_order(long long M, long long N) { return M >= 16384 ? -1 : dense_xcd_cols(M, N); }
+
 moe_status device_status() { return hipGetLastError() == hipSuccess ? MOE_OK : MOE_E_DEVICE; }
 
 // Phase-boundary events of one instrumented call (moe_forward_events): the
@@ -435,7 +445,7 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   const int nsd = shared_down_slices(d);
   sd.ksplit = nsd;
   sd.c_kstride = (long long)d.T * D;
-  sd.xcd_cols = dense_xcd_cols(d.T, D);
+  sd.xcd_cols = dense_order(d.T, D);
 
   GemmArgs da{};
   da.act = d.act;
@@ -938,7 +948,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   hs.max_items = (d.T + tm - 1) / tm;
   hs.C = dAUs;
   hs.ldc = 2LL * Fs;
-  hs.xcd_cols = dense_xcd_cols(d.T, Fs);
+  hs.xcd_cols = dense_order(d.T, Fs);
   hs.aux = at<char>(ws, L.AUs);
   hs.ldaux = 2LL * Fs;
   GemmArgs g1{};
@@ -977,7 +987,7 @@ moe_status moe_backward(const moe_dims* dims, const void* x, const moe_weights* 
   xs.C = dXs;
   xs.ldc = D;
   xs.aux = nullptr;
-  xs.xcd_cols = dense_xcd_cols(d.T, D);
+  xs.xcd_cols = dense_order(d.T, D);
   GemmArgs g2{};
   g2.act = act;
   g2.njobs = 2;

@@ -38,7 +38,8 @@
 // contraction slices of a split dense job; grouped: the 256-row tile table
 // the router wrote).  Block b runs on XCD b % 8.  Grouped jobs: XCD x gets
 // the contiguous item range [x*q, (x+1)*q) and runs all N tiles of an item
-// back to back (an expert's weights are read once).  Dense jobs: the XCDs
+// back to back (an expert's weights are read once); so do dense jobs with
+// xcd_cols = -1 (an item's A rows are read once).  Other dense jobs: the XCDs
 // split the (row block, N tile) grid into an (8 / gc) x gc grid of ranges,
 // gc chosen by the caller so that the L2 misses of the two operands,
 // (M rows x gc + N rows x 8 / gc) x K, are smallest; measured with
@@ -180,7 +181,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   const int nbn = n_tiles(p);
   const int xcd = bid & 7, local = bid >> 3;
   int item, nt;
-  if (p.grouped || p.kgroup) {
+  if (p.grouped || p.kgroup || p.xcd_cols < 0) {
     const int q = (count + 7) >> 3;
     const int pi = local / nbn;
     nt = local - pi * nbn;
@@ -694,7 +695,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
 // chunks of 8 blocks (one per XCD) a job needs: the blocks one XCD runs
 int job_chunks(const GemmJob& j) {
   const int nbn = n_tiles(j);
-  if (j.grouped || j.kgroup) return (int)((max_item_count(j) + 7) / 8 * nbn);
+  if (j.grouped || j.kgroup || j.xcd_cols < 0) return (int)((max_item_count(j) + 7) / 8 * nbn);
   const int gc = xcd_cols(j), gr = 8 / gc;
   return (int)((max_item_count(j) + gr - 1) / gr * ((nbn + gc - 1) / gc));
 }

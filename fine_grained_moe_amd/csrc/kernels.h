@@ -116,7 +116,9 @@ struct GemmJob {
   int ksplit;
   long long c_kstride;
   // dense jobs of launch_gemm_fwd256: the 8 XCDs take a (8 / xcd_cols) x
-  // xcd_cols grid of (row-block, N-tile) ranges (1, 2, 4 or 8; 0 means 1)
+  // xcd_cols grid of (row-block, N-tile) ranges (1, 2, 4 or 8; 0 means 1), N
+  // tiles outer; -1: XCD x takes a contiguous range of row items and runs
+  // each item's N tiles back to back (as grouped jobs)
   int xcd_cols;
   // outputs
   void* C;
