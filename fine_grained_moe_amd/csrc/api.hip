@@ -87,7 +87,7 @@ int shared_down_slices(const moe_dims& d) { return d.act == MOE_BF16 ? 2 : 1; }
 Layout make_layout(const moe_dims& d, int training) {
   Layout L{};
   const size_t es = act_bytes(d.act);
-  const size_t nblk = (size_t)route_blocks(d.T);
+  const size_t nblk = (size_t)route_blocks(d.T, 16);   // the most router blocks of any block size
   const size_t slots = (size_t)d.T * d.k;
   const size_t tiles = (size_t)max_group_tiles((long long)slots, d.E);
   size_t o = 0;
@@ -219,12 +219,12 @@ struct BiasStep {
 // bs (may be null): the bias step, taken by the dispatch launch.
 void enqueue_route(const moe_dims& d, const Layout& L, const void* x, const void* w_router, const float* bias,
                    const moe_routing* r, void* ws, hipStream_t s, const BiasStep* bs = nullptr) {
-  const int nblk = route_blocks(d.T);
   launch_route_topk(d.act, x, w_router, bias, d.T, d.d, d.E, d.k, r->idx, r->gate, at<int32_t>(ws, L.block_counts),
                     at<int32_t>(ws, L.rank), s);
   const TileTable tiles{at<int32_t>(ws, L.tile_e), at<int32_t>(ws, L.tile_m0), at<int32_t>(ws, L.tile_count)};
   const TileTable tiles_fwd{at<int32_t>(ws, L.tile2_e), at<int32_t>(ws, L.tile2_m0), at<int32_t>(ws, L.tile2_count)};
-  launch_route_dispatch(at<int32_t>(ws, L.block_counts), r->idx, at<int32_t>(ws, L.rank), nblk, d.T, d.E, d.k,
+  launch_route_dispatch(at<int32_t>(ws, L.block_counts), r->idx, at<int32_t>(ws, L.rank), route_tpb(d.T, d.act, d.d),
+                        d.T, d.E, d.k,
                         r->counts, r->offsets, tiles, tiles_fwd, r->perm, r->pos, bs ? bs->gamma : 0.f,
                         bs ? bs->bias : nullptr, bs ? bs->stats : nullptr, s);
 }

@@ -8,14 +8,17 @@
 
 namespace fgmoe {
 
-// Tokens handled by one routing workgroup (4 waves, one 16x16 logit tile each).
-constexpr int kRouteTokensPerBlock = 16;
 // Rows of one grouped-GEMM tile: gemm.hip (fp32 forward, backward) and
 // gemm_fwd.hip (bf16 forward).  The router writes a tile table for each.
 constexpr int kTileM = 128;
 constexpr int kTileMFwd = 256;
 
-inline int route_blocks(int T) { return (T + kRouteTokensPerBlock - 1) / kRouteTokensPerBlock; }
+// Tokens owned by one router workgroup: 16, or 64 for bf16 batches of more
+// than 4096 tokens with d a multiple of 256 (above one round of 16-token
+// workgroups on 256 CUs; the router matrix is then read a quarter as often).
+// The per-block loads and ranks of launch_route_topk are per tpb tokens.
+inline int route_tpb(int T, int act, int d) { return (act == 1 && d % 256 == 0 && T > 4096) ? 64 : 16; }
+inline int route_blocks(int T, int tpb) { return (T + tpb - 1) / tpb; }
 // Upper bound of sum_e ceil(count_e / kTileM) over any routing of T*k slots.
 inline long long max_group_tiles(long long slots, int E, int tm = kTileM) {
   return (slots + (long long)E * (tm - 1)) / tm;
@@ -36,7 +39,8 @@ void launch_route_topk(int act, const void* x, const void* w_router, const float
 // bias (may be null): once the loads are known, the bias step with gamma on
 // bias (in place) and, if stats is not null, the balance figures (as
 // launch_bias_update with total T * k).
-void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
+// tpb: route_tpb of the batch (the router's block size).
+void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int tpb, int T,
                            int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
                            int32_t* perm, int32_t* pos, float gamma, float* bias, float* stats, hipStream_t s);
 // stats (may be null): [4] expert-balance figures of the batch

@@ -145,7 +145,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
   }
 
   // ---- partial logits of this wave
-  const int tok0 = blockIdx.x * kRouteTokensPerBlock;
+  const int tok0 = blockIdx.x * 16;
   f32x4_t acc[4];
 #pragma unroll
   for (int et = 0; et < 4; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -241,7 +241,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
   }
   __syncthreads();
   if (tid < E) block_counts[(long long)blockIdx.x * E + tid] = hist[tid];
-  const int na = min(kRouteTokensPerBlock, T_ - tok0) * k;
+  const int na = min(16, T_ - tok0) * k;
   if (tid < na) {
     const int e = sel[tid];
     int rk = 0;
@@ -251,11 +251,213 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 }
 
 // ---------------------------------------------------------------------------
+// The router for large bf16 batches: one workgroup owns 64 tokens, so the
+// 128 KiB router matrix is read a quarter as often and a 16384-token batch is
+// one round of 256 workgroups instead of four rounds of 1,024.  The staging
+// is route_logits_staged's with 64 x rows per chunk (a 128 KiB two-deep
+// ring); wave w multiplies token tiles 2 (w & 1) .. + 1 by expert tiles
+// 2 ((w >> 1) & 1) .. + 1 over k steps 4 (w >> 2) .. + 3 of every chunk, and
+// the two k halves meet in LDS (first half + second half).  Selection,
+// gates, per-block loads and ranks are the 16-token kernel's, over 64
+// tokens; ranks come from a per-wave count of earlier lanes with the same
+// expert plus the counts of the earlier waves.
+// ---------------------------------------------------------------------------
+// s_waitcnt vmcnt(N), the other counters left free (gfx9 encoding: vmcnt
+// bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
+template <int N>
+__device__ __forceinline__ void route_wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 0xF) | ((N >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+}
+
+// RB: bytes of each row per chunk (512: a two-deep ring, the one launched;
+// 256: four-deep, which measured the same on the 16384-token batch).
+template <int RB>
+__device__ __forceinline__ int route64_swz(int row, int piece) {
+  return RB == 512 ? piece ^ ((row & 15) << 1) : piece ^ (row & 15);
+}
+
+template <int K, int RB>
+__global__ __launch_bounds__(512) void route_topk64_kernel(const bf16_t* __restrict__ x,
+                                                           const bf16_t* __restrict__ wr,
+                                                           const float* __restrict__ bias, int T_, int d, int E,
+                                                           int32_t* __restrict__ idx, float* __restrict__ gate,
+                                                           int32_t* __restrict__ block_counts,
+                                                           int32_t* __restrict__ rank) {
+  static_assert(RB == 512 || RB == 256, "row chunks of 256 or 128 elements");
+  constexpr int kXB = 64 * RB, kStageB = 2 * kXB;        // x rows, then router rows
+  constexpr int kRingB = 128 * 1024, kDepth = kRingB / kStageB;
+  constexpr int kPieces = RB / 16;                       // 16-byte pieces per row chunk
+  constexpr int kNI = 8 * RB / 1024;                     // wave instructions per matrix and chunk
+  constexpr int kKS = RB / 128;                          // k steps of 32 per chunk and k half
+  static_assert(2 * 64 * 65 * 4 <= kRingB, "the two partial halves fit in the ring");
+  __shared__ __attribute__((aligned(16))) char lds[kRingB + 64 * 65 * 4 + 64 * K * 4 + 64 * 4 + 64 * 4 +
+                                                    kRouteWaves * 64 * 4];
+  float (*part)[64][65] = reinterpret_cast<float (*)[64][65]>(lds);
+  float (*lgs)[65] = reinterpret_cast<float (*)[65]>(lds + kRingB);
+  int* sel = reinterpret_cast<int*>(lds + kRingB + 64 * 65 * 4);
+  int* hist = sel + 64 * K;
+  float* bias_s = reinterpret_cast<float*>(hist + 64);
+  int (*whist)[64] = reinterpret_cast<int (*)[64]>(bias_s + 64);
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int r = lane & 15, g = lane >> 4;
+  if (tid < 64) {
+    hist[tid] = 0;
+    bias_s[tid] = tid < E ? bias[tid] : 0.f;
+  }
+  whist[wave][lane] = 0;
+  const int tok0 = blockIdx.x * 64;
+
+  // ---- partial logits.  Wave w copies x rows 8w .. 8w+7 and router rows
+  // 8w .. 8w+7 of each chunk; one instruction moves 1 KiB (lane i: row
+  // i / kPieces of the instruction's rows, piece i % kPieces).
+  const int rsub = lane / kPieces, ph = lane % kPieces;
+  constexpr int kRowsPerI = 1024 / RB;
+  const char* src[2 * kNI];
+  int dst[2 * kNI];
+#pragma unroll
+  for (int j = 0; j < kNI; ++j) {
+    const int rr = 8 * wave + kRowsPerI * j + rsub;
+    const int t = min(tok0 + rr, T_ - 1);             // rows past T re-read the last token; never used
+    src[j] = reinterpret_cast<const char*>(x + (long long)t * d) + route64_swz<RB>(rr, ph) * 16;
+    dst[j] = (8 * wave + kRowsPerI * j) * RB;
+    src[kNI + j] = reinterpret_cast<const char*>(wr + (long long)min(rr, E - 1) * d) + route64_swz<RB>(rr, ph) * 16;
+    dst[kNI + j] = kXB + (8 * wave + kRowsPerI * j) * RB;
+  }
+  auto issue = [&](int c) {
+    char* st = lds + (c % kDepth) * kStageB;
+#pragma unroll
+    for (int j = 0; j < 2 * kNI; ++j) {
+      // (operands computed outside the builtin: a template-dependent builtin
+      // argument makes the host pass drop the kernel's launch stub)
+      const char* gsrc = src[j] + c * RB;
+      char* ldst = st + dst[j];
+      __builtin_amdgcn_global_load_lds(gsrc, (route_lds_ptr_t)ldst, 16, 0, 0);
+    }
+  };
+  const int tp = wave & 1, ep = (wave >> 1) & 1, kh = wave >> 2;
+  f32x4_t acc[2][2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  const int nch = d / (RB / 2);
+#pragma unroll
+  for (int c = 0; c < kDepth; ++c)
+    if (c < nch) issue(c);
+  for (int c = 0; c < nch; ++c) {
+    // chunks issued after c: min(nch, c + kDepth) - c - 1, kNI * 2 loads each
+    const int after = min(nch, c + kDepth) - c - 1;
+    if (after >= 3) route_wait_vm<6 * kNI>();
+    else if (after == 2) route_wait_vm<4 * kNI>();
+    else if (after == 1) route_wait_vm<2 * kNI>();
+    else route_wait_vm<0>();
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+    const char* st = lds + (c % kDepth) * kStageB;
+#pragma unroll
+    for (int s = 0; s < kKS; ++s) {
+      const int piece = 4 * (kKS * kh + s) + g;        // k step kKS kh + s, lane group g
+      u32x4_t a[2], b[2];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int xr = (2 * tp + i) * 16 + r, er = (2 * ep + i) * 16 + r;
+        a[i] = ld16(st + xr * RB + route64_swz<RB>(xr, piece) * 16);
+        b[i] = ld16(st + kXB + er * RB + route64_swz<RB>(er, piece) * 16);
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j) acc[i][j] = Mma<bf16_t>::run1(a[i], b[j], acc[i][j]);
+    }
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();                      // every wave is done with buffer c % kDepth
+    asm volatile("" ::: "memory");
+    if (c + kDepth < nch) issue(c + kDepth);
+  }
+  // acc[i][j][q]: token (2 tp + i) * 16 + 4 g + q, expert (2 ep + j) * 16 + r
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) part[kh][(2 * tp + i) * 16 + 4 * g + q][(2 * ep + j) * 16 + r] = acc[i][j][q];
+  __syncthreads();
+  for (int q = tid; q < 64 * 64; q += 512) {
+    const int tt = q >> 6, e = q & 63;
+    lgs[tt][e] = part[0][tt][e] + part[1][tt][e];
+  }
+  __syncthreads();
+
+  // ---- selection: in round i, wave w takes tokens 16 i + 2w and 16 i + 2w + 1
+  // (32 lanes each, two experts per lane, five butterfly merges)
+#pragma unroll 1
+  for (int it = 0; it < 4; ++it) {
+    const int tt = 16 * it + 2 * wave + (lane >> 5), u = lane & 31;
+    uint64_t best[K];
+#pragma unroll
+    for (int i = 0; i < K; ++i) best[i] = 0;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int e = 2 * u + i;
+      const float sc = 1.0f / (1.0f + expf(-lgs[tt][min(e, 63)]));
+      if (e < E) route_insert<K>(best, route_key(sc + bias_s[e], e));
+    }
+#pragma unroll
+    for (int off = 1; off <= 16; off <<= 1) {
+      uint64_t other[K];
+#pragma unroll
+      for (int i = 0; i < K; ++i) {
+        const uint32_t lo = __shfl_xor((uint32_t)best[i], off), hi = __shfl_xor((uint32_t)(best[i] >> 32), off);
+        other[i] = ((uint64_t)hi << 32) | lo;
+      }
+#pragma unroll
+      for (int i = 0; i < K; ++i) route_insert<K>(best, other[i]);
+    }
+    const int tok = tok0 + tt;
+    if (u == 0 && tok < T_) {
+      float ssel[K];
+      float ssum = 0.f;
+#pragma unroll
+      for (int j = 0; j < K; ++j) {
+        const int e = 63 - (int)(uint32_t)best[j];
+        ssel[j] = 1.0f / (1.0f + expf(-lgs[tt][e]));
+        ssum += ssel[j];
+        sel[tt * K + j] = e;
+        idx[(long long)tok * K + j] = e;
+        atomicAdd(&hist[e], 1);
+      }
+#pragma unroll
+      for (int j = 0; j < K; ++j) gate[(long long)tok * K + j] = ssel[j] / ssum;
+    }
+  }
+  __syncthreads();
+  if (tid < E) block_counts[(long long)blockIdx.x * E + tid] = hist[tid];
+
+  // ---- ranks: thread a owns assignment a (at most 64 K <= 512 of them)
+  const int na = min(64, T_ - tok0) * K;
+  const int a = tid;
+  const int e = a < na ? sel[a] : -1;
+  if (a < na) atomicAdd(&whist[wave][e], 1);
+  int rk = 0;
+  for (int j = 0; j < 64; ++j) {
+    const int v = __builtin_amdgcn_readlane(e, j);
+    rk += (j < lane && v == e) ? 1 : 0;
+  }
+  __syncthreads();
+  if (a < na) {
+    for (int w = 0; w < wave; ++w) rk += whist[w][e];
+    rank[(long long)tok0 * K + a] = rk;
+  }
+}
+
+// ---------------------------------------------------------------------------
 // Loads, offsets, the grouped-GEMM tile table and the dispatch order, in one
 // launch without a grid-wide barrier.  A dispatch block of 1024 threads owns
-// kDispatchSub router blocks (256 tokens); it sums the per-router-block expert
-// counts itself (all of them for the loads, those before its first router
-// block for its prefix), so every block knows
+// 256 tokens, i.e. sub = 256 / tpb router blocks of tpb tokens; it sums the
+// per-router-block expert counts itself (all of them for the loads, those
+// before its first router block for its prefix), so every block knows
 //   slot(t, j) = offsets[e] + sum over earlier router blocks of their loads of e
 //                + rank(t, j) (earlier assignments to e in t's router block),
 // i.e. slots of an expert ascend in t*k + j, independent of scheduling.
@@ -263,7 +465,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 // (expert, first row) for every kTileM (kTileMFwd) rows of each expert, in
 // expert order.
 // ---------------------------------------------------------------------------
-constexpr int kDispatchSub = 16;
+constexpr int kDispatchTokens = 256;
 
 // Lane e (one wave, 64 lanes) lists the tm-row tiles of expert e, which has
 // cnt rows, after those of experts 0..e-1.
@@ -290,20 +492,21 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
                                                               TileTable tiles, TileTable tiles_fwd,
                                                               int32_t* __restrict__ perm, int32_t* __restrict__ pos,
                                                               float gamma, float* __restrict__ bias,
-                                                              float* __restrict__ stats) {
+                                                              float* __restrict__ stats, int tpb) {
   __shared__ int part_tot[16][64];
   __shared__ int part_pre[16][64];
-  __shared__ int sub_cnt[kDispatchSub][64];
-  __shared__ int base[kDispatchSub][64];
+  __shared__ int sub_cnt[16][64];
+  __shared__ int base[16][64];
   const int tid = threadIdx.x, e = tid & 63, part = tid >> 6;
-  const int first = blockIdx.x * kDispatchSub;   // first router block of this dispatch block
-  // This block's assignments (at most kDispatchSub * 16 tokens x 8 = 2048,
-  // two per thread): their experts and ranks are requested first, beside the
-  // loads below, so the scatter at the end waits for no further round trip.
-  const long long a0 = (long long)first * kRouteTokensPerBlock * k;
-  const int ntok = max(0, min(kDispatchSub * kRouteTokensPerBlock, T_ - first * kRouteTokensPerBlock));
-  const int na = ntok * k, per = kRouteTokensPerBlock * k;
-  static_assert(kDispatchSub * kRouteTokensPerBlock * 8 <= 2 * 1024, "two assignments per thread");
+  const int sub = kDispatchTokens / tpb;         // router blocks per dispatch block: 16 or 4
+  const int first = blockIdx.x * sub;            // first router block of this dispatch block
+  // This block's assignments (at most 256 tokens x 8 = 2048, two per
+  // thread): their experts and ranks are requested first, beside the loads
+  // below, so the scatter at the end waits for no further round trip.
+  const long long a0 = (long long)first * tpb * k;
+  const int ntok = max(0, min(kDispatchTokens, T_ - first * tpb));
+  const int na = ntok * k, per = tpb * k;
+  static_assert(kDispatchTokens * 8 <= 2 * 1024, "two assignments per thread");
   int my_e[2], my_r[2];
 #pragma unroll
   for (int i = 0; i < 2; ++i) {
@@ -331,7 +534,7 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
   }
   part_tot[part][e] = tot;
   part_pre[part][e] = pre;
-  sub_cnt[part][e] = (e < E && first + part < nblk) ? block_counts[(long long)(first + part) * E + e] : 0;
+  sub_cnt[part][e] = (e < E && part < sub && first + part < nblk) ? block_counts[(long long)(first + part) * E + e] : 0;
   __syncthreads();
 
   if (part == 0) {
@@ -348,7 +551,7 @@ __global__ __launch_bounds__(1024) void route_dispatch_kernel(const int32_t* __r
     }
     const int excl = incl - cnt;
     int run = excl + pr;
-    for (int sb = 0; sb < kDispatchSub; ++sb) {
+    for (int sb = 0; sb < sub; ++sb) {
       base[sb][e] = run;
       run += sub_cnt[sb][e];
     }
@@ -404,14 +607,21 @@ __global__ __launch_bounds__(64) void bias_update_stats_kernel(int E, long long 
 template <typename A, int K>
 void launch_topk_k(const void* x, const void* w_router, const float* bias, int T, int d, int E, int32_t* idx,
                    float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
+  constexpr int act = sizeof(A) == 2 ? 1 : 0;
+  const int tpb = route_tpb(T, act, d), nblk = route_blocks(T, tpb);
   if constexpr (sizeof(A) == 2) {
+    if (tpb == 64) {
+      hipLaunchKernelGGL((route_topk64_kernel<K, 512>), dim3(nblk), dim3(512), 0, s, (const A*)x, (const A*)w_router, bias,
+                         T, d, E, idx, gate, block_counts, rank);
+      return;
+    }
     if (d % kRouteChunk == 0) {
-      hipLaunchKernelGGL((route_topk_kernel<A, K, true>), dim3(route_blocks(T)), dim3(512), 0, s, (const A*)x,
+      hipLaunchKernelGGL((route_topk_kernel<A, K, true>), dim3(nblk), dim3(512), 0, s, (const A*)x,
                          (const A*)w_router, bias, T, d, E, idx, gate, block_counts, rank);
       return;
     }
   }
-  hipLaunchKernelGGL((route_topk_kernel<A, K, false>), dim3(route_blocks(T)), dim3(512), 0, s, (const A*)x,
+  hipLaunchKernelGGL((route_topk_kernel<A, K, false>), dim3(nblk), dim3(512), 0, s, (const A*)x,
                        (const A*)w_router, bias, T, d, E, idx, gate, block_counts, rank);
 }
 template <typename A>
@@ -432,17 +642,18 @@ void launch_topk_t(const void* x, const void* w_router, const float* bias, int T
 // k is 1..8 (checked on the host).
 void launch_route_topk(int act, const void* x, const void* w_router, const float* bias, int T, int d, int E,
                        int k, int32_t* idx, float* gate, int32_t* block_counts, int32_t* rank, hipStream_t s) {
-  if (route_blocks(T) == 0) return;
+  if (T == 0) return;
   if (act == 1) launch_topk_t<bf16_t>(x, w_router, bias, T, d, E, k, idx, gate, block_counts, rank, s);
   else launch_topk_t<float>(x, w_router, bias, T, d, E, k, idx, gate, block_counts, rank, s);
 }
 
-void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int nblk, int T,
+void launch_route_dispatch(const int32_t* block_counts, const int32_t* idx, const int32_t* rank, int tpb, int T,
                            int E, int k, int32_t* counts, int32_t* offsets, TileTable tiles, TileTable tiles_fwd,
                            int32_t* perm, int32_t* pos, float gamma, float* bias, float* stats, hipStream_t s) {
-  const int grid = nblk > 0 ? (nblk + kDispatchSub - 1) / kDispatchSub : 1;   // block 0 runs even for T = 0
+  const int nblk = route_blocks(T, tpb), sub = kDispatchTokens / tpb;
+  const int grid = nblk > 0 ? (nblk + sub - 1) / sub : 1;   // block 0 runs even for T = 0
   hipLaunchKernelGGL(route_dispatch_kernel, dim3(grid), dim3(1024), 0, s, block_counts, idx, rank, nblk, T, E, k,
-                     counts, offsets, tiles, tiles_fwd, perm, pos, gamma, bias, stats);
+                     counts, offsets, tiles, tiles_fwd, perm, pos, gamma, bias, stats, tpb);
 }
 
 void launch_bias_update(int E, long long total, const int32_t* counts, float gamma, float* bias, float* stats,

@@ -126,6 +126,28 @@ def test_route_only_matches_forward_routing():
         np.testing.assert_array_equal(v.cpu().numpy(), rn[k], err_msg=k)
 
 
+@pytest.mark.parametrize("T,k,E,seed", [(4097, 2, 64, 81), (8191, 1, 64, 82), (6001, 3, 17, 83),
+                                         (5003, 8, 64, 84)])
+def test_wide_router_blocks(T, k, E, seed):
+    """bf16 batches above 4096 tokens take the router's 64-token workgroups
+    (ragged last block, k up to 8 = one assignment per thread, E < 64):
+    routing bit-exact against the oracle, gates within 1e-6."""
+    import torch
+    from fine_grained_moe_amd import moe
+    inp = _case("layer_t4096", T=T, seed=seed, k=k, E=E)
+    x, w = H.to_gpu(inp)
+    dims = moe.make_dims(inp.T, inp.d, inp.E, inp.F, inp.Fs, inp.k, inp.act)
+    b = torch.from_numpy(inp.bias.astype(np.float32)).cuda()
+    r = moe.alloc_routing(dims)
+    ws = moe.alloc_workspace(dims)
+    moe.moe_route(dims, x, w["w_router"], b, r, ws)
+    torch.cuda.synchronize()
+    rn = {key: v.cpu().numpy() for key, v in r.items()}
+    ref = om.route(inp.x, inp.w_router, inp.bias, inp.k)
+    H.check_routing_exact(rn, ref, inp.E)
+    np.testing.assert_allclose(rn["gate"], ref.gate, rtol=0, atol=1e-6)
+
+
 def test_run_to_run_bitwise_equal():
     import torch
     from fine_grained_moe_amd import moe
