@@ -722,8 +722,9 @@ moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* n
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   // The serving path normalises h inside its first launch for one tile of
   // up to 16 tokens (measured: 18.5 -> 16.8 us per layer at T = 1); above
-  // that every stage-1 workgroup would redo its tile's norm (1040 of them at
-  // T = 64: 39.4 -> 42.9 us), and the norm is a launch of its own.
+  // that every stage-1 workgroup would redo the norm of its token tiles (with
+  // one tile per workgroup, 1040 of them at T = 64: 39.4 -> 42.9 us), and the
+  // norm is a launch of its own.
   if (d.w_routed == MOE_INT4_G128 && d.T <= 16)
     return forward_int4(d, h, w, bias, h_out, routing, 0, ws, ws_bytes, s, h, false, norm_weight, eps);
   void* x = at<char>(ws, L.xb);

@@ -12,11 +12,12 @@
 // Three launches for a batch of at most 64 tokens (a launch costs about
 // 1.3 us on the device even when empty, so the work is packed into as few
 // dependent steps as the data flow allows):
-//   stage 1  router (one workgroup per 16 tokens: logits on MFMA, top-1,
-//            gate) beside the shared expert's gate/up, which does not
-//            depend on the routing (in the MoE block every workgroup first
-//            normalises its 16 rows of h, and the router's first expert
-//            tile writes them for stage 2);
+//   stage 1  router (logits on MFMA, top-1, gate) beside the shared
+//            expert's gate/up, which does not depend on the routing; a
+//            workgroup per 16 weight rows, over every 16-token tile (in the
+//            MoE block, at most 16 tokens, every workgroup first normalises
+//            the rows of h, and the router's first expert tile writes them
+//            for stage 2);
 //   stage 2  one workgroup writes the routing outputs (loads, offsets,
 //            dispatch order, active experts) and takes the bias step of
 //            moe_forward_bias_step; the shared down in four
@@ -229,7 +230,9 @@ __device__ __forceinline__ void xcd_item(int i, int ntile, int& blk, int& tile) 
 //     and its s go to rkey/rscore [et][t]; the top-1 is the largest of the 4
 //     tile keys (stage 2).
 // LDS per wave: 8 weight blocks (8 KiB), then 16 x rows (8 KiB), whose space
-// takes the wave's partial tile [16][17] after the products.
+// takes the wave's partial tile [16][17] after the products.  Launched for
+// one token tile (at most 16 tokens, with the MoE block's norm); above that
+// decode_stage1_wide_kernel below takes the tiles of a weight block together.
 // ---------------------------------------------------------------------------
 constexpr int kS1Wave = 16384;
 
@@ -313,6 +316,128 @@ __global__ __launch_bounds__(256) void decode_stage1_kernel(DecodeArgs p, int nt
     if (c == 0 && tt * 16 + t < T) {
       p.rkey[et * 64 + tt * 16 + t] = key;
       p.rscore[et * 64 + tt * 16 + t] = ks;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// Stage 1 above 16 tokens (NT = 2 .. 4 token tiles; the MoE block's norm is
+// then a launch of its own, so gamma is not used here).  A workgroup owns one
+// weight block (the same 16 rows as above) and every token tile, so the
+// block is read once per launch instead of once per tile, and the grid is
+// one round of FS / 8 + 4 workgroups instead of NT rounds' worth: a CU takes
+// in 160 KiB at 64 tokens instead of 256 KiB (the bound here is what a CU's
+// vector memory path delivers, about 60 GB/s on this access pattern).  Wave
+// w copies its contraction quarter of the block into LDS and reads it into
+// registers (8 MFMA operands); its LDS space then holds two token tiles at a
+// time.  Every load is issued at the start (the weights, then each tile's
+// rows, row-contiguously into registers), so each wave has up to 40 KiB in
+// flight, and a tile is multiplied, reduced and finished while the later
+// tiles' rows are still arriving.  The four partial tiles meet in LDS in two
+// alternating buffers (one barrier per tile) and are added in wave order, as
+// above.
+// ---------------------------------------------------------------------------
+template <int D, int FS, int NT>
+__global__ __launch_bounds__(256) void decode_stage1_wide_kernel(DecodeArgs p) {
+  static_assert(D == 1024, "one contraction quarter is 512 bytes");
+  static_assert(NT >= 2 && NT <= 4, "17 to 64 tokens");
+  __shared__ __align__(16) char lds[4 * kS1Wave];
+  __shared__ float part[2][4][16 * 17];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int fr = lane & 15, g = lane >> 4;
+  char* wreg = lds + wave * kS1Wave;
+  const int blk = blockIdx.x, T = p.T;
+  const int n_sh = FS / 8;
+  const int r = lane >> 2;                            // the weight row this lane's direct loads fetch
+  const bool is_sh = blk < n_sh;
+  const char* wrow;
+  if (is_sh) {
+    const int f = blk * 8 + (r & 7);
+    wrow = reinterpret_cast<const char*>(p.w_sh_gate_up) + (long long)(r < 8 ? f : FS + f) * D * 2;
+  } else {
+    wrow = reinterpret_cast<const char*>(p.w_router) + (long long)min((blk - n_sh) * 16 + r, p.E - 1) * D * 2;
+  }
+  dma_w<8>(wrow + wave * (D / 2), wreg, lane);
+  __builtin_amdgcn_sched_barrier(0);                  // the weight loads are the oldest in flight
+  // a router item's bias of expert 16 et + (tid % 16), loaded unconditionally
+  // (a load under a branch is waited for where the branch ends)
+  const float bias_c = p.bias[is_sh ? 0 : min((blk - n_sh) * 16 + (tid & 15), p.E - 1)];
+  // this wave's quarter of every tile's rows: lane l of step i holds piece
+  // 64 i + l of the 16 rows (rows past T re-read the last token)
+  constexpr int PR = 32, NS = 8;
+  const char* xq = reinterpret_cast<const char*>(p.x) + wave * (D / 2);
+  u32x4_t v[NT][NS];
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int pc = i * 64 + lane, t = min(tt * 16 + pc / PR, T - 1), c = pc % PR;
+      v[tt][i] = ld16(xq + (long long)t * D * 2 + c * 16);
+    }
+    __builtin_amdgcn_sched_barrier(0);                // tile by tile, in order
+  }
+  // s_waitcnt vmcnt(8 NT + 1): the weight copies, issued first, have landed
+  constexpr int kAfterW = 8 * NT + 1;
+  __builtin_amdgcn_s_waitcnt((kAfterW & 0xF) | ((kAfterW >> 4) << 14) | (0x7 << 4) | (0xF << 8));
+  asm volatile("" ::: "memory");
+  u32x4_t wf[8];
+#pragma unroll
+  for (int b = 0; b < 8; ++b) wf[b] = wfrag(wreg + b * 1024, fr, g);
+
+#pragma unroll
+  for (int tt = 0; tt < NT; ++tt) {
+    // even tiles past the weights, odd tiles over them (their products read
+    // into wf before the first tile's barrier)
+    char* xb = wreg + ((tt & 1) ? 0 : 8192);
+    // every row is stored (rows past T hold the last token again and feed
+    // only outputs that are never written): no branch, so each store waits
+    // for its own load only
+#pragma unroll
+    for (int i = 0; i < NS; ++i) {
+      const int pc = i * 64 + lane, rr = pc / PR, c = pc % PR;
+      st16(xb + rr * 512 + ((c ^ xsw<512>(rr)) << 4), v[tt][i]);
+    }
+    __builtin_amdgcn_s_waitcnt(0xC07F);               // lgkmcnt(0): this wave's rows are in LDS
+    asm volatile("" ::: "memory");
+    f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int b = 0; b < 8; ++b) acc = Mma<bf16_t>::run1(xfrag<512>(xb, fr, 4 * b + g), wf[b], acc);
+    // acc[i]: token row 4g + i of the tile, weight row fr
+    float* pw = part[tt & 1][wave];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) pw[(4 * g + i) * 17 + fr] = acc[i];
+    __syncthreads();
+    const float* pt = part[tt & 1][0];
+    if (is_sh) {
+      const int t = tt * 16 + tid;
+      if (tid < 16 && t < T) {
+        float h[8];
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+          h[c] = siluf_(sum4(pt + tid * 17 + c, 16 * 17)) * sum4(pt + tid * 17 + 8 + c, 16 * 17);
+        st16(p.Hs + (long long)t * FS + blk * 8, pack8(h));
+      }
+    } else {
+      const int et = blk - n_sh;
+      const int t = tid >> 4, c = tid & 15, e = et * 16 + c;
+      const float b = e < p.E ? bias_c : 0.f;
+      const float sc = 1.0f / (1.0f + expf(-sum4(pt + t * 17 + c, 16 * 17)));
+      uint64_t key = e < p.E ? (((uint64_t)float_key(sc + b) << 32) | (uint32_t)(63 - e)) : 0ull;
+      float ks = sc;
+#pragma unroll
+      for (int off = 1; off < 16; off <<= 1) {
+        const uint32_t lo = __shfl_xor((uint32_t)key, off), hi = __shfl_xor((uint32_t)(key >> 32), off);
+        const float os = __shfl_xor(ks, off);
+        const uint64_t o = ((uint64_t)hi << 32) | lo;
+        if (o > key) {
+          key = o;
+          ks = os;
+        }
+      }
+      if (c == 0 && tt * 16 + t < T) {
+        p.rkey[et * 64 + tt * 16 + t] = key;
+        p.rscore[et * 64 + tt * 16 + t] = ks;
+      }
     }
   }
 }
@@ -683,7 +808,14 @@ void launch_decode(const DecodeArgs& a, hipStream_t s) {
     return;
   }
   const int max_active = a.T * a.k < a.E ? a.T * a.k : a.E;
-  hipLaunchKernelGGL((decode_stage1_kernel<D, FS>), dim3((FS / 8) * ntile + 4 * ntile), dim3(256), 0, s, a, ntile);
+  if (ntile == 1)
+    hipLaunchKernelGGL((decode_stage1_kernel<D, FS>), dim3(FS / 8 + 4), dim3(256), 0, s, a, 1);
+  else if (ntile == 2)
+    hipLaunchKernelGGL((decode_stage1_wide_kernel<D, FS, 2>), dim3(FS / 8 + 4), dim3(256), 0, s, a);
+  else if (ntile == 3)
+    hipLaunchKernelGGL((decode_stage1_wide_kernel<D, FS, 3>), dim3(FS / 8 + 4), dim3(256), 0, s, a);
+  else
+    hipLaunchKernelGGL((decode_stage1_wide_kernel<D, FS, 4>), dim3(FS / 8 + 4), dim3(256), 0, s, a);
   // stage 2 and 3 grids sized to one round of resident workgroups (see the kernels)
   if (ntile == 1) {
     hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS, 1, 1>), dim3(1 + 4 * (D / 16) + max_active * (FR / 16)),

@@ -189,9 +189,9 @@ struct DecodeArgs {
   float* part_sh;                    // [4, T, d] fp32 shared down partials (workspace)
   uint16_t* y;                       // [T, d] bf16
   const uint16_t* resid;             // [T, d] bf16 residual added to y, or null
-  // MoE block: x holds h, which stage 1 normalises (x = bf16(h / rms(h) *
-  // gamma)); the normalised rows go to xn for stage 2.  gamma null: x is used
-  // as it is.
+  // MoE block, at most 16 tokens: x holds h, which stage 1 normalises (x =
+  // bf16(h / rms(h) * gamma)); the normalised rows go to xn for stage 2.
+  // gamma null (required above 16 tokens): x is used as it is.
   const float* gamma;                // [d] float32, or null
   float eps;
   uint16_t* xn;                      // [T, d] bf16 (workspace)

@@ -56,7 +56,7 @@ def _run(weights, T, seed, bias=None):
     return y.float().cpu().numpy(), rn, y_ref, ref
 
 
-@pytest.mark.parametrize("T", [1, 8, 13, 17, 33, 64])
+@pytest.mark.parametrize("T", [1, 8, 13, 16, 17, 33, 48, 63, 64])
 def test_int4_top1_decode(weights, T):
     y, rn, y_ref, ref = _run(weights, T, seed=100 + T)
     H.check_routing_exact(rn, ref, 64)
