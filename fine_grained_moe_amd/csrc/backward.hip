@@ -157,10 +157,10 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
 // ---------------------------------------------------------------------------
 // Router and gate gradients, one wave per token: dg_j = <dy_t, o_j>; the
 // selected scores are recomputed from the logits x_t . W_r[e_j]; then the
-// formulas at the top of this file.  dl: [T, k] fp32.  Each lane takes 16
-// consecutive elements of every row (all of its loads in flight at once).
+// formulas at the top of this file.  dl: [T, k] fp32.  Each lane takes two
+// 8-element pieces of every row (all of its loads in flight at once).
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy, const T* __restrict__ ou,
                                                        const T* __restrict__ x, const T* __restrict__ wr,
                                                        const int32_t* __restrict__ idx, const float* __restrict__ gate,
@@ -169,33 +169,46 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
-  int e[8];
-  long long slot[8];
+  int e[KM];
+  long long slot[KM];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
+  for (int j = 0; j < KM; ++j)
     if (j < k) {
       e[j] = idx[(long long)t * k + j];
       slot[j] = pos[(long long)t * k + j];
       // the token of each dispatch-order row (K-major weight gradients)
       if (krow && lane == j) krow[slot[j]] = t;
     }
-  float dga[8], sb[8];
+  float dga[KM], sb[KM];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) dga[j] = sb[j] = 0.f;
-  for (int c = lane * 16; c < d; c += 1024) {
+  for (int j = 0; j < KM; ++j) dga[j] = sb[j] = 0.f;
+  // A lane's pieces of each row: elements c .. c + 7 and c + 512 .. c + 519,
+  // so that every wave load reads one contiguous KiB (bf16).  A piece past d
+  // re-reads the first one and counts zero (no load sits under a branch).
+  for (int c0 = 0; c0 < d; c0 += 1024) {
+    const int ca = c0 + lane * 8, cb = ca + 512;
+    const float ma = ca < d ? 1.f : 0.f, mb = cb < d ? 1.f : 0.f;
+    const int pa = ca < d ? ca : 0, pb = cb < d ? cb : pa;
     float vdy[16], vx[16];
-    load8<T>(dy + (long long)t * d + c, *reinterpret_cast<float(*)[8]>(vdy));
-    load8<T>(dy + (long long)t * d + c + 8, *reinterpret_cast<float(*)[8]>(vdy + 8));
-    load8<T>(x + (long long)t * d + c, *reinterpret_cast<float(*)[8]>(vx));
-    load8<T>(x + (long long)t * d + c + 8, *reinterpret_cast<float(*)[8]>(vx + 8));
+    load8<T>(dy + (long long)t * d + pa, *reinterpret_cast<float(*)[8]>(vdy));
+    load8<T>(dy + (long long)t * d + pb, *reinterpret_cast<float(*)[8]>(vdy + 8));
+    load8<T>(x + (long long)t * d + pa, *reinterpret_cast<float(*)[8]>(vx));
+    load8<T>(x + (long long)t * d + pb, *reinterpret_cast<float(*)[8]>(vx + 8));
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int i = 0; i < 8; ++i) {
+      vdy[i] *= ma;
+      vdy[8 + i] *= mb;
+      vx[i] *= ma;
+      vx[8 + i] *= mb;
+    }
+#pragma unroll
+    for (int j = 0; j < KM; ++j) {
       if (j >= k) break;
       float vo[16], vw[16];
-      load8<T>(ou + slot[j] * d + c, *reinterpret_cast<float(*)[8]>(vo));
-      load8<T>(ou + slot[j] * d + c + 8, *reinterpret_cast<float(*)[8]>(vo + 8));
-      load8<T>(wr + (long long)e[j] * d + c, *reinterpret_cast<float(*)[8]>(vw));
-      load8<T>(wr + (long long)e[j] * d + c + 8, *reinterpret_cast<float(*)[8]>(vw + 8));
+      load8<T>(ou + slot[j] * d + pa, *reinterpret_cast<float(*)[8]>(vo));
+      load8<T>(ou + slot[j] * d + pb, *reinterpret_cast<float(*)[8]>(vo + 8));
+      load8<T>(wr + (long long)e[j] * d + pa, *reinterpret_cast<float(*)[8]>(vw));
+      load8<T>(wr + (long long)e[j] * d + pb, *reinterpret_cast<float(*)[8]>(vw + 8));
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         dga[j] += vdy[i] * vo[i];
@@ -203,9 +216,9 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
       }
     }
   }
-  float dg[8], s[8];
+  float dg[KM], s[KM];
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
+  for (int j = 0; j < KM; ++j) {
     if (j >= k) break;
     float a = dga[j], b = sb[j];
 #pragma unroll
@@ -219,13 +232,13 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
   if (lane == 0) {
     float S = 0.f, G = 0.f;
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j >= k) break;
       S += s[j];
       G += gate[(long long)t * k + j] * dg[j];
     }
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
+    for (int j = 0; j < KM; ++j) {
       if (j >= k) break;
       dl[(long long)t * k + j] = (dg[j] - G) / S * s[j] * (1.f - s[j]);
     }
@@ -307,7 +320,7 @@ __global__ __launch_bounds__(256) void bwd_dwr_reduce_kernel(const float* __rest
 // dx[t] = dXs[t] + sum_j dXp[pos[t, j]] + sum_j dl[t, j] W_r[idx[t, j]], in that
 // order in fp32, rounded once.  Each thread takes 8 consecutive columns.
 // ---------------------------------------------------------------------------
-template <typename T>
+template <typename T, int KM>
 __global__ __launch_bounds__(256) void bwd_dx_kernel(const T* __restrict__ dxs, const T* __restrict__ dxp,
                                                      const T* __restrict__ wr, const float* __restrict__ dl,
                                                      const int32_t* __restrict__ idx, const int32_t* __restrict__ pos,
@@ -316,21 +329,35 @@ __global__ __launch_bounds__(256) void bwd_dx_kernel(const T* __restrict__ dxs, 
   const int per = d / 8;
   if (i8 >= (long long)T_ * per) return;
   const int t = (int)(i8 / per), c = (int)(i8 - (long long)t * per) * 8;
-  float v[8];
+  // the token's slots, experts and router-logit gradients first (k <= KM, all
+  // requested at once), then every row they select
+  int sl[KM], ex[KM];
+  float w[KM];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k) {
+      sl[j] = pos[(long long)t * k + j];
+      ex[j] = idx[(long long)t * k + j];
+      w[j] = dl[(long long)t * k + j];
+    }
+  float v[8], u[KM][8], r[KM][8];
   load8<T>(dxs + (long long)t * d + c, v);
-  for (int j = 0; j < k; ++j) {
-    float u[8];
-    load8<T>(dxp + (long long)pos[(long long)t * k + j] * d + c, u);
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] += u[q];
-  }
-  for (int j = 0; j < k; ++j) {
-    float u[8];
-    load8<T>(wr + (long long)idx[(long long)t * k + j] * d + c, u);
-    const float w = dl[(long long)t * k + j];
+  for (int j = 0; j < KM; ++j)
+    if (j < k) {
+      load8<T>(dxp + (long long)sl[j] * d + c, u[j]);
+      load8<T>(wr + (long long)ex[j] * d + c, r[j]);
+    }
 #pragma unroll
-    for (int q = 0; q < 8; ++q) v[q] += w * u[q];
-  }
+  for (int j = 0; j < KM; ++j)
+    if (j < k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += u[j][q];
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k)
+#pragma unroll
+      for (int q = 0; q < 8; ++q) v[q] += w[j] * r[j][q];
   store8<T>(dx + (long long)t * d + c, v);
 }
 
@@ -394,11 +421,15 @@ void launch_bwd_gate(int act, const void* dy, const void* ou, const void* x, con
                      hipStream_t s) {
   if (T == 0) return;
   const dim3 grid((T + 3) / 4);
-  if (act == 1)
-    hipLaunchKernelGGL(bwd_gate_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dy, (const bf16_t*)ou,
+  // register arrays sized for k <= 2 (the common case) or k <= 8
+  if (act == 1 && k <= 2)
+    hipLaunchKernelGGL((bwd_gate_kernel<bf16_t, 2>), grid, dim3(256), 0, s, (const bf16_t*)dy, (const bf16_t*)ou,
+                       (const bf16_t*)x, (const bf16_t*)wr, idx, gate, pos, T, d, k, dl, krow);
+  else if (act == 1)
+    hipLaunchKernelGGL((bwd_gate_kernel<bf16_t, 8>), grid, dim3(256), 0, s, (const bf16_t*)dy, (const bf16_t*)ou,
                        (const bf16_t*)x, (const bf16_t*)wr, idx, gate, pos, T, d, k, dl, krow);
   else
-    hipLaunchKernelGGL(bwd_gate_kernel<float>, grid, dim3(256), 0, s, (const float*)dy, (const float*)ou,
+    hipLaunchKernelGGL((bwd_gate_kernel<float, 8>), grid, dim3(256), 0, s, (const float*)dy, (const float*)ou,
                        (const float*)x, (const float*)wr, idx, gate, pos, T, d, k, dl, krow);
 }
 
@@ -422,11 +453,14 @@ void launch_bwd_dx(int act, const void* dxs, const void* dxp, const void* wr, co
   const long long n = (long long)T * (d / 8);
   if (n == 0) return;
   const dim3 grid((unsigned)((n + 255) / 256));
-  if (act == 1)
-    hipLaunchKernelGGL(bwd_dx_kernel<bf16_t>, grid, dim3(256), 0, s, (const bf16_t*)dxs, (const bf16_t*)dxp,
+  if (act == 1 && k <= 2)
+    hipLaunchKernelGGL((bwd_dx_kernel<bf16_t, 2>), grid, dim3(256), 0, s, (const bf16_t*)dxs, (const bf16_t*)dxp,
+                       (const bf16_t*)wr, dl, idx, pos, T, d, k, (bf16_t*)dx);
+  else if (act == 1)
+    hipLaunchKernelGGL((bwd_dx_kernel<bf16_t, 8>), grid, dim3(256), 0, s, (const bf16_t*)dxs, (const bf16_t*)dxp,
                        (const bf16_t*)wr, dl, idx, pos, T, d, k, (bf16_t*)dx);
   else
-    hipLaunchKernelGGL(bwd_dx_kernel<float>, grid, dim3(256), 0, s, (const float*)dxs, (const float*)dxp,
+    hipLaunchKernelGGL((bwd_dx_kernel<float, 8>), grid, dim3(256), 0, s, (const float*)dxs, (const float*)dxp,
                        (const float*)wr, dl, idx, pos, T, d, k, (float*)dx);
 }
 
