@@ -35,9 +35,11 @@ template <typename T> __device__ __forceinline__ T from_f32(float v);
 template <> __device__ __forceinline__ float from_f32<float>(float v) { return v; }
 template <> __device__ __forceinline__ bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
-// Activations of the expert FFNs (not the router): exp2 and the hardware
-// reciprocal (about 1 ulp each) instead of an IEEE divide, whose sequence is
-// several times longer; the results are rounded to bf16 or feed bf16 data.
+// Activations of the expert FFNs and the router's scores: exp2 and the
+// hardware reciprocal (about 1 ulp each) instead of an IEEE divide, whose
+// sequence is several times longer; the FFN results are rounded to bf16, and
+// a score error of a few ulp moves no selection that is not a tie to within
+// that much.
 // exp(-z) overflows to +inf for very negative z, and rcp(inf) = 0.
 __device__ __forceinline__ float sigmoidf_(float z) { return __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }
 __device__ __forceinline__ float siluf_(float z) { return z * __builtin_amdgcn_rcpf(1.0f + __expf(-z)); }

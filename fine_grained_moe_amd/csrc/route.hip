@@ -23,8 +23,10 @@ namespace fgmoe {
 //
 // Selection: 32 lanes per token, two experts per lane.  A lane keeps its k
 // best keys (score + bias, then the lower expert on an exact tie, packed as
-// one 64-bit key), then five butterfly merges combine the 32 lanes, which
-// gives the top-k of s + b in descending order with ties to the lower expert.  Gates are the selected scores divided by their sum.
+// one 64-bit key), then five merges combine the 32 lanes (four DPP row
+// rotations and one swizzle, route_select), which gives the top-k of s + b
+// in descending order with ties to the lower expert.  Gates are the selected
+// scores divided by their sum.
 // Per-block expert counts go to block_counts; rank[t*k + j] is the number of
 // earlier assignments (t', j') of the same block with the same expert, which
 // the dispatch kernel turns into the slot.
@@ -44,6 +46,71 @@ __device__ __forceinline__ void route_insert(uint64_t (&l)[K], uint64_t c) {
     const uint64_t t = l[i];
     l[i] = gt ? c : t;
     c = gt ? t : c;
+  }
+}
+
+// A lane's 64-bit key from another lane of the same 16-lane row, rotated by
+// N lanes (DPP row_ror:N, a VALU move), or from lane i ^ 16 of the same 32
+// (ds_swizzle in bit mode: and 0x1F, or 0, xor 0x10).
+template <int N>
+__device__ __forceinline__ uint64_t route_ror64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x120 + N, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x120 + N, 0xF, 0xF, false);
+  return ((uint64_t)hi << 32) | lo;
+}
+__device__ __forceinline__ uint64_t route_swap16(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)v, 0x401F);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), 0x401F);
+  return ((uint64_t)hi << 32) | lo;
+}
+// Merge step S of a token's 32 lanes: S = 0..3 take the list of the lane
+// 1, 2, 4, 8 places on in the same row (after step S a lane's list covers
+// 2^(S+1) consecutive lanes of its row, each step a disjoint union), S = 4
+// the other row's; the top K of a union is within the union of the top Ks.
+template <int K, int S>
+__device__ __forceinline__ void route_merge(uint64_t (&best)[K]) {
+  uint64_t other[K];
+#pragma unroll
+  for (int i = 0; i < K; ++i) other[i] = S < 4 ? route_ror64<(1 << (S & 3))>(best[i]) : route_swap16(best[i]);
+#pragma unroll
+  for (int i = 0; i < K; ++i) route_insert<K>(best, other[i]);
+}
+
+// One token's top K over its 32 lanes: lane u scores experts 2u and 2u + 1
+// (logits lrow), s = sigmoid, key (s + b, 63 - e); after the five merges
+// every lane of the 32 holds the token's top K keys in descending order.
+template <int K>
+__device__ __forceinline__ void route_select(const float* lrow, const float* bias_s, int E, int u,
+                                             uint64_t (&best)[K]) {
+#pragma unroll
+  for (int i = 0; i < K; ++i) best[i] = 0;
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int e = 2 * u + i;
+    const float sc = sigmoidf_(lrow[min(e, 63)]);
+    if (e < E) route_insert<K>(best, route_key(sc + bias_s[e], e));
+  }
+  route_merge<K, 0>(best);
+  route_merge<K, 1>(best);
+  route_merge<K, 2>(best);
+  route_merge<K, 3>(best);
+  route_merge<K, 4>(best);
+}
+
+// Loads and ranks of a block's assignments from emask[e], the block's tokens
+// that selected expert e (bit t; a token selects an expert at most once):
+// expert e's load in the block is popcount(emask[e]), and assignment a =
+// t * K + j of expert e has rank popcount(emask[e] below bit t), the number
+// of earlier assignments of the block to e.  Every thread of the block calls
+// this after a barrier that follows the last update of emask.
+__device__ __forceinline__ void route_loads_ranks(const int* sel, const unsigned long long* emask, int K, int E,
+                                                  int na, int32_t* __restrict__ block_counts,
+                                                  int32_t* __restrict__ rank) {
+  const int tid = threadIdx.x;
+  if (tid < E) block_counts[tid] = __popcll(emask[tid]);
+  for (int a = tid; a < na; a += blockDim.x) {
+    const int t = a / K, e = sel[a];
+    rank[a] = __popcll(emask[e] & ((1ull << t) - 1ull));
   }
 }
 
@@ -126,21 +193,22 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
                                                          int32_t* __restrict__ block_counts,
                                                          int32_t* __restrict__ rank) {
   // One LDS object: the staging ring, whose start later holds the partial
-  // logit tiles, then the reduced logits, selections, histogram and bias.
+  // logit tiles, then the reduced logits, per-expert token masks, selections
+  // and bias.
   constexpr int kRingB = STAGED ? 2 * kRouteStageB : 0;
   constexpr int kPartB = kRouteWaves * 16 * 65 * 4;
   constexpr int kHeadB = kRingB > kPartB ? kRingB : kPartB;
-  __shared__ __attribute__((aligned(16))) char lds[kHeadB + 16 * 65 * 4 + 16 * K * 4 + 64 * 4 + 64 * 4];
+  __shared__ __attribute__((aligned(16))) char lds[kHeadB + 16 * 65 * 4 + 64 * 8 + 16 * K * 4 + 64 * 4];
   float (*part)[16][65] = reinterpret_cast<float (*)[16][65]>(lds);
   float (*lgs)[65] = reinterpret_cast<float (*)[65]>(lds + kHeadB);
-  int* sel = reinterpret_cast<int*>(lds + kHeadB + 16 * 65 * 4);
-  int* hist = sel + 16 * K;
-  float* bias_s = reinterpret_cast<float*>(hist + 64);
+  unsigned long long* emask = reinterpret_cast<unsigned long long*>(lds + kHeadB + 16 * 65 * 4);
+  int* sel = reinterpret_cast<int*>(emask + 64);
+  float* bias_s = reinterpret_cast<float*>(sel + 16 * K);
   constexpr int k = K;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   if (tid < 64) {
-    hist[tid] = 0;
+    emask[tid] = 0;
     bias_s[tid] = tid < E ? bias[tid] : 0.f;
   }
 
@@ -197,31 +265,12 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
   }
   __syncthreads();
 
-  // ---- selection: wave w takes tokens 2w and 2w+1; lane (t = lane / 32,
-  // u = lane % 32) holds experts 2u and 2u+1 of its token, and five butterfly
-  // merges over the token's 32 lanes leave the token's top-k in every one.
+  // ---- selection: wave w takes tokens 2w and 2w+1 (lanes 32 t .. 32 t + 31
+  // for token 2w + t)
   {
     const int tt = 2 * wave + (lane >> 5), u = lane & 31;
     uint64_t best[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i) best[i] = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = 2 * u + i;
-      const float sc = 1.0f / (1.0f + expf(-lgs[tt][min(e, 63)]));
-      if (e < E) route_insert<K>(best, route_key(sc + bias_s[e], e));
-    }
-#pragma unroll
-    for (int off = 1; off <= 16; off <<= 1) {
-      uint64_t other[K];
-#pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const uint32_t lo = __shfl_xor((uint32_t)best[i], off), hi = __shfl_xor((uint32_t)(best[i] >> 32), off);
-        other[i] = ((uint64_t)hi << 32) | lo;
-      }
-#pragma unroll
-      for (int i = 0; i < K; ++i) route_insert<K>(best, other[i]);
-    }
+    route_select<K>(lgs[tt], bias_s, E, u, best);
     const int tok = tok0 + tt;
     if (u == 0 && tok < T_) {
       float ssel[K];
@@ -229,25 +278,19 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         const int e = 63 - (int)(uint32_t)best[j];
-        ssel[j] = 1.0f / (1.0f + expf(-lgs[tt][e]));
+        ssel[j] = sigmoidf_(lgs[tt][e]);
         ssum += ssel[j];
         sel[tt * K + j] = e;
         idx[(long long)tok * K + j] = e;
-        atomicAdd(&hist[e], 1);
+        atomicOr(&emask[e], 1ull << tt);
       }
 #pragma unroll
       for (int j = 0; j < K; ++j) gate[(long long)tok * K + j] = ssel[j] / ssum;
     }
   }
   __syncthreads();
-  if (tid < E) block_counts[(long long)blockIdx.x * E + tid] = hist[tid];
-  const int na = min(16, T_ - tok0) * k;
-  if (tid < na) {
-    const int e = sel[tid];
-    int rk = 0;
-    for (int b = 0; b < tid; ++b) rk += (sel[b] == e) ? 1 : 0;
-    rank[(long long)tok0 * k + tid] = rk;
-  }
+  route_loads_ranks(sel, emask, K, E, min(16, T_ - tok0) * k, block_counts + (long long)blockIdx.x * E,
+                    rank + (long long)tok0 * k);
 }
 
 // ---------------------------------------------------------------------------
@@ -259,8 +302,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 // 2 ((w >> 1) & 1) .. + 1 over k steps 4 (w >> 2) .. + 3 of every chunk, and
 // the two k halves meet in LDS (first half + second half).  Selection,
 // gates, per-block loads and ranks are the 16-token kernel's, over 64
-// tokens; ranks come from a per-wave count of earlier lanes with the same
-// expert plus the counts of the earlier waves.
+// tokens (64-bit token masks per expert).
 // ---------------------------------------------------------------------------
 // s_waitcnt vmcnt(N), the other counters left free (gfx9 encoding: vmcnt
 // bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
@@ -291,21 +333,18 @@ __global__ __launch_bounds__(512) void route_topk64_kernel(const bf16_t* __restr
   constexpr int kNI = 8 * RB / 1024;                     // wave instructions per matrix and chunk
   constexpr int kKS = RB / 128;                          // k steps of 32 per chunk and k half
   static_assert(2 * 64 * 65 * 4 <= kRingB, "the two partial halves fit in the ring");
-  __shared__ __attribute__((aligned(16))) char lds[kRingB + 64 * 65 * 4 + 64 * K * 4 + 64 * 4 + 64 * 4 +
-                                                    kRouteWaves * 64 * 4];
+  __shared__ __attribute__((aligned(16))) char lds[kRingB + 64 * 65 * 4 + 64 * 8 + 64 * K * 4 + 64 * 4];
   float (*part)[64][65] = reinterpret_cast<float (*)[64][65]>(lds);
   float (*lgs)[65] = reinterpret_cast<float (*)[65]>(lds + kRingB);
-  int* sel = reinterpret_cast<int*>(lds + kRingB + 64 * 65 * 4);
-  int* hist = sel + 64 * K;
-  float* bias_s = reinterpret_cast<float*>(hist + 64);
-  int (*whist)[64] = reinterpret_cast<int (*)[64]>(bias_s + 64);
+  unsigned long long* emask = reinterpret_cast<unsigned long long*>(lds + kRingB + 64 * 65 * 4);
+  int* sel = reinterpret_cast<int*>(emask + 64);
+  float* bias_s = reinterpret_cast<float*>(sel + 64 * K);
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int r = lane & 15, g = lane >> 4;
   if (tid < 64) {
-    hist[tid] = 0;
+    emask[tid] = 0;
     bias_s[tid] = tid < E ? bias[tid] : 0.f;
   }
-  whist[wave][lane] = 0;
   const int tok0 = blockIdx.x * 64;
 
   // ---- partial logits.  Wave w copies x rows 8w .. 8w+7 and router rows
@@ -391,30 +430,12 @@ __global__ __launch_bounds__(512) void route_topk64_kernel(const bf16_t* __restr
   __syncthreads();
 
   // ---- selection: in round i, wave w takes tokens 16 i + 2w and 16 i + 2w + 1
-  // (32 lanes each, two experts per lane, five butterfly merges)
+  // (32 lanes each, two experts per lane, route_select)
 #pragma unroll 1
   for (int it = 0; it < 4; ++it) {
     const int tt = 16 * it + 2 * wave + (lane >> 5), u = lane & 31;
     uint64_t best[K];
-#pragma unroll
-    for (int i = 0; i < K; ++i) best[i] = 0;
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int e = 2 * u + i;
-      const float sc = 1.0f / (1.0f + expf(-lgs[tt][min(e, 63)]));
-      if (e < E) route_insert<K>(best, route_key(sc + bias_s[e], e));
-    }
-#pragma unroll
-    for (int off = 1; off <= 16; off <<= 1) {
-      uint64_t other[K];
-#pragma unroll
-      for (int i = 0; i < K; ++i) {
-        const uint32_t lo = __shfl_xor((uint32_t)best[i], off), hi = __shfl_xor((uint32_t)(best[i] >> 32), off);
-        other[i] = ((uint64_t)hi << 32) | lo;
-      }
-#pragma unroll
-      for (int i = 0; i < K; ++i) route_insert<K>(best, other[i]);
-    }
+    route_select<K>(lgs[tt], bias_s, E, u, best);
     const int tok = tok0 + tt;
     if (u == 0 && tok < T_) {
       float ssel[K];
@@ -422,34 +443,19 @@ __global__ __launch_bounds__(512) void route_topk64_kernel(const bf16_t* __restr
 #pragma unroll
       for (int j = 0; j < K; ++j) {
         const int e = 63 - (int)(uint32_t)best[j];
-        ssel[j] = 1.0f / (1.0f + expf(-lgs[tt][e]));
+        ssel[j] = sigmoidf_(lgs[tt][e]);
         ssum += ssel[j];
         sel[tt * K + j] = e;
         idx[(long long)tok * K + j] = e;
-        atomicAdd(&hist[e], 1);
+        atomicOr(&emask[e], 1ull << tt);
       }
 #pragma unroll
       for (int j = 0; j < K; ++j) gate[(long long)tok * K + j] = ssel[j] / ssum;
     }
   }
   __syncthreads();
-  if (tid < E) block_counts[(long long)blockIdx.x * E + tid] = hist[tid];
-
-  // ---- ranks: thread a owns assignment a (at most 64 K <= 512 of them)
-  const int na = min(64, T_ - tok0) * K;
-  const int a = tid;
-  const int e = a < na ? sel[a] : -1;
-  if (a < na) atomicAdd(&whist[wave][e], 1);
-  int rk = 0;
-  for (int j = 0; j < 64; ++j) {
-    const int v = __builtin_amdgcn_readlane(e, j);
-    rk += (j < lane && v == e) ? 1 : 0;
-  }
-  __syncthreads();
-  if (a < na) {
-    for (int w = 0; w < wave; ++w) rk += whist[w][e];
-    rank[(long long)tok0 * K + a] = rk;
-  }
+  route_loads_ranks(sel, emask, K, E, min(64, T_ - tok0) * K, block_counts + (long long)blockIdx.x * E,
+                    rank + (long long)tok0 * K);
 }
 
 // ---------------------------------------------------------------------------
