@@ -13,13 +13,15 @@ namespace fgmoe {
 // ---------------------------------------------------------------------------
 // Router logits + sigmoid + bias + top-k + gates + per-block loads and ranks.
 //
-// A workgroup of 8 waves owns 16 tokens.  The contraction over d is cut into
-// 128-byte chunks dealt to the waves round-robin; for each of its chunks a
-// wave multiplies the 16 token rows by all 64 router rows (four 16x16 MFMA
-// tiles), so every byte of x and of the 128 KiB router matrix is loaded once
-// per workgroup, and all of a wave's loads are requested before its first
-// product (the kernel is bound by load latency).  The 8 partial tiles meet in
-// LDS and are added in a fixed order.
+// A workgroup of 8 waves owns 16 tokens; every byte of x and of the 128 KiB
+// router matrix is loaded once per workgroup.  bf16 (route_logits_staged):
+// the operands are staged through LDS in 256-element chunks and wave w takes
+// expert tile w % 4 over half of each chunk's k steps (two partial tiles per
+// logit).  Otherwise the contraction is cut into 128-byte chunks dealt to the
+// waves round-robin; for each of its chunks a wave multiplies the 16 token
+// rows by all 64 router rows (four 16x16 MFMA tiles), with all of a wave's
+// loads requested before its first product (eight partial tiles per logit).
+// The partial tiles meet in LDS and are added in a fixed order.
 //
 // Selection: 32 lanes per token, two experts per lane.  A lane keeps its k
 // best keys (score + bias, then the lower expert on an exact tie, packed as
@@ -124,7 +126,8 @@ typedef __attribute__((address_space(3))) void* route_lds_ptr_t;
 // measured on gfx950 that made the address unit the bound of the router at
 // about 5 us per block.)  The 16-byte pieces of row r are XOR-swizzled by
 // 2 (r mod 16), so the 16-row operand reads hit distinct LDS banks.  Wave w
-// multiplies k step w of every chunk (16 tokens x 64 experts x 32).
+// multiplies the 16 tokens by expert tile w % 4 over k steps 4 (w / 4) ..
+// + 3 of every chunk, so each logit has two partial sums (the k halves).
 constexpr int kRouteChunk = 256;                        // elements per row chunk
 constexpr int kRouteRowB = kRouteChunk * 2;             // 512 bytes
 constexpr int kRouteXB = 16 * kRouteRowB;               // 8 KiB of x per chunk
@@ -132,7 +135,7 @@ constexpr int kRouteStageB = kRouteXB + 64 * kRouteRowB;   // + 32 KiB of router
 __device__ __forceinline__ int route_swz(int row, int piece) { return piece ^ ((row & 15) << 1); }
 
 __device__ __forceinline__ void route_logits_staged(const bf16_t* __restrict__ x, const bf16_t* __restrict__ wr,
-                                                    int T_, int d, int E, int tok0, char* ring, f32x4_t (&acc)[4]) {
+                                                    int T_, int d, int E, int tok0, char* ring, f32x4_t& acc) {
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   // wave w copies x rows 2w, 2w+1 and router rows 8w .. 8w+7 of each chunk;
   // one instruction moves two 512-byte rows (lane i: row i / 32, piece i % 32)
@@ -168,13 +171,13 @@ __device__ __forceinline__ void route_logits_staged(const bf16_t* __restrict__ x
     __builtin_amdgcn_s_barrier();
     asm volatile("" ::: "memory");
     const char* st = ring + (c & 1) * kRouteStageB;
-    const int piece = 4 * wave + g;                    // k step `wave`, lane group g
-    const u32x4_t a = ld16(st + r * kRouteRowB + route_swz(r, piece) * 16);
+    const int er = (wave & 3) * 16 + r;                // this wave's expert tile
 #pragma unroll
-    for (int et = 0; et < 4; ++et) {
-      const int er = et * 16 + r;
+    for (int s4 = 0; s4 < 4; ++s4) {
+      const int piece = 4 * (4 * (wave >> 2) + s4) + g;   // k step 4 (w / 4) + s4, lane group g
+      const u32x4_t a = ld16(st + r * kRouteRowB + route_swz(r, piece) * 16);
       const u32x4_t b = ld16(st + kRouteXB + er * kRouteRowB + route_swz(er, piece) * 16);
-      acc[et] = Mma<bf16_t>::run1(a, b, acc[et]);
+      acc = Mma<bf16_t>::run1(a, b, acc);
     }
     asm volatile("" ::: "memory");
     __builtin_amdgcn_s_barrier();                      // every wave is done with buffer c % 2
@@ -218,7 +221,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 #pragma unroll
   for (int et = 0; et < 4; ++et) acc[et] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   if constexpr (STAGED) {
-    route_logits_staged(x, wr, T_, d, E, tok0, lds, acc);
+    route_logits_staged(x, wr, T_, d, E, tok0, lds, acc[0]);
   } else {
   const int t = min(tok0 + r, T_ - 1);          // rows past T re-read the last token; never used
   const char* xrow = reinterpret_cast<const char*>(x + (long long)t * d) + g * 32;
@@ -251,16 +254,24 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
       for (int et = 0; et < 4; ++et) acc[et] = Mma<T>::run(a[h], b[h][et], acc[et]);
   }
   }
+  // partial tiles: staged, part[k half][token][expert]; otherwise
+  // part[wave][token][expert] (wave w: k chunks w, w + 8, ...)
+  if constexpr (STAGED) {
 #pragma unroll
-  for (int et = 0; et < 4; ++et)
+    for (int i = 0; i < 4; ++i) part[wave >> 2][4 * g + i][(wave & 3) * 16 + r] = acc[0][i];
+  } else {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) part[wave][4 * g + i][et * 16 + r] = acc[et][i];
+    for (int et = 0; et < 4; ++et)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) part[wave][4 * g + i][et * 16 + r] = acc[et][i];
+  }
   __syncthreads();
-  for (int q = tid; q < 16 * 64; q += 512) {     // fixed-order sum of the 8 partial tiles
+  constexpr int kParts = STAGED ? 2 : kRouteWaves;
+  for (int q = tid; q < 16 * 64; q += 512) {     // fixed-order sum of the partial tiles
     const int tt = q >> 6, e = q & 63;
     float l = 0.f;
 #pragma unroll
-    for (int w = 0; w < kRouteWaves; ++w) l += part[w][tt][e];
+    for (int w = 0; w < kParts; ++w) l += part[w][tt][e];
     lgs[tt][e] = l;
   }
   __syncthreads();
