@@ -78,11 +78,14 @@ moe_status check_training(const moe_dims& d) {
 // workspace first.
 bool int4_prefill_fused(const moe_dims& d) { return d.d / 128 <= kInt4MaxGroups && d.F / 128 <= kInt4MaxGroups; }
 
-// Contraction slices of the shared down GEMM (bf16 forward): 256 x 256
-// tiles over the whole 2048-long contraction would be 64 tiles holding a
-// quarter of the chip for the whole launch.  Two halves measured best on
-// the 4096-token layer (four: more combine traffic, no shorter launch).
-int shared_down_slices(const moe_dims& d) { return d.act == MOE_BF16 ? 2 : 1; }
+// Contraction slices of the shared down GEMM (bf16 forward): at 4096 tokens
+// 256 x 256 tiles over the whole 2048-long contraction would be 64 tiles
+// holding a quarter of the chip for the whole launch.  Two halves measured
+// best there (four: more combine traffic, no shorter launch).  From 16384
+// tokens there are tiles enough for the whole contraction, and one slice
+// writes S once and the combine reads it once (skewed routing at 16384
+// tokens: 436 -> 424 us per step; training at 32768: 2.69 -> 2.65 ms).
+int shared_down_slices(const moe_dims& d) { return d.act == MOE_BF16 && d.T < 16384 ? 2 : 1; }
 
 Layout make_layout(const moe_dims& d, int training) {
   Layout L{};
