@@ -28,19 +28,18 @@ namespace {
 // kofs = exclusive scan; pcol[c] = slot held by padded column c, or -1.
 // Also the tables of the shared expert's weight gradients, whose contraction
 // over Tp tokens is split into S slices of `step` columns (a multiple of 64):
-// ksh[i] = i * step, ksh[S + i] = its length.  One workgroup of 1024 threads.
+// ksh[i] = i * step, ksh[S + i] = its length.  Workgroup e (of E, 256
+// threads) writes expert e's padded range of pcol; workgroup 0 also the
+// tables and the tail of pcol past the last range.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(1024) void bwd_prep_kernel(const int32_t* __restrict__ counts,
-                                                        const int32_t* __restrict__ offsets, int E, int Pmax, int Tp,
-                                                        int S, int step, int32_t* __restrict__ kofs,
-                                                        int32_t* __restrict__ klen, int32_t* __restrict__ ksh,
-                                                        int32_t* __restrict__ pcol, int32_t* __restrict__ krow_pad,
-                                                        int32_t* __restrict__ zrow) {
+__global__ __launch_bounds__(256) void bwd_prep_kernel(const int32_t* __restrict__ counts,
+                                                       const int32_t* __restrict__ offsets, int E, int Pmax, int Tp,
+                                                       int S, int step, int32_t* __restrict__ kofs,
+                                                       int32_t* __restrict__ klen, int32_t* __restrict__ ksh,
+                                                       int32_t* __restrict__ pcol, int32_t* __restrict__ krow_pad,
+                                                       int32_t* __restrict__ zrow) {
   __shared__ int s_kofs[64], s_klen[64];
-  const int tid = threadIdx.x;
-  // K-major weight gradients: the token map's readable tail and the zero row
-  if (krow_pad && tid < 32) krow_pad[tid] = 0;
-  if (zrow && tid < 128) zrow[tid] = 0;
+  const int tid = threadIdx.x, e = blockIdx.x;
   if (tid < 64) {
     const int c = tid < E ? counts[tid] : 0;
     const int kl = (c + kPadK - 1) / kPadK * kPadK;
@@ -51,21 +50,28 @@ __global__ __launch_bounds__(1024) void bwd_prep_kernel(const int32_t* __restric
     }
     s_kofs[tid] = incl - kl;
     s_klen[tid] = kl;
-    if (tid < E) {
+    if (e == 0 && tid < E) {
       kofs[tid] = incl - kl;
       klen[tid] = kl;
     }
   }
-  if (tid < S) {
-    ksh[tid] = tid * step;
-    ksh[S + tid] = max(0, min(step, Tp - tid * step));
+  if (e == 0) {
+    // K-major weight gradients: the token map's readable tail and the zero row
+    if (krow_pad && tid < 32) krow_pad[tid] = 0;
+    if (zrow && tid < 128) zrow[tid] = 0;
+    if (tid < S) {
+      ksh[tid] = tid * step;
+      ksh[S + tid] = max(0, min(step, Tp - tid * step));
+    }
   }
   __syncthreads();
-  for (int c = tid; c < Pmax; c += blockDim.x) pcol[c] = -1;
-  __syncthreads();
-  for (int e = 0; e < E; ++e) {
-    const int c0 = s_kofs[e], n = counts[e], o = offsets[e];
-    for (int i = tid; i < n; i += blockDim.x) pcol[c0 + i] = o + i;
+  if (e < E) {
+    const int c0 = s_kofs[e], n = counts[e], o = offsets[e], kl = s_klen[e];
+    for (int i = tid; i < kl; i += blockDim.x) pcol[c0 + i] = i < n ? o + i : -1;
+  }
+  if (e == 0) {
+    const int end = E > 0 ? s_kofs[E - 1] + s_klen[E - 1] : 0;
+    for (int c = end + tid; c < Pmax; c += blockDim.x) pcol[c] = -1;
   }
 }
 
@@ -154,6 +160,22 @@ __global__ __launch_bounds__(256) void transpose_kernel(TransposeArgs a) {
   }
 }
 
+// Sum of v over the wave, the same in every lane: DPP rotations by 1, 2, 4
+// and 8 lanes within each 16-lane row (after them every lane holds its row's
+// sum: each step adds a disjoint neighbouring range), then the four row sums
+// (lanes 0, 16, 32, 48) added in row order.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x121, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x122, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x124, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x128, 0xF, 0xF, false));
+  const float r0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float r1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float r2 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float r3 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return ((r0 + r1) + r2) + r3;
+}
+
 // ---------------------------------------------------------------------------
 // Router and gate gradients, one wave per token: dg_j = <dy_t, o_j>; the
 // selected scores are recomputed from the logits x_t . W_r[e_j]; then the
@@ -169,50 +191,102 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
   const int lane = threadIdx.x & 63;
   const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
   if (t >= T_) return;
-  int e[KM];
-  long long slot[KM];
-#pragma unroll
-  for (int j = 0; j < KM; ++j)
-    if (j < k) {
-      e[j] = idx[(long long)t * k + j];
-      slot[j] = pos[(long long)t * k + j];
-      // the token of each dispatch-order row (K-major weight gradients)
-      if (krow && lane == j) krow[slot[j]] = t;
-    }
+  // A lane's pieces of each row: elements c .. c + 7 and c + 512 .. c + 519,
+  // so that every wave load reads one contiguous KiB (bf16).  A piece past d
+  // re-reads the first one and counts zero.  Every load is unconditional
+  // (entry j past k re-reads entry k - 1), so none sits under a branch and
+  // waits at its end; the dispatch-order token map is written at the end.
+  // experts and slots are non-negative: zero-extended into the 64-bit row
+  // offsets, which (unlike a sign extension) takes no instruction on the
+  // loaded value, so nothing waits for the loads before the rows are requested
+  uint32_t e[KM], slot[KM];
+  float gt[KM];
   float dga[KM], sb[KM];
 #pragma unroll
   for (int j = 0; j < KM; ++j) dga[j] = sb[j] = 0.f;
-  // A lane's pieces of each row: elements c .. c + 7 and c + 512 .. c + 519,
-  // so that every wave load reads one contiguous KiB (bf16).  A piece past d
-  // re-reads the first one and counts zero (no load sits under a branch).
-  for (int c0 = 0; c0 < d; c0 += 1024) {
-    const int ca = c0 + lane * 8, cb = ca + 512;
-    const float ma = ca < d ? 1.f : 0.f, mb = cb < d ? 1.f : 0.f;
-    const int pa = ca < d ? ca : 0, pb = cb < d ? cb : pa;
-    float vdy[16], vx[16];
-    load8<T>(dy + (long long)t * d + pa, *reinterpret_cast<float(*)[8]>(vdy));
-    load8<T>(dy + (long long)t * d + pb, *reinterpret_cast<float(*)[8]>(vdy + 8));
-    load8<T>(x + (long long)t * d + pa, *reinterpret_cast<float(*)[8]>(vx));
-    load8<T>(x + (long long)t * d + pb, *reinterpret_cast<float(*)[8]>(vx + 8));
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      vdy[i] *= ma;
-      vdy[8 + i] *= mb;
-      vx[i] *= ma;
-      vx[8 + i] *= mb;
-    }
+  auto load_meta = [&]() {
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
-      if (j >= k) break;
-      float vo[16], vw[16];
-      load8<T>(ou + slot[j] * d + pa, *reinterpret_cast<float(*)[8]>(vo));
-      load8<T>(ou + slot[j] * d + pb, *reinterpret_cast<float(*)[8]>(vo + 8));
-      load8<T>(wr + (long long)e[j] * d + pa, *reinterpret_cast<float(*)[8]>(vw));
-      load8<T>(wr + (long long)e[j] * d + pb, *reinterpret_cast<float(*)[8]>(vw + 8));
+      const long long q = (long long)t * k + min(j, k - 1);
+      e[j] = (uint32_t)idx[q];
+      slot[j] = (uint32_t)pos[q];
+      gt[j] = gate[q];
+    }
+  };
+  if constexpr (sizeof(T) == 2) {
+    // bf16: the products are taken on the packed pairs (v_dot2c_f32_bf16: two
+    // exact bf16 products added into the fp32 sum), no unpacking.  The
+    // token's experts and slots are requested first, its own rows behind them
+    // (the vector memory counter completes in order, so waiting for the slots
+    // leaves the rows in flight), then the expert rows.
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+    auto dot = [](uint32_t a, uint32_t b, float c) {
+      return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c,
+                                             false);
+    };
+    const u32x4_t zero = {0u, 0u, 0u, 0u};
+    auto chunk = [&](int c0, bool meta_first) {
+      const int ca = c0 + lane * 8, cb = ca + 512;
+      const bool va = ca < d, vb = cb < d;
+      const int pa = va ? ca : 0, pb = vb ? cb : pa;
+      if (meta_first) load_meta();
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t ydy0 = ld16(dy + (long long)t * d + pa), ydy1 = ld16(dy + (long long)t * d + pb);
+      const u32x4_t yx0 = ld16(x + (long long)t * d + pa), yx1 = ld16(x + (long long)t * d + pb);
+      __builtin_amdgcn_sched_barrier(0);
+      u32x4_t yo[KM][2], yw[KM][2];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        dga[j] += vdy[i] * vo[i];
-        sb[j] += vx[i] * vw[i];
+      for (int j = 0; j < KM; ++j) {
+        yo[j][0] = ld16(ou + (unsigned long long)slot[j] * d + pa);
+        yo[j][1] = ld16(ou + (unsigned long long)slot[j] * d + pb);
+        yw[j][0] = ld16(wr + (unsigned long long)e[j] * d + pa);
+        yw[j][1] = ld16(wr + (unsigned long long)e[j] * d + pb);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      const u32x4_t ydy[2] = {va ? ydy0 : zero, vb ? ydy1 : zero}, yx[2] = {va ? yx0 : zero, vb ? yx1 : zero};
+#pragma unroll
+      for (int j = 0; j < KM; ++j)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            dga[j] = dot(ydy[h][q], yo[j][h][q], dga[j]);
+            sb[j] = dot(yx[h][q], yw[j][h][q], sb[j]);
+          }
+    };
+    chunk(0, true);
+    for (int c0 = 1024; c0 < d; c0 += 1024) chunk(c0, false);
+  } else {
+    load_meta();
+    for (int c0 = 0; c0 < d; c0 += 1024) {
+      const int ca = c0 + lane * 8, cb = ca + 512;
+      const float ma = ca < d ? 1.f : 0.f, mb = cb < d ? 1.f : 0.f;
+      const int pa = ca < d ? ca : 0, pb = cb < d ? cb : pa;
+      float vdy[16], vx[16];
+      load8<T>(dy + (long long)t * d + pa, *reinterpret_cast<float(*)[8]>(vdy));
+      load8<T>(dy + (long long)t * d + pb, *reinterpret_cast<float(*)[8]>(vdy + 8));
+      load8<T>(x + (long long)t * d + pa, *reinterpret_cast<float(*)[8]>(vx));
+      load8<T>(x + (long long)t * d + pb, *reinterpret_cast<float(*)[8]>(vx + 8));
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        vdy[i] *= ma;
+        vdy[8 + i] *= mb;
+        vx[i] *= ma;
+        vx[8 + i] *= mb;
+      }
+#pragma unroll
+      for (int j = 0; j < KM; ++j) {
+        if (j >= k) break;
+        float vo[16], vw[16];
+        load8<T>(ou + (unsigned long long)slot[j] * d + pa, *reinterpret_cast<float(*)[8]>(vo));
+        load8<T>(ou + (unsigned long long)slot[j] * d + pb, *reinterpret_cast<float(*)[8]>(vo + 8));
+        load8<T>(wr + (unsigned long long)e[j] * d + pa, *reinterpret_cast<float(*)[8]>(vw));
+        load8<T>(wr + (unsigned long long)e[j] * d + pb, *reinterpret_cast<float(*)[8]>(vw + 8));
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          dga[j] += vdy[i] * vo[i];
+          sb[j] += vx[i] * vw[i];
+        }
       }
     }
   }
@@ -220,22 +294,20 @@ __global__ __launch_bounds__(256) void bwd_gate_kernel(const T* __restrict__ dy,
 #pragma unroll
   for (int j = 0; j < KM; ++j) {
     if (j >= k) break;
-    float a = dga[j], b = sb[j];
-#pragma unroll
-    for (int o = 32; o >= 1; o >>= 1) {
-      a += __shfl_xor(a, o);
-      b += __shfl_xor(b, o);
-    }
-    dg[j] = a;
-    s[j] = 1.0f / (1.0f + expf(-b));
+    dg[j] = wave_sum(dga[j]);
+    s[j] = 1.0f / (1.0f + expf(-wave_sum(sb[j])));
   }
+  // the token of each dispatch-order row (K-major weight gradients)
+#pragma unroll
+  for (int j = 0; j < KM; ++j)
+    if (j < k && krow && lane == j) krow[slot[j]] = t;
   if (lane == 0) {
     float S = 0.f, G = 0.f;
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
       if (j >= k) break;
       S += s[j];
-      G += gate[(long long)t * k + j] * dg[j];
+      G += gt[j] * dg[j];
     }
 #pragma unroll
     for (int j = 0; j < KM; ++j) {
@@ -402,8 +474,8 @@ void launch_fill_zero(void* p, size_t bytes, hipStream_t s) {
 void launch_bwd_prep(const int32_t* counts, const int32_t* offsets, int E, int Pmax, int Tp, int S, int step,
                      int32_t* kofs, int32_t* klen, int32_t* ksh, int32_t* pcol, int32_t* krow_pad, int32_t* zrow,
                      hipStream_t s) {
-  hipLaunchKernelGGL(bwd_prep_kernel, dim3(1), dim3(1024), 0, s, counts, offsets, E, Pmax, Tp, S, step, kofs, klen, ksh,
-                     pcol, krow_pad, zrow);
+  hipLaunchKernelGGL(bwd_prep_kernel, dim3(E > 0 ? E : 1), dim3(256), 0, s, counts, offsets, E, Pmax, Tp, S, step, kofs,
+                     klen, ksh, pcol, krow_pad, zrow);
 }
 
 void launch_splitk_reduce(const float* part, long long n, int S, float* out, hipStream_t s) {
