@@ -23,12 +23,11 @@ namespace fgmoe {
 // loads requested before its first product (eight partial tiles per logit).
 // The partial tiles meet in LDS and are added in a fixed order.
 //
-// Selection: 32 lanes per token, two experts per lane.  A lane keeps its k
+// Selection: 8 lanes per token, eight experts per lane.  A lane keeps its k
 // best keys (score + bias, then the lower expert on an exact tie, packed as
-// one 64-bit key), then five merges combine the 32 lanes (four DPP row
-// rotations and one swizzle, route_select), which gives the top-k of s + b
-// in descending order with ties to the lower expert.  Gates are the selected
-// scores divided by their sum.
+// one 64-bit key), then three DPP merges combine the 8 lanes (route_select),
+// which gives the top-k of s + b in descending order with ties to the lower
+// expert.  Gates are the selected scores divided by their sum.
 // Per-block expert counts go to block_counts; rank[t*k + j] is the number of
 // earlier assignments (t', j') of the same block with the same expert, which
 // the dispatch kernel turns into the slot.
@@ -51,52 +50,53 @@ __device__ __forceinline__ void route_insert(uint64_t (&l)[K], uint64_t c) {
   }
 }
 
-// A lane's 64-bit key from another lane of the same 16-lane row, rotated by
-// N lanes (DPP row_ror:N, a VALU move), or from lane i ^ 16 of the same 32
-// (ds_swizzle in bit mode: and 0x1F, or 0, xor 0x10).
-template <int N>
-__device__ __forceinline__ uint64_t route_ror64(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, 0x120 + N, 0xF, 0xF, false);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), 0x120 + N, 0xF, 0xF, false);
+// A lane's 64-bit key from another lane of its group of 8 (DPP, a VALU
+// move): CTRL 0xB1 = quad_perm [1,0,3,2] (lane ^ 1), 0x4E = quad_perm
+// [2,3,0,1] (lane ^ 2), 0x141 = row_half_mirror (lane 7 - i of the 8).
+template <int CTRL>
+__device__ __forceinline__ uint64_t route_dpp64(uint64_t v) {
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xF, 0xF, false);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xF, 0xF, false);
   return ((uint64_t)hi << 32) | lo;
 }
-__device__ __forceinline__ uint64_t route_swap16(uint64_t v) {
-  const uint32_t lo = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)v, 0x401F);
-  const uint32_t hi = (uint32_t)__builtin_amdgcn_ds_swizzle((int)(uint32_t)(v >> 32), 0x401F);
-  return ((uint64_t)hi << 32) | lo;
-}
-// Merge step S of a token's 32 lanes: S = 0..3 take the list of the lane
-// 1, 2, 4, 8 places on in the same row (after step S a lane's list covers
-// 2^(S+1) consecutive lanes of its row, each step a disjoint union), S = 4
-// the other row's; the top K of a union is within the union of the top Ks.
-template <int K, int S>
+template <int K, int CTRL>
 __device__ __forceinline__ void route_merge(uint64_t (&best)[K]) {
   uint64_t other[K];
 #pragma unroll
-  for (int i = 0; i < K; ++i) other[i] = S < 4 ? route_ror64<(1 << (S & 3))>(best[i]) : route_swap16(best[i]);
+  for (int i = 0; i < K; ++i) other[i] = route_dpp64<CTRL>(best[i]);
 #pragma unroll
   for (int i = 0; i < K; ++i) route_insert<K>(best, other[i]);
 }
 
-// One token's top K over its 32 lanes: lane u scores experts 2u and 2u + 1
-// (logits lrow), s = sigmoid, key (s + b, 63 - e); after the five merges
-// every lane of the 32 holds the token's top K keys in descending order.
+// One token's top K over a group of 8 lanes: lane v scores experts 8v ..
+// 8v + 7 (logits lrow), s = sigmoid, key (s + b, 63 - e), and keeps its K
+// best; three merges (with lane ^ 1, lane ^ 2, then the mirrored lane of the
+// other half, each a disjoint union; the top K of a union is within the
+// union of the top Ks) leave the token's top K, descending, in all 8 lanes.
 template <int K>
-__device__ __forceinline__ void route_select(const float* lrow, const float* bias_s, int E, int u,
+__device__ __forceinline__ void route_select(const float* lrow, const float* bias_s, int E, int v,
                                              uint64_t (&best)[K]) {
 #pragma unroll
   for (int i = 0; i < K; ++i) best[i] = 0;
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int e = 2 * u + i;
-    const float sc = sigmoidf_(lrow[min(e, 63)]);
+  for (int i = 0; i < 8; ++i) {
+    const int e = 8 * v + i;
+    const float sc = sigmoidf_(lrow[e]);
     if (e < E) route_insert<K>(best, route_key(sc + bias_s[e], e));
   }
-  route_merge<K, 0>(best);
-  route_merge<K, 1>(best);
-  route_merge<K, 2>(best);
-  route_merge<K, 3>(best);
-  route_merge<K, 4>(best);
+  route_merge<K, 0xB1>(best);
+  route_merge<K, 0x4E>(best);
+  route_merge<K, 0x141>(best);
+}
+
+// Workgroup barrier for LDS data only: this wave's LDS accesses are complete
+// (lgkmcnt(0)) and every wave has reached the barrier.  Unlike __syncthreads
+// it does not wait for the wave's global stores (the selections and gates
+// written just before), which would cost a round trip to L2.
+__device__ __forceinline__ void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
 }
 
 // Loads and ranks of a block's assignments from emask[e], the block's tokens
@@ -276,14 +276,14 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
   }
   __syncthreads();
 
-  // ---- selection: wave w takes tokens 2w and 2w+1 (lanes 32 t .. 32 t + 31
-  // for token 2w + t)
-  {
-    const int tt = 2 * wave + (lane >> 5), u = lane & 31;
+  // ---- selection: waves 0 and 1 take the 16 tokens, 8 lanes each
+  // (route_select); lane 0 of a token's group writes its selections
+  if (wave < 2) {
+    const int tt = 8 * wave + (lane >> 3), v = lane & 7;
     uint64_t best[K];
-    route_select<K>(lgs[tt], bias_s, E, u, best);
+    route_select<K>(lgs[tt], bias_s, E, v, best);
     const int tok = tok0 + tt;
-    if (u == 0 && tok < T_) {
+    if (v == 0 && tok < T_) {
       float ssel[K];
       float ssum = 0.f;
 #pragma unroll
@@ -299,7 +299,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
       for (int j = 0; j < K; ++j) gate[(long long)tok * K + j] = ssel[j] / ssum;
     }
   }
-  __syncthreads();
+  lds_barrier();
   route_loads_ranks(sel, emask, K, E, min(16, T_ - tok0) * k, block_counts + (long long)blockIdx.x * E,
                     rank + (long long)tok0 * k);
 }
@@ -313,7 +313,7 @@ __global__ __launch_bounds__(512) void route_topk_kernel(const T* __restrict__ x
 // 2 ((w >> 1) & 1) .. + 1 over k steps 4 (w >> 2) .. + 3 of every chunk, and
 // the two k halves meet in LDS (first half + second half).  Selection,
 // gates, per-block loads and ranks are the 16-token kernel's, over 64
-// tokens (64-bit token masks per expert).
+// tokens (every wave selects for 8 of them; 64-bit token masks per expert).
 // ---------------------------------------------------------------------------
 // s_waitcnt vmcnt(N), the other counters left free (gfx9 encoding: vmcnt
 // bits [3:0] and [15:14], expcnt [6:4], lgkmcnt [11:8]).
@@ -440,15 +440,14 @@ __global__ __launch_bounds__(512) void route_topk64_kernel(const bf16_t* __restr
   }
   __syncthreads();
 
-  // ---- selection: in round i, wave w takes tokens 16 i + 2w and 16 i + 2w + 1
-  // (32 lanes each, two experts per lane, route_select)
-#pragma unroll 1
-  for (int it = 0; it < 4; ++it) {
-    const int tt = 16 * it + 2 * wave + (lane >> 5), u = lane & 31;
+  // ---- selection: wave w takes tokens 8w .. 8w + 7, 8 lanes each
+  // (route_select); lane 0 of a token's group writes its selections
+  {
+    const int tt = 8 * wave + (lane >> 3), v = lane & 7;
     uint64_t best[K];
-    route_select<K>(lgs[tt], bias_s, E, u, best);
+    route_select<K>(lgs[tt], bias_s, E, v, best);
     const int tok = tok0 + tt;
-    if (u == 0 && tok < T_) {
+    if (v == 0 && tok < T_) {
       float ssel[K];
       float ssum = 0.f;
 #pragma unroll
@@ -464,7 +463,7 @@ __global__ __launch_bounds__(512) void route_topk64_kernel(const bf16_t* __restr
       for (int j = 0; j < K; ++j) gate[(long long)tok * K + j] = ssel[j] / ssum;
     }
   }
-  __syncthreads();
+  lds_barrier();
   route_loads_ranks(sel, emask, K, E, min(64, T_ - tok0) * K, block_counts + (long long)blockIdx.x * E,
                     rank + (long long)tok0 * K);
 }
