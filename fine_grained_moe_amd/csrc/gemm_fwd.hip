@@ -628,6 +628,54 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   const int n = nt * BN + wn * WN + NI * fr;               // first column of this lane (not SwiGLU)
   const int fh = nt * (BN / 2) + wn * (WN / 2) + HN * fr;  // first h column of this lane (SwiGLU)
   if (SWIGLU ? fh >= p.N : n >= p.N) return;
+  if (!SWIGLU && KM != 1 && p.epi == EPI_SWIGLU_BWD) {
+    // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u).
+    // The saved rows of the next 16-row block are requested before this
+    // block's arithmetic (a row per (mi, i); rows past the item re-read its
+    // last row, so no load sits under a lane condition and waits where the
+    // condition ends): the loads of one block overlap the math and stores of
+    // the one before instead of a round trip per row.
+    const T* const aub = reinterpret_cast<const T*>(p.aux);
+    u32x4_t ra[2][4], ru[2][4];
+    auto load_block = [&](int mi, u32x4_t (&xa)[4], u32x4_t (&xu)[4]) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lr = min(wm * WM + mi * 16 + 4 * g + i, rows - 1);
+        const T* au = aub + (long long)(row_base + lr) * p.ldaux;
+        xa[i] = ld16(au + n);
+        xu[i] = ld16(au + p.N + n);
+      }
+    };
+    load_block(0, ra[0], ru[0]);
+#pragma unroll
+    for (int mi = 0; mi < 4; ++mi) {
+      if (mi + 1 < 4) load_block(mi + 1, ra[(mi + 1) & 1], ru[(mi + 1) & 1]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int lr = wm * WM + mi * 16 + 4 * g + i;
+        if (lr >= rows) continue;
+        const long long row = row_base + lr;
+        const float sc = p.gate ? row_scale[lr] : 1.f;
+        float da[NI], du[NI], hs[NI];
+#pragma unroll
+        for (int ni = 0; ni < NI; ++ni) {
+          const uint32_t wa = ra[mi & 1][i][ni >> 1], wu = ru[mi & 1][i][ni >> 1];
+          const float a = bf16_to_f32((bf16_t)((ni & 1) ? (wa >> 16) : (wa & 0xFFFFu)));
+          const float u = bf16_to_f32((bf16_t)((ni & 1) ? (wu >> 16) : (wu & 0xFFFFu)));
+          const float dh = acc[mi][ni][i] * sc;
+          const float sg = sigmoidf_(a);
+          const float si = a * sg;
+          da[ni] = dh * u * (sg * (1.f + a * (1.f - sg)));
+          du[ni] = dh * si;
+          hs[ni] = sc * (si * u);
+        }
+        store_vec<T, NI>(C + row * p.ldc + n, da);
+        store_vec<T, NI>(C + row * p.ldc + p.N + n, du);
+        if (p.hg) store_vec<T, NI>(reinterpret_cast<T*>(p.hg) + row * p.N + n, hs);
+      }
+    }
+    return;
+  }
 #pragma unroll
   for (int mi = 0; mi < 4; ++mi) {
 #pragma unroll
@@ -658,25 +706,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
         }
         store_vec<T, NI>(C + row * p.ldc + n, v);
         if (aux) store_vec<T, NI>(aux + row * p.ldaux + n, raw);
-      } else if (p.epi == EPI_SWIGLU_BWD) {
-        // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u)
-        const float sc = p.gate ? row_scale[lr] : 1.f;
-        const T* au = reinterpret_cast<const T*>(p.aux) + row * p.ldaux;
-        float a[NI], u[NI], da[NI], du[NI], hs[NI];
-        load_vec<T, NI>(au + n, a);
-        load_vec<T, NI>(au + p.N + n, u);
-#pragma unroll
-        for (int ni = 0; ni < NI; ++ni) {
-          const float dh = acc[mi][ni][i] * sc;
-          const float sg = sigmoidf_(a[ni]);
-          const float si = a[ni] * sg;
-          da[ni] = dh * u[ni] * (sg * (1.f + a[ni] * (1.f - sg)));
-          du[ni] = dh * si;
-          hs[ni] = sc * (si * u[ni]);
-        }
-        store_vec<T, NI>(C + row * p.ldc + n, da);
-        store_vec<T, NI>(C + row * p.ldc + p.N + n, du);
-        if (p.hg) store_vec<T, NI>(reinterpret_cast<T*>(p.hg) + row * p.N + n, hs);
       } else if (p.epi == EPI_STORE_F32) {
         float v[NI];
 #pragma unroll
