@@ -227,27 +227,37 @@ def bench_decode(moe, synth, torch, np, n_layers=23, iters=46, graph_reps=20):
         e1.record()
         torch.cuda.synchronize()
         eager_us = e0.elapsed_time(e1) * 1e3 / iters
-        # the same 23 forwards, captured once and replayed
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
-            for i in range(n_layers):
-                moe.moe_forward(dims, x, layers[i], bias, y, r, ws)
-        g.replay()
-        torch.cuda.synchronize()
-        e0.record()
-        for _ in range(graph_reps):
+        # the same 23 forwards, captured once and replayed; then with each
+        # layer naming the next (moe_weights.next, the last naming the first,
+        # as a serving loop runs them token after token)
+        def replay_us(ls):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                for i in range(n_layers):
+                    moe.moe_forward(dims, x, ls[i], bias, y, r, ws)
             g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / (graph_reps * n_layers)
-        del g
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(graph_reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del g
+            return e0.elapsed_time(e1) * 1e3 / (graph_reps * n_layers)
+
+        us = replay_us(layers)
+        us_hint = replay_us([dict(layers[i], next=layers[(i + 1) % n_layers]) for i in range(n_layers)])
         uniq = int((r["counts"] > 0).sum().item())
         nbytes = decode_bytes(T, d, E, F, Fs, uniq)
         gbps = nbytes / (us * 1e-6) / 1e9
+        gbps_hint = nbytes / (us_hint * 1e-6) / 1e9
         out[f"T{T}"] = dict(us=round(us, 2), eager_us=round(eager_us, 2), unique_experts=uniq, bytes=nbytes,
-                            gbps=round(gbps, 1), frac_hbm=round(gbps / (PEAK_HBM_BPS / 1e9), 4))
+                            gbps=round(gbps, 1), frac_hbm=round(gbps / (PEAK_HBM_BPS / 1e9), 4),
+                            us_next_layer_hint=round(us_hint, 2),
+                            frac_hbm_next_layer_hint=round(gbps_hint / (PEAK_HBM_BPS / 1e9), 4))
         log(f"decode T={T}: {us:.1f} us per forward (graph replay; eager {eager_us:.1f} us), {uniq} experts, "
-            f"{gbps:.0f} GB/s ({gbps / 8000:.1%} of HBM)")
+            f"{gbps:.0f} GB/s ({gbps / 8000:.1%} of HBM); with the next-layer hint {us_hint:.1f} us "
+            f"({gbps_hint / 8000:.1%})")
     # The floor the three dependent launches of a forward put under it: three
     # minimal dependent kernels (one-element adds) per forward, 23 forwards,
     # captured and replayed the same way.
@@ -333,6 +343,10 @@ def bench_stack(moe, synth, torch, np, n_layers=23, reps=10, graph_reps=20):
               w_down=torch.from_numpy(qd).cuda(), s_down=bf(sd), w_sh_gate_up=bf(base.w_sh_gate_up),
               w_sh_down=bf(base.w_sh_down))
     qlayers = [w0] + [{n: t.clone() for n, t in w0.items()} for _ in range(n_layers - 1)]
+    # each layer names the one after it (moe_weights.next): its router and
+    # shared gate/up rows are read into the caches during this layer's last
+    # launch; the last layer names none
+    hinted = [dict(qlayers[i], next=qlayers[i + 1]) for i in range(n_layers - 1)] + [qlayers[-1]]
     bias = torch.zeros(E, device="cuda")
     out["int4_top1"] = {}
     for T in (1, 8, 64):
@@ -341,29 +355,33 @@ def bench_stack(moe, synth, torch, np, n_layers=23, reps=10, graph_reps=20):
         r = moe.alloc_routing(dims)
         ws = moe.alloc_workspace(dims)
 
-        def qstack():
-            for i in range(n_layers):
-                moe.moe_forward_block(dims, h[i % 2], gamma, 1e-6, qlayers[i], bias, h[(i + 1) % 2], r, ws)
+        def replay_us(layers):
+            def qstack():
+                for i in range(n_layers):
+                    moe.moe_forward_block(dims, h[i % 2], gamma, 1e-6, layers[i], bias, h[(i + 1) % 2], r, ws)
 
-        qstack()
-        torch.cuda.synchronize()
-        g = torch.cuda.CUDAGraph()
-        with torch.cuda.graph(g):
             qstack()
-        g.replay()
-        torch.cuda.synchronize()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        for _ in range(graph_reps):
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                qstack()
             g.replay()
-        e1.record()
-        torch.cuda.synchronize()
-        us = e0.elapsed_time(e1) * 1e3 / graph_reps
-        del g
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(graph_reps):
+                g.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            del g
+            return e0.elapsed_time(e1) * 1e3 / graph_reps
+
+        us_plain = replay_us(qlayers)
+        us = replay_us(hinted)
         out["int4_top1"][f"T{T}"] = dict(us_per_stack=round(us, 1), us_per_layer=round(us / n_layers, 2),
-                                         tokens_per_s=T / (us * 1e-6))
-        log(f"stack int4 top-1 T={T}: {us:.1f} us per {n_layers}-layer stack (graph replay, "
-            f"{us / n_layers:.1f} us per layer), {T / (us * 1e-6):.0f} tokens/s")
+                                         tokens_per_s=T / (us * 1e-6), us_per_stack_no_hint=round(us_plain, 1))
+        log(f"stack int4 top-1 T={T}: {us:.1f} us per {n_layers}-layer stack (graph replay, next-layer hint; "
+            f"{us / n_layers:.1f} us per layer), {T / (us * 1e-6):.0f} tokens/s; without the hint {us_plain:.1f} us")
     return out
 
 

@@ -536,6 +536,37 @@ __device__ void decode_write_routing(const DecodeArgs& p, const Book& B) {
   if (tid == 0) *p.n_active = B.n_active;
 }
 
+// Prefetch of the next layer's router and shared gate/up (DecodeArgs::pf_*),
+// by workgroups past stage 3's items.  Mirror m reads the 16 weight rows that
+// the next layer's stage-1 workgroup m reads (shared gate/up rows 8m .. + 7
+// and Fs + 8m .. + 7, or router rows 16 (m - Fs / 8) .. + 15).  Workgroup b
+// of a launch runs on XCD b mod 8 and the mirror's index is m past a
+// multiple of 8, so its rows land in the L2 of the XCD that reads them next
+// (measured: a mirror one XCD off makes the next layer slower than none).
+// The loads go to LDS and are never read.
+template <int D, int FS>
+__device__ void decode_prefetch(const DecodeArgs& p, int m, char* lds) {
+  if (m >= FS / 8 + 4) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  char* dst = lds + wave * 1024;
+  static_assert(D * 2 % 1024 == 0, "whole 1 KiB pieces of a row");
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {                      // wave w: rows 4w .. 4w + 3
+    const int r = 4 * wave + i;
+    const char* row;
+    if (m < FS / 8) {
+      const int f = m * 8 + (r & 7);
+      row = reinterpret_cast<const char*>(p.pf_sh_gate_up + (long long)(r < 8 ? f : FS + f) * D);
+    } else {
+      row = reinterpret_cast<const char*>(p.pf_router + (long long)min((m - FS / 8) * 16 + r, p.E - 1) * D);
+    }
+#pragma unroll
+    for (int q = 0; q < D * 2 / 1024; ++q)
+      __builtin_amdgcn_global_load_lds(row + q * 1024 + lane * 16, (lds_ptr_t)dst, 16, 0, 0);
+  }
+  __builtin_amdgcn_s_waitcnt(0);                     // every load has landed before the wave ends
+}
+
 // ---------------------------------------------------------------------------
 // Stage 2.  Operands go to the MFMAs straight from global memory: these
 // workgroups are bound by the latency of their two dependent round trips
@@ -725,9 +756,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4))) void d
 // (as in stage 2).
 // ---------------------------------------------------------------------------
 template <int D, int FR, int CBN>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CBN == 1 ? 4 : 3))) void decode_stage3_kernel(DecodeArgs p) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(CBN == 1 ? 4 : 3))) void decode_stage3_kernel(DecodeArgs p, int n_items) {
   constexpr int W = 32 * CBN, LS = W + 1;            // output columns per item, LDS row stride
-  __shared__ float lds[4 * 16 * LS];
+  __shared__ __align__(16) float lds[4 * 16 * LS];
+  static_assert(4 * 16 * LS * 4 >= 4 * 1024, "a 1 KiB prefetch target per wave");
+  if ((int)blockIdx.x >= n_items) {
+    decode_prefetch<D, kDecodeFs>(p, blockIdx.x - n_items, reinterpret_cast<char*>(lds));
+    return;
+  }
   static_assert(FR / kGroup == 4, "one scale group per wave");
   constexpr int ncb = D / W, NTL = W / 16, TPT = W / 8;   // 16-column tiles, threads per token
   const int a = blockIdx.x / ncb, cb = blockIdx.x - a * ncb;
@@ -827,10 +863,19 @@ void launch_decode(const DecodeArgs& a, hipStream_t s) {
     hipLaunchKernelGGL((decode_stage2_kernel<D, FR, FS, 4, 1>), dim3(1 + 4 * (D / 16) + max_active * (FR / 16)),
                        dim3(256), 0, s, a, ntile);
   }
-  if (a.T <= 32)
-    hipLaunchKernelGGL((decode_stage3_kernel<D, FR, 1>), dim3(max_active * (D / 32)), dim3(256), 0, s, a);
-  else
-    hipLaunchKernelGGL((decode_stage3_kernel<D, FR, 2>), dim3(max_active * (D / 64)), dim3(256), 0, s, a);
+  // stage 3's items, then (with a next layer) the prefetch mirrors of its
+  // stage-1 workgroups; the item count is a multiple of 8, so each mirror
+  // keeps its workgroup's XCD.  (Mirrors of the next stage 2's shared-down
+  // reads, in this stage or in stage 2, measured no gain: those workgroups
+  // are not on the critical path.)
+  const int n_pf = a.pf_router && a.pf_sh_gate_up ? FS / 8 + 4 : 0;
+  if (a.T <= 32) {
+    const int n3 = max_active * (D / 32);
+    hipLaunchKernelGGL((decode_stage3_kernel<D, FR, 1>), dim3(n3 + n_pf), dim3(256), 0, s, a, n3);
+  } else {
+    const int n3 = max_active * (D / 64);
+    hipLaunchKernelGGL((decode_stage3_kernel<D, FR, 2>), dim3(n3 + n_pf), dim3(256), 0, s, a, n3);
+  }
 }
 
 }  // namespace fgmoe

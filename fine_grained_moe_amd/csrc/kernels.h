@@ -203,6 +203,10 @@ struct DecodeArgs {
   float* step_bias;                  // [E] in/out (the bias the router read)
   float step_gamma;
   float* step_stats;                 // [4] balance figures, or null
+  // the next layer's router and shared gate/up (the same shapes), read into
+  // the L2 caches by stage 3, or null
+  const uint16_t* pf_router;
+  const uint16_t* pf_sh_gate_up;
 };
 void launch_decode(const DecodeArgs& a, hipStream_t s);
 

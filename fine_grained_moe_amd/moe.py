@@ -39,7 +39,8 @@ class MoeDims(ctypes.Structure):
 
 
 class MoeWeights(ctypes.Structure):
-    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS]
+    # next: another MoeWeights (the following layer's, a prefetch hint), or null
+    _fields_ = [(n, ctypes.c_void_p) for n in WEIGHT_FIELDS] + [("next", ctypes.c_void_p)]
 
 
 class MoeRouting(ctypes.Structure):
@@ -149,7 +150,13 @@ def _host_ptr(t) -> Optional[int]:
 
 
 def _struct(cls, fields, tensors: Dict[str, torch.Tensor]):
-    return cls(*[_ptr(tensors.get(f)) for f in fields])
+    s = cls(*[_ptr(tensors.get(f)) for f in fields])
+    nxt = tensors.get("next") if cls is MoeWeights else None
+    if nxt is not None:
+        # the following layer's weights (a prefetch hint); kept alive with s
+        s._next = _struct(MoeWeights, WEIGHT_FIELDS, nxt)
+        s.next = ctypes.addressof(s._next)
+    return s
 
 
 def _check(code: int, where: str) -> None:

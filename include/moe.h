@@ -73,7 +73,7 @@ typedef struct {
  * int4 format (an assumed container; the article says only "int4"):
  * symmetric, one bf16 scale per 128 consecutive elements of a row,
  * w = q * scale with q a two's-complement nibble in [-8, 7]. */
-typedef struct {
+typedef struct moe_weights {
   const void* w_router;
   const void* w_gate_up;
   const void* w_down;
@@ -81,6 +81,16 @@ typedef struct {
   const void* s_down;
   const void* w_sh_gate_up;
   const void* w_sh_down;
+  /* Optional (null: none).  The weights of the layer the caller runs next on
+   * the same stream, with the same dims: a prefetch hint for a stack of
+   * layers, whose weights do not depend on the activations.  The int4 top-1
+   * serving path (w_routed = MOE_INT4_G128, T <= 64) reads next's router and
+   * shared gate/up rows during its last launch, each weight block through
+   * the XCD whose L2 the next layer's first launch reads it through, so the
+   * next call finds them in cache.  Results never depend on it; other paths
+   * ignore it.  The struct is read during the call only (a captured graph
+   * keeps the device pointers it held). */
+  const struct moe_weights* next;
 } moe_weights;
 
 /* (host struct of device pointers) Routing produced by moe_route/moe_forward.

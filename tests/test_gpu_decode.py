@@ -123,3 +123,41 @@ def test_int4_decode_graph_replay_matches_eager(weights):
         # eager work between replays, on the same weights and its own buffers
         moe.moe_forward(dims, other, dev, bias, y_other, moe.alloc_routing(dims), moe.alloc_workspace(dims))
         torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [1, 8, 16, 17, 64])
+def test_next_layer_hint_changes_no_bits(weights, T):
+    """The next-layer prefetch hint (moe_weights.next) only moves the next
+    layer's router and shared gate/up rows into the caches: y and the routing
+    are bitwise those of the call without it, for the layer forward and the
+    MoE block, and the hinted layer's own call is unchanged too."""
+    import torch
+    from fine_grained_moe_amd import moe
+    dev, _ = weights
+    other = {n: (t.flip(0).contiguous() if n in ("w_router", "w_sh_gate_up") else t) for n, t in dev.items()}
+    inp = synth.make_layer(T=T, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=300 + T)
+    dims = moe.make_dims(T, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+    x = torch.from_numpy(inp.x).to(device="cuda", dtype=torch.bfloat16)
+    bias = torch.zeros(64, device="cuda")
+    ws = moe.alloc_workspace(dims)
+    gw = torch.ones(1024, device="cuda")
+    outs = []
+    for w in (dev, dict(dev, next=other), dict(dev, next=dev)):
+        y = torch.empty_like(x)
+        r = moe.alloc_routing(dims)
+        moe.moe_forward(dims, x, w, bias, y, r, ws)
+        hb = torch.empty_like(x)
+        rb = moe.alloc_routing(dims)
+        moe.moe_forward_block(dims, x, gw, 1e-6, w, bias, hb, rb, ws)
+        # the layer run next, after a call that hinted it
+        y2 = torch.empty_like(x)
+        moe.moe_forward(dims, x, other, bias, y2, moe.alloc_routing(dims), ws)
+        torch.cuda.synchronize()
+        outs.append((y.view(torch.int16).cpu(), {k: v.cpu() for k, v in r.items()}, hb.view(torch.int16).cpu(),
+                     y2.view(torch.int16).cpu()))
+    for o in outs[1:]:
+        assert torch.equal(o[0], outs[0][0])
+        for k in outs[0][1]:
+            assert torch.equal(o[1][k], outs[0][1][k]), k
+        assert torch.equal(o[2], outs[0][2])
+        assert torch.equal(o[3], outs[0][3])
