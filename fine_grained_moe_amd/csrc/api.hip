@@ -397,7 +397,13 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   sg.aux = training ? at<char>(ws, L.AUs) : nullptr;
   sg.ldaux = 2LL * Fs;
 
+  // int4 experts: tiles of few rows spread them over all eight waves, which
+  // then share the in-register dequantisation (measured on the int4 prefill
+  // at 4096 tokens, about 64 rows per expert: gate/up 78 -> 74 us, down 53 ->
+  // 49 us; no change on the bf16 layer, whose loop does not wait for the
+  // MFMAs of the active waves)
   GemmArgs ga{};
+  ga.small_layouts = routed_int4 ? 1 : 0;
   ga.act = d.act;
   ga.njobs = 2;
   ga.order = 1;                                      // routed tiles first: they run longest
@@ -451,6 +457,7 @@ moe_status enqueue_expert_gemms(const moe_dims& d, const Layout& L, const void* 
   sd.xcd_cols = dense_order(d.T, D);
 
   GemmArgs da{};
+  da.small_layouts = routed_int4 ? 1 : 0;
   da.act = d.act;
   da.njobs = 2;
   da.order = 2;                                      // shared tiles first: twice the contraction of a routed tile

@@ -56,7 +56,7 @@ namespace {
 
 constexpr int NTHR = 512;                    // 8 waves
 constexpr int BM = kTileMFwd, BN = 256;      // workgroup tile
-constexpr int WM = 64, WN = 128, NI = WN / 16, HN = NI / 2;   // one wave's output piece
+constexpr int WM = 64;                       // rows of one wave's output piece
 constexpr int kStages = 5;                   // LDS ring depth (5 x 32 KiB: all of a CU's LDS)
 constexpr int ATILE = BM * kRowB, BTILE = BN * kRowB;        // one stage of each operand
 constexpr int kStageBytes = ATILE + BTILE;
@@ -167,7 +167,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   __shared__ __attribute__((aligned(16))) char lds[kStages * kStageBytes];
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
 
   int jid, bid;
   select_job(args, blockIdx.x, jid, bid);
@@ -223,8 +222,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   // K-major: the expert's rows that exist (the rest of its last stage reads zeros)
   const int kcnt = KA ? max(0, min(klen, p.K - (int)kofs)) : klen;
   rows = rows < BM ? rows : BM;
-  // this wave's 64-row band holds rows of the item
-  const bool active = wm * WM < rows;
 
   // Row scales of the gate-scaled epilogue: thread r < 256 fetches perm of
   // row r now and the gate two K steps before the end (after the wait that
@@ -372,21 +369,6 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     for (int j = 0; j < kLoads; ++j) issue_one(s, j);
   };
 
-  // ---- LDS -> MFMA operand rows of this wave (16 consecutive LDS rows per tile)
-  const int fr = lane & 15, g = lane >> 4;
-  int arow_l[4], brow_l[NI];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi) arow_l[mi] = wm * WM + mi * 16 + fr;
-#pragma unroll
-  for (int ni = 0; ni < NI; ++ni)
-    brow_l[ni] = (SWIGLU ? (ni < HN ? wn * 64 + ni * 16 : BN / 2 + wn * 64 + (ni - HN) * 16) : wn * WN + ni * 16) + fr;
-
-  f32x4_t acc[4][NI];
-#pragma unroll
-  for (int mi = 0; mi < 4; ++mi)
-#pragma unroll
-    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
   // int4 B: the tile's bf16 scales, [K / 128 groups][256 LDS rows], in ring
   // buffer 0's B space past the 4 KiB its int4 stage uses (never a load
   // target), filled before the ring and made visible by a barrier.
@@ -401,6 +383,40 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
     }
     __syncthreads();
   }
+  // ---- LDS -> MFMA operand rows of this wave (16 consecutive LDS rows per
+  // tile).  Wave layouts (WC: column groups of waves): 2 (4 row bands x 2,
+  // a wave 64 x 128, eight fragments), 4 (2 x 4, 64 x 64, four) and 8 (1 x 8,
+  // 64 x 32, two).  The LDS layout of B and the stage loads are the same in
+  // every layout: a wave of layout WC takes NI of the eight fragments of
+  // wave group wn2 of layout 2 (sub-block sub), so a lane's NI output columns
+  // stay adjacent.  With args.small_layouts, tiles of at most 128 rows take
+  // layout 4 and SwiGLU tiles of at most 64 rows layout 8 (the other
+  // instantiations' registers do not hold a third layout): every wave then
+  // has rows to multiply, two per SIMD instead of one or none.
+  const int fr = lane & 15, g = lane >> 4;
+  auto tile_body = [&](auto wc_tag) {
+  constexpr int WC = decltype(wc_tag)::value;
+  static_assert(WC == 2 || KM == 0, "K-major operands use the 4 x 2 layout");
+  constexpr int NI = 16 / WC, HN = NI / 2, NSUB = WC / 2;
+  const int wm = wave / WC, wn = wave % WC;
+  const int wn2 = wn / NSUB, sub = wn % NSUB;
+  const bool active = wm * WM < rows;
+  int arow_l[4], brow_l[NI];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi) arow_l[mi] = wm * WM + mi * 16 + fr;
+#pragma unroll
+  for (int li = 0; li < NI; ++li) {
+    // the fragment's index in layout 2
+    const int ni = SWIGLU ? (li < HN ? sub * HN + li : 4 + sub * HN + (li - HN)) : sub * NI + li;
+    brow_l[li] = (SWIGLU ? (ni < 4 ? wn2 * 64 + ni * 16 : BN / 2 + wn2 * 64 + (ni - 4) * 16) : wn2 * 128 + ni * 16) + fr;
+  }
+
+  f32x4_t acc[4][NI];
+#pragma unroll
+  for (int mi = 0; mi < 4; ++mi)
+#pragma unroll
+    for (int ni = 0; ni < NI; ++ni) acc[mi][ni] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
   // Lane (fr, g)'s int4 operand of LDS B row r: the 8 nibbles of elements
   // 8g .. 8g + 7 of the stage, and the row's scale for stage s's group.
   auto qword = [&](const char* Bs, int r) { return *reinterpret_cast<const uint32_t*>(Bs + r * 16 + 4 * g); };
@@ -488,11 +504,21 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
           } else {
             fb[ni] = ld16(Bn + swz(brow_l[ni], g));
           }
-          if (ni < 4) fn[ni] = ld16(An + swz(arow_l[ni], g));
+          if constexpr (NI >= 4) {
+            if (ni < 4) fn[ni] = ld16(An + swz(arow_l[ni], g));
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4 / NI; ++q) fn[ni * (4 / NI) + q] = ld16(An + swz(arow_l[ni * (4 / NI) + q], g));
+          }
         }
       }
       if constexpr (decltype(with_loads)::value) {
-        if (ni & 1) issue_one(s + kStages - 1, ni >> 1);
+        if constexpr (NI == 8) {
+          if (ni & 1) issue_one(s + kStages - 1, ni >> 1);
+        } else {
+#pragma unroll
+          for (int q = 0; q < kLoads / NI; ++q) issue_one(s + kStages - 1, ni * (kLoads / NI) + q);
+        }
       }
       __builtin_amdgcn_sched_barrier(0);   // keep the reads and loads spread out
     }
@@ -612,7 +638,7 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       if (lr >= rows) continue;
 #pragma unroll
       for (int ni = 0; ni < NI; ++ni) {
-        const int n = nt * BN + wn * WN + 16 * ni + 4 * g;
+        const int n = nt * BN + wn * 128 + 16 * ni + 4 * g;
         if (n < p.N)
           *reinterpret_cast<f32x4_t*>(Ck + (long long)(row_base + lr) * p.ldc + n) = acc[mi][ni];
       }
@@ -625,10 +651,10 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
   T* C = reinterpret_cast<T*>(p.C) + kz * p.c_kstride;
   float* const Cf = reinterpret_cast<float*>(p.C) + (long long)e * p.c_estride;   // EPI_STORE_F32 (kgroup)
   T* aux = reinterpret_cast<T*>(p.aux);
-  const int n = nt * BN + wn * WN + NI * fr;               // first column of this lane (not SwiGLU)
-  const int fh = nt * (BN / 2) + wn * (WN / 2) + HN * fr;  // first h column of this lane (SwiGLU)
+  const int n = nt * BN + wn2 * 128 + 8 * fr + sub * NI;         // first column of this lane (not SwiGLU)
+  const int fh = nt * (BN / 2) + wn2 * 64 + 4 * fr + sub * HN;   // first h column of this lane (SwiGLU)
   if (SWIGLU ? fh >= p.N : n >= p.N) return;
-  if (!SWIGLU && KM != 1 && p.epi == EPI_SWIGLU_BWD) {
+  if (WC == 2 && !SWIGLU && KM != 1 && p.epi == EPI_SWIGLU_BWD) {
     // SwiGLU backward: dH = s * acc, then (da, du) from the saved (a, u).
     // The saved rows of the next 16-row block are requested before this
     // block's arithmetic (a row per (mi, i); rows past the item re-read its
@@ -719,6 +745,19 @@ __global__ __launch_bounds__(NTHR, 1) void gemm256_kernel(GemmArgs args) {
       }
     }
   }
+  };
+  // the wave layout of this tile (row-major jobs: by the rows it holds)
+  if constexpr (KM == 0) {
+    if (SWIGLU && args.small_layouts && rows <= 64) {
+      tile_body(std::integral_constant<int, 8>{});
+      return;
+    }
+    if (args.small_layouts && rows <= 128) {
+      tile_body(std::integral_constant<int, 4>{});
+      return;
+    }
+  }
+  tile_body(std::integral_constant<int, 2>{});
 }
 
 // chunks of 8 blocks (one per XCD) a job needs: the blocks one XCD runs

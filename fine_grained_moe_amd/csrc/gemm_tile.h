@@ -35,10 +35,13 @@ constexpr int kRowB = 64;
 __device__ __forceinline__ int swz_piece(int row, int piece) { return piece ^ (((row >> 3) & 1) << 1); }
 __device__ __forceinline__ int swz(int row, int piece) { return row * kRowB + (swz_piece(row, piece) << 4); }
 
-// N consecutive outputs (N = 2, 4 or 8), rounded to T.
+// N consecutive outputs (N = 1, 2, 4 or 8), rounded to T.
 template <typename T, int N>
 __device__ __forceinline__ void store_vec(T* p, const float (&v)[N]) {
-  if constexpr (sizeof(T) == 2) {
+  if constexpr (N == 1) {
+    if constexpr (sizeof(T) == 2) *reinterpret_cast<uint16_t*>(p) = f32_to_bf16(v[0]);
+    else *reinterpret_cast<float*>(p) = v[0];
+  } else if constexpr (sizeof(T) == 2) {
     uint32_t w[N / 2];
 #pragma unroll
     for (int i = 0; i < N; i += 2)

@@ -143,6 +143,9 @@ struct GemmArgs {
   int order;               // two jobs: 0 = chunks alternate, 1 = job 0's chunks first, 2 = job 1's first
   int chunks[2];           // filled by launch_gemm
   GemmJob job[2];
+  // launch_gemm_fwd256, row-major operands: tiles of at most 128 rows (64,
+  // SwiGLU) spread their 64-row band(s) over all eight waves
+  int small_layouts;
 };
 void launch_gemm(const GemmArgs& a, hipStream_t s);
 // bf16 jobs with the SwiGLU, row-scale, SwiGLU-backward or store epilogue
