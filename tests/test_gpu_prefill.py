@@ -78,6 +78,34 @@ def test_int4_prefill(T):
     _check(inp, b, q, y, rn, "nanocolibri")
 
 
+def _tiered_bias(E=64, hot=0.12):
+    """Biases that give, at 4096 tokens, experts of every tile class: most
+    with at most 64 rows, some with 65-128, some with 129-256, and two with
+    more than 256 (whole 256-row tiles plus a ragged one)."""
+    b = np.zeros(E, np.float32)
+    b[:2] = hot
+    b[2:6] = hot / 2
+    b[6:12] = hot / 4
+    return b
+
+
+def _tile_classes(counts):
+    c = np.asarray(counts)
+    return [int((c[c > 0] <= 64).sum()), int(((c > 64) & (c <= 128)).sum()), int(((c > 128) & (c <= 256)).sum()),
+            int((c > 256).sum())]
+
+
+def test_int4_prefill_every_tile_layout():
+    """Skewed loads at 4096 tokens: the routed tiles of one forward run in the
+    1 x 8 (at most 64 rows), 2 x 4 (at most 128) and 4 x 2 wave layouts, and
+    an expert spans several 256-row tiles."""
+    inp, b, q = _int4_layer(4096, seed=31, bias=_tiered_bias())
+    y, rn = _run(inp, b, q)
+    classes = _tile_classes(rn["counts"])
+    assert all(n > 0 for n in classes), classes
+    _check(inp, b, q, y, rn, f"tiered loads {classes}")
+
+
 def test_int4_prefill_other_shape():
     """Not the decode shape: d = 256, 8 experts of width 128, shared 256."""
     inp, b, q = _int4_layer(200, seed=7, d=256, E=8, F=128, Fs=256)
@@ -152,14 +180,17 @@ def test_int4_prefill_block():
     assert np.all(rerr <= rbound), ("worst row", float((rerr / rbound).max()))
 
 
-def test_int4_prefill_fused_equals_bf16_path_bitwise():
+@pytest.mark.parametrize("T,tiered", [(300, False), (4096, True)])
+def test_int4_prefill_fused_equals_bf16_path_bitwise(T, tiered):
     """The prefill's GEMMs expand each int4 operand fragment to bf16(q *
-    scale) in registers.  Fed the same values as bf16 weights (the host's
-    exact q * scale, rounded once to bf16), the bf16 layer (k = 1) runs the
-    same products in the same order: the outputs must be the same bits."""
+    scale) in registers, in the small-tile wave layouts where a tile has few
+    rows.  Fed the same values as bf16 weights (the host's exact q * scale,
+    rounded once to bf16), the bf16 layer (k = 1, every tile in the 4 x 2
+    layout) runs the same products in the same order for every output
+    element: the outputs must be the same bits."""
     import torch
     from fine_grained_moe_amd import moe
-    inp, b, q = _int4_layer(300, seed=23)
+    inp, b, q = _int4_layer(T, seed=23 if not tiered else 31, bias=_tiered_bias() if tiered else None)
     qg, sg, qd, sd = q
     y4, rn4 = _run(inp, b, q)
     dims = moe.make_dims(inp.T, inp.d, inp.E, inp.F, inp.Fs, 1, "bf16")
