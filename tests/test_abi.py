@@ -265,3 +265,24 @@ def test_noalloc_refuses_what_does_not_fit(lib):
     assert f(ctypes.byref(bad), 0x1000, ctypes.byref(W), 0x2000, 0x3000, ctypes.byref(R), None) == lib.MOE_E_UNSUPPORTED
     fits = lib.make_dims(500, 1024, 64, 512, 2048, 2, "bf16")
     assert lib.moe_workspace_bytes(fits) <= lib.MOE_NOALLOC_SCRATCH_BYTES
+
+
+def test_weights_struct_carries_the_next_layer(lib, monkeypatch):
+    """moe_weights ends with `next`, a pointer to another moe_weights (the
+    next-layer hint): the binding lays it out as eight pointers and fills
+    `next` from a nested weights dict, keeping that struct alive with it.
+    (Stand-in device addresses: the binding's pointer helper accepts only GPU
+    tensors.)"""
+    assert [f[0] for f in lib.MoeWeights._fields_] == list(lib.WEIGHT_FIELDS) + ["next"]
+    assert ctypes.sizeof(lib.MoeWeights) == 8 * ctypes.sizeof(ctypes.c_void_p)
+    monkeypatch.setattr(lib, "_ptr", lambda a: a)
+    cur = {f: 0x10000 * (i + 1) for i, f in enumerate(lib.WEIGHT_FIELDS)}
+    nxt = {f: 0x1000000 * (i + 1) for i, f in enumerate(lib.WEIGHT_FIELDS)}
+    w = lib._struct(lib.MoeWeights, lib.WEIGHT_FIELDS, dict(cur, next=nxt))
+    assert w.w_router == cur["w_router"]
+    assert w.next == ctypes.addressof(w._next)
+    n = lib.MoeWeights.from_address(w.next)
+    for f in lib.WEIGHT_FIELDS:
+        assert getattr(n, f) == nxt[f], f
+    assert n.next is None                    # the hinted layer names no further layer
+    assert lib._struct(lib.MoeWeights, lib.WEIGHT_FIELDS, cur).next is None
