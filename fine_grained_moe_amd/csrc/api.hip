@@ -564,13 +564,13 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   a.xn = at<uint16_t>(ws, L.xb);
   a.slot = slot;
   a.n_slots = n_slots;
-  // the bias step: stage 2's first workgroup takes it once the loads are
-  // known (the router in stage 1 is the bias's only reader)
   // the next layer's router and shared gate/up, read into the caches by stage 3
   if (w->next && w->next->w_router && w->next->w_sh_gate_up) {
     a.pf_router = (const uint16_t*)w->next->w_router;
     a.pf_sh_gate_up = (const uint16_t*)w->next->w_sh_gate_up;
   }
+  // the bias step: stage 2's first workgroup takes it once the loads are
+  // known (the router in stage 1 is the bias's only reader)
   a.step_bias = bs ? bs->bias : nullptr;
   a.step_gamma = bs ? bs->gamma : 0.f;
   a.step_stats = bs ? bs->stats : nullptr;
