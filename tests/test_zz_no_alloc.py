@@ -77,3 +77,43 @@ def test_too_large_is_refused():
     with pytest.raises(moe.MoeError) as ei:
         moe.moe_forward_noalloc(dims, x, w, torch.zeros(64, device="cuda"), torch.empty_like(x), r)
     assert ei.value.code == moe.MOE_E_WORKSPACE
+
+
+def test_captured_in_a_graph_replays_exactly():
+    """The allocation-free forward is for callers under HIP graph capture:
+    captured once for the bf16 layer (300 tokens), every replay gives
+    exactly the eager moe_forward result, with other eager calls of the
+    entry point on another batch (sharing the static array) and host
+    synchronisations between the replays."""
+    import torch
+    from fine_grained_moe_amd import moe
+    inp = synth.make_workload("layer_t4096", T=300, seed=76)
+    H.remove_near_ties(inp)
+    x, w = H.to_gpu(inp)
+    dims = moe.make_dims(300, inp.d, inp.E, inp.F, inp.Fs, inp.k, "bf16")
+    bias = torch.from_numpy(inp.bias).cuda()
+    y_ref, r_ref = torch.empty_like(x), moe.alloc_routing(dims)
+    moe.moe_forward(dims, x, w, bias, y_ref, r_ref, moe.alloc_workspace(dims))
+    other = synth.make_workload("layer_t4096", T=77, seed=77)
+    xo, _ = H.to_gpu(other)
+    dims_o = moe.make_dims(77, inp.d, inp.E, inp.F, inp.Fs, inp.k, "bf16")
+    y, r = torch.empty_like(x), moe.alloc_routing(dims)
+    # an eager call first: the entry point takes its array's device address
+    # on its first call on a device, outside the capture
+    moe.moe_forward_noalloc(dims_o, xo, w, bias, torch.empty_like(xo), moe.alloc_routing(dims_o))
+    torch.cuda.synchronize()
+    s = torch.cuda.Stream()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        moe.moe_forward_noalloc(dims, x, w, bias, y, r, stream=s)
+    for rep in range(3):
+        y.fill_(float("nan"))
+        for t in r.values():
+            t.fill_(-7)
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ref), rep
+        for n in r:
+            assert torch.equal(r[n], r_ref[n]), (rep, n)
+        moe.moe_forward_noalloc(dims_o, xo, w, bias, torch.empty_like(xo), moe.alloc_routing(dims_o))
+        torch.cuda.synchronize()
