@@ -49,13 +49,9 @@ moe_status check_dims(const moe_dims* d) {
   if (d->E > 64 || d->k > d->E || d->k > 8) return MOE_E_UNSUPPORTED;
   if (d->d % 128 || d->F % 64 || d->Fs % 64) return MOE_E_UNSUPPORTED;
   if (d->w_routed == MOE_INT4_G128) {
-    // top-1 serving: bf16 activations, one expert per token.  Up to
-    // kDecodeMaxT tokens the decode kernels (built for the NanoColibri
-    // shape); above, the prefill (the active experts dequantised, then the
-    // grouped GEMMs), whose groups of 128 run along d and F.
-    if (d->act != MOE_BF16 || d->k != 1) return MOE_E_UNSUPPORTED;
-    if (d->T <= kDecodeMaxT ? !decode_shape_supported(d->d, d->F, d->Fs) : d->F % 128 != 0)
-      return MOE_E_UNSUPPORTED;
+    // top-1 serving: bf16 activations, one expert per token, groups of 128
+    // along d and F (int4_decode picks the kernels)
+    if (d->act != MOE_BF16 || d->k != 1 || d->F % 128 != 0) return MOE_E_UNSUPPORTED;
   }
   const long long slots = (long long)d->T * d->k;
   const long long wide = std::max<long long>(d->d, 2LL * d->F);
@@ -63,6 +59,12 @@ moe_status check_dims(const moe_dims* d) {
   if ((long long)d->T * std::max<long long>(d->d, 2LL * d->Fs) >= (1LL << 31)) return MOE_E_UNSUPPORTED;
   return MOE_OK;
 }
+
+// int4 top-1 batches the decode kernels take: up to kDecodeMaxT tokens at the
+// layer shape they are built for.  Every other int4 batch runs the prefill
+// path (route, the grouped GEMMs on the packed experts, combine), which
+// serves any shape with F a multiple of 128 and any T.
+bool int4_decode(const moe_dims& d) { return d.T <= kDecodeMaxT && decode_shape_supported(d.d, d.F, d.Fs); }
 
 // Training needs the backward GEMM tiles (128 output columns over F and Fs)
 // and the bf16/fp32 routed experts.
@@ -107,7 +109,7 @@ Layout make_layout(const moe_dims& d, int training) {
   L.xb = take((size_t)d.T * d.d * es);           // the MoE block's normalised input
   L.H = take(slots * d.F * es);
   L.Hs = take((size_t)d.T * d.Fs * es);
-  if (d.w_routed == MOE_INT4_G128 && d.T <= kDecodeMaxT) {
+  if (d.w_routed == MOE_INT4_G128 && int4_decode(d)) {
     L.active = take((size_t)d.E * 3 * 4);
     L.n_active = take(4);
     L.rkey = take(4 * 64 * 8);
@@ -481,7 +483,7 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
                         int n_slots = 0, const Phases* ph = nullptr) {
   if (training) return MOE_E_UNSUPPORTED;
   // expert streaming (slot table): the decode path only
-  if (slot && d.T > kDecodeMaxT) return MOE_E_UNSUPPORTED;
+  if (slot && !int4_decode(d)) return MOE_E_UNSUPPORTED;
   const size_t E = d.E, D = d.d, F = d.F, Fs = d.Fs;
   const size_t EW = slot ? (size_t)n_slots : E;   // expert weight blocks held
   std::vector<Range> rs = {{x, (size_t)d.T * D * 2, false},
@@ -504,7 +506,7 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
   if (!ws || ws_bytes < L.total) return MOE_E_WORKSPACE;
   rs.push_back({ws, L.total, true});
   if (any_alias(rs)) return MOE_E_ALIAS;
-  if (d.T > kDecodeMaxT && int4_prefill_fused(d)) {
+  if (!int4_decode(d) && int4_prefill_fused(d)) {
     // Prefill: route, then the grouped GEMMs read the int4 experts directly
     // (each operand fragment expanded to bf16(q * scale) in registers).
     mark_phase(ph, 0, s);
@@ -512,7 +514,7 @@ moe_status forward_int4(const moe_dims& d, const void* x, const moe_weights* w, 
     mark_phase(ph, 1, s);
     return enqueue_expert_gemms(d, L, x, w, y, routing, 0, ws, s, resid, ph, true);
   }
-  if (d.T > kDecodeMaxT) {
+  if (!int4_decode(d)) {
     // Prefill with contractions too long for a tile's scales in LDS: route,
     // dequantise every expert that received tokens into the workspace (bf16,
     // one rounding of q * scale), then the bf16 expert GEMMs.
@@ -714,7 +716,7 @@ moe_status moe_forward_cached(const moe_dims* dims, const void* x, const moe_wei
   if (st != MOE_OK) return st;
   if (!w || !routing || !slot) return MOE_E_ARG;
   if (n_slots < 1 || n_slots > dims->E) return MOE_E_ARG;
-  if (dims->w_routed != MOE_INT4_G128 || dims->T > kDecodeMaxT) return MOE_E_UNSUPPORTED;
+  if (dims->w_routed != MOE_INT4_G128 || !int4_decode(*dims)) return MOE_E_UNSUPPORTED;
   return forward_int4(*dims, x, w, bias, y, routing, 0, ws, ws_bytes, reinterpret_cast<hipStream_t>(stream),
                       nullptr, false, nullptr, 0.f, nullptr, slot, n_slots);
 }
@@ -740,7 +742,7 @@ moe_status moe_forward_block(const moe_dims* dims, const void* h, const float* n
   // that every stage-1 workgroup would redo the norm of its token tiles (with
   // one tile per workgroup, 1040 of them at T = 64: 39.4 -> 42.9 us), and the
   // norm is a launch of its own.
-  if (d.w_routed == MOE_INT4_G128 && d.T <= 16)
+  if (d.w_routed == MOE_INT4_G128 && d.T <= 16 && int4_decode(d))
     return forward_int4(d, h, w, bias, h_out, routing, 0, ws, ws_bytes, s, h, false, norm_weight, eps);
   void* x = at<char>(ws, L.xb);
   launch_rmsnorm(h, norm_weight, eps, d.T, d.d, x, s);

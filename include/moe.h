@@ -140,12 +140,13 @@ moe_status moe_route(const moe_dims* dims, const void* x, const void* w_router, 
  * bias: [E] float32, read only (moe_bias_update changes it).  routing: filled
  * as by moe_route.  training = 1 stores in ws what moe_backward needs.
  * With w_routed = MOE_INT4_G128 this is the top-1 serving path (k = 1,
- * gate = 1).  Up to 64 tokens the int4 experts are dequantised inside the
- * decode kernels, built for the NanoColibri shape (d = 1024, F = 512,
- * Fs = 2048); above 64 tokens (the prefill) the experts that received tokens
- * are dequantised to bf16 in the workspace (one rounding of q * scale) and
- * run through the grouped GEMMs, for any shape with F % 128 == 0.  Other int4
- * requests return MOE_E_UNSUPPORTED. */
+ * gate = 1; F % 128 == 0, else MOE_E_UNSUPPORTED).  Up to 64 tokens at the
+ * NanoColibri shape (d = 1024, F = 512, Fs = 2048) the int4 experts are
+ * dequantised inside the decode kernels; every other batch (the prefill,
+ * and small batches of other shapes) runs the grouped GEMMs, which expand
+ * each int4 operand fragment to bf16(q * scale) in registers (one rounding
+ * of an exact product; d and F up to 3072, above that the experts that
+ * received tokens are first dequantised to bf16 in the workspace). */
 moe_status moe_forward(const moe_dims* dims, const void* x, const moe_weights* w, const float* bias,
                        void* y, const moe_routing* routing, int training,
                        void* ws, size_t ws_bytes, void* stream);
@@ -188,7 +189,8 @@ moe_status moe_forward_noalloc(const moe_dims* dims, const void* x, const moe_we
 /* Expert streaming (the opening section's proof-of-loop paragraph: a token
  * touches the resident shared expert plus a couple of small routed experts
  * streamed from larger storage).  moe_forward on the int4 top-1 decode path
- * (w_routed = MOE_INT4_G128, T <= 64; else MOE_E_UNSUPPORTED) with the routed
+ * (w_routed = MOE_INT4_G128, T <= 64 at the decode kernels' shape; else
+ * MOE_E_UNSUPPORTED) with the routed
  * weights held in n_slots slots: w->w_gate_up, s_gate_up, w_down, s_down are
  * [n_slots, ...] arrays in the moe_weights int4 layout, and expert e's
  * weights are in slot slot[e].

@@ -183,17 +183,19 @@ def test_int4_requires_top1_bf16(lib):
 
 
 def test_int4_shapes_decode_and_prefill(lib):
-    """Up to 64 tokens the int4 path is the decode kernels (NanoColibri shape
-    only); above, the prefill takes any shape whose F is a multiple of 128.
+    """Up to 64 tokens at the NanoColibri shape the int4 path is the decode
+    kernels; every other batch (above 64 tokens, or another shape) runs the
+    prefill's grouped GEMMs, for any shape whose F is a multiple of 128.
     Its GEMMs read the packed experts directly while a tile's scales fit in
     LDS (d / 128 and F / 128 at most 24): then it needs no more workspace than
     the bf16 layer; beyond that it keeps dequantised copies of the experts."""
     ws = lambda T, d=1024, E=64, F=512, Fs=2048: lib.moe_workspace_bytes(
         lib.make_dims(T, d, E, F, Fs, 1, "bf16", w_routed="int4"))
     assert ws(64) > 0 and ws(65) > 0 and ws(4096) > 0
-    assert ws(64, d=256, E=8, F=128, Fs=256) == 0                  # not the decode shape
-    assert ws(65, d=256, E=8, F=128, Fs=256) > 0
-    assert ws(65, F=192) == 0                                       # groups of 128 along F
+    other = dict(d=256, E=8, F=128, Fs=256)                         # not the decode shape: the prefill path
+    assert ws(64, **other) == lib.moe_workspace_bytes(lib.make_dims(64, 256, 8, 128, 256, 1, "bf16"))
+    assert ws(1, **other) > 0 and ws(65, **other) > 0
+    assert ws(65, F=192) == 0 and ws(8, F=192) == 0                 # groups of 128 along F
     bf16_layer = lib.moe_workspace_bytes(lib.make_dims(4096, 1024, 64, 512, 2048, 1, "bf16"))
     assert ws(4096) == bf16_layer
     long_d = lambda T: lib.moe_workspace_bytes(lib.make_dims(T, 3200, 8, 128, 256, 1, "bf16", w_routed="int4"))

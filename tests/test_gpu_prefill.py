@@ -142,12 +142,25 @@ def test_int4_prefill_run_to_run_bitwise():
     assert torch.equal(outs[0], outs[1])
 
 
-def test_int4_prefill_block():
-    """The MoE block (RMSNorm in, residual out) on the prefill path."""
+@pytest.mark.parametrize("T", [1, 8, 64])
+def test_int4_small_batch_other_shape(T):
+    """Up to 64 tokens at a shape the decode kernels are not built for, the
+    int4 top-1 forward runs the prefill path (route, grouped GEMMs on the
+    packed experts, combine) and matches the oracle."""
+    inp, b, q = _int4_layer(T, seed=400 + T, d=256, E=8, F=128, Fs=256)
+    y, rn = _run(inp, b, q)
+    _check(inp, b, q, y, rn, "small batch, other shape")
+
+
+@pytest.mark.parametrize("T,shape", [(130, {}), (8, dict(d=256, E=8, F=128, Fs=256))])
+def test_int4_prefill_block(T, shape):
+    """The MoE block (RMSNorm in, residual out) on the prefill path: above
+    64 tokens, and at 8 tokens of a shape the decode kernels are not built
+    for (the norm then runs as its own launch)."""
     import torch
     from fine_grained_moe_amd import moe
-    T, d = 130, 1024
-    inp, b, q = _int4_layer(1, seed=17)
+    inp, b, q = _int4_layer(1, seed=17, **shape)
+    d, E = inp.d, inp.E
     rng = np.random.default_rng(17)
     gamma = (1.0 + 0.1 * rng.standard_normal(d)).astype(np.float32)
     h = synth.round_to_bf16((rng.standard_normal((T, d)) * rng.uniform(0.5, 4.0, (T, 1))).astype(np.float32))
@@ -158,7 +171,7 @@ def test_int4_prefill_block():
         if bad.size == 0:
             break
         h[bad] = synth.round_to_bf16(rng.standard_normal((bad.size, d)).astype(np.float32))
-    dims = moe.make_dims(T, d, 64, 512, 2048, 1, "bf16", w_routed="int4")
+    dims = moe.make_dims(T, d, E, inp.F, inp.Fs, 1, "bf16", w_routed="int4")
     ht = _bf(h)
     out = torch.empty_like(ht)
     r = moe.alloc_routing(dims)
@@ -168,7 +181,7 @@ def test_int4_prefill_block():
     qg, sg, qd, sd = q
     h_ref, _, ref = om.block_forward(h, gamma, inp.w_router, om.dequantize_int4(qg, sg), om.dequantize_int4(qd, sd),
                                      inp.w_sh_gate_up, inp.w_sh_down, b, 1)
-    H.check_routing_exact({k: v.cpu().numpy() for k, v in r.items()}, ref, 64)
+    H.check_routing_exact({k: v.cpu().numpy() for k, v in r.items()}, ref, E)
     h_out = out.float().cpu().numpy().astype(np.float64)
     y_ref = h_ref - h.astype(np.float64)
     err = float(np.linalg.norm(h_out - h_ref))
