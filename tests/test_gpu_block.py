@@ -92,7 +92,7 @@ def test_block_bf16(T):
     _check(h, h_out, h_ref, f"bf16 block T={T}")
 
 
-@pytest.mark.parametrize("T", [1, 8, 64])
+@pytest.mark.parametrize("T", [1, 8, 16, 17, 40, 64])
 def test_block_int4_top1(T):
     from fine_grained_moe_amd import moe
     base = synth.make_layer(T=1, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=7)
@@ -137,3 +137,25 @@ def test_block_stack_of_three_layers():
         _check(h_gpu[ok], out[ok], ref[ok], f"stack layer {i} ({int((~ok).sum())} near-tie rows left out)")
         h_gpu = out.astype(np.float32)
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("T", [17, 40, 64])
+def test_block_int4_rows_do_not_depend_on_the_batch(T):
+    """The int4 serving block normalises h in its first launch up to 16 tokens
+    and in a norm launch of its own above: both give each row the same bits,
+    so the first 16 rows of a T-token block equal the 16-token block's."""
+    import torch
+    base = synth.make_layer(T=1, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=7)
+    qg, sg = om.quantize_int4(base.w_gate_up)
+    qd, sd = om.quantize_int4(base.w_down)
+    w = dict(w_router=_bf(base.w_router), w_gate_up=torch.from_numpy(qg).cuda(), s_gate_up=_bf(sg),
+             w_down=torch.from_numpy(qd).cuda(), s_down=_bf(sd), w_sh_gate_up=_bf(base.w_sh_gate_up),
+             w_sh_down=_bf(base.w_sh_down))
+    from fine_grained_moe_amd import moe
+    h, gamma = _residual_stream(T, 1024, base.w_router, 1, seed=300 + T)
+    bias = np.zeros(64, np.float32)
+    outs = {}
+    for n in (T, 16):
+        dims = moe.make_dims(n, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+        outs[n], _ = _run_block(dims, h[:n], gamma, w, bias)
+    np.testing.assert_array_equal(outs[T][:16], outs[16])

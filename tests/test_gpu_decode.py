@@ -161,3 +161,30 @@ def test_next_layer_hint_changes_no_bits(weights, T):
             assert torch.equal(o[1][k], outs[0][1][k]), k
         assert torch.equal(o[2], outs[0][2])
         assert torch.equal(o[3], outs[0][3])
+
+
+@pytest.mark.parametrize("T", [17, 33, 64])
+def test_decode_rows_do_not_depend_on_the_batch(weights, T):
+    """Each token's output is computed from its own row only, in an order that
+    does not depend on the batch: at 17 .. 64 tokens (several token tiles,
+    the multi-tile stage-1 kernel) the first 16 outputs are the same bits as
+    those of the 16-token batch (one tile) of the same rows."""
+    import torch
+    from fine_grained_moe_amd import moe
+    dev, host = weights
+    inp = synth.make_layer(T=T, d=1024, E=64, F=512, Fs=2048, k=1, act="bf16", seed=900 + T)
+    x = torch.from_numpy(inp.x).to(device="cuda", dtype=torch.bfloat16)
+    bt = torch.zeros(64, device="cuda")
+
+    def fwd(n):
+        dims = moe.make_dims(n, 1024, 64, 512, 2048, 1, "bf16", w_routed="int4")
+        y = torch.empty_like(x[:n])
+        r = moe.alloc_routing(dims)
+        moe.moe_forward(dims, x[:n].contiguous(), dev, bt, y, r, moe.alloc_workspace(dims))
+        torch.cuda.synchronize()
+        return y, r["idx"].clone()
+
+    y_all, idx_all = fwd(T)
+    y_16, idx_16 = fwd(16)
+    assert torch.equal(idx_all[:16], idx_16)
+    assert torch.equal(y_all[:16], y_16)
